@@ -1,0 +1,176 @@
+"""Seeded synthetic inputs for the RWKV-7 WKV recurrence.
+
+This module is shared by the GPU path's callers (tests, bench) and by the
+tests that feed the fp64 oracle.  It holds only input synthesis: random draws,
+the decay parameterisation that produces the kernel's w input, the
+L2-normalised removal key, and bf16 encoding.  It contains none of the
+recurrence's arithmetic.
+
+Distributions (stated per workload below) follow the hxa07D time-mix
+(zenn.dev "RWKV hxa07D architecture explained", forward listing and
+sections 3, 6 and 8): the decay is w = exp(-exp(-softplus(-z) - 0.5)), the
+kernel receives a = -kk and b = kk * alpha with kk the per-head L2-normalised
+key, and grouped KV heads are repeated contiguously.
+
+Layouts (all C-contiguous):
+  r, w, a, b : [B, T, H, D]
+  k, v       : [B, T, H_kv, D]
+  state      : [B, H, D, D] fp32, state[b, h, i, j] = S_ij (i value row, j key column)
+  r_k        : [H, D] fp32
+Decode workloads carry a leading step axis: r..b are [steps, B, 1, H, D].
+
+bf16 tensors are returned as uint16 bit patterns (round-to-nearest-even from
+fp32, which itself is round-to-nearest from the fp64 value).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Dict, Optional
+
+import numpy as np
+
+__all__ = [
+    "Workload", "WORKLOADS", "make_inputs", "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "workload",
+]
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    rounded = u + np.uint32(0x7FFF) + lsb
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: shapes, dtypes, decay mode and the seed."""
+    name: str
+    kind: str                 # "forward" or "decode"
+    B: int
+    T: int
+    H: int
+    D: int
+    H_kv: int
+    in_dtype: str             # "f32" or "bf16" for r, w, k, v, a, b
+    y_dtype: str              # "f32" or "bf16"
+    w_mode: str               # "decay": w given; "logneglog": kernel input x, decay = exp(-exp(x))
+    s0_std: float             # 0 -> zero initial state (passed as None)
+    seed: int
+    steps: int = 1            # decode steps (decode workloads only)
+    chunk_len: int = 64
+    y_scale: float = 1.0
+    rk_std: float = 0.0       # > 0 -> per-head/dim bonus weights r_k ~ N(0, rk_std^2)
+    kk_from_k: bool = False   # removal key = normalise(repeated k) instead of an independent draw
+    algo: str = "auto"
+    note: str = ""
+
+    @property
+    def head_tokens(self) -> int:
+        return self.B * self.T * self.H * self.steps
+
+
+# The five workloads.  Seeds are 1000 + the workload's position in this list.
+WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
+    Workload("fwd_f32_b1_t64_h2_d64", "forward", B=1, T=64, H=2, D=64, H_kv=2,
+             in_dtype="f32", y_dtype="f32", w_mode="decay", s0_std=0.0, seed=1001,
+             note="small fp32 forward, zero initial state"),
+    Workload("fwd_bf16_b8_t1024_h32_d64", "forward", B=8, T=1024, H=32, D=64, H_kv=32,
+             in_dtype="bf16", y_dtype="bf16", w_mode="decay", s0_std=0.0, seed=1002,
+             note="bf16 forward, C=2048, zero initial state"),
+    Workload("prefill_bf16_b4_t4096_h40_d64_l64", "forward", B=4, T=4096, H=40, D=64, H_kv=40,
+             in_dtype="bf16", y_dtype="bf16", w_mode="decay", s0_std=0.1, seed=1003,
+             chunk_len=64, algo="chunked",
+             note="2.9B-shaped layer (C=2560), chunked prefill, random initial state"),
+    Workload("decode_bf16_b256_h64_d64_x32", "decode", B=256, T=1, H=64, D=64, H_kv=64,
+             in_dtype="bf16", y_dtype="bf16", w_mode="decay", s0_std=0.1, seed=1004, steps=32,
+             note="256 sequences x 32 successive decode steps, 256 MiB fp32 state"),
+    Workload("hxa07d_bf16_b2_t16384_h32_kv8_d128", "forward", B=2, T=16384, H=32, D=128, H_kv=8,
+             in_dtype="bf16", y_dtype="bf16", w_mode="logneglog", s0_std=0.0, seed=1005,
+             y_scale=128.0 ** -0.5, rk_std=0.1, kk_from_k=True,
+             note="hxa07D-style long context: GQA 8 KV heads x4, log-decay input, fused epilogue"),
+]}
+
+
+def workload(name: str, **overrides) -> Workload:
+    """Look up a workload by name, optionally overriding fields (e.g. smaller T)."""
+    return replace(WORKLOADS[name], **overrides)
+
+
+def _softplus(x: np.ndarray) -> np.ndarray:
+    return np.logaddexp(0.0, x)
+
+
+def _l2_normalize(x: np.ndarray, eps: float = 1e-12) -> np.ndarray:
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, eps)
+
+
+def _encode(x64: np.ndarray, dtype: str) -> np.ndarray:
+    x32 = np.ascontiguousarray(x64, dtype=np.float32)
+    if dtype == "f32":
+        return x32
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x32)
+    raise ValueError(dtype)
+
+
+def make_inputs(wl: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Draw the workload's inputs.
+
+    Draw order from one PCG64 stream (float64 normals, C order): r, k, v, z,
+    kappa_raw (skipped when kk_from_k), alpha_raw, state0 (when s0_std > 0),
+    r_k (when rk_std > 0).
+
+    Returns a dict with keys r, w, k, v, a, b (encoded per in_dtype), state0
+    (fp32 or None), r_k (fp32 or None).  For decode workloads each per-token
+    tensor has a leading [steps] axis.
+    """
+    rng = np.random.Generator(np.random.PCG64(wl.seed if seed is None else seed))
+    lead = (wl.steps,) if wl.kind == "decode" else ()
+    shp_q = lead + (wl.B, wl.T, wl.H, wl.D)
+    shp_kv = lead + (wl.B, wl.T, wl.H_kv, wl.D)
+    rep = wl.H // wl.H_kv
+    out: Dict[str, Optional[np.ndarray]] = {}
+
+    out["r"] = _encode(rng.standard_normal(shp_q), wl.in_dtype)
+    k64 = rng.standard_normal(shp_kv)
+    out["k"] = _encode(k64, wl.in_dtype)
+    out["v"] = _encode(rng.standard_normal(shp_kv), wl.in_dtype)
+
+    z = rng.standard_normal(shp_q) * 2.0
+    if wl.w_mode == "decay":
+        w = np.exp(-np.exp(-_softplus(-z) - 0.5))
+    elif wl.w_mode == "logneglog":
+        w = -_softplus(z) - 0.5          # log(-log(decay)); decay = exp(-exp(w))
+    else:
+        raise ValueError(wl.w_mode)
+    del z
+    out["w"] = _encode(w, wl.in_dtype)
+    del w
+
+    if wl.kk_from_k:
+        kk = _l2_normalize(np.repeat(k64, rep, axis=-2))
+    else:
+        kk = _l2_normalize(rng.standard_normal(shp_q))
+    del k64
+    alpha = 1.0 / (1.0 + np.exp(-rng.standard_normal(shp_q)))
+    out["a"] = _encode(-kk, wl.in_dtype)
+    out["b"] = _encode(kk * alpha, wl.in_dtype)
+    del kk, alpha
+
+    if wl.s0_std > 0:
+        out["state0"] = (rng.standard_normal((wl.B, wl.H, wl.D, wl.D)) * wl.s0_std).astype(np.float32)
+    else:
+        out["state0"] = None
+    if wl.rk_std > 0:
+        out["r_k"] = (rng.standard_normal((wl.H, wl.D)) * wl.rk_std).astype(np.float32)
+    else:
+        out["r_k"] = None
+    return out

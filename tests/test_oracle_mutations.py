@@ -1,0 +1,80 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Every mutation replaces one piece of oracle/wkv7_oracle.py (on the CPU, via
+monkeypatch) with a plausible slip; the test passes only if some pin in
+tests/oracle_pins.py then raises.
+"""
+import numpy as np
+import pytest
+
+from oracle import wkv7_oracle as O
+from tests import oracle_pins as P
+
+
+def _mm(S, x):
+    return np.matmul(S, x[..., :, None])[..., 0]
+
+
+def _tr(S):
+    return np.swapaxes(S, -1, -2)
+
+
+MUTATIONS = {
+    # removal projection
+    "removal_transposed": ("_removal", lambda S, a: _mm(_tr(S), a)),
+    "removal_dropped": ("_removal", lambda S, a: np.zeros(S.shape[:-1])),
+    # state transition
+    "b_term_dropped": ("_transition", lambda S, w, sa, b, v, k: S * w[..., None, :] + v[..., :, None] * k[..., None, :]),
+    "b_term_sign": ("_transition", lambda S, w, sa, b, v, k:
+                    S * w[..., None, :] - sa[..., :, None] * b[..., None, :] + v[..., :, None] * k[..., None, :]),
+    "b_term_outer_swapped": ("_transition", lambda S, w, sa, b, v, k:
+                             S * w[..., None, :] + b[..., :, None] * sa[..., None, :] + v[..., :, None] * k[..., None, :]),
+    "decay_on_rows": ("_transition", lambda S, w, sa, b, v, k:
+                      S * w[..., :, None] + sa[..., :, None] * b[..., None, :] + v[..., :, None] * k[..., None, :]),
+    "kv_outer_swapped": ("_transition", lambda S, w, sa, b, v, k:
+                         S * w[..., None, :] + sa[..., :, None] * b[..., None, :] + k[..., :, None] * v[..., None, :]),
+    "decay_dropped": ("_transition", lambda S, w, sa, b, v, k:
+                      S + sa[..., :, None] * b[..., None, :] + v[..., :, None] * k[..., None, :]),
+    "decay_after_add": ("_transition", lambda S, w, sa, b, v, k:
+                        (S + sa[..., :, None] * b[..., None, :] + v[..., :, None] * k[..., None, :]) * w[..., None, :]),
+    # readout
+    "readout_transposed": ("_readout", lambda S, r: _mm(_tr(S), r)),
+    "readout_before_update": ("_step", lambda S, r, w, k, v, a, b:
+                              (O._transition(S, w, O._removal(S, a), b, v, k), O._readout(S, r))),
+    # epilogue
+    "epilogue_scale_dropped": ("_epilogue", lambda y, r, k, v, rk, ys:
+                               y + (np.sum(r * k * rk, axis=-1)[..., None] * v if rk is not None else 0.0)),
+    "epilogue_bonus_on_r": ("_epilogue", lambda y, r, k, v, rk, ys:
+                            y * ys + (np.sum(r * k * rk, axis=-1)[..., None] * r if rk is not None else 0.0)),
+    "epilogue_rk_dropped": ("_epilogue", lambda y, r, k, v, rk, ys:
+                            y * ys + (np.sum(r * k, axis=-1)[..., None] * v if rk is not None else 0.0)),
+    # log-decay conversion
+    "logneglog_sign": ("decay_from_logneglog", lambda x: np.exp(-np.exp(-x))),
+    "logneglog_single_exp": ("decay_from_logneglog", lambda x: np.exp(x)),
+    # grouped KV heads
+    "gqa_interleaved": ("_expand_kv", lambda x, H: np.tile(x, (1,) * (x.ndim - 2) + (H // x.shape[-2], 1))),
+}
+
+
+def _any_pin_fails():
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed.append(pin.__name__)
+        except (ValueError, IndexError, np.linalg.LinAlgError):
+            failed.append(pin.__name__ + " (error)")
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failed = _any_pin_fails()
+    assert failed, f"planted mistake {name!r} passed every pin"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert _any_pin_fails() == []
