@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark: one step = one wkv7_forward over the whole synthetic batch.
+
+Default workload: bf16 forward, B=8, T=1024, H=32, D=64 (C=2048), zero
+initial state, bf16 y and fp32 final state.  Inputs are resident in HBM before
+the timed region; K steps are bracketed by a device synchronisation on both
+sides and timed with HIP events on the stream the kernels are launched on.
+
+Prints one JSON line with the throughput (head-tokens/s), the roofline of the
+dominant kernel and the fp64 CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--algo auto|scan|chunked]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "wkv7 head-tokens/sec + % of binding VALU/HBM roofline, 1×MI355X"
+PEAK_FP32_VALU_TFLOPS = 157.3     # MI355X fp32 vector peak (AMD spec)
+PEAK_HBM_GBS = 8000.0             # MI355X HBM3E peak (AMD spec)
+PEAK_BF16_MFMA_TFLOPS = 2500.0    # dense bf16 matrix peak
+
+KERNEL_SOURCES = {
+    "scan": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_scan.hip",
+    "chunked": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_chunked.hip",
+    "decode": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_decode.hip",
+}
+
+
+def source_sha(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in (KERNEL_SOURCES[kind], "linear_rnn_sequence_wkv7_amd/csrc/wkv7_device.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl) -> int:
+    """Bytes the operation must move per launch: inputs read once (k, v once
+    per KV head), y written once, the state read (if given) and written once."""
+    sin = 2 if wl.in_dtype == "bf16" else 4
+    sy = 2 if wl.y_dtype == "bf16" else 4
+    ht = wl.B * wl.T * wl.H
+    per_tok = wl.H * wl.D * (4 * sin + sy) + wl.H_kv * wl.D * 2 * sin
+    state = wl.B * wl.H * wl.D * wl.D * 4 * (2 if wl.s0_std > 0 else 1)
+    rk = wl.H * wl.D * 4 if wl.rk_std > 0 else 0
+    return wl.B * wl.T * per_tok + state + rk if ht else 0
+
+
+def algorithmic_flops(wl) -> int:
+    """9 D^2 per head-token: S a (2 D^2), the update (5 D^2), S r (2 D^2)."""
+    return 9 * wl.D * wl.D * wl.B * wl.T * wl.H
+
+
+def traffic_from_profile(kind: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None
+    when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kind}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != source_sha(kind):
+        return None
+    return int(rec["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(wl, x, n_pairs: int):
+    """The fp64 oracle, as it stands, on n_pairs whole sequences of the workload."""
+    from oracle import wkv7_oracle  # noqa: F401  (CPU baseline leg only)
+    from tests import parity as P
+    pairs = P.sample_pairs(wl, n_pairs, seed=wl.seed)
+    t0 = time.perf_counter()
+    P.oracle_pairs(x, wl, pairs)
+    dt = time.perf_counter() - t0
+    return {"value": len(pairs) * wl.T / dt, "unit": "head-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(pairs)} of {wl.B * wl.H} (batch, head) sequences x all {wl.T} tokens, "
+                      f"fp64 numpy, single thread, {dt:.1f} s"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fwd_bf16_b8_t1024_h32_d64")
+    ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunked"])
+    ap.add_argument("--cpu-pairs", type=int, default=128, help="sequences in the CPU-oracle sample (0: skip)")
+    a = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE {world}); "
+              "every (batch, head) pair is independent, so a multi-GPU run would shard the batch, "
+              "which this build does not do.", file=sys.stderr)
+        return 2
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    from linear_rnn_sequence_wkv7_amd import inputs as G
+    from linear_rnn_sequence_wkv7_amd import wkv7
+
+    wl = G.WORKLOADS[a.workload]
+    torch.cuda.set_device(0)
+    x = G.make_inputs(wl)
+
+    def dev(arr):
+        if arr is None:
+            return None
+        if arr.dtype == np.uint16:
+            return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(arr).cuda()
+
+    d = {k: dev(v) for k, v in x.items()}
+    stream = torch.cuda.current_stream()
+
+    if wl.kind == "decode":
+        kind = "decode"
+        sa = d["state0"]
+        sb = torch.empty_like(sa)
+        y = torch.empty((wl.B, 1, wl.H, wl.D), dtype=torch.bfloat16, device="cuda")
+        bufs = [sa, sb]
+        n_steps_avail = wl.steps
+
+        def one_step(i):
+            s_in, s_out = bufs[i % 2], bufs[(i + 1) % 2]
+            j = i % n_steps_avail
+            wkv7.wkv7_decode_step(*(d[k][j] for k in ("r", "w", "k", "v", "a", "b")), s_in,
+                                  w_mode=wl.w_mode, y_scale=wl.y_scale, r_k=d["r_k"], y=y, state_out=s_out)
+        head_tokens_per_step = wl.B * wl.H
+        nbytes = wl.B * wl.H * (2 * wl.D * wl.D * 4) + wl.B * wl.D * (wl.H * 5 + wl.H_kv * 2) * 2
+        flops = 9 * wl.D * wl.D * wl.B * wl.H
+    else:
+        kind = wkv7.wkv7_resolve_algo(wl.B, wl.T, wl.H, wl.D, H_kv=wl.H_kv, algo=a.algo if a.algo != "auto" else wl.algo,
+                                      in_dtype=wl.in_dtype, y_dtype=wl.y_dtype, w_mode=wl.w_mode)
+        algo = kind
+        y = torch.empty((wl.B, wl.T, wl.H, wl.D), dtype=torch.bfloat16 if wl.y_dtype == "bf16" else torch.float32,
+                        device="cuda")
+        s_out = torch.empty((wl.B, wl.H, wl.D, wl.D), dtype=torch.float32, device="cuda")
+
+        def one_step(i):
+            wkv7.wkv7_forward(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state0"], w_mode=wl.w_mode,
+                              y_dtype=wl.y_dtype, algo=algo, chunk_len=wl.chunk_len, y_scale=wl.y_scale,
+                              r_k=d["r_k"], y=y, state_out=s_out)
+        head_tokens_per_step = wl.B * wl.T * wl.H
+        nbytes = algorithmic_bytes(wl)
+        flops = algorithmic_flops(wl)
+
+    for i in range(a.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for i in range(a.steps):
+        one_step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1) / a.steps      # one launch per step: the kernel's average duration
+
+    value = head_tokens_per_step / (ms / 1e3)
+    if kind == "scan":
+        achieved = flops / (ms / 1e3) / 1e12
+        roof = {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_FP32_VALU_TFLOPS}
+        dtype = "f32"
+    else:
+        achieved = nbytes / (ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+        dtype = "f32" if kind == "decode" else "bf16"
+    roof["traffic"] = traffic_from_profile(kind, wl.name)
+    roof["kernel"] = kind
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = flops
+    roof["valu_frac"] = flops / (ms / 1e3) / 1e12 / PEAK_FP32_VALU_TFLOPS
+    roof["hbm_frac"] = nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "head-tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "H_kv": wl.H_kv, "D": wl.D,
+                   "io_dtype": wl.in_dtype, "y_dtype": wl.y_dtype, "kernel": kind},
+        "roofline": roof,
+        "wall_s_timed_region": t_wall,
+    }
+    if a.cpu_pairs > 0 and wl.kind == "forward":
+        out["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_pairs)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

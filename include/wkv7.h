@@ -1,0 +1,134 @@
+/*
+ * wkv7.h -- C ABI of libwkv7.so: the RWKV-7 "Goose" WKV recurrence on AMD
+ * MI355X (gfx950).
+ *
+ * The operation (per batch b, head h; state S is D x D fp32, rows i index the
+ * value, columns j the key):
+ *
+ *     S_t = S_{t-1} (diag(w_t) + a_t b_t^T) + v_t k_t^T        (update)
+ *     y_t = y_scale * (S_t r_t) + [r_k] (sum_j r_tj k_tj r_k[h,j]) v_t
+ *
+ * The update is the full state update of the generalised delta rule (wiki
+ * note "RWKV-7 Goose: Expressive Dynamic State Evolution", section
+ * "generalised delta rule"), with the kernel vectors a = -kappa_hat and
+ * b = kappa_hat * alpha of the hxa07D article (zenn.dev "RWKV hxa07D
+ * architecture explained", section 8: the kernel is called with -kk and
+ * kk*a).  The readout uses the state after the update (youngju.dev RWKV-7
+ * article, time-mix pseudocode).  y_scale and r_k are the hxa07D output
+ * epilogue (same article, section 9); the log-decay input mode is its
+ * section 3 and grouped KV heads its section 6.
+ *
+ * Layouts (row-major, contiguous, element strides implied by the sizes):
+ *     r, w, a, b, y : [B, T, H, D]
+ *     k, v          : [B, T, H_kv, D]      head h reads KV head h / (H / H_kv)
+ *     state         : [B, H, D, D] fp32,  state[b][h][i][j] = S_ij
+ *     r_k           : [H, D] fp32
+ * Element types: r, w, k, v, a, b all have desc->in_dtype (fp32 or bf16);
+ * y has desc->y_dtype; the state is always fp32.
+ *
+ * Ownership and memory: every pointer is DEVICE memory on the current HIP
+ * device, owned by the caller.  The library never allocates, frees or keeps
+ * a pointer after the call returns.  All data pointers must be 16-byte
+ * aligned.  state_in == state_out (in place) is allowed; y must not overlap
+ * any input.
+ *
+ * Streams: work is enqueued on `stream` (a hipStream_t; NULL = the legacy
+ * default stream) and the call returns without synchronising.  A fault in a
+ * kernel surfaces at the caller's next synchronisation.  The library keeps no
+ * mutable global state apart from a per-device architecture check done once,
+ * so calls from several host threads are safe.
+ *
+ * Errors: functions return WKV7_OK (0) or a positive WKV7_E* code.  All
+ * argument checks run before any HIP call, so a rejected call touches no
+ * device.  wkv7_strerror() names a code; wkv7_last_error() gives a detail
+ * message for the calling thread's most recent failure.
+ */
+#ifndef WKV7_H
+#define WKV7_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WKV7_ABI_VERSION 1
+
+enum wkv7_status {
+    WKV7_OK = 0,
+    WKV7_EINVAL = 1,        /* null/misaligned pointer, negative size, H % H_kv != 0, bad enum */
+    WKV7_EUNSUPPORTED = 2,  /* D not 64/128, unsupported mode/algorithm combination */
+    WKV7_EDEVICE = 3,       /* current device is not gfx950, or a HIP device query failed */
+    WKV7_ELAUNCH = 4        /* a kernel launch reported an error */
+};
+
+enum wkv7_dtype { WKV7_F32 = 0, WKV7_BF16 = 1 };
+
+/* How the w input is read. */
+enum wkv7_w_mode {
+    WKV7_W_DECAY = 0,       /* w is the decay itself, in (0, 1] */
+    WKV7_W_LOGNEGLOG = 1    /* w holds log(-log(decay)); decay = exp(-exp(w)) */
+};
+
+enum wkv7_algo {
+    WKV7_ALGO_AUTO = 0,     /* library picks (see wkv7_resolve_algo) */
+    WKV7_ALGO_SCAN = 1,     /* token-by-token scan, state in registers */
+    WKV7_ALGO_CHUNKED = 2   /* chunk-parallel form on bf16 matrix cores, fp32 accumulation */
+};
+
+typedef struct wkv7_desc {
+    int32_t B;          /* batch (sequences), >= 0 */
+    int32_t T;          /* tokens per sequence, >= 0 (decode_step requires 1) */
+    int32_t H;          /* heads, >= 0 */
+    int32_t H_kv;       /* KV heads; H % H_kv == 0 (0 means H_kv = H) */
+    int32_t D;          /* head size: 64 or 128 */
+    int32_t in_dtype;   /* wkv7_dtype of r, w, k, v, a, b */
+    int32_t y_dtype;    /* wkv7_dtype of y */
+    int32_t w_mode;     /* wkv7_w_mode */
+    int32_t algo;       /* wkv7_algo (forward only; decode_step ignores it) */
+    int32_t chunk_len;  /* chunk length for ALGO_CHUNKED: 64 (0 means 64) */
+    float   y_scale;    /* multiplies S_t r_t; 1.0f for the plain readout */
+    int32_t reserved;   /* must be 0 */
+    const float* r_k;   /* [H, D] fp32 device pointer, or NULL for no bonus term */
+} wkv7_desc;
+
+/* Forward over T tokens for every (b, h).
+ *   state_in  : initial state, or NULL for zeros.
+ *   y         : output [B, T, H, D] of y_dtype (may be NULL only when B*T*H == 0).
+ *   state_out : final state, or NULL to skip writing it.
+ * T == 0 copies state_in (or zeros) to state_out and writes no y. */
+int wkv7_forward(const wkv7_desc* desc,
+                 const void* r, const void* w, const void* k, const void* v,
+                 const void* a, const void* b,
+                 const float* state_in, void* y, float* state_out,
+                 void* stream);
+
+/* One decode token per sequence (desc->T must be 1): the same operation as
+ * wkv7_forward with T = 1, run by a kernel that streams the B*H states
+ * through HBM once (read state_in, write state_out).  state_in may be NULL
+ * (zeros); state_out must not be NULL. */
+int wkv7_decode_step(const wkv7_desc* desc,
+                     const void* r, const void* w, const void* k, const void* v,
+                     const void* a, const void* b,
+                     const float* state_in, void* y, float* state_out,
+                     void* stream);
+
+/* Which algorithm wkv7_forward would run for this descriptor (WKV7_ALGO_SCAN or
+ * WKV7_ALGO_CHUNKED), or a negative wkv7_status if the descriptor is invalid.
+ * Host only: no HIP call. */
+int wkv7_resolve_algo(const wkv7_desc* desc);
+
+/* Static name of a status code. */
+const char* wkv7_strerror(int code);
+
+/* Detail message of the calling thread's most recent failed call ("" if none). */
+const char* wkv7_last_error(void);
+
+/* WKV7_ABI_VERSION of the built library. */
+int wkv7_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WKV7_H */

@@ -1,0 +1,83 @@
+"""Build libwkv7.so for gfx950 with hipcc (in-tree).
+
+    python -m linear_rnn_sequence_wkv7_amd.build          # compile every source, link
+    python -m linear_rnn_sequence_wkv7_amd.build --asm    # also write gfx950 assembly to _build/
+
+Objects go to _build/ at the repository root; the library is written next to
+this file.  Every call recompiles.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libwkv7.so")
+ARCH = "gfx950"
+
+SOURCES = ["wkv7_api.cpp", "wkv7_scan.hip", "wkv7_decode.hip", "wkv7_chunked.hip"]
+
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    # Packed fp32 VALU ops are kept out of the generated code.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}")
+    return r.stdout
+
+
+def build(asm: bool = False, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    jobs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        jobs.append([cc, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        if asm and src.endswith(".hip"):
+            jobs.append([cc, *COMMON, "-x", "hip", "--cuda-device-only", "-S",
+                         os.path.join(CSRC, src), "-o",
+                         os.path.join(BUILD, os.path.splitext(src)[0] + f"-{ARCH}.s")])
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        for out in ex.map(_run, jobs):
+            if verbose and out.strip():
+                print(out)
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--asm", action="store_true")
+    ap.add_argument("-v", "--verbose", action="store_true")
+    a = ap.parse_args(argv)
+    print(build(asm=a.asm, verbose=a.verbose))
+
+
+if __name__ == "__main__":
+    sys.exit(main())

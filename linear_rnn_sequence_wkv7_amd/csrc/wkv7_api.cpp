@@ -1,0 +1,187 @@
+// C-ABI entry points of libwkv7.so: argument validation (before any HIP
+// call), a once-per-device architecture check, algorithm choice and dispatch
+// to the kernel launchers.  See include/wkv7.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "wkv7_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// 0 = unchecked, 1 = gfx950, 2 = other architecture.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return fail(WKV7_EDEVICE, "hipGetDevice failed");
+    if (dev >= kMaxDevices) return fail(WKV7_EDEVICE, "device index %d out of range", dev);
+    int st = g_arch_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return fail(WKV7_EDEVICE, "hipGetDeviceProperties failed on device %d", dev);
+        st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch_state[dev].store(st, std::memory_order_release);
+        if (st == 2)
+            return fail(WKV7_EDEVICE, "device %d is %s; this library is built for gfx950 only",
+                        dev, prop.gcnArchName);
+    }
+    if (st != 1) return fail(WKV7_EDEVICE, "device %d is not gfx950", dev);
+    return WKV7_OK;
+}
+
+// Validate the descriptor and fill the size/mode fields of Params.
+int check_desc(const wkv7_desc* d, wkv7::Params* p) {
+    if (!d) return fail(WKV7_EINVAL, "desc is NULL");
+    if (d->reserved != 0) return fail(WKV7_EINVAL, "desc->reserved must be 0");
+    if (d->B < 0 || d->T < 0 || d->H < 0 || d->H_kv < 0)
+        return fail(WKV7_EINVAL, "negative size (B=%d T=%d H=%d H_kv=%d)", d->B, d->T, d->H, d->H_kv);
+    if (d->D <= 0) return fail(WKV7_EINVAL, "D must be positive (got %d)", d->D);
+    if (d->D != 64 && d->D != 128) return fail(WKV7_EUNSUPPORTED, "D=%d; supported head sizes are 64 and 128", d->D);
+    int H_kv = d->H_kv == 0 ? d->H : d->H_kv;
+    if (d->H > 0 && (H_kv > d->H || d->H % H_kv != 0))
+        return fail(WKV7_EINVAL, "H=%d is not a multiple of H_kv=%d", d->H, H_kv);
+    if (d->in_dtype != WKV7_F32 && d->in_dtype != WKV7_BF16)
+        return fail(WKV7_EINVAL, "in_dtype %d unknown", d->in_dtype);
+    if (d->y_dtype != WKV7_F32 && d->y_dtype != WKV7_BF16)
+        return fail(WKV7_EINVAL, "y_dtype %d unknown", d->y_dtype);
+    if (d->w_mode != WKV7_W_DECAY && d->w_mode != WKV7_W_LOGNEGLOG)
+        return fail(WKV7_EINVAL, "w_mode %d unknown", d->w_mode);
+    if (d->algo < WKV7_ALGO_AUTO || d->algo > WKV7_ALGO_CHUNKED)
+        return fail(WKV7_EINVAL, "algo %d unknown", d->algo);
+    int L = d->chunk_len == 0 ? 64 : d->chunk_len;
+    if (L != 64) return fail(WKV7_EUNSUPPORTED, "chunk_len=%d; supported: 64", d->chunk_len);
+    if (!std::isfinite(d->y_scale)) return fail(WKV7_EINVAL, "y_scale is not finite");
+    if (d->r_k && !aligned16(d->r_k)) return fail(WKV7_EINVAL, "r_k is not 16-byte aligned");
+    // Grid and index limits: (b, h) pairs index a 1-D grid; element offsets are 64-bit.
+    int64_t bh = int64_t(d->B) * d->H;
+    if (bh > (int64_t(1) << 30)) return fail(WKV7_EUNSUPPORTED, "B*H=%lld too large", (long long)bh);
+    int64_t elems = bh * d->T * d->D;
+    if (elems > (int64_t(1) << 46)) return fail(WKV7_EUNSUPPORTED, "B*T*H*D too large");
+    p->B = d->B; p->T = d->T; p->H = d->H; p->H_kv = H_kv; p->D = d->D;
+    p->in_dtype = d->in_dtype; p->y_dtype = d->y_dtype; p->w_mode = d->w_mode;
+    p->chunk_len = L; p->y_scale = d->y_scale; p->r_k = d->r_k;
+    return WKV7_OK;
+}
+
+int check_ptrs(const wkv7::Params& p, const void* const* in6, const void* y,
+               const float* s0, const float* s1) {
+    static const char* names[6] = {"r", "w", "k", "v", "a", "b"};
+    bool has_tokens = int64_t(p.B) * p.T * p.H > 0;
+    if (has_tokens) {
+        for (int i = 0; i < 6; ++i) {
+            if (!in6[i]) return fail(WKV7_EINVAL, "%s is NULL", names[i]);
+            if (!aligned16(in6[i])) return fail(WKV7_EINVAL, "%s is not 16-byte aligned", names[i]);
+        }
+        if (!y) return fail(WKV7_EINVAL, "y is NULL");
+        if (!aligned16(y)) return fail(WKV7_EINVAL, "y is not 16-byte aligned");
+        for (int i = 0; i < 6; ++i)
+            if (in6[i] == y) return fail(WKV7_EINVAL, "y aliases input %s", names[i]);
+    }
+    if (s0 && !aligned16(s0)) return fail(WKV7_EINVAL, "state_in is not 16-byte aligned");
+    if (s1 && !aligned16(s1)) return fail(WKV7_EINVAL, "state_out is not 16-byte aligned");
+    return WKV7_OK;
+}
+
+int resolve_algo(const wkv7::Params& p, int requested) {
+    if (requested == WKV7_ALGO_SCAN) return WKV7_ALGO_SCAN;
+    if (requested == WKV7_ALGO_CHUNKED) return WKV7_ALGO_CHUNKED;
+    return WKV7_ALGO_SCAN;
+}
+
+int finish_launch(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(WKV7_ELAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(WKV7_ELAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+    return WKV7_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                 const void* v, const void* a, const void* b, const float* state_in,
+                 void* y, float* state_out, void* stream) {
+    g_last_error[0] = '\0';
+    wkv7::Params p{};
+    int rc = check_desc(desc, &p);
+    if (rc) return rc;
+    const void* in6[6] = {r, w, k, v, a, b};
+    if ((rc = check_ptrs(p, in6, y, state_in, state_out))) return rc;
+    int algo = resolve_algo(p, desc->algo);
+    if (algo == WKV7_ALGO_CHUNKED) return fail(WKV7_EUNSUPPORTED, "chunked algorithm not built");
+    p.r = r; p.w = w; p.k = k; p.v = v; p.a = a; p.b = b;
+    p.s0 = state_in; p.y = y; p.s1 = state_out;
+    if (int64_t(p.B) * p.H == 0) return WKV7_OK;
+    if ((rc = check_device())) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (p.T == 0) {
+        if (!state_out) return WKV7_OK;
+        return finish_launch(wkv7::launch_state_copy(p, s), "state copy");
+    }
+    if (algo == WKV7_ALGO_CHUNKED) return finish_launch(wkv7::launch_chunked(p, s), "chunked");
+    return finish_launch(wkv7::launch_scan(p, s), "scan");
+}
+
+int wkv7_decode_step(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                     const void* v, const void* a, const void* b, const float* state_in,
+                     void* y, float* state_out, void* stream) {
+    g_last_error[0] = '\0';
+    wkv7::Params p{};
+    int rc = check_desc(desc, &p);
+    if (rc) return rc;
+    if (p.T != 1) return fail(WKV7_EINVAL, "decode_step needs T == 1 (got %d)", p.T);
+    const void* in6[6] = {r, w, k, v, a, b};
+    if ((rc = check_ptrs(p, in6, y, state_in, state_out))) return rc;
+    if (int64_t(p.B) * p.H > 0 && !state_out) return fail(WKV7_EINVAL, "state_out is NULL");
+    p.r = r; p.w = w; p.k = k; p.v = v; p.a = a; p.b = b;
+    p.s0 = state_in; p.y = y; p.s1 = state_out;
+    if (int64_t(p.B) * p.H == 0) return WKV7_OK;
+    if ((rc = check_device())) return rc;
+    return finish_launch(wkv7::launch_decode(p, reinterpret_cast<hipStream_t>(stream)), "decode");
+}
+
+int wkv7_resolve_algo(const wkv7_desc* desc) {
+    wkv7::Params p{};
+    int rc = check_desc(desc, &p);
+    if (rc) return -rc;
+    return resolve_algo(p, desc->algo);
+}
+
+const char* wkv7_strerror(int code) {
+    switch (code) {
+        case WKV7_OK: return "ok";
+        case WKV7_EINVAL: return "invalid argument";
+        case WKV7_EUNSUPPORTED: return "unsupported configuration";
+        case WKV7_EDEVICE: return "unsupported or unavailable device";
+        case WKV7_ELAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char* wkv7_last_error(void) { return g_last_error; }
+
+int wkv7_abi_version(void) { return WKV7_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// Internal interface between the C-ABI entry points (wkv7_api.cpp) and the
+// kernel launchers (wkv7_scan.hip, wkv7_chunked.hip, wkv7_decode.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "../../include/wkv7.h"
+
+namespace wkv7 {
+
+// Validated, resolved arguments of one call.  Sizes are those of wkv7_desc
+// (H_kv already defaulted, chunk_len already defaulted).
+struct Params {
+    int B, T, H, H_kv, D;
+    int in_dtype, y_dtype, w_mode, chunk_len;
+    float y_scale;
+    const float* r_k;
+    const void *r, *w, *k, *v, *a, *b;
+    const float* s0;   // may be null: zero initial state
+    void* y;
+    float* s1;         // may be null: final state not written
+};
+
+// Each launcher enqueues its kernel(s) on `stream` and returns the HIP status
+// of the launch.  They assume Params passed validation in wkv7_api.cpp.
+hipError_t launch_scan(const Params& p, hipStream_t stream);
+hipError_t launch_chunked(const Params& p, hipStream_t stream);
+hipError_t launch_decode(const Params& p, hipStream_t stream);
+// state_out <- state_in (or zeros) for T == 0.
+hipError_t launch_state_copy(const Params& p, hipStream_t stream);
+
+}  // namespace wkv7

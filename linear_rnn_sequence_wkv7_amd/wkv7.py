@@ -1,0 +1,200 @@
+"""Thin Python binding over libwkv7.so (argument marshalling only).
+
+Torch supplies device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  The names mirror the C ABI in
+include/wkv7.h: wkv7_forward, wkv7_decode_step, wkv7_resolve_algo.
+
+If the library is missing, every call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "wkv7_forward", "wkv7_decode_step", "wkv7_resolve_algo", "Wkv7Error", "lib_path", "load_library",
+    "WKV7_OK", "WKV7_EINVAL", "WKV7_EUNSUPPORTED", "WKV7_EDEVICE", "WKV7_ELAUNCH",
+    "ALGOS", "W_MODES", "Desc", "EXPORTED_SYMBOLS",
+]
+
+WKV7_OK, WKV7_EINVAL, WKV7_EUNSUPPORTED, WKV7_EDEVICE, WKV7_ELAUNCH = 0, 1, 2, 3, 4
+_DTYPES = {"f32": 0, "bf16": 1}
+W_MODES = {"decay": 0, "logneglog": 1}
+ALGOS = {"auto": 0, "scan": 1, "chunked": 2}
+EXPORTED_SYMBOLS = ("wkv7_forward", "wkv7_decode_step", "wkv7_resolve_algo", "wkv7_strerror",
+                    "wkv7_last_error", "wkv7_abi_version")
+
+
+class Wkv7Error(RuntimeError):
+    def __init__(self, code: int, where: str, detail: str):
+        super().__init__(f"{where}: {_status_name(code)} ({code}): {detail}")
+        self.code = code
+
+
+class Desc(ctypes.Structure):
+    """Mirror of struct wkv7_desc."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("H_kv", ctypes.c_int32),
+        ("D", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32),
+        ("w_mode", ctypes.c_int32), ("algo", ctypes.c_int32), ("chunk_len", ctypes.c_int32),
+        ("y_scale", ctypes.c_float), ("reserved", ctypes.c_int32), ("r_k", ctypes.c_void_p),
+    ]
+
+
+def lib_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwkv7.so")
+
+
+_LIB = None
+
+
+def load_library():
+    """Load libwkv7.so (once) and declare the C signatures.  Raises if it is not built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m linear_rnn_sequence_wkv7_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    sig = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    for name in ("wkv7_forward", "wkv7_decode_step"):
+        fn = getattr(lib, name)
+        fn.argtypes = sig
+        fn.restype = ctypes.c_int
+    lib.wkv7_resolve_algo.argtypes = [ctypes.POINTER(Desc)]
+    lib.wkv7_resolve_algo.restype = ctypes.c_int
+    lib.wkv7_strerror.argtypes = [ctypes.c_int]
+    lib.wkv7_strerror.restype = ctypes.c_char_p
+    lib.wkv7_last_error.argtypes = []
+    lib.wkv7_last_error.restype = ctypes.c_char_p
+    lib.wkv7_abi_version.argtypes = []
+    lib.wkv7_abi_version.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def _status_name(code: int) -> str:
+    try:
+        return load_library().wkv7_strerror(code).decode()
+    except Exception:  # pragma: no cover - only while reporting another failure
+        return "status"
+
+
+def make_desc(B, T, H, D, *, H_kv=None, in_dtype="bf16", y_dtype="bf16", w_mode="decay",
+              algo="auto", chunk_len=64, y_scale=1.0, r_k_ptr=None) -> Desc:
+    return Desc(B=B, T=T, H=H, H_kv=H if H_kv is None else H_kv, D=D,
+                in_dtype=_DTYPES[in_dtype], y_dtype=_DTYPES[y_dtype], w_mode=W_MODES[w_mode],
+                algo=ALGOS[algo], chunk_len=chunk_len, y_scale=float(y_scale), reserved=0,
+                r_k=r_k_ptr)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_name(t) -> str:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return "f32"
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_inputs(r, w, k, v, a, b, state, r_k):
+    torch = _torch()
+    if r.dim() != 4:
+        raise ValueError("r must be [B, T, H, D]")
+    B, T, H, D = r.shape
+    dev = r.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    dt = r.dtype
+    for name, x in (("w", w), ("a", a), ("b", b)):
+        if tuple(x.shape) != (B, T, H, D):
+            raise ValueError(f"{name} must have shape {(B, T, H, D)}, got {tuple(x.shape)}")
+    if k.dim() != 4 or tuple(k.shape[:2]) != (B, T) or k.shape[3] != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, T, H_kv, D] with matching shapes")
+    for name, x in (("r", r), ("w", w), ("k", k), ("v", v), ("a", a), ("b", b)):
+        if x.dtype != dt:
+            raise TypeError(f"{name} has dtype {x.dtype}, expected {dt} like r")
+        if x.device != dev or not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous and on {dev}")
+    if state is not None:
+        if tuple(state.shape) != (B, H, D, D) or state.dtype != torch.float32:
+            raise ValueError(f"state must be float32 [B, H, D, D] = {(B, H, D, D)}")
+        if state.device != dev or not state.is_contiguous():
+            raise ValueError(f"state must be contiguous and on {dev}")
+    if r_k is not None:
+        if tuple(r_k.shape) != (H, D) or r_k.dtype != torch.float32 or r_k.device != dev or not r_k.is_contiguous():
+            raise ValueError(f"r_k must be contiguous float32 [H, D] = {(H, D)} on {dev}")
+    return B, T, H, int(k.shape[2]), D
+
+
+def _call(fn_name, desc, r, w, k, v, a, b, state, y, state_out):
+    torch = _torch()
+    lib = load_library()
+    stream = torch.cuda.current_stream(r.device).cuda_stream
+    with torch.cuda.device(r.device):
+        rc = getattr(lib, fn_name)(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                   _ptr(state), _ptr(y), _ptr(state_out), stream)
+    if rc != WKV7_OK:
+        raise Wkv7Error(rc, fn_name, lib.wkv7_last_error().decode())
+
+
+def wkv7_forward(r, w, k, v, a, b, state=None, *, w_mode: str = "decay", y_dtype: Optional[str] = None,
+                 algo: str = "auto", chunk_len: int = 64, y_scale: float = 1.0, r_k=None,
+                 y=None, state_out=None, return_state: bool = True) -> Tuple[object, object]:
+    """Run wkv7_forward on torch GPU tensors.
+
+    r, w, a, b: [B, T, H, D]; k, v: [B, T, H_kv, D]; all float32 or all bfloat16, contiguous.
+    state: [B, H, D, D] float32 or None (zeros).  r_k: [H, D] float32 or None.
+    y_dtype: "f32" | "bf16" (default: the input dtype).  Outputs are allocated
+    unless `y` / `state_out` are given (state_out may equal state: in place).
+    Returns (y, state_out); state_out is None when return_state is False.
+    """
+    torch = _torch()
+    B, T, H, H_kv, D = _check_inputs(r, w, k, v, a, b, state, r_k)
+    ydt = y_dtype or _dtype_name(r)
+    if y is None:
+        y = torch.empty((B, T, H, D), dtype=torch.float32 if ydt == "f32" else torch.bfloat16, device=r.device)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=r.device)
+    desc = make_desc(B, T, H, D, H_kv=H_kv, in_dtype=_dtype_name(r), y_dtype=ydt, w_mode=w_mode, algo=algo,
+                     chunk_len=chunk_len, y_scale=y_scale, r_k_ptr=_ptr(r_k))
+    _call("wkv7_forward", desc, r, w, k, v, a, b, state, y, state_out)
+    return y, state_out
+
+
+def wkv7_decode_step(r, w, k, v, a, b, state, *, w_mode: str = "decay", y_dtype: Optional[str] = None,
+                     y_scale: float = 1.0, r_k=None, y=None, state_out=None) -> Tuple[object, object]:
+    """One token per sequence: inputs [B, 1, H, D] (k, v [B, 1, H_kv, D]); state [B, H, D, D] or None."""
+    torch = _torch()
+    B, T, H, H_kv, D = _check_inputs(r, w, k, v, a, b, state, r_k)
+    if T != 1:
+        raise ValueError("decode_step takes exactly one token per sequence (T == 1)")
+    ydt = y_dtype or _dtype_name(r)
+    if y is None:
+        y = torch.empty((B, 1, H, D), dtype=torch.float32 if ydt == "f32" else torch.bfloat16, device=r.device)
+    if state_out is None:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=r.device)
+    desc = make_desc(B, 1, H, D, H_kv=H_kv, in_dtype=_dtype_name(r), y_dtype=ydt, w_mode=w_mode,
+                     y_scale=y_scale, r_k_ptr=_ptr(r_k))
+    _call("wkv7_decode_step", desc, r, w, k, v, a, b, state, y, state_out)
+    return y, state_out
+
+
+def wkv7_resolve_algo(B, T, H, D, *, H_kv=None, algo="auto", **kw) -> str:
+    """Which algorithm wkv7_forward runs for these sizes ("scan" or "chunked")."""
+    rc = load_library().wkv7_resolve_algo(ctypes.byref(make_desc(B, T, H, D, H_kv=H_kv, algo=algo, **kw)))
+    if rc < 0:
+        raise Wkv7Error(-rc, "wkv7_resolve_algo", load_library().wkv7_last_error().decode())
+    return {1: "scan", 2: "chunked"}[rc]

@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments before touching any device (CPU only: no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_rnn_sequence_wkv7_amd import wkv7 as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(W.lib_path()), reason="libwkv7.so not built")
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(wkv7_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) >= {"wkv7_forward", "wkv7_decode_step"}
+    lib = W.load_library()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+    assert set(names) == set(W.EXPORTED_SYMBOLS)
+
+
+def test_abi_version_and_strerror():
+    lib = W.load_library()
+    assert lib.wkv7_abi_version() == 1
+    assert lib.wkv7_strerror(0) == b"ok"
+    assert lib.wkv7_strerror(W.WKV7_EINVAL) == b"invalid argument"
+    assert lib.wkv7_strerror(99) == b"unknown status"
+
+
+FAKE = 0x10000   # aligned, never dereferenced: every case below fails validation first
+
+
+def _call(desc, ptrs=None, fn="wkv7_forward"):
+    lib = W.load_library()
+    p = ptrs or {}
+    args = [p.get(k, FAKE) for k in ("r", "w", "k", "v", "a", "b")] + \
+           [p.get("s0"), p.get("y", FAKE + 4096), p.get("s1"), None]
+    return getattr(lib, fn)(ctypes.byref(desc) if desc is not None else None, *args)
+
+
+def good(**kw):
+    d = dict(B=2, T=8, H=4, D=64)
+    d.update(kw)
+    return W.make_desc(d.pop("B"), d.pop("T"), d.pop("H"), d.pop("D"), **d)
+
+
+@pytest.mark.parametrize("desc,code", [
+    (None, W.WKV7_EINVAL),
+    (good(D=96), W.WKV7_EUNSUPPORTED),
+    (good(D=0), W.WKV7_EINVAL),
+    (good(B=-1), W.WKV7_EINVAL),
+    (good(T=-3), W.WKV7_EINVAL),
+    (good(H=4, H_kv=3), W.WKV7_EINVAL),
+    (good(H=4, H_kv=8), W.WKV7_EINVAL),
+    (good(chunk_len=32), W.WKV7_EUNSUPPORTED),
+])
+def test_bad_descriptor_rejected(desc, code):
+    assert _call(desc) == code
+    assert _call(desc, fn="wkv7_decode_step") == code
+
+
+def test_bad_enum_and_reserved():
+    d = good(); d.in_dtype = 7
+    assert _call(d) == W.WKV7_EINVAL
+    d = good(); d.w_mode = 2
+    assert _call(d) == W.WKV7_EINVAL
+    d = good(); d.algo = 9
+    assert _call(d) == W.WKV7_EINVAL
+    d = good(); d.reserved = 1
+    assert _call(d) == W.WKV7_EINVAL
+    d = good(); d.y_scale = float("nan")
+    assert _call(d) == W.WKV7_EINVAL
+    assert b"y_scale" in W.load_library().wkv7_last_error()
+
+
+@pytest.mark.parametrize("key", ["r", "w", "k", "v", "a", "b", "y"])
+def test_null_and_misaligned_pointers(key):
+    assert _call(good(), {key: None}) == W.WKV7_EINVAL
+    assert _call(good(), {key: FAKE + 8}) == W.WKV7_EINVAL
+    assert _call(good(), {"s0": FAKE + 4}) == W.WKV7_EINVAL
+    assert _call(good(), {"s1": FAKE + 4}) == W.WKV7_EINVAL
+
+
+def test_y_aliasing_input_rejected():
+    assert _call(good(), {"y": FAKE}) == W.WKV7_EINVAL
+
+
+def test_decode_needs_one_token_and_state_out():
+    assert _call(good(T=2), fn="wkv7_decode_step") == W.WKV7_EINVAL
+    assert _call(good(T=1), fn="wkv7_decode_step") == W.WKV7_EINVAL  # state_out NULL
+
+
+def test_empty_problem_is_a_no_op():
+    # B*H == 0 returns before any device call.
+    assert _call(good(B=0)) == W.WKV7_OK
+    assert _call(good(H=0)) == W.WKV7_OK
+    assert _call(good(B=0, T=1), {"s1": FAKE + 8192}, fn="wkv7_decode_step") == W.WKV7_OK
+
+
+def test_resolve_algo():
+    assert W.wkv7_resolve_algo(2, 8, 4, 64, algo="scan") == "scan"
+    assert W.wkv7_resolve_algo(2, 8, 4, 64, algo="chunked") == "chunked"
+    assert W.wkv7_resolve_algo(2, 8, 4, 64) in ("scan", "chunked")
+    with pytest.raises(W.Wkv7Error):
+        W.wkv7_resolve_algo(2, 8, 4, 96)
