@@ -103,10 +103,12 @@ int check_ptrs(const wkv7::Params& p, const void* const* in6, const void* y,
     return WKV7_OK;
 }
 
+// AUTO: the chunked matrix-core form once a sequence spans at least one full
+// chunk and the head size has a chunked kernel; the scan otherwise.
 int resolve_algo(const wkv7::Params& p, int requested) {
     if (requested == WKV7_ALGO_SCAN) return WKV7_ALGO_SCAN;
     if (requested == WKV7_ALGO_CHUNKED) return WKV7_ALGO_CHUNKED;
-    return WKV7_ALGO_SCAN;
+    return (p.D == 64 && p.T >= p.chunk_len) ? WKV7_ALGO_CHUNKED : WKV7_ALGO_SCAN;
 }
 
 int finish_launch(hipError_t e, const char* what) {
@@ -130,7 +132,8 @@ int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void
     const void* in6[6] = {r, w, k, v, a, b};
     if ((rc = check_ptrs(p, in6, y, state_in, state_out))) return rc;
     int algo = resolve_algo(p, desc->algo);
-    if (algo == WKV7_ALGO_CHUNKED) return fail(WKV7_EUNSUPPORTED, "chunked algorithm not built");
+    if (algo == WKV7_ALGO_CHUNKED && p.D != 64)
+        return fail(WKV7_EUNSUPPORTED, "chunked algorithm supports D=64 (got D=%d)", p.D);
     p.r = r; p.w = w; p.k = k; p.v = v; p.a = a; p.b = b;
     p.s0 = state_in; p.y = y; p.s1 = state_out;
     if (int64_t(p.B) * p.H == 0) return WKV7_OK;
