@@ -62,8 +62,9 @@ def algorithmic_flops(wl) -> int:
 
 
 def traffic_from_profile(kind: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, or None
-    when absent or taken on a different kernel source."""
+    """HBM bytes per launch from committed rocprofv3 counter runs (FETCH_SIZE
+    plus WRITE_SIZE, each scaled by what the counter reads for a plain copy of
+    known size), or None when absent or taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kind}_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -94,8 +95,22 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fwd_bf16_b8_t1024_h32_d64")
     ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunked"])
-    ap.add_argument("--cpu-pairs", type=int, default=128, help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-pairs", type=int, default=256, help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (a reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     a = ap.parse_args(argv)
+
+    if a.copy_calibration_mib > 0:
+        import torch
+        n = a.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_mib": a.copy_calibration_mib, "copies": 3}), flush=True)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:

@@ -48,15 +48,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int L = 64;          // chunk length
 constexpr int DH = 64;         // head size handled by this kernel
-constexpr int NTHR = 256;
+constexpr int NTHR = 512;      // 8 waves: two per value strip
 constexpr int P72 = 72;        // bf16 pitch of the 64 x 64 operand matrices (144 B rows)
 constexpr int MAT = 64 * P72 * 2;
 constexpr int PD = 20;         // pitch of the 16 x 16 diagonal blocks
-constexpr int PG = 68;         // fp32 pitch of the decay-prefix scratch
+constexpr int PE = 68;         // fp32 pitch of the decay tables
 
 // LDS map (bytes).  Region 1 holds B~, K~ during P1..P2 and A_ab, A_rb and the
-// fp32 diagonal blocks of A_ab afterwards; region 2 holds the prefix scratch
-// during P1 and A_ak, A_rk afterwards.
+// fp32 diagonal blocks of A_ab afterwards; region 2 holds the decay tables
+// 2^g, 2^-g and the column-segment totals during P1 and A_ak, A_rk afterwards.
 constexpr int OFF_AT = 0;
 constexpr int OFF_RTH = OFF_AT + MAT;
 constexpr int OFF_RTL = OFF_RTH + MAT;
@@ -72,20 +72,23 @@ constexpr int OFF_AAB = OFF_R1;            // A_ab [t][s] bf16
 constexpr int OFF_ARB = OFF_R1 + MAT;      // A_rb [t][s] bf16
 constexpr int OFF_ADIAG = OFF_R1 + 2 * MAT;  // fp32 [4][16][PD] diagonal blocks of A_ab
 constexpr int OFF_R2 = OFF_R1 + 3 * MAT;
-constexpr int OFF_G = OFF_R2;              // fp32 [64][PG] decay prefix
-constexpr int OFF_TOT = OFF_R2 + 64 * PG * 4;  // fp32 [4][64] segment totals
+constexpr int OFF_E = OFF_R2;              // fp32 [64][PE] 2^g
+constexpr int OFF_EI = OFF_R2 + 64 * PE * 4;   // fp32 [64][PE] 2^-g
+constexpr int OFF_TOT = OFF_EI + 64 * PE * 4;  // fp32 [8][64] column-segment totals
 constexpr int OFF_AKH = OFF_R2;            // A_ak [t][s] hi / lo
 constexpr int OFF_AKL = OFF_R2 + MAT;
 constexpr int OFF_RKH = OFF_R2 + 2 * MAT;  // A_rk [t][s] hi / lo
 constexpr int OFF_RKL = OFF_R2 + 3 * MAT;
 constexpr int OFF_DINV = OFF_R2 + 4 * MAT;   // bf16 [4][16][PD] inverses of diagonal blocks
-constexpr int OFF_GL = OFF_DINV + 4 * 16 * PD * 2;
-constexpr int OFF_BONUS = OFF_GL + 256;
-constexpr int OFF_VTL = OFF_BONUS + 256;   // V^T lo part (fp32 inputs only)
+constexpr int OFF_EL = OFF_DINV + 4 * 16 * PD * 2;   // fp32 [64] 2^g_L
+constexpr int OFF_BONUS = OFF_EL + 256;    // fp32 [64] hxa07D bonus coefficient per token
+constexpr int OFF_XS = OFF_BONUS + 256;    // state halves exchanged by the two waves of a strip
+constexpr int XS_BYTES = 4 * 4 * 2 * 64 * 8;
+constexpr int OFF_VTL = OFF_XS + XS_BYTES; // V^T lo part (fp32 inputs only)
 constexpr int SMEM_BF16 = OFF_VTL;
 constexpr int SMEM_F32 = OFF_VTL + MAT;
 static_assert(4 * 16 * PD * 4 <= MAT, "diagonal blocks fit");
-static_assert(64 * PG * 4 + 1024 <= 2 * MAT, "prefix scratch fits");
+static_assert(2 * 64 * PE * 4 + 8 * 64 * 4 <= 4 * MAT, "decay tables fit");
 static_assert(SMEM_F32 <= 160 * 1024, "LDS budget");
 
 struct ChunkArgs {
@@ -134,29 +137,24 @@ template <typename T> __device__ __forceinline__ void sts(char* base, int byte_o
     *reinterpret_cast<T*>(base + byte_off) = v;
 }
 
-// One token row (16 consecutive elements) of an input tensor, undecoded.
-template <typename Tin> struct Row16;
-template <> struct Row16<bf16_t> {
-    uint4 x[2];
-    __device__ __forceinline__ void load(const bf16_t* p, bool ok) {
-        if (ok) {
-            x[0] = reinterpret_cast<const uint4*>(p)[0];
-            x[1] = reinterpret_cast<const uint4*>(p)[1];
-        } else {
-            x[0] = x[1] = make_uint4(0, 0, 0, 0);
-        }
-    }
+// Loads below are unconditional, from addresses clamped into the tensor, so
+// that no control-flow join forces an early wait on them; tokens past the end
+// are masked where the values are used.
+// 8 consecutive elements of one token row, undecoded (row threads).
+template <typename Tin> struct Row8;
+template <> struct Row8<bf16_t> {
+    uint4 x;
+    __device__ __forceinline__ void load(const bf16_t* p) { x = *reinterpret_cast<const uint4*>(p); }
     __device__ __forceinline__ float get(int e) const {
-        const uint4& u = x[e >> 3];
-        const uint32_t d = (e & 6) == 0 ? u.x : (e & 6) == 2 ? u.y : (e & 6) == 4 ? u.z : u.w;
+        const uint32_t d = e < 2 ? x.x : e < 4 ? x.y : e < 6 ? x.z : x.w;
         return (e & 1) ? __uint_as_float(d & 0xffff0000u) : __uint_as_float(d << 16);
     }
 };
-template <> struct Row16<float> {
-    float4 x[4];
-    __device__ __forceinline__ void load(const float* p, bool ok) {
-        #pragma unroll
-        for (int c = 0; c < 4; ++c) x[c] = ok ? reinterpret_cast<const float4*>(p)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+template <> struct Row8<float> {
+    float4 x[2];
+    __device__ __forceinline__ void load(const float* p) {
+        x[0] = reinterpret_cast<const float4*>(p)[0];
+        x[1] = reinterpret_cast<const float4*>(p)[1];
     }
     __device__ __forceinline__ float get(int e) const {
         const float4& u = x[e >> 2];
@@ -164,13 +162,19 @@ template <> struct Row16<float> {
     }
 };
 
+// One element of a column (column threads), as fp32 bits.
+__device__ __forceinline__ uint32_t ld_raw(const bf16_t* p) { return uint32_t(*p) << 16; }
+__device__ __forceinline__ uint32_t ld_raw(const float* p) { return __float_as_uint(*p); }
+
 template <typename Tin, typename Ty, bool LOGW, bool EPI>
 __global__ __launch_bounds__(NTHR)
 void chunked_kernel(ChunkArgs g) {
     constexpr bool VSPLIT = sizeof(Tin) == 4;   // fp32 v is not exact in bf16
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, known wave-uniform
+    const int l = tid & 63, lr = l & 15, lq = l >> 4;
+    const int strip = w & 3, hf = w >> 2;      // value rows [16 strip, 16 strip + 16); half of the work
     const int H = g.H, T = g.T;
     const int bh = blockIdx.x;
     const int bb = bh / H, h = bh - bb * H;
@@ -186,278 +190,303 @@ void chunked_kernel(ChunkArgs g) {
     const Tin* bp = static_cast<const Tin*>(g.b);
     Ty* yp = static_cast<Ty*>(g.y);
 
-    // State, transposed: ST[jt][r] = S[i = 16w + lr][j = 16jt + 4lq + r].
-    f32x4 ST[4];
-    const int i_row = 16 * w + lr;
+    // This wave's half of its strip's state, transposed:
+    // ST[u][r] = S[i = 16 strip + lr][j = 16 (2 hf + u) + 4 lq + r].
+    f32x4 ST[2];
+    const int i_row = 16 * strip + lr;
     const int64_t sbase = int64_t(bh) * DH * DH + int64_t(i_row) * DH;
     #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
+    for (int u = 0; u < 2; ++u) {
+        const int jt = 2 * hf + u;
         if (g.s0) {
             const float4 x = *reinterpret_cast<const float4*>(g.s0 + sbase + 16 * jt + 4 * lq);
-            ST[jt] = f32x4{x.x, x.y, x.z, x.w};
+            ST[u] = f32x4{x.x, x.y, x.z, x.w};
         } else {
-            ST[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            ST[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
 
-    // P1 thread mapping: token row t1 = tid / 4, columns [16 q1, 16 q1 + 16).
-    const int t1 = tid >> 2, q1 = tid & 3;
-    float rk16[16];
+    // Column threads (P1a): key column jc = l, tokens [8 w, 8 w + 8).
+    // Row threads (P1b): token tr = tid / 8, key columns [8 qr, 8 qr + 8).
+    const int jc = l, pc = w;
+    const int tr = tid >> 3, qr = tid & 7;
+    float rk8[8];
     if constexpr (EPI) {
         #pragma unroll
-        for (int e = 0; e < 16; ++e) rk16[e] = g.r_k[h * DH + 16 * q1 + e];
+        for (int e = 0; e < 8; ++e) rk8[e] = g.r_k[h * DH + 8 * qr + e];
     }
-    Row16<Tin> rr, ww, kk, vv, aa, bbv;
-    auto load_rows = [&](int c0) {
-        const int t = c0 + t1;
-        const bool ok = t < T;
-        const int tt = ok ? t : 0;
-        rr.load(rp + base_q + tt * step_q + 16 * q1, ok);
-        ww.load(wp + base_q + tt * step_q + 16 * q1, ok);
-        kk.load(kp + base_kv + tt * step_kv + 16 * q1, ok);
-        vv.load(vp + base_kv + tt * step_kv + 16 * q1, ok);
-        aa.load(ap + base_q + tt * step_q + 16 * q1, ok);
-        bbv.load(bp + base_q + tt * step_q + 16 * q1, ok);
+    uint32_t cw[8], cb[8], ck[8], cv[8];
+    Row8<Tin> rr, ra, rb, rkv;
+    auto load_chunk = [&](int c0) {
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int tt = min(c0 + 8 * pc + e, T - 1);
+            cw[e] = ld_raw(wp + base_q + tt * step_q + jc);
+            cb[e] = ld_raw(bp + base_q + tt * step_q + jc);
+            ck[e] = ld_raw(kp + base_kv + tt * step_kv + jc);
+            cv[e] = ld_raw(vp + base_kv + tt * step_kv + jc);
+        }
+        const int tt = min(c0 + tr, T - 1);
+        rr.load(rp + base_q + tt * step_q + 8 * qr);
+        ra.load(ap + base_q + tt * step_q + 8 * qr);
+        rb.load(bp + base_q + tt * step_q + 8 * qr);
+        rkv.load(kp + base_kv + tt * step_kv + 8 * qr);
     };
-    load_rows(0);
+    load_chunk(0);
+
+    // Lane offsets of the MFMA operand patterns inside a 64 x 64 bf16 matrix.
+    const int op16 = (lr * P72 + 4 * lq) * 2;    // 16x16x16 operand: row lr, k = 4 lq .. 4 lq + 3
+    const int op32 = (lr * P72 + 8 * lq) * 2;    // 16x16x32 operand: row lr, k = 8 lq .. 8 lq + 7
+    const int xs_own = ((strip * 4 + 2 * hf) * 2 * 64 + l) * 8;
+    const int xs_oth = ((strip * 4 + 2 * (1 - hf)) * 2 * 64 + l) * 8;
 
     const int nchunks = (T + L - 1) / L;
     for (int ch = 0; ch < nchunks; ++ch) {
         const int c0 = ch * L;
-        const bool tok_ok = c0 + t1 < T;
-        // ---------------- P1: decay prefix and scaled operands ----------------
-        float lw[16];
+        // Publish this wave's state half (bf16 hi / lo B operands) for its partner.
         #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const float x = ww.get(e);
-            lw[e] = !tok_ok ? 0.f : LOGW ? -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e : __builtin_amdgcn_logf(x);
+        for (int u = 0; u < 2; ++u) {
+            s16x4 sh, sl;
+            to_operand(ST[u], sh, sl);
+            sts<s16x4>(smem + OFF_XS, xs_own + (u * 2 + 0) * 64 * 8, sh);
+            sts<s16x4>(smem + OFF_XS, xs_own + (u * 2 + 1) * 64 * 8, sl);
         }
+
+        // ---------------- P1a: decay prefix down each key column ----------------
+        float pre[8];
         {
-            char* G = smem + OFF_G;
-            #pragma unroll
-            for (int e = 0; e < 16; e += 4)
-                sts<float4>(G, (t1 * PG + 16 * q1 + e) * 4, make_float4(lw[e], lw[e + 1], lw[e + 2], lw[e + 3]));
-        }
-        __syncthreads();
-        {
-            // Column prefix: thread (j, segment p) scans tokens [16p, 16p + 16).
-            const int j = tid & 63, p = tid >> 6;
-            char* G = smem + OFF_G;
-            float pre[16];
             float run = 0.f;
             #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                run += lds<float>(G, ((16 * p + e) * PG + j) * 4);
+            for (int e = 0; e < 8; ++e) {
+                const float x = __uint_as_float(cw[e]);
+                const bool ok = c0 + 8 * pc + e < T;
+                const float lw = !ok ? 0.f : LOGW ? -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e
+                                                  : __builtin_amdgcn_logf(x);
+                run += lw;
                 pre[e] = run;
             }
-            sts<float>(smem + OFF_TOT, (p * 64 + j) * 4, run);
-            __syncthreads();
-            float off = 0.f;
-            for (int pp = 0; pp < p; ++pp) off += lds<float>(smem + OFF_TOT, (pp * 64 + j) * 4);
-            #pragma unroll
-            for (int e = 0; e < 16; ++e) sts<float>(G, ((16 * p + e) * PG + j) * 4, pre[e] + off);
+            sts<float>(smem + OFF_TOT, (pc * 64 + jc) * 4, run);
         }
         __syncthreads();
-        float bonus_part = 0.f;
         {
-            const char* G = smem + OFF_G;
-            uint32_t at[8], rth[8], rtl[8], bt[8], kth[8], ktl[8];
+            float off = 0.f, total = 0.f;
             #pragma unroll
-            for (int e = 0; e < 16; e += 2) {
-                float E[2], Ep[2], Ei[2], Eh[2];
+            for (int pp = 0; pp < 8; ++pp) {
+                const float tp = lds<float>(smem + OFF_TOT, (pp * 64 + jc) * 4);
+                off += pp < pc ? tp : 0.f;
+                total += tp;
+            }
+            const float EL = __builtin_amdgcn_exp2f(total);
+            if (pc == 0) sts<float>(smem + OFF_EL, jc * 4, EL);
+            uint32_t bh4[4], khh[4], khl[4], vh[4], vl[4];
+            #pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                float Eh[2];
                 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const int j = 16 * q1 + e + u;
-                    const float gt = lds<float>(G, (t1 * PG + j) * 4);
-                    const float gp = t1 > 0 ? lds<float>(G, ((t1 - 1) * PG + j) * 4) : 0.f;
-                    const float gl = lds<float>(G, (63 * PG + j) * 4);
-                    E[u] = __builtin_amdgcn_exp2f(gt);
-                    Ep[u] = __builtin_amdgcn_exp2f(gp);
-                    Ei[u] = __builtin_amdgcn_exp2f(-gt);
-                    Eh[u] = __builtin_amdgcn_exp2f(gl - gt);
+                    const float gv = pre[e + u] + off;
+                    const float E = __builtin_amdgcn_exp2f(gv);
+                    const float Ei = __builtin_amdgcn_exp2f(-gv);
+                    sts<float>(smem + OFF_E, ((8 * pc + e + u) * PE + jc) * 4, E);
+                    sts<float>(smem + OFF_EI, ((8 * pc + e + u) * PE + jc) * 4, Ei);
+                    Eh[u] = EL * Ei;
                 }
-                const float a0 = aa.get(e), a1 = aa.get(e + 1);
-                const float r0 = rr.get(e), r1 = rr.get(e + 1);
-                const float b0 = bbv.get(e), b1 = bbv.get(e + 1);
-                const float k0 = kk.get(e), k1 = kk.get(e + 1);
-                at[e / 2] = pack_bf16(a0 * Ep[0], a1 * Ep[1]);
-                split2(r0 * E[0], r1 * E[1], rth[e / 2], rtl[e / 2]);
-                bt[e / 2] = pack_bf16(b0 * Ei[0], b1 * Ei[1]);
-                split2(k0 * Ei[0], k1 * Ei[1], kth[e / 2], ktl[e / 2]);
-                // Transposed operands: V^T, Bh^T, Kh^T (hi/lo), element by element.
-                const float bh0 = b0 * Eh[0], bh1 = b1 * Eh[1];
-                uint32_t khh, khl;
-                split2(k0 * Eh[0], k1 * Eh[1], khh, khl);
-                const int j0 = 16 * q1 + e;
-                uint32_t vpk, vpl;
-                split2(vv.get(e), vv.get(e + 1), vpk, vpl);
-                if constexpr (VSPLIT) {
-                    sts<uint16_t>(smem + OFF_VTL, ((j0) * P72 + t1) * 2, uint16_t(vpl));
-                    sts<uint16_t>(smem + OFF_VTL, ((j0 + 1) * P72 + t1) * 2, uint16_t(vpl >> 16));
-                }
-                const uint32_t bhp = pack_bf16(bh0, bh1);
-                sts<uint16_t>(smem + OFF_VT, ((j0) * P72 + t1) * 2, uint16_t(vpk));
-                sts<uint16_t>(smem + OFF_VT, ((j0 + 1) * P72 + t1) * 2, uint16_t(vpk >> 16));
-                sts<uint16_t>(smem + OFF_BHT, ((j0) * P72 + t1) * 2, uint16_t(bhp));
-                sts<uint16_t>(smem + OFF_BHT, ((j0 + 1) * P72 + t1) * 2, uint16_t(bhp >> 16));
-                sts<uint16_t>(smem + OFF_KHTH, ((j0) * P72 + t1) * 2, uint16_t(khh));
-                sts<uint16_t>(smem + OFF_KHTH, ((j0 + 1) * P72 + t1) * 2, uint16_t(khh >> 16));
-                sts<uint16_t>(smem + OFF_KHTL, ((j0) * P72 + t1) * 2, uint16_t(khl));
-                sts<uint16_t>(smem + OFF_KHTL, ((j0 + 1) * P72 + t1) * 2, uint16_t(khl >> 16));
-                if constexpr (EPI) bonus_part += r0 * k0 * rk16[e] + r1 * k1 * rk16[e + 1];
+                // Tokens past the end are identity tokens: b = k = v = 0.
+                const bool ok0 = c0 + 8 * pc + e < T, ok1 = c0 + 8 * pc + e + 1 < T;
+                const float b0 = ok0 ? __uint_as_float(cb[e]) : 0.f, b1 = ok1 ? __uint_as_float(cb[e + 1]) : 0.f;
+                const float k0 = ok0 ? __uint_as_float(ck[e]) : 0.f, k1 = ok1 ? __uint_as_float(ck[e + 1]) : 0.f;
+                const float v0 = ok0 ? __uint_as_float(cv[e]) : 0.f, v1 = ok1 ? __uint_as_float(cv[e + 1]) : 0.f;
+                bh4[e / 2] = pack_bf16(b0 * Eh[0], b1 * Eh[1]);
+                split2(k0 * Eh[0], k1 * Eh[1], khh[e / 2], khl[e / 2]);
+                split2(v0, v1, vh[e / 2], vl[e / 2]);
             }
-            const int ro = (t1 * P72 + 16 * q1) * 2;
-            sts<uint4>(smem + OFF_AT, ro, make_uint4(at[0], at[1], at[2], at[3]));
-            sts<uint4>(smem + OFF_AT, ro + 16, make_uint4(at[4], at[5], at[6], at[7]));
-            sts<uint4>(smem + OFF_RTH, ro, make_uint4(rth[0], rth[1], rth[2], rth[3]));
-            sts<uint4>(smem + OFF_RTH, ro + 16, make_uint4(rth[4], rth[5], rth[6], rth[7]));
-            sts<uint4>(smem + OFF_RTL, ro, make_uint4(rtl[0], rtl[1], rtl[2], rtl[3]));
-            sts<uint4>(smem + OFF_RTL, ro + 16, make_uint4(rtl[4], rtl[5], rtl[6], rtl[7]));
-            if (t1 == 63) {
+            const int o = (jc * P72 + 8 * pc) * 2;
+            sts<uint4>(smem + OFF_BHT, o, make_uint4(bh4[0], bh4[1], bh4[2], bh4[3]));
+            sts<uint4>(smem + OFF_KHTH, o, make_uint4(khh[0], khh[1], khh[2], khh[3]));
+            sts<uint4>(smem + OFF_KHTL, o, make_uint4(khl[0], khl[1], khl[2], khl[3]));
+            sts<uint4>(smem + OFF_VT, o, make_uint4(vh[0], vh[1], vh[2], vh[3]));
+            if constexpr (VSPLIT) sts<uint4>(smem + OFF_VTL, o, make_uint4(vl[0], vl[1], vl[2], vl[3]));
+        }
+        __syncthreads();
+
+        // ---------------- P1b: row-major scaled operands ----------------
+        {
+            float E[8], Ei[8], Ep[8];
+            const int oe = (tr * PE + 8 * qr) * 4;
+            const float4 e0 = lds<float4>(smem + OFF_E, oe), e1 = lds<float4>(smem + OFF_E, oe + 16);
+            const float4 i0 = lds<float4>(smem + OFF_EI, oe), i1 = lds<float4>(smem + OFF_EI, oe + 16);
+            E[0] = e0.x; E[1] = e0.y; E[2] = e0.z; E[3] = e0.w; E[4] = e1.x; E[5] = e1.y; E[6] = e1.z; E[7] = e1.w;
+            Ei[0] = i0.x; Ei[1] = i0.y; Ei[2] = i0.z; Ei[3] = i0.w; Ei[4] = i1.x; Ei[5] = i1.y; Ei[6] = i1.z; Ei[7] = i1.w;
+            if (tr > 0) {
+                const float4 p0 = lds<float4>(smem + OFF_E, oe - PE * 4), p1 = lds<float4>(smem + OFF_E, oe - PE * 4 + 16);
+                Ep[0] = p0.x; Ep[1] = p0.y; Ep[2] = p0.z; Ep[3] = p0.w; Ep[4] = p1.x; Ep[5] = p1.y; Ep[6] = p1.z; Ep[7] = p1.w;
+            } else {
                 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    sts<float>(smem + OFF_GL, (16 * q1 + e) * 4, lds<float>(G, (63 * PG + 16 * q1 + e) * 4));
+                for (int e = 0; e < 8; ++e) Ep[e] = 1.f;
             }
-            // Region 1 (B~, K~) is not read before the next barrier by anyone
-            // but the prefix scratch lives in region 2, so these stores are safe now.
-            sts<uint4>(smem + OFF_BT, ro, make_uint4(bt[0], bt[1], bt[2], bt[3]));
-            sts<uint4>(smem + OFF_BT, ro + 16, make_uint4(bt[4], bt[5], bt[6], bt[7]));
-            sts<uint4>(smem + OFF_KTH, ro, make_uint4(kth[0], kth[1], kth[2], kth[3]));
-            sts<uint4>(smem + OFF_KTH, ro + 16, make_uint4(kth[4], kth[5], kth[6], kth[7]));
-            sts<uint4>(smem + OFF_KTL, ro, make_uint4(ktl[0], ktl[1], ktl[2], ktl[3]));
-            sts<uint4>(smem + OFF_KTL, ro + 16, make_uint4(ktl[4], ktl[5], ktl[6], ktl[7]));
+            uint32_t at[4], rth[4], rtl[4], bt[4], kth[4], ktl[4];
+            float bonus_part = 0.f;
+            const float okm = c0 + tr < T ? 1.f : 0.f;   // identity token past the end
+            #pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float r0 = okm * rr.get(e), r1 = okm * rr.get(e + 1);
+                const float k0 = okm * rkv.get(e), k1 = okm * rkv.get(e + 1);
+                at[e / 2] = pack_bf16(okm * ra.get(e) * Ep[e], okm * ra.get(e + 1) * Ep[e + 1]);
+                split2(r0 * E[e], r1 * E[e + 1], rth[e / 2], rtl[e / 2]);
+                bt[e / 2] = pack_bf16(okm * rb.get(e) * Ei[e], okm * rb.get(e + 1) * Ei[e + 1]);
+                split2(k0 * Ei[e], k1 * Ei[e + 1], kth[e / 2], ktl[e / 2]);
+                if constexpr (EPI) bonus_part += r0 * k0 * rk8[e] + r1 * k1 * rk8[e + 1];
+            }
+            const int o = (tr * P72 + 8 * qr) * 2;
+            sts<uint4>(smem + OFF_AT, o, make_uint4(at[0], at[1], at[2], at[3]));
+            sts<uint4>(smem + OFF_RTH, o, make_uint4(rth[0], rth[1], rth[2], rth[3]));
+            sts<uint4>(smem + OFF_RTL, o, make_uint4(rtl[0], rtl[1], rtl[2], rtl[3]));
+            sts<uint4>(smem + OFF_BT, o, make_uint4(bt[0], bt[1], bt[2], bt[3]));
+            sts<uint4>(smem + OFF_KTH, o, make_uint4(kth[0], kth[1], kth[2], kth[3]));
+            sts<uint4>(smem + OFF_KTL, o, make_uint4(ktl[0], ktl[1], ktl[2], ktl[3]));
+            if constexpr (EPI) {
+                // The eight threads of a token row are lanes 8m .. 8m + 7 of one wave.
+                bonus_part += dpp<kDppQuadXor1>(bonus_part);
+                bonus_part += dpp<kDppQuadXor2>(bonus_part);
+                bonus_part += dpp<kDppRowHalfMirror>(bonus_part);
+                if (qr == 0) sts<float>(smem + OFF_BONUS, tr * 4, bonus_part);
+            }
         }
-        if constexpr (EPI) {
-            // The four threads of a token row are one quad.
-            bonus_part += dpp<kDppQuadXor1>(bonus_part);
-            bonus_part += dpp<kDppQuadXor2>(bonus_part);
-            if (q1 == 0) sts<float>(smem + OFF_BONUS, t1 * 4, bonus_part);
-        }
-        // Next chunk's rows: in flight during P2..P7.
-        if (ch + 1 < nchunks) load_rows(c0 + L);
         __syncthreads();
 
         // ---------------- P2: the four L x L matrices ----------------
-        // Tile list (tb, sb), sb <= tb; wave w takes tiles w, w + 4, w + 8.
-        // Each tile is computed as C'[s][t] = Y[s] . X[t] so that a lane holds
-        // 4 consecutive s of one t: a row-major [t][s] store of 4 elements.
-        f32x4 acc_ab[3], acc_ak[3], acc_rb[3], acc_rk[3];
-        int tile_tb[3], tile_sb[3];
+        // Tile list (tb, sb), sb <= tb in row order; wave w computes tiles
+        // (w & 3) + 4n of group w >> 2: group 0 = A_ab, A_ak; group 1 = A_rb, A_rk.
+        // Each tile is C'[s][t] = Y[s] . X[t], so a lane holds 4 consecutive s of
+        // one t: a row-major [t][s] store of 4 elements.
+        const int grp = hf;
+        f32x4 acc0[3], acc1[3];
         #pragma unroll
         for (int n = 0; n < 3; ++n) {
-            const int id = w + 4 * n;
-            int tb = 0, sb = 0;
-            // id -> (tb, sb) over the lower triangle in row order.
-            tb = id >= 6 ? 3 : id >= 3 ? 2 : id >= 1 ? 1 : 0;
-            sb = id - (tb * (tb + 1)) / 2;
-            tile_tb[n] = tb; tile_sb[n] = sb;
-            acc_ab[n] = acc_ak[n] = acc_rb[n] = acc_rk[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int id = strip + 4 * n;
+            const int tb = id >= 6 ? 3 : id >= 3 ? 2 : id >= 1 ? 1 : 0;
+            const int sb = id - (tb * (tb + 1)) / 2;
+            acc0[n] = acc1[n] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (id < 10) {
                 #pragma unroll
                 for (int kq = 0; kq < 2; ++kq) {
-                    const int ya = ((16 * sb + lr) * P72 + 32 * kq + 8 * lq) * 2;  // Y row s
-                    const int xb = ((16 * tb + lr) * P72 + 32 * kq + 8 * lq) * 2;  // X row t
+                    const int ya = (16 * sb * P72 + 32 * kq) * 2 + op32;
+                    const int xb = (16 * tb * P72 + 32 * kq) * 2 + op32;
                     const bf16x8 Bt8 = lds<bf16x8>(smem + OFF_BT, ya);
                     const bf16x8 Kh8 = lds<bf16x8>(smem + OFF_KTH, ya);
                     const bf16x8 Kl8 = lds<bf16x8>(smem + OFF_KTL, ya);
-                    const bf16x8 At8 = lds<bf16x8>(smem + OFF_AT, xb);
-                    const bf16x8 Rh8 = lds<bf16x8>(smem + OFF_RTH, xb);
-                    const bf16x8 Rl8 = lds<bf16x8>(smem + OFF_RTL, xb);
-                    acc_ab[n] = mfma32(Bt8, At8, acc_ab[n]);
-                    acc_ak[n] = mfma32(Kh8, At8, acc_ak[n]);
-                    acc_ak[n] = mfma32(Kl8, At8, acc_ak[n]);
-                    acc_rb[n] = mfma32(Bt8, Rh8, acc_rb[n]);
-                    acc_rb[n] = mfma32(Bt8, Rl8, acc_rb[n]);
-                    acc_rk[n] = mfma32(Kh8, Rh8, acc_rk[n]);
-                    acc_rk[n] = mfma32(Kh8, Rl8, acc_rk[n]);
-                    acc_rk[n] = mfma32(Kl8, Rh8, acc_rk[n]);
+                    if (grp == 0) {
+                        const bf16x8 At8 = lds<bf16x8>(smem + OFF_AT, xb);
+                        acc0[n] = mfma32(Bt8, At8, acc0[n]);
+                        acc1[n] = mfma32(Kh8, At8, acc1[n]);
+                        acc1[n] = mfma32(Kl8, At8, acc1[n]);
+                    } else {
+                        const bf16x8 Rh8 = lds<bf16x8>(smem + OFF_RTH, xb);
+                        const bf16x8 Rl8 = lds<bf16x8>(smem + OFF_RTL, xb);
+                        acc0[n] = mfma32(Bt8, Rh8, acc0[n]);
+                        acc0[n] = mfma32(Bt8, Rl8, acc0[n]);
+                        acc1[n] = mfma32(Kh8, Rh8, acc1[n]);
+                        acc1[n] = mfma32(Kh8, Rl8, acc1[n]);
+                        acc1[n] = mfma32(Kl8, Rh8, acc1[n]);
+                    }
                 }
             }
         }
-        __syncthreads();   // every wave has read B~ / K~ (region 1) and the prefix scratch is dead
+        __syncthreads();   // B~ / K~ (region 1) and the decay tables (region 2) are dead now
         #pragma unroll
         for (int n = 0; n < 3; ++n) {
-            const int id = w + 4 * n;
+            const int id = strip + 4 * n;
             if (id < 10) {
-                const int tb = tile_tb[n], sb = tile_sb[n];
-                const int t = 16 * tb + lr;            // C' column
-                const int s0 = 16 * sb + 4 * lq;       // C' rows s0 .. s0 + 3
-                f32x4 ab = acc_ab[n], ak = acc_ak[n], rb = acc_rb[n], rkk = acc_rk[n];
+                const int tb = id >= 6 ? 3 : id >= 3 ? 2 : id >= 1 ? 1 : 0;
+                const int sb = id - (tb * (tb + 1)) / 2;
+                const int o = ((16 * tb + lr) * P72 + 16 * sb + 4 * lq) * 2;
+                f32x4 c0v = acc0[n], c1v = acc1[n];
                 if (tb == sb) {
+                    // group 0 is strictly lower (s < t), group 1 lower with diagonal (s <= t).
                     #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int sl = 4 * lq + r;
-                        if (sl >= lr) { ab[r] = 0.f; ak[r] = 0.f; }
-                        if (sl > lr) { rb[r] = 0.f; rkk[r] = 0.f; }
+                        if (grp == 0 ? sl >= lr : sl > lr) { c0v[r] = 0.f; c1v[r] = 0.f; }
                     }
-                    // fp32 copy of the diagonal block for the exact inverse.
-                    sts<float4>(smem + OFF_ADIAG, ((tb * 16 + lr) * PD + 4 * lq) * 4,
-                                make_float4(ab[0], ab[1], ab[2], ab[3]));
+                    if (grp == 0)
+                        sts<float4>(smem + OFF_ADIAG, ((tb * 16 + lr) * PD + 4 * lq) * 4,
+                                    make_float4(c0v[0], c0v[1], c0v[2], c0v[3]));
                 }
-                const int o = (t * P72 + s0) * 2;
-                sts<uint2>(smem + OFF_AAB, o, make_uint2(pack_bf16(ab[0], ab[1]), pack_bf16(ab[2], ab[3])));
-                sts<uint2>(smem + OFF_ARB, o, make_uint2(pack_bf16(rb[0], rb[1]), pack_bf16(rb[2], rb[3])));
                 uint32_t h0, l0, h1, l1;
-                split2(ak[0], ak[1], h0, l0); split2(ak[2], ak[3], h1, l1);
-                sts<uint2>(smem + OFF_AKH, o, make_uint2(h0, h1));
-                sts<uint2>(smem + OFF_AKL, o, make_uint2(l0, l1));
-                split2(rkk[0], rkk[1], h0, l0); split2(rkk[2], rkk[3], h1, l1);
-                sts<uint2>(smem + OFF_RKH, o, make_uint2(h0, h1));
-                sts<uint2>(smem + OFF_RKL, o, make_uint2(l0, l1));
+                split2(c1v[0], c1v[1], h0, l0);
+                split2(c1v[2], c1v[3], h1, l1);
+                const uint2 c0p = make_uint2(pack_bf16(c0v[0], c0v[1]), pack_bf16(c0v[2], c0v[3]));
+                sts<uint2>(smem + (grp == 0 ? OFF_AAB : OFF_ARB), o, c0p);
+                sts<uint2>(smem + (grp == 0 ? OFF_AKH : OFF_RKH), o, make_uint2(h0, h1));
+                sts<uint2>(smem + (grp == 0 ? OFF_AKL : OFF_RKL), o, make_uint2(l0, l1));
             }
         }
-        {
+        if (tid < 256) {
             // Zero the upper tiles (t-block 0, s-block 1) and (2, 3) of A_ak and A_rk,
             // which the 32-deep products of P4/P6 read.
-            const int tile = tid >> 6, m = (tid >> 5) & 1, rw = (tid & 31) >> 1, half = tid & 1;
+            const int mat = tid >> 6, m = (tid >> 5) & 1, rw = (tid & 31) >> 1, half = tid & 1;
             const int offs[4] = {OFF_AKH, OFF_AKL, OFF_RKH, OFF_RKL};
             const int tb = m ? 2 : 0, sb = tb + 1;
-            sts<uint4>(smem + offs[tile], ((16 * tb + rw) * P72 + 16 * sb + 8 * half) * 2, make_uint4(0, 0, 0, 0));
+            sts<uint4>(smem + offs[mat], ((16 * tb + rw) * P72 + 16 * sb + 8 * half) * 2, make_uint4(0, 0, 0, 0));
         }
         __syncthreads();
 
         // ---------------- P3: inverses of the diagonal blocks of I - A_ab ----------------
-        if (l < 16) {
+        if (w < 4 && l < 16) {
             const int c = l;
             float x[16];
             #pragma unroll
             for (int t = 0; t < 16; ++t) {
                 float acc = (t == c) ? 1.f : 0.f;
                 #pragma unroll
-                for (int s = 0; s < t; ++s) acc = fmaf(lds<float>(smem + OFF_ADIAG, ((w * 16 + t) * PD + s) * 4), x[s], acc);
+                for (int s2 = 0; s2 < t; ++s2)
+                    acc = fmaf(lds<float>(smem + OFF_ADIAG, ((w * 16 + t) * PD + s2) * 4), x[s2], acc);
                 x[t] = acc;
             }
             #pragma unroll
             for (int t = 0; t < 16; ++t)
-                sts<uint16_t>(smem + OFF_DINV, ((w * 16 + t) * PD + c) * 2, __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[t])));
+                sts<uint16_t>(smem + OFF_DINV, ((w * 16 + t) * PD + c) * 2,
+                              __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[t])));
         }
         __syncthreads();
 
-        // ---------------- P4: RHS = At S0^T + A_ak V for this wave's value rows ----------------
-        // State as 16x16x16 B operands (k = key column j = 16 jt + 4 lq + r, n = value row).
-        s16x4 Sh[4], Sl[4];
+        // ---------------- P4: RHS = At S0^T + A_ak V (whole strip, both halves) ----------------
+        // State operands of the whole strip: key tiles 2 hf + u from this wave's
+        // registers (own), 2 (1 - hf) + u from the partner (other).  Register
+        // arrays are indexed by compile-time u only; hf enters LDS addresses.
+        s16x4 Sh[2][2], Sl[2][2];          // [own = 0 / other = 1][u]
+        int jtile[2][2];
         #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) to_operand(ST[jt], Sh[jt], Sl[jt]);
+        for (int u = 0; u < 2; ++u) {
+            to_operand(ST[u], Sh[0][u], Sl[0][u]);
+            Sh[1][u] = lds<s16x4>(smem + OFF_XS, xs_oth + (u * 2 + 0) * 64 * 8);
+            Sl[1][u] = lds<s16x4>(smem + OFF_XS, xs_oth + (u * 2 + 1) * 64 * 8);
+            jtile[0][u] = 2 * hf + u;
+            jtile[1][u] = 2 * (1 - hf) + u;
+        }
         // V^T as 16x16x32 B operands (k = token s = 32 kq + 8 lq + e, n = value row).
         bf16x8 VB[2], VBl[2];
         #pragma unroll
         for (int kq = 0; kq < 2; ++kq) {
-            VB[kq] = lds<bf16x8>(smem + OFF_VT, (i_row * P72 + 32 * kq + 8 * lq) * 2);
-            if constexpr (VSPLIT) VBl[kq] = lds<bf16x8>(smem + OFF_VTL, (i_row * P72 + 32 * kq + 8 * lq) * 2);
+            VB[kq] = lds<bf16x8>(smem + OFF_VT, (16 * strip * P72 + 32 * kq) * 2 + op32);
+            if constexpr (VSPLIT) VBl[kq] = lds<bf16x8>(smem + OFF_VTL, (16 * strip * P72 + 32 * kq) * 2 + op32);
         }
         f32x4 RHS[4];
         #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-                const s16x4 A4 = lds<s16x4>(smem + OFF_AT, ((16 * tb + lr) * P72 + 16 * jt + 4 * lq) * 2);
-                acc = mfma16(A4, Sh[jt], acc);
-                acc = mfma16(A4, Sl[jt], acc);
+            for (int o2 = 0; o2 < 2; ++o2) {
+                #pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const s16x4 A4 = lds<s16x4>(smem + OFF_AT, (16 * tb * P72 + 16 * jtile[o2][u]) * 2 + op16);
+                    acc = mfma16(A4, Sh[o2][u], acc);
+                    acc = mfma16(A4, Sl[o2][u], acc);
+                }
             }
             #pragma unroll
             for (int kq = 0; kq <= tb / 2; ++kq) {
-                const int o = ((16 * tb + lr) * P72 + 32 * kq + 8 * lq) * 2;
+                const int o = (16 * tb * P72 + 32 * kq) * 2 + op32;
                 const bf16x8 Ah8 = lds<bf16x8>(smem + OFF_AKH, o);
                 acc = mfma32(Ah8, VB[kq], acc);
                 acc = mfma32(lds<bf16x8>(smem + OFF_AKL, o), VB[kq], acc);
@@ -467,14 +496,13 @@ void chunked_kernel(ChunkArgs g) {
         }
 
         // ---------------- P5: SA = (I - A_ab)^-1 RHS, blocked forward substitution ----------------
-        f32x4 SA[4];
         s16x4 SAh[4], SAl[4];
         #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {
             f32x4 x = RHS[ib];
             #pragma unroll
             for (int jb = 0; jb < ib; ++jb) {
-                const s16x4 A4 = lds<s16x4>(smem + OFF_AAB, ((16 * ib + lr) * P72 + 16 * jb + 4 * lq) * 2);
+                const s16x4 A4 = lds<s16x4>(smem + OFF_AAB, (16 * ib * P72 + 16 * jb) * 2 + op16);
                 x = mfma16(A4, SAh[jb], x);
                 x = mfma16(A4, SAl[jb], x);
             }
@@ -484,40 +512,50 @@ void chunked_kernel(ChunkArgs g) {
             f32x4 sa = {0.f, 0.f, 0.f, 0.f};
             sa = mfma16(D4, xh, sa);
             sa = mfma16(D4, xl, sa);
-            SA[ib] = sa;
             to_operand(sa, SAh[ib], SAl[ib]);
         }
 
-        // ---------------- P6: Y = Rt S0^T + A_rb SA + A_rk V ----------------
+        // Next chunk's inputs: in flight during P6, P7 and the start of the next chunk.
+        if (ch + 1 < nchunks) load_chunk(c0 + L);
+
+        // ---------------- P6: Y = Rt S0^T + A_rb SA + A_rk V, token tiles 2 hf, 2 hf + 1 ----------------
         #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
+        for (int u = 0; u < 2; ++u) {
+            const int tb = 2 * hf + u;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-                const int o = ((16 * tb + lr) * P72 + 16 * jt + 4 * lq) * 2;
-                const s16x4 Rh4 = lds<s16x4>(smem + OFF_RTH, o);
-                const s16x4 Rl4 = lds<s16x4>(smem + OFF_RTL, o);
-                acc = mfma16(Rh4, Sh[jt], acc);
-                acc = mfma16(Rh4, Sl[jt], acc);
-                acc = mfma16(Rl4, Sh[jt], acc);
+            for (int o2 = 0; o2 < 2; ++o2) {
+                #pragma unroll
+                for (int uu = 0; uu < 2; ++uu) {
+                    const int o = (16 * tb * P72 + 16 * jtile[o2][uu]) * 2 + op16;
+                    const s16x4 Rh4 = lds<s16x4>(smem + OFF_RTH, o);
+                    const s16x4 Rl4 = lds<s16x4>(smem + OFF_RTL, o);
+                    acc = mfma16(Rh4, Sh[o2][uu], acc);
+                    acc = mfma16(Rh4, Sl[o2][uu], acc);
+                    acc = mfma16(Rl4, Sh[o2][uu], acc);
+                }
             }
             #pragma unroll
-            for (int sb = 0; sb <= tb; ++sb) {
-                const s16x4 A4 = lds<s16x4>(smem + OFF_ARB, ((16 * tb + lr) * P72 + 16 * sb + 4 * lq) * 2);
-                acc = mfma16(A4, SAh[sb], acc);
-                acc = mfma16(A4, SAl[sb], acc);
+            for (int sb = 0; sb < 4; ++sb) {
+                if (sb <= tb) {
+                    const s16x4 A4 = lds<s16x4>(smem + OFF_ARB, (16 * tb * P72 + 16 * sb) * 2 + op16);
+                    acc = mfma16(A4, SAh[sb], acc);
+                    acc = mfma16(A4, SAl[sb], acc);
+                }
             }
             #pragma unroll
-            for (int kq = 0; kq <= tb / 2; ++kq) {
-                const int o = ((16 * tb + lr) * P72 + 32 * kq + 8 * lq) * 2;
-                const bf16x8 Rh8 = lds<bf16x8>(smem + OFF_RKH, o);
-                acc = mfma32(Rh8, VB[kq], acc);
-                acc = mfma32(lds<bf16x8>(smem + OFF_RKL, o), VB[kq], acc);
-                if constexpr (VSPLIT) acc = mfma32(Rh8, VBl[kq], acc);
+            for (int kq = 0; kq < 2; ++kq) {
+                if (kq <= tb / 2) {
+                    const int o = (16 * tb * P72 + 32 * kq) * 2 + op32;
+                    const bf16x8 Rh8 = lds<bf16x8>(smem + OFF_RKH, o);
+                    acc = mfma32(Rh8, VB[kq], acc);
+                    acc = mfma32(lds<bf16x8>(smem + OFF_RKL, o), VB[kq], acc);
+                    if constexpr (VSPLIT) acc = mfma32(Rh8, VBl[kq], acc);
+                }
             }
             // acc[r] = Y[t = 16 tb + 4 lq + r][i_row]
             const int tl0 = 16 * tb + 4 * lq;
-            float vtr[4], bon[4];
+            float vtr[4] = {0.f, 0.f, 0.f, 0.f}, bon[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (EPI) {
                 const uint2 vraw = lds<uint2>(smem + OFF_VT, (i_row * P72 + tl0) * 2);
                 vtr[0] = lo_f32(vraw.x); vtr[1] = hi_f32(vraw.x); vtr[2] = lo_f32(vraw.y); vtr[3] = hi_f32(vraw.y);
@@ -537,38 +575,37 @@ void chunked_kernel(ChunkArgs g) {
             }
         }
 
-        // ---------------- P7: S_L^T = 2^g_L S0^T + Bh^T SA + Kh^T V ----------------
+        // ---------------- P7: S_L^T = 2^g_L S0^T + Bh^T SA + Kh^T V, key tiles 2 hf, 2 hf + 1 ----------------
         #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            const float4 gl4 = lds<float4>(smem + OFF_GL, (16 * jt + 4 * lq) * 4);
-            f32x4 acc = ST[jt];
-            acc[0] *= __builtin_amdgcn_exp2f(gl4.x);
-            acc[1] *= __builtin_amdgcn_exp2f(gl4.y);
-            acc[2] *= __builtin_amdgcn_exp2f(gl4.z);
-            acc[3] *= __builtin_amdgcn_exp2f(gl4.w);
+        for (int u = 0; u < 2; ++u) {
+            const int jt = 2 * hf + u;
+            const float4 el4 = lds<float4>(smem + OFF_EL, (16 * jt + 4 * lq) * 4);
+            f32x4 acc = ST[u];
+            acc[0] *= el4.x; acc[1] *= el4.y; acc[2] *= el4.z; acc[3] *= el4.w;
             #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                const s16x4 B4 = lds<s16x4>(smem + OFF_BHT, ((16 * jt + lr) * P72 + 16 * tb + 4 * lq) * 2);
+                const s16x4 B4 = lds<s16x4>(smem + OFF_BHT, (16 * jt * P72 + 16 * tb) * 2 + op16);
                 acc = mfma16(B4, SAh[tb], acc);
                 acc = mfma16(B4, SAl[tb], acc);
             }
             #pragma unroll
             for (int kq = 0; kq < 2; ++kq) {
-                const int o = ((16 * jt + lr) * P72 + 32 * kq + 8 * lq) * 2;
+                const int o = (16 * jt * P72 + 32 * kq) * 2 + op32;
                 const bf16x8 Kh8 = lds<bf16x8>(smem + OFF_KHTH, o);
                 acc = mfma32(Kh8, VB[kq], acc);
                 acc = mfma32(lds<bf16x8>(smem + OFF_KHTL, o), VB[kq], acc);
                 if constexpr (VSPLIT) acc = mfma32(Kh8, VBl[kq], acc);
             }
-            ST[jt] = acc;
+            ST[u] = acc;
         }
         __syncthreads();   // all LDS operands of this chunk consumed before P1 rewrites them
     }
 
     if (g.s1) {
         #pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-            *reinterpret_cast<float4*>(g.s1 + sbase + 16 * jt + 4 * lq) = make_float4(ST[jt][0], ST[jt][1], ST[jt][2], ST[jt][3]);
+        for (int u = 0; u < 2; ++u)
+            *reinterpret_cast<float4*>(g.s1 + sbase + 16 * (2 * hf + u) + 4 * lq) =
+                make_float4(ST[u][0], ST[u][1], ST[u][2], ST[u][3]);
     }
 }
 
