@@ -448,9 +448,9 @@ void chunked_kernel(ChunkArgs g) {
                 sts<uint16_t>(smem + OFF_DINV, ((w * 16 + t) * PD + c) * 2,
                               __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[t])));
         }
-        __syncthreads();
+        // No barrier here: P4 does not read the inverses.
 
-        // ---------------- P4: RHS = At S0^T + A_ak V (whole strip, both halves) ----------------
+        // ---------------- P4: RHS = At S0^T + A_ak V (whole strip), Y's SA-free part ----------------
         // State operands of the whole strip: key tiles 2 hf + u from this wave's
         // registers (own), 2 (1 - hf) + u from the partner (other).  Register
         // arrays are indexed by compile-time u only; hf enters LDS addresses.
@@ -495,6 +495,38 @@ void chunked_kernel(ChunkArgs g) {
             RHS[tb] = acc;
         }
 
+        f32x4 Yacc[2];
+        #pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tb = 2 * hf + u;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            #pragma unroll
+            for (int o2 = 0; o2 < 2; ++o2) {
+                #pragma unroll
+                for (int uu = 0; uu < 2; ++uu) {
+                    const int o = (16 * tb * P72 + 16 * jtile[o2][uu]) * 2 + op16;
+                    const s16x4 Rh4 = lds<s16x4>(smem + OFF_RTH, o);
+                    const s16x4 Rl4 = lds<s16x4>(smem + OFF_RTL, o);
+                    acc = mfma16(Rh4, Sh[o2][uu], acc);
+                    acc = mfma16(Rh4, Sl[o2][uu], acc);
+                    acc = mfma16(Rl4, Sh[o2][uu], acc);
+                }
+            }
+            #pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                if (kq <= tb / 2) {
+                    const int o = (16 * tb * P72 + 32 * kq) * 2 + op32;
+                    const bf16x8 Rh8 = lds<bf16x8>(smem + OFF_RKH, o);
+                    acc = mfma32(Rh8, VB[kq], acc);
+                    acc = mfma32(lds<bf16x8>(smem + OFF_RKL, o), VB[kq], acc);
+                    if constexpr (VSPLIT) acc = mfma32(Rh8, VBl[kq], acc);
+                }
+            }
+            Yacc[u] = acc;
+        }
+
+        __syncthreads();   // inverses of the diagonal blocks published
+
         // ---------------- P5: SA = (I - A_ab)^-1 RHS, blocked forward substitution ----------------
         s16x4 SAh[4], SAl[4];
         #pragma unroll
@@ -518,39 +550,17 @@ void chunked_kernel(ChunkArgs g) {
         // Next chunk's inputs: in flight during P6, P7 and the start of the next chunk.
         if (ch + 1 < nchunks) load_chunk(c0 + L);
 
-        // ---------------- P6: Y = Rt S0^T + A_rb SA + A_rk V, token tiles 2 hf, 2 hf + 1 ----------------
+        // ---------------- P6: Y += A_rb SA on token tiles 2 hf, 2 hf + 1; epilogue; store ----------------
         #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int tb = 2 * hf + u;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            #pragma unroll
-            for (int o2 = 0; o2 < 2; ++o2) {
-                #pragma unroll
-                for (int uu = 0; uu < 2; ++uu) {
-                    const int o = (16 * tb * P72 + 16 * jtile[o2][uu]) * 2 + op16;
-                    const s16x4 Rh4 = lds<s16x4>(smem + OFF_RTH, o);
-                    const s16x4 Rl4 = lds<s16x4>(smem + OFF_RTL, o);
-                    acc = mfma16(Rh4, Sh[o2][uu], acc);
-                    acc = mfma16(Rh4, Sl[o2][uu], acc);
-                    acc = mfma16(Rl4, Sh[o2][uu], acc);
-                }
-            }
+            f32x4 acc = Yacc[u];
             #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
                 if (sb <= tb) {
                     const s16x4 A4 = lds<s16x4>(smem + OFF_ARB, (16 * tb * P72 + 16 * sb) * 2 + op16);
                     acc = mfma16(A4, SAh[sb], acc);
                     acc = mfma16(A4, SAl[sb], acc);
-                }
-            }
-            #pragma unroll
-            for (int kq = 0; kq < 2; ++kq) {
-                if (kq <= tb / 2) {
-                    const int o = (16 * tb * P72 + 32 * kq) * 2 + op32;
-                    const bf16x8 Rh8 = lds<bf16x8>(smem + OFF_RKH, o);
-                    acc = mfma32(Rh8, VB[kq], acc);
-                    acc = mfma32(lds<bf16x8>(smem + OFF_RKL, o), VB[kq], acc);
-                    if constexpr (VSPLIT) acc = mfma32(Rh8, VBl[kq], acc);
                 }
             }
             // acc[r] = Y[t = 16 tb + 4 lq + r][i_row]
