@@ -13,29 +13,39 @@
 //   Y   = Rt S0^T + A_rb SA + A_rk V              Rt_t = r_t 2^(g_t)
 //   S_L = S0 diag(2^g_L) + SA^T Bh + V^T Kh       Bh_s = b_s 2^(g_L - g_s), Kh likewise
 //
-// All matrix products run on v_mfma_f32_16x16x{16,32}_bf16.  Operands that
-// decide the result to within the tolerance are split into bf16 hi + lo parts
+// All matrix products run on v_mfma_f32_16x16x32_bf16.  Operands that decide
+// the result to within the tolerance are split into bf16 hi + lo parts
 // (x = hi + lo to ~16 mantissa bits) and multiplied term by term: the scaled r
 // and k that form A_rk / A_rb, A_rk and A_ak themselves, the state in its
 // products, K-hat, the removal projections RHS / SA, and v itself when the
 // inputs are fp32 (bf16 inputs are exact as bf16).  The state itself is
 // carried in fp32 registers and its decay 2^g_L is applied elementwise.
 //
-// Mapping: one 256-thread workgroup per (b, h); wave w owns value rows
-// i in [16w, 16w+16).  Everything that depends on the state -- RHS, the
-// blocked triangular solve for SA, Y and the new state -- stays in that
-// wave's registers: the fp32 C layout of a 16x16 MFMA result is exactly the B
-// operand layout of a 16x16x16 MFMA, and the state is kept transposed
-// (S^T tiles: lane = value row, registers = key columns) so that it is the B
-// operand of At S0^T and Rt S0^T directly.  Only quantities that do not
-// depend on the state (decay prefix, scaled operands, the four L x L
-// matrices, the inverses of the diagonal 16 x 16 blocks of I - A_ab) are
-// built cooperatively in LDS, with barriers between those phases.
+// Mapping: one 512-thread workgroup (8 waves) per (b, h).  Waves w and w + 4
+// share the value rows i in [16 (w mod 4), +16) ("strip"); each keeps half of
+// the strip's state in registers, transposed (S^T tiles: lane = value row,
+// registers = 4 consecutive key columns), which is exactly the C layout of a
+// 16x16 MFMA result and the B-operand layout of a 16-deep product.  Two such
+// 16-deep products are fused into one 32-deep MFMA: the matrices that are
+// multiplied against register-resident operands (At, Rt, Bt, Kt along the key
+// axis; A_ab, A_rb, Bh^T along the token axis) are stored in LDS with that
+// axis interleaved in pairs of 16-blocks (position 32 p + 8 q + 4 e + r holds
+// index 16 (2 p + e) + 4 q + r), so one 16-byte read gives the A operand of a
+// pair.  A single 16-deep product against a split operand x = hi + lo is fused
+// the same way: A = [a, a], B = [hi, lo].  The halves of the strip's state are
+// exchanged once per chunk through LDS.  Only quantities that do not depend
+// on the state (decay prefix, scaled operands, the four L x L matrices, the
+// inverses of the diagonal 16 x 16 blocks of I - A_ab) are built
+// cooperatively, with barriers between those phases.
+//
+// Global memory is read and written through buffer descriptors that cover
+// the valid tokens of one chunk of one sequence: tokens past the end read as
+// zero (identity tokens: a = b = k = v = r = 0; w is set to 1 explicitly) and
+// their y stores are dropped by the range check.
 //
 // Domain: the per-column decay product over one chunk must stay above 2^-126
 // (2^(-g) is formed explicitly); the hxa07D decay parameterisation keeps
-// w >= exp(-exp(-0.5)) = 0.545, i.e. |g_L| <= 56.  A ragged last chunk is
-// padded with identity tokens (w = 1, a = b = k = v = r = 0).
+// w >= exp(-exp(-0.5)) = 0.545, i.e. |g_L| <= 56.
 #include "wkv7_internal.h"
 #include "wkv7_device.h"
 
@@ -43,8 +53,10 @@ namespace wkv7 {
 namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int L = 64;          // chunk length
 constexpr int DH = 64;         // head size handled by this kernel
@@ -57,6 +69,8 @@ constexpr int PE = 68;         // fp32 pitch of the decay tables
 // LDS map (bytes).  Region 1 holds B~, K~ during P1..P2 and A_ab, A_rb and the
 // fp32 diagonal blocks of A_ab afterwards; region 2 holds the decay tables
 // 2^g, 2^-g and the column-segment totals during P1 and A_ak, A_rk afterwards.
+// Pair-interleaved axis (see above): At, Rt, Bt, Kt (key axis), A_ab, A_rb,
+// Bh^T (token axis).  Natural order: A_ak, A_rk, Kh^T, V^T.
 constexpr int OFF_AT = 0;
 constexpr int OFF_RTH = OFF_AT + MAT;
 constexpr int OFF_RTL = OFF_RTH + MAT;
@@ -70,7 +84,7 @@ constexpr int OFF_KTH = OFF_R1 + MAT;      // K~ [s][j] hi / lo
 constexpr int OFF_KTL = OFF_R1 + 2 * MAT;
 constexpr int OFF_AAB = OFF_R1;            // A_ab [t][s] bf16
 constexpr int OFF_ARB = OFF_R1 + MAT;      // A_rb [t][s] bf16
-constexpr int OFF_ADIAG = OFF_R1 + 2 * MAT;  // fp32 [4][16][PD] diagonal blocks of A_ab
+constexpr int OFF_ADIAG = OFF_R1 + 2 * MAT;  // fp32 [4][s][t] (pitch PD) diagonal blocks of A_ab, transposed
 constexpr int OFF_R2 = OFF_R1 + 3 * MAT;
 constexpr int OFF_E = OFF_R2;              // fp32 [64][PE] 2^g
 constexpr int OFF_EI = OFF_R2 + 64 * PE * 4;   // fp32 [64][PE] 2^-g
@@ -83,13 +97,20 @@ constexpr int OFF_DINV = OFF_R2 + 4 * MAT;   // bf16 [4][16][PD] inverses of dia
 constexpr int OFF_EL = OFF_DINV + 4 * 16 * PD * 2;   // fp32 [64] 2^g_L
 constexpr int OFF_BONUS = OFF_EL + 256;    // fp32 [64] hxa07D bonus coefficient per token
 constexpr int OFF_XS = OFF_BONUS + 256;    // state halves exchanged by the two waves of a strip
-constexpr int XS_BYTES = 4 * 4 * 2 * 64 * 8;
+constexpr int XS_BYTES = 4 * 2 * 2 * 64 * 16;   // [strip][half][hi/lo][lane] 16 B
 constexpr int OFF_VTL = OFF_XS + XS_BYTES; // V^T lo part (fp32 inputs only)
 constexpr int SMEM_BF16 = OFF_VTL;
 constexpr int SMEM_F32 = OFF_VTL + MAT;
 static_assert(4 * 16 * PD * 4 <= MAT, "diagonal blocks fit");
 static_assert(2 * 64 * PE * 4 + 8 * 64 * 4 <= 4 * MAT, "decay tables fit");
 static_assert(SMEM_F32 <= 160 * 1024, "LDS budget");
+
+// Position of index k (0..63) on a pair-interleaved axis.
+__host__ __device__ constexpr int pairpos(int k) {
+    return 32 * (k >> 5) + 8 * ((k >> 2) & 3) + 4 * ((k >> 4) & 1) + (k & 3);
+}
+static_assert(pairpos(0) == 0 && pairpos(16) == 4 && pairpos(4) == 8 && pairpos(20) == 12 && pairpos(35) == 35 &&
+              pairpos(51) == 39 && pairpos(63) == 63, "pair interleave");
 
 struct ChunkArgs {
     const void *r, *w, *k, *v, *a, *b;
@@ -101,11 +122,11 @@ struct ChunkArgs {
     float y_scale;
 };
 
-__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 cat(s16x4 a, s16x4 b) {
+    return __builtin_bit_cast(bf16x8, s16x8(__builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7)));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
@@ -121,7 +142,7 @@ __device__ __forceinline__ void split2(float x, float y, uint32_t& hi, uint32_t&
     lo = pack_bf16(x - lo_f32(hi), y - hi_f32(hi));
 }
 
-// C-layout fp32 tile (4 consecutive k) -> 16x16x16 B operand, hi and lo parts.
+// C-layout fp32 tile (4 consecutive k) -> 16-deep B operand, hi and lo parts.
 __device__ __forceinline__ void to_operand(const f32x4 c, s16x4& hi, s16x4& lo) {
     uint32_t h0, l0, h1, l1;
     split2(c[0], c[1], h0, l0);
@@ -137,39 +158,71 @@ template <typename T> __device__ __forceinline__ void sts(char* base, int byte_o
     *reinterpret_cast<T*>(base + byte_off) = v;
 }
 
-// Loads below are unconditional, from addresses clamped into the tensor, so
-// that no control-flow join forces an early wait on them; tokens past the end
-// are masked where the values are used.
+// Raw buffer descriptor over [base, base + bytes); word 3 selects the 32-bit
+// data format that gfx9-family raw buffer accesses need.  Accesses at byte
+// offsets >= bytes read zero / are dropped.  Offsets are always passed in the
+// VGPR operand (soffset 0), which the range check covers.
+// The arguments are wave-uniform; reading them through readfirstlane keeps the
+// descriptor in SGPRs (a descriptor in VGPRs costs a waterfall loop per access).
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), 0, int(n), kRsrcWord3);
+}
+
+template <typename T> struct Buf;
+template <> struct Buf<bf16_t> {
+    // One element as fp32 bits.
+    static __device__ __forceinline__ uint32_t load1(rsrc_t r, uint32_t off) {
+        return uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0)) << 16;
+    }
+    static __device__ __forceinline__ void store1(rsrc_t r, uint32_t off, float x) {
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), r, off, 0, 0);
+    }
+};
+template <> struct Buf<float> {
+    static __device__ __forceinline__ uint32_t load1(rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    }
+    static __device__ __forceinline__ void store1(rsrc_t r, uint32_t off, float x) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+    }
+};
+
 // 8 consecutive elements of one token row, undecoded (row threads).
 template <typename Tin> struct Row8;
 template <> struct Row8<bf16_t> {
     uint4 x;
-    __device__ __forceinline__ void load(const bf16_t* p) { x = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
+        x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
     __device__ __forceinline__ float get(int e) const {
         const uint32_t d = e < 2 ? x.x : e < 4 ? x.y : e < 6 ? x.z : x.w;
         return (e & 1) ? __uint_as_float(d & 0xffff0000u) : __uint_as_float(d << 16);
     }
 };
 template <> struct Row8<float> {
-    float4 x[2];
-    __device__ __forceinline__ void load(const float* p) {
-        x[0] = reinterpret_cast<const float4*>(p)[0];
-        x[1] = reinterpret_cast<const float4*>(p)[1];
+    uint4 x[2];
+    __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
+        x[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        x[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
     }
     __device__ __forceinline__ float get(int e) const {
-        const float4& u = x[e >> 2];
-        return (e & 3) == 0 ? u.x : (e & 3) == 1 ? u.y : (e & 3) == 2 ? u.z : u.w;
+        const uint4& u = x[e >> 2];
+        return __uint_as_float((e & 3) == 0 ? u.x : (e & 3) == 1 ? u.y : (e & 3) == 2 ? u.z : u.w);
     }
 };
 
-// One element of a column (column threads), as fp32 bits.
-__device__ __forceinline__ uint32_t ld_raw(const bf16_t* p) { return uint32_t(*p) << 16; }
-__device__ __forceinline__ uint32_t ld_raw(const float* p) { return __float_as_uint(*p); }
+template <int V> struct IC { static constexpr int value = V; };
 
 template <typename Tin, typename Ty, bool LOGW, bool EPI>
 __global__ __launch_bounds__(NTHR)
 void chunked_kernel(ChunkArgs g) {
     constexpr bool VSPLIT = sizeof(Tin) == 4;   // fp32 v is not exact in bf16
+    constexpr uint32_t SI = sizeof(Tin), SY = sizeof(Ty);
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, known wave-uniform
@@ -179,16 +232,16 @@ void chunked_kernel(ChunkArgs g) {
     const int bh = blockIdx.x;
     const int bb = bh / H, h = bh - bb * H;
     const int hk = h / (H / g.H_kv);
-    const int64_t step_q = int64_t(H) * DH, step_kv = int64_t(g.H_kv) * DH;
-    const int64_t base_q = (int64_t(bb) * T * H + h) * DH;
-    const int64_t base_kv = (int64_t(bb) * T * g.H_kv + hk) * DH;
-    const Tin* rp = static_cast<const Tin*>(g.r);
-    const Tin* wp = static_cast<const Tin*>(g.w);
-    const Tin* kp = static_cast<const Tin*>(g.k);
-    const Tin* vp = static_cast<const Tin*>(g.v);
-    const Tin* ap = static_cast<const Tin*>(g.a);
-    const Tin* bp = static_cast<const Tin*>(g.b);
-    Ty* yp = static_cast<Ty*>(g.y);
+    // Bytes per token of the [B, T, H(_kv), D] tensors, and the first token of this sequence.
+    const uint32_t stq = uint32_t(H) * DH * SI, stkv = uint32_t(g.H_kv) * DH * SI, sty = uint32_t(H) * DH * SY;
+    const int64_t tok0 = int64_t(bb) * T;
+    const char* rp = static_cast<const char*>(g.r);
+    const char* wp = static_cast<const char*>(g.w);
+    const char* kp = static_cast<const char*>(g.k);
+    const char* vp = static_cast<const char*>(g.v);
+    const char* ap = static_cast<const char*>(g.a);
+    const char* bp = static_cast<const char*>(g.b);
+    char* yp = static_cast<char*>(g.y);
 
     // This wave's half of its strip's state, transposed:
     // ST[u][r] = S[i = 16 strip + lr][j = 16 (2 hf + u) + 4 lq + r].
@@ -215,41 +268,60 @@ void chunked_kernel(ChunkArgs g) {
         #pragma unroll
         for (int e = 0; e < 8; ++e) rk8[e] = g.r_k[h * DH + 8 * qr + e];
     }
+    // Chunk-relative byte offsets (the descriptors move with the chunk).
+    const uint32_t col_q = uint32_t(8 * pc) * stq + uint32_t(h * DH + jc) * SI;
+    const uint32_t col_kv = uint32_t(8 * pc) * stkv + uint32_t(hk * DH + jc) * SI;
+    const uint32_t row_q = uint32_t(tr) * stq + uint32_t(h * DH + 8 * qr) * SI;
+    const uint32_t row_kv = uint32_t(tr) * stkv + uint32_t(hk * DH + 8 * qr) * SI;
+    const uint32_t y_lane = uint32_t(4 * lq) * sty + uint32_t(h * DH + i_row) * SY;
+
     uint32_t cw[8], cb[8], ck[8], cv[8];
     Row8<Tin> rr, ra, rb, rkv;
     auto load_chunk = [&](int c0) {
+        // Valid tokens of the chunk (0 past the end: every load reads zero).
+        const int nv = max(0, min(T - c0, L));
+        const int64_t t0 = nv > 0 ? tok0 + c0 : 0;
+        const rsrc_t Rr = make_rsrc(rp + t0 * stq, uint32_t(nv) * stq);
+        const rsrc_t Rw = make_rsrc(wp + t0 * stq, uint32_t(nv) * stq);
+        const rsrc_t Ra = make_rsrc(ap + t0 * stq, uint32_t(nv) * stq);
+        const rsrc_t Rb = make_rsrc(bp + t0 * stq, uint32_t(nv) * stq);
+        const rsrc_t Rk = make_rsrc(kp + t0 * stkv, uint32_t(nv) * stkv);
+        const rsrc_t Rv = make_rsrc(vp + t0 * stkv, uint32_t(nv) * stkv);
         #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int tt = min(c0 + 8 * pc + e, T - 1);
-            cw[e] = ld_raw(wp + base_q + tt * step_q + jc);
-            cb[e] = ld_raw(bp + base_q + tt * step_q + jc);
-            ck[e] = ld_raw(kp + base_kv + tt * step_kv + jc);
-            cv[e] = ld_raw(vp + base_kv + tt * step_kv + jc);
+            cw[e] = Buf<Tin>::load1(Rw, col_q + uint32_t(e) * stq);
+            cb[e] = Buf<Tin>::load1(Rb, col_q + uint32_t(e) * stq);
+            ck[e] = Buf<Tin>::load1(Rk, col_kv + uint32_t(e) * stkv);
+            cv[e] = Buf<Tin>::load1(Rv, col_kv + uint32_t(e) * stkv);
         }
-        const int tt = min(c0 + tr, T - 1);
-        rr.load(rp + base_q + tt * step_q + 8 * qr);
-        ra.load(ap + base_q + tt * step_q + 8 * qr);
-        rb.load(bp + base_q + tt * step_q + 8 * qr);
-        rkv.load(kp + base_kv + tt * step_kv + 8 * qr);
+        rr.load(Rr, row_q);
+        ra.load(Ra, row_q);
+        rb.load(Rb, row_q);
+        rkv.load(Rk, row_kv);
     };
     load_chunk(0);
 
-    // Lane offsets of the MFMA operand patterns inside a 64 x 64 bf16 matrix.
-    const int op16 = (lr * P72 + 4 * lq) * 2;    // 16x16x16 operand: row lr, k = 4 lq .. 4 lq + 3
-    const int op32 = (lr * P72 + 8 * lq) * 2;    // 16x16x32 operand: row lr, k = 8 lq .. 8 lq + 7
-    const int xs_own = ((strip * 4 + 2 * hf) * 2 * 64 + l) * 8;
-    const int xs_oth = ((strip * 4 + 2 * (1 - hf)) * 2 * 64 + l) * 8;
+    // Lane offset of the 32-deep operand pattern inside a 64 x 64 bf16 matrix:
+    // row lr, k = 8 lq .. 8 lq + 7.
+    const int op32 = (lr * P72 + 8 * lq) * 2;
+    // 16-deep operand of 16-block jb on a pair-interleaved axis: row lr, 4 elements.
+    auto op_single = [&](int row0, int jb) { return ((row0 + lr) * P72 + 32 * (jb >> 1) + 8 * lq + 4 * (jb & 1)) * 2; };
+    const int xs_own = ((strip * 2 + hf) * 2 * 64 + l) * 16;
+    const int xs_oth = ((strip * 2 + (1 - hf)) * 2 * 64 + l) * 16;
 
     const int nchunks = (T + L - 1) / L;
     for (int ch = 0; ch < nchunks; ++ch) {
         const int c0 = ch * L;
-        // Publish this wave's state half (bf16 hi / lo B operands) for its partner.
-        #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            s16x4 sh, sl;
-            to_operand(ST[u], sh, sl);
-            sts<s16x4>(smem + OFF_XS, xs_own + (u * 2 + 0) * 64 * 8, sh);
-            sts<s16x4>(smem + OFF_XS, xs_own + (u * 2 + 1) * 64 * 8, sl);
+        // Own state half as the B operand of the key pair hf (hi / lo); published for the partner.
+        bf16x8 SoH, SoL;
+        {
+            s16x4 h0, l0, h1, l1;
+            to_operand(ST[0], h0, l0);
+            to_operand(ST[1], h1, l1);
+            SoH = cat(h0, h1);
+            SoL = cat(l0, l1);
+            sts<bf16x8>(smem + OFF_XS, xs_own, SoH);
+            sts<bf16x8>(smem + OFF_XS, xs_own + 64 * 16, SoL);
         }
 
         // ---------------- P1a: decay prefix down each key column ----------------
@@ -259,10 +331,9 @@ void chunked_kernel(ChunkArgs g) {
             #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float x = __uint_as_float(cw[e]);
-                const bool ok = c0 + 8 * pc + e < T;
-                const float lw = !ok ? 0.f : LOGW ? -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e
-                                                  : __builtin_amdgcn_logf(x);
-                run += lw;
+                const bool ok = c0 + 8 * pc + e < T;     // wave-uniform; w = 1 past the end
+                const float lw = LOGW ? -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e : __builtin_amdgcn_logf(x);
+                run += ok ? lw : 0.f;
                 pre[e] = run;
             }
             sts<float>(smem + OFF_TOT, (pc * 64 + jc) * 4, run);
@@ -291,21 +362,25 @@ void chunked_kernel(ChunkArgs g) {
                     sts<float>(smem + OFF_EI, ((8 * pc + e + u) * PE + jc) * 4, Ei);
                     Eh[u] = EL * Ei;
                 }
-                // Tokens past the end are identity tokens: b = k = v = 0.
-                const bool ok0 = c0 + 8 * pc + e < T, ok1 = c0 + 8 * pc + e + 1 < T;
-                const float b0 = ok0 ? __uint_as_float(cb[e]) : 0.f, b1 = ok1 ? __uint_as_float(cb[e + 1]) : 0.f;
-                const float k0 = ok0 ? __uint_as_float(ck[e]) : 0.f, k1 = ok1 ? __uint_as_float(ck[e + 1]) : 0.f;
-                const float v0 = ok0 ? __uint_as_float(cv[e]) : 0.f, v1 = ok1 ? __uint_as_float(cv[e + 1]) : 0.f;
+                const float b0 = __uint_as_float(cb[e]), b1 = __uint_as_float(cb[e + 1]);
+                const float k0 = __uint_as_float(ck[e]), k1 = __uint_as_float(ck[e + 1]);
                 bh4[e / 2] = pack_bf16(b0 * Eh[0], b1 * Eh[1]);
                 split2(k0 * Eh[0], k1 * Eh[1], khh[e / 2], khl[e / 2]);
-                split2(v0, v1, vh[e / 2], vl[e / 2]);
+                if constexpr (VSPLIT) {
+                    split2(__uint_as_float(cv[e]), __uint_as_float(cv[e + 1]), vh[e / 2], vl[e / 2]);
+                } else {
+                    vh[e / 2] = (cv[e] >> 16) | (cv[e + 1] & 0xffff0000u);   // bf16 bits as they are
+                }
             }
             const int o = (jc * P72 + 8 * pc) * 2;
-            sts<uint4>(smem + OFF_BHT, o, make_uint4(bh4[0], bh4[1], bh4[2], bh4[3]));
             sts<uint4>(smem + OFF_KHTH, o, make_uint4(khh[0], khh[1], khh[2], khh[3]));
             sts<uint4>(smem + OFF_KHTL, o, make_uint4(khl[0], khl[1], khl[2], khl[3]));
             sts<uint4>(smem + OFF_VT, o, make_uint4(vh[0], vh[1], vh[2], vh[3]));
             if constexpr (VSPLIT) sts<uint4>(smem + OFF_VTL, o, make_uint4(vl[0], vl[1], vl[2], vl[3]));
+            // Bh^T on the pair-interleaved token axis: tokens 8 pc + (0..3) and 8 pc + (4..7).
+            const int ob = (jc * P72 + pairpos(8 * pc)) * 2;
+            sts<uint2>(smem + OFF_BHT, ob, make_uint2(bh4[0], bh4[1]));
+            sts<uint2>(smem + OFF_BHT, ob + 16, make_uint2(bh4[2], bh4[3]));
         }
         __syncthreads();
 
@@ -326,24 +401,30 @@ void chunked_kernel(ChunkArgs g) {
             }
             uint32_t at[4], rth[4], rtl[4], bt[4], kth[4], ktl[4];
             float bonus_part = 0.f;
-            const float okm = c0 + tr < T ? 1.f : 0.f;   // identity token past the end
             #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const float r0 = okm * rr.get(e), r1 = okm * rr.get(e + 1);
-                const float k0 = okm * rkv.get(e), k1 = okm * rkv.get(e + 1);
-                at[e / 2] = pack_bf16(okm * ra.get(e) * Ep[e], okm * ra.get(e + 1) * Ep[e + 1]);
+                const float r0 = rr.get(e), r1 = rr.get(e + 1);
+                const float k0 = rkv.get(e), k1 = rkv.get(e + 1);
+                at[e / 2] = pack_bf16(ra.get(e) * Ep[e], ra.get(e + 1) * Ep[e + 1]);
                 split2(r0 * E[e], r1 * E[e + 1], rth[e / 2], rtl[e / 2]);
-                bt[e / 2] = pack_bf16(okm * rb.get(e) * Ei[e], okm * rb.get(e + 1) * Ei[e + 1]);
+                bt[e / 2] = pack_bf16(rb.get(e) * Ei[e], rb.get(e + 1) * Ei[e + 1]);
                 split2(k0 * Ei[e], k1 * Ei[e + 1], kth[e / 2], ktl[e / 2]);
                 if constexpr (EPI) bonus_part += r0 * k0 * rk8[e] + r1 * k1 * rk8[e + 1];
             }
-            const int o = (tr * P72 + 8 * qr) * 2;
-            sts<uint4>(smem + OFF_AT, o, make_uint4(at[0], at[1], at[2], at[3]));
-            sts<uint4>(smem + OFF_RTH, o, make_uint4(rth[0], rth[1], rth[2], rth[3]));
-            sts<uint4>(smem + OFF_RTL, o, make_uint4(rtl[0], rtl[1], rtl[2], rtl[3]));
-            sts<uint4>(smem + OFF_BT, o, make_uint4(bt[0], bt[1], bt[2], bt[3]));
-            sts<uint4>(smem + OFF_KTH, o, make_uint4(kth[0], kth[1], kth[2], kth[3]));
-            sts<uint4>(smem + OFF_KTL, o, make_uint4(ktl[0], ktl[1], ktl[2], ktl[3]));
+            // Pair-interleaved key axis: columns 8 qr + (0..3) and 8 qr + (4..7).
+            const int o = (tr * P72 + pairpos(8 * qr)) * 2;
+            sts<uint2>(smem + OFF_AT, o, make_uint2(at[0], at[1]));
+            sts<uint2>(smem + OFF_AT, o + 16, make_uint2(at[2], at[3]));
+            sts<uint2>(smem + OFF_RTH, o, make_uint2(rth[0], rth[1]));
+            sts<uint2>(smem + OFF_RTH, o + 16, make_uint2(rth[2], rth[3]));
+            sts<uint2>(smem + OFF_RTL, o, make_uint2(rtl[0], rtl[1]));
+            sts<uint2>(smem + OFF_RTL, o + 16, make_uint2(rtl[2], rtl[3]));
+            sts<uint2>(smem + OFF_BT, o, make_uint2(bt[0], bt[1]));
+            sts<uint2>(smem + OFF_BT, o + 16, make_uint2(bt[2], bt[3]));
+            sts<uint2>(smem + OFF_KTH, o, make_uint2(kth[0], kth[1]));
+            sts<uint2>(smem + OFF_KTH, o + 16, make_uint2(kth[2], kth[3]));
+            sts<uint2>(smem + OFF_KTL, o, make_uint2(ktl[0], ktl[1]));
+            sts<uint2>(smem + OFF_KTL, o + 16, make_uint2(ktl[2], ktl[3]));
             if constexpr (EPI) {
                 // The eight threads of a token row are lanes 8m .. 8m + 7 of one wave.
                 bonus_part += dpp<kDppQuadXor1>(bonus_part);
@@ -399,49 +480,62 @@ void chunked_kernel(ChunkArgs g) {
             if (id < 10) {
                 const int tb = id >= 6 ? 3 : id >= 3 ? 2 : id >= 1 ? 1 : 0;
                 const int sb = id - (tb * (tb + 1)) / 2;
-                const int o = ((16 * tb + lr) * P72 + 16 * sb + 4 * lq) * 2;
                 f32x4 c0v = acc0[n], c1v = acc1[n];
                 if (tb == sb) {
                     // group 0 is strictly lower (s < t), group 1 lower with diagonal (s <= t).
+                    const int lim = lr + grp;
                     #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int sl = 4 * lq + r;
-                        if (grp == 0 ? sl >= lr : sl > lr) { c0v[r] = 0.f; c1v[r] = 0.f; }
+                        const bool z = 4 * lq + r >= lim;
+                        c0v[r] = z ? 0.f : c0v[r];
+                        c1v[r] = z ? 0.f : c1v[r];
                     }
-                    if (grp == 0)
-                        sts<float4>(smem + OFF_ADIAG, ((tb * 16 + lr) * PD + 4 * lq) * 4,
-                                    make_float4(c0v[0], c0v[1], c0v[2], c0v[3]));
+                    if (grp == 0) {
+                        // transposed: [block][s][t]
+                        #pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            sts<float>(smem + OFF_ADIAG, ((tb * 16 + 4 * lq + r) * PD + lr) * 4, c0v[r]);
+                    }
                 }
                 uint32_t h0, l0, h1, l1;
                 split2(c1v[0], c1v[1], h0, l0);
                 split2(c1v[2], c1v[3], h1, l1);
                 const uint2 c0p = make_uint2(pack_bf16(c0v[0], c0v[1]), pack_bf16(c0v[2], c0v[3]));
-                sts<uint2>(smem + (grp == 0 ? OFF_AAB : OFF_ARB), o, c0p);
+                const int orow = (16 * tb + lr) * P72;
+                sts<uint2>(smem + (grp == 0 ? OFF_AAB : OFF_ARB), (orow + pairpos(16 * sb + 4 * lq)) * 2, c0p);
+                const int o = (orow + 16 * sb + 4 * lq) * 2;
                 sts<uint2>(smem + (grp == 0 ? OFF_AKH : OFF_RKH), o, make_uint2(h0, h1));
                 sts<uint2>(smem + (grp == 0 ? OFF_AKL : OFF_RKL), o, make_uint2(l0, l1));
             }
         }
         if (tid < 256) {
             // Zero the upper tiles (t-block 0, s-block 1) and (2, 3) of A_ak and A_rk,
-            // which the 32-deep products of P4/P6 read.
+            // which the 32-deep products of P4 read.
             const int mat = tid >> 6, m = (tid >> 5) & 1, rw = (tid & 31) >> 1, half = tid & 1;
-            const int offs[4] = {OFF_AKH, OFF_AKL, OFF_RKH, OFF_RKL};
+            const int base = mat == 0 ? OFF_AKH : mat == 1 ? OFF_AKL : mat == 2 ? OFF_RKH : OFF_RKL;
             const int tb = m ? 2 : 0, sb = tb + 1;
-            sts<uint4>(smem + offs[mat], ((16 * tb + rw) * P72 + 16 * sb + 8 * half) * 2, make_uint4(0, 0, 0, 0));
+            sts<uint4>(smem + base, ((16 * tb + rw) * P72 + 16 * sb + 8 * half) * 2, make_uint4(0, 0, 0, 0));
         }
         __syncthreads();
 
         // ---------------- P3: inverses of the diagonal blocks of I - A_ab ----------------
+        // Column c of (I - A)^-1 by forward substitution, column-oriented: once x_s is
+        // final, x_t += A[t][s] x_s for every t > s.
         if (w < 4 && l < 16) {
             const int c = l;
             float x[16];
             #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                float acc = (t == c) ? 1.f : 0.f;
+            for (int t = 0; t < 16; ++t) x[t] = (t == c) ? 1.f : 0.f;
+            #pragma unroll
+            for (int s = 0; s < 15; ++s) {
+                float a[16];
                 #pragma unroll
-                for (int s2 = 0; s2 < t; ++s2)
-                    acc = fmaf(lds<float>(smem + OFF_ADIAG, ((w * 16 + t) * PD + s2) * 4), x[s2], acc);
-                x[t] = acc;
+                for (int q = (s + 1) >> 2; q < 4; ++q) {
+                    const float4 v4 = lds<float4>(smem + OFF_ADIAG, ((w * 16 + s) * PD + 4 * q) * 4);
+                    a[4 * q] = v4.x; a[4 * q + 1] = v4.y; a[4 * q + 2] = v4.z; a[4 * q + 3] = v4.w;
+                }
+                #pragma unroll
+                for (int t = s + 1; t < 16; ++t) x[t] = fmaf(a[t], x[s], x[t]);
             }
             #pragma unroll
             for (int t = 0; t < 16; ++t)
@@ -451,20 +545,11 @@ void chunked_kernel(ChunkArgs g) {
         // No barrier here: P4 does not read the inverses.
 
         // ---------------- P4: RHS = At S0^T + A_ak V (whole strip), Y's SA-free part ----------------
-        // State operands of the whole strip: key tiles 2 hf + u from this wave's
-        // registers (own), 2 (1 - hf) + u from the partner (other).  Register
-        // arrays are indexed by compile-time u only; hf enters LDS addresses.
-        s16x4 Sh[2][2], Sl[2][2];          // [own = 0 / other = 1][u]
-        int jtile[2][2];
-        #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            to_operand(ST[u], Sh[0][u], Sl[0][u]);
-            Sh[1][u] = lds<s16x4>(smem + OFF_XS, xs_oth + (u * 2 + 0) * 64 * 8);
-            Sl[1][u] = lds<s16x4>(smem + OFF_XS, xs_oth + (u * 2 + 1) * 64 * 8);
-            jtile[0][u] = 2 * hf + u;
-            jtile[1][u] = 2 * (1 - hf) + u;
-        }
-        // V^T as 16x16x32 B operands (k = token s = 32 kq + 8 lq + e, n = value row).
+        // State operands: key pair hf from this wave's registers (own), pair 1 - hf from the partner.
+        const bf16x8 SxH = lds<bf16x8>(smem + OFF_XS, xs_oth);
+        const bf16x8 SxL = lds<bf16x8>(smem + OFF_XS, xs_oth + 64 * 16);
+        const int po = 32 * hf, px = 32 * (1 - hf);   // column of the own / other key pair
+        // V^T as 32-deep B operands (k = token s = 32 kq + 8 lq + e, n = value row).
         bf16x8 VB[2], VBl[2];
         #pragma unroll
         for (int kq = 0; kq < 2; ++kq) {
@@ -475,15 +560,13 @@ void chunked_kernel(ChunkArgs g) {
         #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            #pragma unroll
-            for (int o2 = 0; o2 < 2; ++o2) {
-                #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const s16x4 A4 = lds<s16x4>(smem + OFF_AT, (16 * tb * P72 + 16 * jtile[o2][u]) * 2 + op16);
-                    acc = mfma16(A4, Sh[o2][u], acc);
-                    acc = mfma16(A4, Sl[o2][u], acc);
-                }
-            }
+            const int ro = (16 * tb * P72) * 2 + op32;
+            const bf16x8 Ao = lds<bf16x8>(smem + OFF_AT, ro + po * 2);
+            const bf16x8 Ax = lds<bf16x8>(smem + OFF_AT, ro + px * 2);
+            acc = mfma32(Ao, SoH, acc);
+            acc = mfma32(Ao, SoL, acc);
+            acc = mfma32(Ax, SxH, acc);
+            acc = mfma32(Ax, SxL, acc);
             #pragma unroll
             for (int kq = 0; kq <= tb / 2; ++kq) {
                 const int o = (16 * tb * P72 + 32 * kq) * 2 + op32;
@@ -500,18 +583,17 @@ void chunked_kernel(ChunkArgs g) {
         for (int u = 0; u < 2; ++u) {
             const int tb = 2 * hf + u;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            #pragma unroll
-            for (int o2 = 0; o2 < 2; ++o2) {
-                #pragma unroll
-                for (int uu = 0; uu < 2; ++uu) {
-                    const int o = (16 * tb * P72 + 16 * jtile[o2][uu]) * 2 + op16;
-                    const s16x4 Rh4 = lds<s16x4>(smem + OFF_RTH, o);
-                    const s16x4 Rl4 = lds<s16x4>(smem + OFF_RTL, o);
-                    acc = mfma16(Rh4, Sh[o2][uu], acc);
-                    acc = mfma16(Rh4, Sl[o2][uu], acc);
-                    acc = mfma16(Rl4, Sh[o2][uu], acc);
-                }
-            }
+            const int ro = (16 * tb * P72) * 2 + op32;
+            const bf16x8 Rho = lds<bf16x8>(smem + OFF_RTH, ro + po * 2);
+            const bf16x8 Rlo = lds<bf16x8>(smem + OFF_RTL, ro + po * 2);
+            const bf16x8 Rhx = lds<bf16x8>(smem + OFF_RTH, ro + px * 2);
+            const bf16x8 Rlx = lds<bf16x8>(smem + OFF_RTL, ro + px * 2);
+            acc = mfma32(Rho, SoH, acc);
+            acc = mfma32(Rho, SoL, acc);
+            acc = mfma32(Rlo, SoH, acc);
+            acc = mfma32(Rhx, SxH, acc);
+            acc = mfma32(Rhx, SxL, acc);
+            acc = mfma32(Rlx, SxH, acc);
             #pragma unroll
             for (int kq = 0; kq < 2; ++kq) {
                 if (kq <= tb / 2) {
@@ -532,57 +614,71 @@ void chunked_kernel(ChunkArgs g) {
         #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {
             f32x4 x = RHS[ib];
-            #pragma unroll
-            for (int jb = 0; jb < ib; ++jb) {
-                const s16x4 A4 = lds<s16x4>(smem + OFF_AAB, (16 * ib * P72 + 16 * jb) * 2 + op16);
-                x = mfma16(A4, SAh[jb], x);
-                x = mfma16(A4, SAl[jb], x);
+            if (ib >= 2) {   // 16-blocks 0 and 1 as one pair
+                const bf16x8 A8 = lds<bf16x8>(smem + OFF_AAB, (16 * ib * P72) * 2 + op32);
+                x = mfma32(A8, cat(SAh[0], SAh[1]), x);
+                x = mfma32(A8, cat(SAl[0], SAl[1]), x);
+            }
+            if (ib == 1 || ib == 3) {   // the remaining single 16-block ib - 1
+                const s16x4 A4 = lds<s16x4>(smem + OFF_AAB, op_single(16 * ib, ib - 1));
+                x = mfma32(cat(A4, A4), cat(SAh[ib - 1], SAl[ib - 1]), x);
             }
             s16x4 xh, xl;
             to_operand(x, xh, xl);
             const s16x4 D4 = lds<s16x4>(smem + OFF_DINV, ((16 * ib + lr) * PD + 4 * lq) * 2);
-            f32x4 sa = {0.f, 0.f, 0.f, 0.f};
-            sa = mfma16(D4, xh, sa);
-            sa = mfma16(D4, xl, sa);
+            const f32x4 sa = mfma32(cat(D4, D4), cat(xh, xl), f32x4{0.f, 0.f, 0.f, 0.f});
             to_operand(sa, SAh[ib], SAl[ib]);
         }
+        const bf16x8 SPh[2] = {cat(SAh[0], SAh[1]), cat(SAh[2], SAh[3])};
+        const bf16x8 SPl[2] = {cat(SAl[0], SAl[1]), cat(SAl[2], SAl[3])};
 
         // Next chunk's inputs: in flight during P6, P7 and the start of the next chunk.
-        if (ch + 1 < nchunks) load_chunk(c0 + L);
+        load_chunk(c0 + L);
 
         // ---------------- P6: Y += A_rb SA on token tiles 2 hf, 2 hf + 1; epilogue; store ----------------
-        #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int tb = 2 * hf + u;
-            f32x4 acc = Yacc[u];
-            #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                if (sb <= tb) {
-                    const s16x4 A4 = lds<s16x4>(smem + OFF_ARB, (16 * tb * P72 + 16 * sb) * 2 + op16);
-                    acc = mfma16(A4, SAh[sb], acc);
-                    acc = mfma16(A4, SAl[sb], acc);
+        {
+            const int nv = max(0, min(T - c0, L));
+            const rsrc_t Ry = make_rsrc(yp + (tok0 + c0) * sty, uint32_t(nv) * sty);
+            auto p6 = [&](auto HFC) {
+                constexpr int HF = decltype(HFC)::value;
+                #pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int tb = 2 * HF + u;
+                    f32x4 acc = Yacc[u];
+                    #pragma unroll
+                    for (int p = 0; p < 2; ++p) {
+                        if (2 * p + 1 <= tb) {
+                            const bf16x8 A8 = lds<bf16x8>(smem + OFF_ARB, (16 * tb * P72 + 32 * p) * 2 + op32);
+                            acc = mfma32(A8, SPh[p], acc);
+                            acc = mfma32(A8, SPl[p], acc);
+                        }
+                    }
+                    if ((tb & 1) == 0) {   // diagonal block tb, not covered by a pair
+                        const s16x4 A4 = lds<s16x4>(smem + OFF_ARB, op_single(16 * tb, tb));
+                        acc = mfma32(cat(A4, A4), cat(SAh[tb], SAl[tb]), acc);
+                    }
+                    // acc[r] = Y[t = 16 tb + 4 lq + r][i_row]
+                    const int tl0 = 16 * tb + 4 * lq;
+                    float vtr[4] = {0.f, 0.f, 0.f, 0.f}, bon[4] = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (EPI) {
+                        const uint2 vraw = lds<uint2>(smem + OFF_VT, (i_row * P72 + tl0) * 2);
+                        vtr[0] = lo_f32(vraw.x); vtr[1] = hi_f32(vraw.x); vtr[2] = lo_f32(vraw.y); vtr[3] = hi_f32(vraw.y);
+                        if constexpr (VSPLIT) {
+                            const uint2 vlo = lds<uint2>(smem + OFF_VTL, (i_row * P72 + tl0) * 2);
+                            vtr[0] += lo_f32(vlo.x); vtr[1] += hi_f32(vlo.x); vtr[2] += lo_f32(vlo.y); vtr[3] += hi_f32(vlo.y);
+                        }
+                        const float4 bq = lds<float4>(smem + OFF_BONUS, tl0 * 4);
+                        bon[0] = bq.x; bon[1] = bq.y; bon[2] = bq.z; bon[3] = bq.w;
+                    }
+                    #pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float yv = acc[r] * g.y_scale;
+                        if constexpr (EPI) yv = fmaf(bon[r], vtr[r], yv);
+                        Buf<Ty>::store1(Ry, y_lane + uint32_t(16 * tb + r) * sty, yv);
+                    }
                 }
-            }
-            // acc[r] = Y[t = 16 tb + 4 lq + r][i_row]
-            const int tl0 = 16 * tb + 4 * lq;
-            float vtr[4] = {0.f, 0.f, 0.f, 0.f}, bon[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (EPI) {
-                const uint2 vraw = lds<uint2>(smem + OFF_VT, (i_row * P72 + tl0) * 2);
-                vtr[0] = lo_f32(vraw.x); vtr[1] = hi_f32(vraw.x); vtr[2] = lo_f32(vraw.y); vtr[3] = hi_f32(vraw.y);
-                if constexpr (VSPLIT) {
-                    const uint2 vlo = lds<uint2>(smem + OFF_VTL, (i_row * P72 + tl0) * 2);
-                    vtr[0] += lo_f32(vlo.x); vtr[1] += hi_f32(vlo.x); vtr[2] += lo_f32(vlo.y); vtr[3] += hi_f32(vlo.y);
-                }
-                const float4 bq = lds<float4>(smem + OFF_BONUS, tl0 * 4);
-                bon[0] = bq.x; bon[1] = bq.y; bon[2] = bq.z; bon[3] = bq.w;
-            }
-            #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = c0 + tl0 + r;
-                float yv = acc[r] * g.y_scale;
-                if constexpr (EPI) yv = fmaf(bon[r], vtr[r], yv);
-                if (t < T) st1(yp, base_q + t * step_q + i_row, yv);
-            }
+            };
+            if (hf == 0) p6(IC<0>{}); else p6(IC<1>{});
         }
 
         // ---------------- P7: S_L^T = 2^g_L S0^T + Bh^T SA + Kh^T V, key tiles 2 hf, 2 hf + 1 ----------------
@@ -593,10 +689,10 @@ void chunked_kernel(ChunkArgs g) {
             f32x4 acc = ST[u];
             acc[0] *= el4.x; acc[1] *= el4.y; acc[2] *= el4.z; acc[3] *= el4.w;
             #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const s16x4 B4 = lds<s16x4>(smem + OFF_BHT, (16 * jt * P72 + 16 * tb) * 2 + op16);
-                acc = mfma16(B4, SAh[tb], acc);
-                acc = mfma16(B4, SAl[tb], acc);
+            for (int p = 0; p < 2; ++p) {
+                const bf16x8 B8 = lds<bf16x8>(smem + OFF_BHT, (16 * jt * P72 + 32 * p) * 2 + op32);
+                acc = mfma32(B8, SPh[p], acc);
+                acc = mfma32(B8, SPl[p], acc);
             }
             #pragma unroll
             for (int kq = 0; kq < 2; ++kq) {
@@ -647,6 +743,8 @@ hipError_t dispatch_modes(const Params& p, hipStream_t s) {
 
 hipError_t launch_chunked(const Params& p, hipStream_t stream) {
     if (p.D != DH || p.chunk_len != L) return hipErrorInvalidValue;
+    // Byte offsets inside one chunk's descriptor are 32-bit.
+    if (int64_t(L) * p.H * DH * 4 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     if (p.in_dtype == WKV7_BF16)
         return p.y_dtype == WKV7_BF16 ? dispatch_modes<bf16_t, bf16_t>(p, stream) : dispatch_modes<bf16_t, float>(p, stream);
     return p.y_dtype == WKV7_BF16 ? dispatch_modes<float, bf16_t>(p, stream) : dispatch_modes<float, float>(p, stream);
