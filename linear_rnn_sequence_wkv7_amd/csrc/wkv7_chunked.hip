@@ -38,6 +38,11 @@
 // inverses of the diagonal 16 x 16 blocks of I - A_ab) are built
 // cooperatively, with barriers between those phases.
 //
+// Every MFMA accumulator chain uses that one opcode: on gfx950, feeding the
+// result of one MFMA opcode into another as its accumulator gave wrong values
+// whenever the two issued close together (the compiler's wait states did not
+// cover it), so a single 16-deep term is padded to 32 with zeros instead.
+//
 // Global memory is read and written through buffer descriptors that cover
 // the valid tokens of one chunk of one sequence: tokens past the end read as
 // zero (identity tokens: a = b = k = v = r = 0; w is set to 1 explicitly) and
@@ -268,12 +273,27 @@ void chunked_kernel(ChunkArgs g) {
         #pragma unroll
         for (int e = 0; e < 8; ++e) rk8[e] = g.r_k[h * DH + 8 * qr + e];
     }
-    // Chunk-relative byte offsets (the descriptors move with the chunk).
-    const uint32_t col_q = uint32_t(8 * pc) * stq + uint32_t(h * DH + jc) * SI;
-    const uint32_t col_kv = uint32_t(8 * pc) * stkv + uint32_t(hk * DH + jc) * SI;
+    // Chunk-relative byte offsets (the descriptors move with the chunk), kept as
+    // per-lane values in VGPRs: the column threads' 8 tokens, the row threads'
+    // token, and the 4 x 2 y elements of a lane.
+    uint32_t col_q[8], col_kv[8], y_off[2][4];
+    #pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        col_q[e] = uint32_t(8 * pc + e) * stq + uint32_t(h * DH + jc) * SI;
+        col_kv[e] = uint32_t(8 * pc + e) * stkv + uint32_t(hk * DH + jc) * SI;
+        asm volatile("" : "+v"(col_q[e]));
+        asm volatile("" : "+v"(col_kv[e]));
+    }
+    #pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            y_off[u][r] = uint32_t(16 * (2 * hf + u) + 4 * lq + r) * sty + uint32_t(h * DH + i_row) * SY;
+            asm volatile("" : "+v"(y_off[u][r]));
+        }
+    }
     const uint32_t row_q = uint32_t(tr) * stq + uint32_t(h * DH + 8 * qr) * SI;
     const uint32_t row_kv = uint32_t(tr) * stkv + uint32_t(hk * DH + 8 * qr) * SI;
-    const uint32_t y_lane = uint32_t(4 * lq) * sty + uint32_t(h * DH + i_row) * SY;
 
     uint32_t cw[8], cb[8], ck[8], cv[8];
     Row8<Tin> rr, ra, rb, rkv;
@@ -289,10 +309,10 @@ void chunked_kernel(ChunkArgs g) {
         const rsrc_t Rv = make_rsrc(vp + t0 * stkv, uint32_t(nv) * stkv);
         #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            cw[e] = Buf<Tin>::load1(Rw, col_q + uint32_t(e) * stq);
-            cb[e] = Buf<Tin>::load1(Rb, col_q + uint32_t(e) * stq);
-            ck[e] = Buf<Tin>::load1(Rk, col_kv + uint32_t(e) * stkv);
-            cv[e] = Buf<Tin>::load1(Rv, col_kv + uint32_t(e) * stkv);
+            cw[e] = Buf<Tin>::load1(Rw, col_q[e]);
+            cb[e] = Buf<Tin>::load1(Rb, col_q[e]);
+            ck[e] = Buf<Tin>::load1(Rk, col_kv[e]);
+            cv[e] = Buf<Tin>::load1(Rv, col_kv[e]);
         }
         rr.load(Rr, row_q);
         ra.load(Ra, row_q);
@@ -325,29 +345,36 @@ void chunked_kernel(ChunkArgs g) {
         }
 
         // ---------------- P1a: decay prefix down each key column ----------------
+        // Decay mode: running products of w, 2^-g as a reciprocal; log-decay mode:
+        // running sums of log2 w = -exp(x) log2(e), then exp2.
         float pre[8];
         {
-            float run = 0.f;
+            float run = LOGW ? 0.f : 1.f;
             #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float x = __uint_as_float(cw[e]);
                 const bool ok = c0 + 8 * pc + e < T;     // wave-uniform; w = 1 past the end
-                const float lw = LOGW ? -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e : __builtin_amdgcn_logf(x);
-                run += ok ? lw : 0.f;
+                if constexpr (LOGW) run += ok ? -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e : 0.f;
+                else run *= ok ? x : 1.f;
                 pre[e] = run;
             }
             sts<float>(smem + OFF_TOT, (pc * 64 + jc) * 4, run);
         }
         __syncthreads();
         {
-            float off = 0.f, total = 0.f;
+            float off = LOGW ? 0.f : 1.f, total = off;
             #pragma unroll
             for (int pp = 0; pp < 8; ++pp) {
                 const float tp = lds<float>(smem + OFF_TOT, (pp * 64 + jc) * 4);
-                off += pp < pc ? tp : 0.f;
-                total += tp;
+                if constexpr (LOGW) {
+                    off += pp < pc ? tp : 0.f;
+                    total += tp;
+                } else {
+                    off *= pp < pc ? tp : 1.f;
+                    total *= tp;
+                }
             }
-            const float EL = __builtin_amdgcn_exp2f(total);
+            const float EL = LOGW ? __builtin_amdgcn_exp2f(total) : total;
             if (pc == 0) sts<float>(smem + OFF_EL, jc * 4, EL);
             uint32_t bh4[4], khh[4], khl[4], vh[4], vl[4];
             #pragma unroll
@@ -355,9 +382,15 @@ void chunked_kernel(ChunkArgs g) {
                 float Eh[2];
                 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const float gv = pre[e + u] + off;
-                    const float E = __builtin_amdgcn_exp2f(gv);
-                    const float Ei = __builtin_amdgcn_exp2f(-gv);
+                    float E, Ei;
+                    if constexpr (LOGW) {
+                        const float gv = pre[e + u] + off;
+                        E = __builtin_amdgcn_exp2f(gv);
+                        Ei = __builtin_amdgcn_exp2f(-gv);
+                    } else {
+                        E = pre[e + u] * off;
+                        Ei = __builtin_amdgcn_rcpf(E);
+                    }
                     sts<float>(smem + OFF_E, ((8 * pc + e + u) * PE + jc) * 4, E);
                     sts<float>(smem + OFF_EI, ((8 * pc + e + u) * PE + jc) * 4, Ei);
                     Eh[u] = EL * Ei;
@@ -436,18 +469,17 @@ void chunked_kernel(ChunkArgs g) {
         __syncthreads();
 
         // ---------------- P2: the four L x L matrices ----------------
-        // Tile list (tb, sb), sb <= tb in row order; wave w computes tiles
-        // (w & 3) + 4n of group w >> 2: group 0 = A_ab, A_ak; group 1 = A_rb, A_rk.
+        // Tile list (tb, sb), sb <= tb in row order (ids 0..9); wave w computes
+        // tiles w and w + 8 of all four matrices, sharing the B~ / K~ reads.
         // Each tile is C'[s][t] = Y[s] . X[t], so a lane holds 4 consecutive s of
         // one t: a row-major [t][s] store of 4 elements.
-        const int grp = hf;
-        f32x4 acc0[3], acc1[3];
+        auto tile_tb = [](int id) { return id >= 6 ? 3 : id >= 3 ? 2 : id >= 1 ? 1 : 0; };
+        f32x4 Aab[2], Aak[2], Arb[2], Ark[2];
         #pragma unroll
-        for (int n = 0; n < 3; ++n) {
-            const int id = strip + 4 * n;
-            const int tb = id >= 6 ? 3 : id >= 3 ? 2 : id >= 1 ? 1 : 0;
-            const int sb = id - (tb * (tb + 1)) / 2;
-            acc0[n] = acc1[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < 2; ++n) {
+            const int id = w + 8 * n;
+            const int tb = tile_tb(id), sb = id - (tile_tb(id) * (tile_tb(id) + 1)) / 2;
+            Aab[n] = Aak[n] = Arb[n] = Ark[n] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (id < 10) {
                 #pragma unroll
                 for (int kq = 0; kq < 2; ++kq) {
@@ -456,56 +488,56 @@ void chunked_kernel(ChunkArgs g) {
                     const bf16x8 Bt8 = lds<bf16x8>(smem + OFF_BT, ya);
                     const bf16x8 Kh8 = lds<bf16x8>(smem + OFF_KTH, ya);
                     const bf16x8 Kl8 = lds<bf16x8>(smem + OFF_KTL, ya);
-                    if (grp == 0) {
-                        const bf16x8 At8 = lds<bf16x8>(smem + OFF_AT, xb);
-                        acc0[n] = mfma32(Bt8, At8, acc0[n]);
-                        acc1[n] = mfma32(Kh8, At8, acc1[n]);
-                        acc1[n] = mfma32(Kl8, At8, acc1[n]);
-                    } else {
-                        const bf16x8 Rh8 = lds<bf16x8>(smem + OFF_RTH, xb);
-                        const bf16x8 Rl8 = lds<bf16x8>(smem + OFF_RTL, xb);
-                        acc0[n] = mfma32(Bt8, Rh8, acc0[n]);
-                        acc0[n] = mfma32(Bt8, Rl8, acc0[n]);
-                        acc1[n] = mfma32(Kh8, Rh8, acc1[n]);
-                        acc1[n] = mfma32(Kh8, Rl8, acc1[n]);
-                        acc1[n] = mfma32(Kl8, Rh8, acc1[n]);
-                    }
+                    const bf16x8 At8 = lds<bf16x8>(smem + OFF_AT, xb);
+                    const bf16x8 Rh8 = lds<bf16x8>(smem + OFF_RTH, xb);
+                    const bf16x8 Rl8 = lds<bf16x8>(smem + OFF_RTL, xb);
+                    Aab[n] = mfma32(Bt8, At8, Aab[n]);
+                    Aak[n] = mfma32(Kh8, At8, Aak[n]);
+                    Aak[n] = mfma32(Kl8, At8, Aak[n]);
+                    Arb[n] = mfma32(Bt8, Rh8, Arb[n]);
+                    Arb[n] = mfma32(Bt8, Rl8, Arb[n]);
+                    Ark[n] = mfma32(Kh8, Rh8, Ark[n]);
+                    Ark[n] = mfma32(Kh8, Rl8, Ark[n]);
+                    Ark[n] = mfma32(Kl8, Rh8, Ark[n]);
                 }
             }
         }
         __syncthreads();   // B~ / K~ (region 1) and the decay tables (region 2) are dead now
         #pragma unroll
-        for (int n = 0; n < 3; ++n) {
-            const int id = strip + 4 * n;
+        for (int n = 0; n < 2; ++n) {
+            const int id = w + 8 * n;
             if (id < 10) {
-                const int tb = id >= 6 ? 3 : id >= 3 ? 2 : id >= 1 ? 1 : 0;
-                const int sb = id - (tb * (tb + 1)) / 2;
-                f32x4 c0v = acc0[n], c1v = acc1[n];
+                const int tb = tile_tb(id), sb = id - (tile_tb(id) * (tile_tb(id) + 1)) / 2;
+                f32x4 ab = Aab[n], ak = Aak[n], rb = Arb[n], rk = Ark[n];
                 if (tb == sb) {
-                    // group 0 is strictly lower (s < t), group 1 lower with diagonal (s <= t).
-                    const int lim = lr + grp;
+                    // A_ab, A_ak strictly lower (s < t); A_rb, A_rk lower with diagonal (s <= t).
                     #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const bool z = 4 * lq + r >= lim;
-                        c0v[r] = z ? 0.f : c0v[r];
-                        c1v[r] = z ? 0.f : c1v[r];
+                        const int sl = 4 * lq + r;
+                        ab[r] = sl >= lr ? 0.f : ab[r];
+                        ak[r] = sl >= lr ? 0.f : ak[r];
+                        rb[r] = sl > lr ? 0.f : rb[r];
+                        rk[r] = sl > lr ? 0.f : rk[r];
                     }
-                    if (grp == 0) {
-                        // transposed: [block][s][t]
-                        #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            sts<float>(smem + OFF_ADIAG, ((tb * 16 + 4 * lq + r) * PD + lr) * 4, c0v[r]);
-                    }
+                    // transposed: [block][s][t]
+                    #pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sts<float>(smem + OFF_ADIAG, ((tb * 16 + 4 * lq + r) * PD + lr) * 4, ab[r]);
                 }
-                uint32_t h0, l0, h1, l1;
-                split2(c1v[0], c1v[1], h0, l0);
-                split2(c1v[2], c1v[3], h1, l1);
-                const uint2 c0p = make_uint2(pack_bf16(c0v[0], c0v[1]), pack_bf16(c0v[2], c0v[3]));
                 const int orow = (16 * tb + lr) * P72;
-                sts<uint2>(smem + (grp == 0 ? OFF_AAB : OFF_ARB), (orow + pairpos(16 * sb + 4 * lq)) * 2, c0p);
+                const int op = (orow + pairpos(16 * sb + 4 * lq)) * 2;
+                sts<uint2>(smem + OFF_AAB, op, make_uint2(pack_bf16(ab[0], ab[1]), pack_bf16(ab[2], ab[3])));
+                sts<uint2>(smem + OFF_ARB, op, make_uint2(pack_bf16(rb[0], rb[1]), pack_bf16(rb[2], rb[3])));
                 const int o = (orow + 16 * sb + 4 * lq) * 2;
-                sts<uint2>(smem + (grp == 0 ? OFF_AKH : OFF_RKH), o, make_uint2(h0, h1));
-                sts<uint2>(smem + (grp == 0 ? OFF_AKL : OFF_RKL), o, make_uint2(l0, l1));
+                uint32_t h0, l0, h1, l1;
+                split2(ak[0], ak[1], h0, l0);
+                split2(ak[2], ak[3], h1, l1);
+                sts<uint2>(smem + OFF_AKH, o, make_uint2(h0, h1));
+                sts<uint2>(smem + OFF_AKL, o, make_uint2(l0, l1));
+                split2(rk[0], rk[1], h0, l0);
+                split2(rk[2], rk[3], h1, l1);
+                sts<uint2>(smem + OFF_RKH, o, make_uint2(h0, h1));
+                sts<uint2>(smem + OFF_RKL, o, make_uint2(l0, l1));
             }
         }
         if (tid < 256) {
@@ -519,28 +551,39 @@ void chunked_kernel(ChunkArgs g) {
         __syncthreads();
 
         // ---------------- P3: inverses of the diagonal blocks of I - A_ab ----------------
-        // Column c of (I - A)^-1 by forward substitution, column-oriented: once x_s is
-        // final, x_t += A[t][s] x_s for every t > s.
-        if (w < 4 && l < 16) {
-            const int c = l;
-            float x[16];
-            #pragma unroll
-            for (int t = 0; t < 16; ++t) x[t] = (t == c) ? 1.f : 0.f;
-            #pragma unroll
-            for (int s = 0; s < 15; ++s) {
-                float a[16];
+        // N = block w of A_ab is strictly lower triangular, so N^16 = 0 and
+        // (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8); the factors are polynomials
+        // in N and commute.  A C-layout tile of M is the B operand of M and the A
+        // operand of M^T, so products are formed from tiles of both orientations.
+        if (w < 4) {
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            const s16x4 z4 = {0, 0, 0, 0};
+            // prod(C(X^T), C(Y)) = C(X Y), operands split hi + lo: [xh, xl].[yh, yh] + [xh, 0].[yl, 0].
+            auto prod = [&](const f32x4 xt, const f32x4 y) {
+                s16x4 xh, xl, yh, yl;
+                to_operand(xt, xh, xl);
+                to_operand(y, yh, yl);
+                const f32x4 c = mfma32(cat(xh, xl), cat(yh, yh), zero);
+                return mfma32(cat(xh, z4), cat(yl, z4), c);
+            };
+            f32x4 Nn, Nt, I4;
+            {
+                const float4 cn = lds<float4>(smem + OFF_ADIAG, ((w * 16 + lr) * PD + 4 * lq) * 4);
+                Nn = f32x4{cn.x, cn.y, cn.z, cn.w};            // C(N):   N[4 lq + r][lr]
                 #pragma unroll
-                for (int q = (s + 1) >> 2; q < 4; ++q) {
-                    const float4 v4 = lds<float4>(smem + OFF_ADIAG, ((w * 16 + s) * PD + 4 * q) * 4);
-                    a[4 * q] = v4.x; a[4 * q + 1] = v4.y; a[4 * q + 2] = v4.z; a[4 * q + 3] = v4.w;
+                for (int r = 0; r < 4; ++r) {
+                    Nt[r] = lds<float>(smem + OFF_ADIAG, ((w * 16 + 4 * lq + r) * PD + lr) * 4);   // C(N^T)
+                    I4[r] = (4 * lq + r == lr) ? 1.f : 0.f;
                 }
-                #pragma unroll
-                for (int t = s + 1; t < 16; ++t) x[t] = fmaf(a[t], x[s], x[t]);
             }
-            #pragma unroll
-            for (int t = 0; t < 16; ++t)
-                sts<uint16_t>(smem + OFF_DINV, ((w * 16 + t) * PD + c) * 2,
-                              __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[t])));
+            const f32x4 N2 = prod(Nt, Nn), N2t = prod(Nn, Nt);
+            const f32x4 N4 = prod(N2t, N2), N4t = prod(N2, N2t);
+            const f32x4 N8 = prod(N4t, N4);
+            const f32x4 Gt = prod(N2 + I4, Nt + I4);       // C((F1 F2)^T) = C(F2^T F1^T)
+            const f32x4 G4t = prod(N4 + I4, Gt);           // C(F4^T F2^T F1^T)
+            const f32x4 Dt = prod(N8 + I4, G4t);           // C(D^T): lane holds D[lr][4 lq + r]
+            sts<uint2>(smem + OFF_DINV, ((w * 16 + lr) * PD + 4 * lq) * 2,
+                       make_uint2(pack_bf16(Dt[0], Dt[1]), pack_bf16(Dt[2], Dt[3])));
         }
         // No barrier here: P4 does not read the inverses.
 
@@ -674,7 +717,7 @@ void chunked_kernel(ChunkArgs g) {
                     for (int r = 0; r < 4; ++r) {
                         float yv = acc[r] * g.y_scale;
                         if constexpr (EPI) yv = fmaf(bon[r], vtr[r], yv);
-                        Buf<Ty>::store1(Ry, y_lane + uint32_t(16 * tb + r) * sty, yv);
+                        Buf<Ty>::store1(Ry, y_off[u][r], yv);
                     }
                 }
             };
