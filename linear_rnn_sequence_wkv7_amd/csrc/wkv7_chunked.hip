@@ -71,8 +71,8 @@ constexpr int MAT = 64 * P72 * 2;
 constexpr int PD = 20;         // pitch of the 16 x 16 diagonal blocks
 constexpr int PE = 68;         // fp32 pitch of the decay tables
 
-// LDS map (bytes).  Region 1 holds B~, K~ during P1..P2 and A_ab, A_rb and the
-// fp32 diagonal blocks of A_ab afterwards; region 2 holds the decay tables
+// LDS map (bytes).  Region 1 holds B~, K~ during P1..P2 and A_ab, A_rb
+// afterwards; region 2 holds the decay tables
 // 2^g, 2^-g and the column-segment totals during P1 and A_ak, A_rk afterwards.
 // Pair-interleaved axis (see above): At, Rt, Bt, Kt (key axis), A_ab, A_rb,
 // Bh^T (token axis).  Natural order: A_ak, A_rk, Kh^T, V^T.
@@ -89,7 +89,6 @@ constexpr int OFF_KTH = OFF_R1 + MAT;      // K~ [s][j] hi / lo
 constexpr int OFF_KTL = OFF_R1 + 2 * MAT;
 constexpr int OFF_AAB = OFF_R1;            // A_ab [t][s] bf16
 constexpr int OFF_ARB = OFF_R1 + MAT;      // A_rb [t][s] bf16
-constexpr int OFF_ADIAG = OFF_R1 + 2 * MAT;  // fp32 [4][s][t] (pitch PD) diagonal blocks of A_ab, transposed
 constexpr int OFF_R2 = OFF_R1 + 3 * MAT;
 constexpr int OFF_E = OFF_R2;              // fp32 [64][PE] 2^g
 constexpr int OFF_EI = OFF_R2 + 64 * PE * 4;   // fp32 [64][PE] 2^-g
@@ -106,7 +105,6 @@ constexpr int XS_BYTES = 4 * 2 * 2 * 64 * 16;   // [strip][half][hi/lo][lane] 16
 constexpr int OFF_VTL = OFF_XS + XS_BYTES; // V^T lo part (fp32 inputs only)
 constexpr int SMEM_BF16 = OFF_VTL;
 constexpr int SMEM_F32 = OFF_VTL + MAT;
-static_assert(4 * 16 * PD * 4 <= MAT, "diagonal blocks fit");
 static_assert(2 * 64 * PE * 4 + 8 * 64 * 4 <= 4 * MAT, "decay tables fit");
 static_assert(SMEM_F32 <= 160 * 1024, "LDS budget");
 
@@ -468,19 +466,25 @@ void chunked_kernel(ChunkArgs g) {
         }
         __syncthreads();
 
-        // ---------------- P2: the four L x L matrices ----------------
-        // Tile list (tb, sb), sb <= tb in row order (ids 0..9); wave w computes
-        // tiles w and w + 8 of all four matrices, sharing the B~ / K~ reads.
-        // Each tile is C'[s][t] = Y[s] . X[t], so a lane holds 4 consecutive s of
-        // one t: a row-major [t][s] store of 4 elements.
+        // ---------------- P2: the four L x L matrices; inverses of the diagonal blocks ----------------
+        // Tile ids 0..9 list (tb, sb), sb <= tb, in row order.  Waves 4..7 take the
+        // diagonal tile (strip, strip); waves 0..3 the off-diagonal tiles
+        // {1, 3}, {4, 6}, {7}, {8}; a wave computes all four matrices of its tiles,
+        // sharing the B~ / K~ reads.  Each tile is C'[s][t] = Y[s] . X[t], so a lane
+        // holds 4 consecutive s of one t: a row-major [t][s] store of 4 elements.
         auto tile_tb = [](int id) { return id >= 6 ? 3 : id >= 3 ? 2 : id >= 1 ? 1 : 0; };
+        auto tile_id = [&](int n) {
+            return hf ? (n == 0 ? strip * (strip + 3) / 2 : -1)
+                      : (n == 0 ? min(1 + 3 * strip, 8) : (strip < 2 ? 3 + 3 * strip : -1));
+        };
         f32x4 Aab[2], Aak[2], Arb[2], Ark[2];
+        f32x4 Nsw = {0.f, 0.f, 0.f, 0.f};   // diagonal block N of A_ab in C layout (waves 4..7)
         #pragma unroll
         for (int n = 0; n < 2; ++n) {
-            const int id = w + 8 * n;
+            const int id = tile_id(n);
             const int tb = tile_tb(id), sb = id - (tile_tb(id) * (tile_tb(id) + 1)) / 2;
             Aab[n] = Aak[n] = Arb[n] = Ark[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (id < 10) {
+            if (id >= 0) {
                 #pragma unroll
                 for (int kq = 0; kq < 2; ++kq) {
                     const int ya = (16 * sb * P72 + 32 * kq) * 2 + op32;
@@ -499,14 +503,47 @@ void chunked_kernel(ChunkArgs g) {
                     Ark[n] = mfma32(Kh8, Rh8, Ark[n]);
                     Ark[n] = mfma32(Kh8, Rl8, Ark[n]);
                     Ark[n] = mfma32(Kl8, Rh8, Ark[n]);
+                    if (hf) Nsw = mfma32(At8, Bt8, Nsw);   // same block, operands swapped
                 }
             }
+        }
+        if (hf) {
+            // N = block `strip` of A_ab is strictly lower triangular, so N^16 = 0 and
+            // (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8); the factors are
+            // polynomials in N and commute.  A C-layout tile of M is the B operand of M
+            // and the A operand of M^T, so the products use tiles of both orientations:
+            // Aab[0] is C(N^T) (lane: t = lr, s = 4 lq + r), Nsw is C(N) (s = lr, t = 4 lq + r).
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            const s16x4 z4 = {0, 0, 0, 0};
+            // prod(C(X^T), C(Y)) = C(X Y), operands split hi + lo: [xh, xl].[yh, yh] + [xh, 0].[yl, 0].
+            auto prod = [&](const f32x4 xt, const f32x4 y) {
+                s16x4 xh, xl, yh, yl;
+                to_operand(xt, xh, xl);
+                to_operand(y, yh, yl);
+                const f32x4 c = mfma32(cat(xh, xl), cat(yh, yh), zero);
+                return mfma32(cat(xh, z4), cat(yl, z4), c);
+            };
+            f32x4 Nn, Nt, I4;
+            #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                Nt[r] = 4 * lq + r >= lr ? 0.f : Aab[0][r];
+                Nn[r] = lr >= 4 * lq + r ? 0.f : Nsw[r];
+                I4[r] = (4 * lq + r == lr) ? 1.f : 0.f;
+            }
+            const f32x4 N2 = prod(Nt, Nn), N2t = prod(Nn, Nt);
+            const f32x4 N4 = prod(N2t, N2), N4t = prod(N2, N2t);
+            const f32x4 N8 = prod(N4t, N4);
+            const f32x4 Gt = prod(N2 + I4, Nt + I4);       // C((F1 F2)^T) = C(F2^T F1^T)
+            const f32x4 G4t = prod(N4 + I4, Gt);           // C(F4^T F2^T F1^T)
+            const f32x4 Dt = prod(N8 + I4, G4t);           // C(D^T): lane holds D[lr][4 lq + r]
+            sts<uint2>(smem + OFF_DINV, ((strip * 16 + lr) * PD + 4 * lq) * 2,
+                       make_uint2(pack_bf16(Dt[0], Dt[1]), pack_bf16(Dt[2], Dt[3])));
         }
         __syncthreads();   // B~ / K~ (region 1) and the decay tables (region 2) are dead now
         #pragma unroll
         for (int n = 0; n < 2; ++n) {
-            const int id = w + 8 * n;
-            if (id < 10) {
+            const int id = tile_id(n);
+            if (id >= 0) {
                 const int tb = tile_tb(id), sb = id - (tile_tb(id) * (tile_tb(id) + 1)) / 2;
                 f32x4 ab = Aab[n], ak = Aak[n], rb = Arb[n], rk = Ark[n];
                 if (tb == sb) {
@@ -519,10 +556,6 @@ void chunked_kernel(ChunkArgs g) {
                         rb[r] = sl > lr ? 0.f : rb[r];
                         rk[r] = sl > lr ? 0.f : rk[r];
                     }
-                    // transposed: [block][s][t]
-                    #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        sts<float>(smem + OFF_ADIAG, ((tb * 16 + 4 * lq + r) * PD + lr) * 4, ab[r]);
                 }
                 const int orow = (16 * tb + lr) * P72;
                 const int op = (orow + pairpos(16 * sb + 4 * lq)) * 2;
@@ -548,44 +581,7 @@ void chunked_kernel(ChunkArgs g) {
             const int tb = m ? 2 : 0, sb = tb + 1;
             sts<uint4>(smem + base, ((16 * tb + rw) * P72 + 16 * sb + 8 * half) * 2, make_uint4(0, 0, 0, 0));
         }
-        __syncthreads();
-
-        // ---------------- P3: inverses of the diagonal blocks of I - A_ab ----------------
-        // N = block w of A_ab is strictly lower triangular, so N^16 = 0 and
-        // (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8); the factors are polynomials
-        // in N and commute.  A C-layout tile of M is the B operand of M and the A
-        // operand of M^T, so products are formed from tiles of both orientations.
-        if (w < 4) {
-            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            const s16x4 z4 = {0, 0, 0, 0};
-            // prod(C(X^T), C(Y)) = C(X Y), operands split hi + lo: [xh, xl].[yh, yh] + [xh, 0].[yl, 0].
-            auto prod = [&](const f32x4 xt, const f32x4 y) {
-                s16x4 xh, xl, yh, yl;
-                to_operand(xt, xh, xl);
-                to_operand(y, yh, yl);
-                const f32x4 c = mfma32(cat(xh, xl), cat(yh, yh), zero);
-                return mfma32(cat(xh, z4), cat(yl, z4), c);
-            };
-            f32x4 Nn, Nt, I4;
-            {
-                const float4 cn = lds<float4>(smem + OFF_ADIAG, ((w * 16 + lr) * PD + 4 * lq) * 4);
-                Nn = f32x4{cn.x, cn.y, cn.z, cn.w};            // C(N):   N[4 lq + r][lr]
-                #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    Nt[r] = lds<float>(smem + OFF_ADIAG, ((w * 16 + 4 * lq + r) * PD + lr) * 4);   // C(N^T)
-                    I4[r] = (4 * lq + r == lr) ? 1.f : 0.f;
-                }
-            }
-            const f32x4 N2 = prod(Nt, Nn), N2t = prod(Nn, Nt);
-            const f32x4 N4 = prod(N2t, N2), N4t = prod(N2, N2t);
-            const f32x4 N8 = prod(N4t, N4);
-            const f32x4 Gt = prod(N2 + I4, Nt + I4);       // C((F1 F2)^T) = C(F2^T F1^T)
-            const f32x4 G4t = prod(N4 + I4, Gt);           // C(F4^T F2^T F1^T)
-            const f32x4 Dt = prod(N8 + I4, G4t);           // C(D^T): lane holds D[lr][4 lq + r]
-            sts<uint2>(smem + OFF_DINV, ((w * 16 + lr) * PD + 4 * lq) * 2,
-                       make_uint2(pack_bf16(Dt[0], Dt[1]), pack_bf16(Dt[2], Dt[3])));
-        }
-        // No barrier here: P4 does not read the inverses.
+        __syncthreads();   // everything P4..P7 read from LDS is in place; no barrier until the chunk ends
 
         // ---------------- P4: RHS = At S0^T + A_ak V (whole strip), Y's SA-free part ----------------
         // State operands: key pair hf from this wave's registers (own), pair 1 - hf from the partner.
@@ -649,8 +645,6 @@ void chunked_kernel(ChunkArgs g) {
             }
             Yacc[u] = acc;
         }
-
-        __syncthreads();   // inverses of the diagonal blocks published
 
         // ---------------- P5: SA = (I - A_ab)^-1 RHS, blocked forward substitution ----------------
         s16x4 SAh[4], SAl[4];
