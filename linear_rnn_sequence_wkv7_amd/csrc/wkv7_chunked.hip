@@ -221,6 +221,10 @@ template <> struct Row8<float> {
 
 template <int V> struct IC { static constexpr int value = V; };
 
+// Token tiles of Y computed by the wave of half hf: {0, 3} and {1, 2}, which
+// balances the triangular products A_rk V and A_rb SA between the two halves.
+__host__ __device__ constexpr int ytile(int hf, int u) { return hf ? 1 + u : 3 * u; }
+
 template <typename Tin, typename Ty, bool LOGW, bool EPI>
 __global__ __launch_bounds__(NTHR)
 void chunked_kernel(ChunkArgs g) {
@@ -286,7 +290,7 @@ void chunked_kernel(ChunkArgs g) {
     for (int u = 0; u < 2; ++u) {
         #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            y_off[u][r] = uint32_t(16 * (2 * hf + u) + 4 * lq + r) * sty + uint32_t(h * DH + i_row) * SY;
+            y_off[u][r] = uint32_t(16 * ytile(hf, u) + 4 * lq + r) * sty + uint32_t(h * DH + i_row) * SY;
             asm volatile("" : "+v"(y_off[u][r]));
         }
     }
@@ -620,7 +624,7 @@ void chunked_kernel(ChunkArgs g) {
         f32x4 Yacc[2];
         #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int tb = 2 * hf + u;
+            const int tb = ytile(hf, u);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             const int ro = (16 * tb * P72) * 2 + op32;
             const bf16x8 Rho = lds<bf16x8>(smem + OFF_RTH, ro + po * 2);
@@ -672,7 +676,7 @@ void chunked_kernel(ChunkArgs g) {
         // Next chunk's inputs: in flight during P6, P7 and the start of the next chunk.
         load_chunk(c0 + L);
 
-        // ---------------- P6: Y += A_rb SA on token tiles 2 hf, 2 hf + 1; epilogue; store ----------------
+        // ---------------- P6: Y += A_rb SA on token tiles ytile(hf, 0..1); epilogue; store ----------------
         {
             const int nv = max(0, min(T - c0, L));
             const rsrc_t Ry = make_rsrc(yp + (tok0 + c0) * sty, uint32_t(nv) * sty);
@@ -680,7 +684,7 @@ void chunked_kernel(ChunkArgs g) {
                 constexpr int HF = decltype(HFC)::value;
                 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const int tb = 2 * HF + u;
+                    const int tb = ytile(HF, u);
                     f32x4 acc = Yacc[u];
                     #pragma unroll
                     for (int p = 0; p < 2; ++p) {
