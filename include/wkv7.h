@@ -86,7 +86,8 @@ typedef struct wkv7_desc {
     int32_t y_dtype;    /* wkv7_dtype of y */
     int32_t w_mode;     /* wkv7_w_mode */
     int32_t algo;       /* wkv7_algo (forward only; decode_step ignores it) */
-    int32_t chunk_len;  /* chunk length for ALGO_CHUNKED: 64 (0 means 64) */
+    int32_t chunk_len;  /* chunk length of ALGO_CHUNKED, fixed per head size: 64 at D = 64,
+                           32 at D = 128; 0 selects it, other values are EUNSUPPORTED */
     float   y_scale;    /* multiplies S_t r_t; 1.0f for the plain readout */
     int32_t reserved;   /* must be 0 */
     const float* r_k;   /* [H, D] fp32 device pointer, or NULL for no bonus term */
@@ -115,7 +116,8 @@ int wkv7_decode_step(const wkv7_desc* desc,
 
 /* Which algorithm wkv7_forward would run for this descriptor (WKV7_ALGO_SCAN or
  * WKV7_ALGO_CHUNKED), or a negative wkv7_status if the descriptor is invalid.
- * Host only: no HIP call. */
+ * AUTO picks the chunked form once T covers one chunk (T >= chunk length),
+ * the scan otherwise.  Host only: no HIP call. */
 int wkv7_resolve_algo(const wkv7_desc* desc);
 
 /* Static name of a status code. */

@@ -69,8 +69,11 @@ int check_desc(const wkv7_desc* d, wkv7::Params* p) {
         return fail(WKV7_EINVAL, "w_mode %d unknown", d->w_mode);
     if (d->algo < WKV7_ALGO_AUTO || d->algo > WKV7_ALGO_CHUNKED)
         return fail(WKV7_EINVAL, "algo %d unknown", d->algo);
-    int L = d->chunk_len == 0 ? 64 : d->chunk_len;
-    if (L != 64) return fail(WKV7_EUNSUPPORTED, "chunk_len=%d; supported: 64", d->chunk_len);
+    // Each chunked kernel has one chunk length: 64 at D = 64, 32 at D = 128.
+    const int L_native = d->D == 64 ? 64 : 32;
+    int L = d->chunk_len == 0 ? L_native : d->chunk_len;
+    if (L != L_native)
+        return fail(WKV7_EUNSUPPORTED, "chunk_len=%d; supported at D=%d: %d (or 0)", d->chunk_len, d->D, L_native);
     if (!std::isfinite(d->y_scale)) return fail(WKV7_EINVAL, "y_scale is not finite");
     if (d->r_k && !aligned16(d->r_k)) return fail(WKV7_EINVAL, "r_k is not 16-byte aligned");
     // Grid and index limits: (b, h) pairs index a 1-D grid; element offsets are 64-bit.
@@ -108,7 +111,7 @@ int check_ptrs(const wkv7::Params& p, const void* const* in6, const void* y,
 int resolve_algo(const wkv7::Params& p, int requested) {
     if (requested == WKV7_ALGO_SCAN) return WKV7_ALGO_SCAN;
     if (requested == WKV7_ALGO_CHUNKED) return WKV7_ALGO_CHUNKED;
-    return (p.D == 64 && p.T >= p.chunk_len) ? WKV7_ALGO_CHUNKED : WKV7_ALGO_SCAN;
+    return p.T >= p.chunk_len ? WKV7_ALGO_CHUNKED : WKV7_ALGO_SCAN;
 }
 
 int finish_launch(hipError_t e, const char* what) {
@@ -132,8 +135,6 @@ int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void
     const void* in6[6] = {r, w, k, v, a, b};
     if ((rc = check_ptrs(p, in6, y, state_in, state_out))) return rc;
     int algo = resolve_algo(p, desc->algo);
-    if (algo == WKV7_ALGO_CHUNKED && p.D != 64)
-        return fail(WKV7_EUNSUPPORTED, "chunked algorithm supports D=64 (got D=%d)", p.D);
     p.r = r; p.w = w; p.k = k; p.v = v; p.a = a; p.b = b;
     p.s0 = state_in; p.y = y; p.s1 = state_out;
     if (int64_t(p.B) * p.H == 0) return WKV7_OK;
@@ -143,7 +144,9 @@ int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void
         if (!state_out) return WKV7_OK;
         return finish_launch(wkv7::launch_state_copy(p, s), "state copy");
     }
-    if (algo == WKV7_ALGO_CHUNKED) return finish_launch(wkv7::launch_chunked(p, s), "chunked");
+    if (algo == WKV7_ALGO_CHUNKED)
+        return p.D == 64 ? finish_launch(wkv7::launch_chunked(p, s), "chunked")
+                         : finish_launch(wkv7::launch_chunked128(p, s), "chunked (D=128)");
     return finish_launch(wkv7::launch_scan(p, s), "scan");
 }
 

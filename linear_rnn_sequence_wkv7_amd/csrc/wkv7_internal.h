@@ -25,7 +25,8 @@ struct Params {
 // Each launcher enqueues its kernel(s) on `stream` and returns the HIP status
 // of the launch.  They assume Params passed validation in wkv7_api.cpp.
 hipError_t launch_scan(const Params& p, hipStream_t stream);
-hipError_t launch_chunked(const Params& p, hipStream_t stream);
+hipError_t launch_chunked(const Params& p, hipStream_t stream);      // D = 64, L = 64
+hipError_t launch_chunked128(const Params& p, hipStream_t stream);   // D = 128, L = 32
 hipError_t launch_decode(const Params& p, hipStream_t stream);
 // state_out <- state_in (or zeros) for T == 0.
 hipError_t launch_state_copy(const Params& p, hipStream_t stream);

@@ -64,7 +64,7 @@ class Workload:
     s0_std: float             # 0 -> zero initial state (passed as None)
     seed: int
     steps: int = 1            # decode steps (decode workloads only)
-    chunk_len: int = 64
+    chunk_len: int = 0          # 0: the chunked kernel's own length (64 at D=64, 32 at D=128)
     y_scale: float = 1.0
     rk_std: float = 0.0       # > 0 -> per-head/dim bonus weights r_k ~ N(0, rk_std^2)
     kk_from_k: bool = False   # removal key = normalise(repeated k) instead of an independent draw

@@ -84,7 +84,7 @@ def _status_name(code: int) -> str:
 
 
 def make_desc(B, T, H, D, *, H_kv=None, in_dtype="bf16", y_dtype="bf16", w_mode="decay",
-              algo="auto", chunk_len=64, y_scale=1.0, r_k_ptr=None) -> Desc:
+              algo="auto", chunk_len=0, y_scale=1.0, r_k_ptr=None) -> Desc:
     return Desc(B=B, T=T, H=H, H_kv=H if H_kv is None else H_kv, D=D,
                 in_dtype=_DTYPES[in_dtype], y_dtype=_DTYPES[y_dtype], w_mode=W_MODES[w_mode],
                 algo=ALGOS[algo], chunk_len=chunk_len, y_scale=float(y_scale), reserved=0,
@@ -151,7 +151,7 @@ def _call(fn_name, desc, r, w, k, v, a, b, state, y, state_out):
 
 
 def wkv7_forward(r, w, k, v, a, b, state=None, *, w_mode: str = "decay", y_dtype: Optional[str] = None,
-                 algo: str = "auto", chunk_len: int = 64, y_scale: float = 1.0, r_k=None,
+                 algo: str = "auto", chunk_len: int = 0, y_scale: float = 1.0, r_k=None,
                  y=None, state_out=None, return_state: bool = True) -> Tuple[object, object]:
     """Run wkv7_forward on torch GPU tensors.
 

@@ -66,6 +66,7 @@ def good(**kw):
     (good(H=4, H_kv=3), W.WKV7_EINVAL),
     (good(H=4, H_kv=8), W.WKV7_EINVAL),
     (good(chunk_len=32), W.WKV7_EUNSUPPORTED),
+    (good(D=128, chunk_len=64), W.WKV7_EUNSUPPORTED),
 ])
 def test_bad_descriptor_rejected(desc, code):
     assert _call(desc) == code
@@ -113,6 +114,13 @@ def test_empty_problem_is_a_no_op():
 def test_resolve_algo():
     assert W.wkv7_resolve_algo(2, 8, 4, 64, algo="scan") == "scan"
     assert W.wkv7_resolve_algo(2, 8, 4, 64, algo="chunked") == "chunked"
-    assert W.wkv7_resolve_algo(2, 8, 4, 64) in ("scan", "chunked")
+    # AUTO: chunked once T covers one chunk (64 tokens at D = 64, 32 at D = 128).
+    assert W.wkv7_resolve_algo(2, 63, 4, 64) == "scan"
+    assert W.wkv7_resolve_algo(2, 64, 4, 64) == "chunked"
+    assert W.wkv7_resolve_algo(2, 31, 4, 128) == "scan"
+    assert W.wkv7_resolve_algo(2, 32, 4, 128) == "chunked"
+    assert W.wkv7_resolve_algo(2, 32, 4, 128, chunk_len=32) == "chunked"
+    with pytest.raises(W.Wkv7Error):
+        W.wkv7_resolve_algo(2, 8, 4, 128, chunk_len=64)
     with pytest.raises(W.Wkv7Error):
         W.wkv7_resolve_algo(2, 8, 4, 96)

@@ -71,8 +71,6 @@ SWEEP = [
 @pytest.mark.parametrize("algo", FWD_ALGOS)
 @pytest.mark.parametrize("case", SWEEP, ids=lambda c: "D{}_B{}_T{}_H{}_kv{}_{}_{}_{}_s{}_e{}".format(*c))
 def test_forward_sweep(case, algo):
-    if algo == "chunked" and case[0] != 64:
-        pytest.skip("the chunked kernel covers D = 64")
     wl = make_case(*case, seed=7 + case[2])
     x = G.make_inputs(wl)
     y_ref, s_ref = oracle_full(wl, x)
@@ -81,10 +79,11 @@ def test_forward_sweep(case, algo):
     P.check("state", s, s_ref, TAU[algo])
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("algo", FWD_ALGOS)
-def test_state_in_place_and_split(algo):
+def test_state_in_place_and_split(algo, D):
     """state_out may alias state_in; forward(T1) then forward(T2) from its state == forward(T1+T2)."""
-    wl = make_case(64, 2, 96, 2, 2, "bf16", "f32", "decay", 0.1, False, seed=3)
+    wl = make_case(D, 2, 96, 2, 2, "bf16", "f32", "decay", 0.1, False, seed=3)
     x = G.make_inputs(wl)
     y_ref, s_ref = oracle_full(wl, x)
     d = dev_inputs(x)
@@ -115,9 +114,10 @@ def test_zero_tokens_copies_state():
     assert np.all(to_host(s) == 0.0)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("algo", FWD_ALGOS)
-def test_bitwise_deterministic(algo):
-    wl = make_case(64, 2, 150, 4, 4, "bf16", "bf16", "decay", 0.1, False, seed=9)
+def test_bitwise_deterministic(algo, D):
+    wl = make_case(D, 2, 150, 4, 4, "bf16", "bf16", "decay", 0.1, False, seed=9)
     x = G.make_inputs(wl)
     y1, s1 = run_forward(wl, x, algo)
     y2, s2 = run_forward(wl, x, algo)
@@ -218,8 +218,6 @@ def test_workload_prefill(algo):
 
 @pytest.mark.parametrize("algo", FWD_ALGOS)
 def test_workload_hxa07d(algo):
-    if algo == "chunked":
-        pytest.skip("the chunked kernel covers D = 64")
     _sampled(G.WORKLOADS["hxa07d_bf16_b2_t16384_h32_kv8_d128"], algo, 4)
 
 
