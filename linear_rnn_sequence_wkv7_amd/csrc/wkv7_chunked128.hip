@@ -236,8 +236,11 @@ void chunked128_kernel(Args g) {
     // Column threads (P1a): key column jc, tokens [8 pc, 8 pc + 8); threads with
     // jc < 32 also carry value column 32 q + jc.  Row threads (P1b): token tr,
     // key columns [8 qr, 8 qr + 8).
+    // Row-thread lanes: 8 key groups x 2 tokens per 16-lane LDS pass, which keeps the
+    // 8-byte operand stores free of bank conflicts at this pitch; lanes l and l ^ 32
+    // share a token.
     const int jc = tid & (DK - 1), pc = tid >> 7;
-    const int tr = tid >> 4, qr = tid & 15;
+    const int tr = 4 * w + ((l >> 3) & 3), qr = (l & 7) | ((l >> 5) << 3);
     float rk8[8];
     if constexpr (EPI) {
         #pragma unroll
@@ -414,18 +417,22 @@ void chunked128_kernel(Args g) {
             sts<uint2>(smem + OFF_KTL, o, make_uint2(ktl[0], ktl[1]));
             sts<uint2>(smem + OFF_KTL, o + 16, make_uint2(ktl[2], ktl[3]));
             if constexpr (EPI) {
-                // The 16 threads of a token row are one 16-lane row of a wave.
-                bonus_part = sum16(bonus_part);
+                // The 16 threads of a token row: 8 consecutive lanes and the same 8 lanes + 32.
+                bonus_part += dpp<kDppQuadXor1>(bonus_part);
+                bonus_part += dpp<kDppQuadXor2>(bonus_part);
+                bonus_part += dpp<kDppRowHalfMirror>(bonus_part);
+                bonus_part += __shfl_xor(bonus_part, 32);
                 if (qr == 0) sts<float>(smem + OFF_BONUS, tr * 4, bonus_part);
             }
         }
         __syncthreads();
 
         // ---------------- P2: the four L x L matrices; inverses of the diagonal blocks ----------------
-        // Units (tile, group) for waves 0..5: tile w >> 1 of (0,0), (1,0), (1,1);
-        // group w & 1: 0 = A_ab, A_ak; 1 = A_rb, A_rk.  Waves 0 and 4 own the
-        // diagonal blocks of A_ab and also form their inverses.
-        const int ptile = w >> 1, pgrp = w & 1;
+        // Units (tile, group) of tiles 0 = (0,0), 1 = (1,0), 2 = (1,1) and groups
+        // 0 = A_ab, A_ak; 1 = A_rb, A_rk: waves 0..5 take (0,0) (2,0) (0,1) (2,1)
+        // (1,1) (1,0), so that waves 0 and 1, which own the diagonal blocks of A_ab
+        // and form their inverses, sit on different SIMDs.  Waves 6, 7 clear tiles.
+        const int ptile = w < 4 ? 2 * (w & 1) : 1, pgrp = w < 4 ? (w >> 1) : (w == 4 ? 1 : 0);
         const int ptb = ptile >= 1 ? 1 : 0, psb = ptile == 2 ? 1 : 0;
         const bool pdiag = pgrp == 0 && ptb == psb && w < 6;
         f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, Nsw = acc0;
