@@ -32,6 +32,7 @@ PEAK_BF16_MFMA_TFLOPS = 2500.0    # dense bf16 matrix peak
 KERNEL_SOURCES = {
     "scan": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_scan.hip",
     "chunked": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_chunked.hip",
+    "chunked128": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_chunked128.hip",
     "decode": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_decode.hip",
 }
 
@@ -156,9 +157,9 @@ def main(argv=None) -> int:
         nbytes = wl.B * wl.H * (2 * wl.D * wl.D * 4) + wl.B * wl.D * (wl.H * 5 + wl.H_kv * 2) * 2
         flops = 9 * wl.D * wl.D * wl.B * wl.H
     else:
-        kind = wkv7.wkv7_resolve_algo(wl.B, wl.T, wl.H, wl.D, H_kv=wl.H_kv, algo=a.algo if a.algo != "auto" else wl.algo,
+        algo = wkv7.wkv7_resolve_algo(wl.B, wl.T, wl.H, wl.D, H_kv=wl.H_kv, algo=a.algo if a.algo != "auto" else wl.algo,
                                       in_dtype=wl.in_dtype, y_dtype=wl.y_dtype, w_mode=wl.w_mode)
-        algo = kind
+        kind = "chunked128" if algo == "chunked" and wl.D == 128 else algo
         y = torch.empty((wl.B, wl.T, wl.H, wl.D), dtype=torch.bfloat16 if wl.y_dtype == "bf16" else torch.float32,
                         device="cuda")
         s_out = torch.empty((wl.B, wl.H, wl.D, wl.D), dtype=torch.float32, device="cuda")

@@ -435,33 +435,26 @@ void chunked128_kernel(Args g) {
         const int ptile = w < 4 ? 2 * (w & 1) : 1, pgrp = w < 4 ? (w >> 1) : (w == 4 ? 1 : 0);
         const int ptb = ptile >= 1 ? 1 : 0, psb = ptile == 2 ? 1 : 0;
         const bool pdiag = pgrp == 0 && ptb == psb && w < 6;
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, Nsw = acc0;
-        if (w < 6) {
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+        if (pdiag) {
+            // Diagonal unit: A_ab and its swapped form first, so that the inverse chain
+            // can overlap the A_ak products.
+            f32x4 Nsw = acc0;   // C(N): the block with operands swapped
             #pragma unroll
             for (int kq = 0; kq < 4; ++kq) {
-                const int ya = (16 * psb * PK + 32 * kq) * 2 + opK;
                 const int xb = (16 * ptb * PK + 32 * kq) * 2 + opK;
-                const bf16x8 Bt8 = lds<bf16x8>(smem + OFF_BT, ya);
-                const bf16x8 Kh8 = lds<bf16x8>(smem + OFF_KTH, ya);
-                const bf16x8 Kl8 = lds<bf16x8>(smem + OFF_KTL, ya);
-                if (pgrp == 0) {
-                    const bf16x8 At8 = lds<bf16x8>(smem + OFF_AT, xb);
-                    acc0 = mfma32(Bt8, At8, acc0);
-                    acc1 = mfma32(Kh8, At8, acc1);
-                    acc1 = mfma32(Kl8, At8, acc1);
-                    if (pdiag) Nsw = mfma32(At8, Bt8, Nsw);
-                } else {
-                    const bf16x8 Rh8 = lds<bf16x8>(smem + OFF_RTH, xb);
-                    const bf16x8 Rl8 = lds<bf16x8>(smem + OFF_RTL, xb);
-                    acc0 = mfma32(Bt8, Rh8, acc0);
-                    acc0 = mfma32(Bt8, Rl8, acc0);
-                    acc1 = mfma32(Kh8, Rh8, acc1);
-                    acc1 = mfma32(Kh8, Rl8, acc1);
-                    acc1 = mfma32(Kl8, Rh8, acc1);
-                }
+                const bf16x8 Bt8 = lds<bf16x8>(smem + OFF_BT, xb);
+                const bf16x8 At8 = lds<bf16x8>(smem + OFF_AT, xb);
+                acc0 = mfma32(Bt8, At8, acc0);
+                Nsw = mfma32(At8, Bt8, Nsw);
             }
-        }
-        if (pdiag) {
+            #pragma unroll
+            for (int kq = 0; kq < 4; ++kq) {
+                const int xb = (16 * ptb * PK + 32 * kq) * 2 + opK;
+                const bf16x8 At8 = lds<bf16x8>(smem + OFF_AT, xb);
+                acc1 = mfma32(lds<bf16x8>(smem + OFF_KTH, xb), At8, acc1);
+                acc1 = mfma32(lds<bf16x8>(smem + OFF_KTL, xb), At8, acc1);
+            }
             // (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8) for the strictly lower block N;
             // acc0 is C(N^T) (t = lr, s = 4 lq + r), Nsw is C(N) (s = lr, t = 4 lq + r).
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -488,6 +481,29 @@ void chunked128_kernel(Args g) {
             const f32x4 Dt = prod(N8 + I4, G4t);           // lane holds D[lr][4 lq + r]
             sts<uint2>(smem + OFF_DINV, ((ptb * 16 + lr) * PD + 4 * lq) * 2,
                        make_uint2(pack_bf16(Dt[0], Dt[1]), pack_bf16(Dt[2], Dt[3])));
+        } else if (w < 6) {
+            #pragma unroll
+            for (int kq = 0; kq < 4; ++kq) {
+                const int ya = (16 * psb * PK + 32 * kq) * 2 + opK;
+                const int xb = (16 * ptb * PK + 32 * kq) * 2 + opK;
+                const bf16x8 Bt8 = lds<bf16x8>(smem + OFF_BT, ya);
+                const bf16x8 Kh8 = lds<bf16x8>(smem + OFF_KTH, ya);
+                const bf16x8 Kl8 = lds<bf16x8>(smem + OFF_KTL, ya);
+                if (pgrp == 0) {
+                    const bf16x8 At8 = lds<bf16x8>(smem + OFF_AT, xb);
+                    acc0 = mfma32(Bt8, At8, acc0);
+                    acc1 = mfma32(Kh8, At8, acc1);
+                    acc1 = mfma32(Kl8, At8, acc1);
+                } else {
+                    const bf16x8 Rh8 = lds<bf16x8>(smem + OFF_RTH, xb);
+                    const bf16x8 Rl8 = lds<bf16x8>(smem + OFF_RTL, xb);
+                    acc0 = mfma32(Bt8, Rh8, acc0);
+                    acc0 = mfma32(Bt8, Rl8, acc0);
+                    acc1 = mfma32(Kh8, Rh8, acc1);
+                    acc1 = mfma32(Kh8, Rl8, acc1);
+                    acc1 = mfma32(Kl8, Rh8, acc1);
+                }
+            }
         }
         __syncthreads();   // B~ / K~ (region 1) are dead now
         if (w < 6) {
