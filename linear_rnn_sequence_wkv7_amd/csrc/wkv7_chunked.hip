@@ -71,9 +71,10 @@ constexpr int MAT = 64 * P72 * 2;
 constexpr int PD = 20;         // pitch of the 16 x 16 diagonal blocks
 constexpr int PE = 68;         // fp32 pitch of the decay tables
 
-// LDS map (bytes).  Region 1 holds B~, K~ during P1..P2 and A_ab, A_rb
-// afterwards; region 2 holds the decay tables
-// 2^g, 2^-g and the column-segment totals during P1 and A_ak, A_rk afterwards.
+// LDS map (bytes).  Region 1 holds B~, K~ during P1b..P2 and A_ab, A_rb
+// afterwards; region 2 holds the decay tables 2^g, 2^-g of the next chunk from
+// P5 on (written after every wave has left P4) until P1b, and A_ak, A_rk from
+// P2 to P4.
 // Pair-interleaved axis (see above): At, Rt, Bt, Kt (key axis), A_ab, A_rb,
 // Bh^T (token axis).  Natural order: A_ak, A_rk, Kh^T, V^T.
 constexpr int OFF_AT = 0;
@@ -92,7 +93,6 @@ constexpr int OFF_ARB = OFF_R1 + MAT;      // A_rb [t][s] bf16
 constexpr int OFF_R2 = OFF_R1 + 3 * MAT;
 constexpr int OFF_E = OFF_R2;              // fp32 [64][PE] 2^g
 constexpr int OFF_EI = OFF_R2 + 64 * PE * 4;   // fp32 [64][PE] 2^-g
-constexpr int OFF_TOT = OFF_EI + 64 * PE * 4;  // fp32 [8][64] column-segment totals
 constexpr int OFF_AKH = OFF_R2;            // A_ak [t][s] hi / lo
 constexpr int OFF_AKL = OFF_R2 + MAT;
 constexpr int OFF_RKH = OFF_R2 + 2 * MAT;  // A_rk [t][s] hi / lo
@@ -102,10 +102,11 @@ constexpr int OFF_EL = OFF_DINV + 4 * 16 * PD * 2;   // fp32 [64] 2^g_L
 constexpr int OFF_BONUS = OFF_EL + 256;    // fp32 [64] hxa07D bonus coefficient per token
 constexpr int OFF_XS = OFF_BONUS + 256;    // state halves exchanged by the two waves of a strip
 constexpr int XS_BYTES = 4 * 2 * 2 * 64 * 16;   // [strip][half][hi/lo][lane] 16 B
-constexpr int OFF_VTL = OFF_XS + XS_BYTES; // V^T lo part (fp32 inputs only)
+constexpr int OFF_TOT = OFF_XS + XS_BYTES; // fp32 [8][64] column-segment totals (own slot: written during P5)
+constexpr int OFF_VTL = OFF_TOT + 8 * 64 * 4; // V^T lo part (fp32 inputs only)
 constexpr int SMEM_BF16 = OFF_VTL;
 constexpr int SMEM_F32 = OFF_VTL + MAT;
-static_assert(2 * 64 * PE * 4 + 8 * 64 * 4 <= 4 * MAT, "decay tables fit");
+static_assert(2 * 64 * PE * 4 <= 4 * MAT, "decay tables fit");
 static_assert(SMEM_F32 <= 160 * 1024, "LDS budget");
 
 // Position of index k (0..63) on a pair-interleaved axis.
@@ -331,6 +332,89 @@ void chunked_kernel(ChunkArgs g) {
     const int xs_own = ((strip * 2 + hf) * 2 * 64 + l) * 16;
     const int xs_oth = ((strip * 2 + (1 - hf)) * 2 * 64 + l) * 16;
 
+    // ---------------- P1a: decay prefix down each key column ----------------
+    // Runs one chunk ahead: the prefix of chunk c + 1 during P5 of chunk c, its
+    // tables after the barrier that follows P5.  Decay mode: running products of
+    // w, 2^-g as a reciprocal; log-decay mode: running sums of log2 w =
+    // -exp(x) log2(e), then exp2.  The outputs that P6 / P7 of chunk c still read
+    // from LDS (Kh^T, V^T, Bh^T, 2^g_L) stay in registers (d_*) until chunk c + 1
+    // begins.
+    float pre[8];
+    uint32_t d_bh4[4], d_khh[4], d_khl[4], d_vh[4], d_vl[4];
+    float d_EL = 0.f;
+    auto p1a_prefix = [&](int c0) {
+        float run = LOGW ? 0.f : 1.f;
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = __uint_as_float(cw[e]);
+            const bool ok = c0 + 8 * pc + e < T;     // wave-uniform; w = 1 past the end
+            if constexpr (LOGW) run += ok ? -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e : 0.f;
+            else run *= ok ? x : 1.f;
+            pre[e] = run;
+        }
+        sts<float>(smem + OFF_TOT, (pc * 64 + jc) * 4, run);
+    };
+    auto p1a_tables = [&]() {
+        float off = LOGW ? 0.f : 1.f, total = off;
+        #pragma unroll
+        for (int pp = 0; pp < 8; ++pp) {
+            const float tp = lds<float>(smem + OFF_TOT, (pp * 64 + jc) * 4);
+            if constexpr (LOGW) {
+                off += pp < pc ? tp : 0.f;
+                total += tp;
+            } else {
+                off *= pp < pc ? tp : 1.f;
+                total *= tp;
+            }
+        }
+        const float EL = LOGW ? __builtin_amdgcn_exp2f(total) : total;
+        d_EL = EL;
+        #pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            float Eh[2];
+            #pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                float E, Ei;
+                if constexpr (LOGW) {
+                    const float gv = pre[e + u] + off;
+                    E = __builtin_amdgcn_exp2f(gv);
+                    Ei = __builtin_amdgcn_exp2f(-gv);
+                } else {
+                    E = pre[e + u] * off;
+                    Ei = __builtin_amdgcn_rcpf(E);
+                }
+                sts<float>(smem + OFF_E, ((8 * pc + e + u) * PE + jc) * 4, E);
+                sts<float>(smem + OFF_EI, ((8 * pc + e + u) * PE + jc) * 4, Ei);
+                Eh[u] = EL * Ei;
+            }
+            const float b0 = __uint_as_float(cb[e]), b1 = __uint_as_float(cb[e + 1]);
+            const float k0 = __uint_as_float(ck[e]), k1 = __uint_as_float(ck[e + 1]);
+            d_bh4[e / 2] = pack_bf16(b0 * Eh[0], b1 * Eh[1]);
+            split2(k0 * Eh[0], k1 * Eh[1], d_khh[e / 2], d_khl[e / 2]);
+            if constexpr (VSPLIT) {
+                split2(__uint_as_float(cv[e]), __uint_as_float(cv[e + 1]), d_vh[e / 2], d_vl[e / 2]);
+            } else {
+                d_vh[e / 2] = (cv[e] >> 16) | (cv[e + 1] & 0xffff0000u);   // bf16 bits as they are
+            }
+        }
+    };
+    auto p1a_store = [&]() {
+        if (pc == 0) sts<float>(smem + OFF_EL, jc * 4, d_EL);
+        const int o = (jc * P72 + 8 * pc) * 2;
+        sts<uint4>(smem + OFF_KHTH, o, make_uint4(d_khh[0], d_khh[1], d_khh[2], d_khh[3]));
+        sts<uint4>(smem + OFF_KHTL, o, make_uint4(d_khl[0], d_khl[1], d_khl[2], d_khl[3]));
+        sts<uint4>(smem + OFF_VT, o, make_uint4(d_vh[0], d_vh[1], d_vh[2], d_vh[3]));
+        if constexpr (VSPLIT) sts<uint4>(smem + OFF_VTL, o, make_uint4(d_vl[0], d_vl[1], d_vl[2], d_vl[3]));
+        // Bh^T on the pair-interleaved token axis: tokens 8 pc + (0..3) and 8 pc + (4..7).
+        const int ob = (jc * P72 + pairpos(8 * pc)) * 2;
+        sts<uint2>(smem + OFF_BHT, ob, make_uint2(d_bh4[0], d_bh4[1]));
+        sts<uint2>(smem + OFF_BHT, ob + 16, make_uint2(d_bh4[2], d_bh4[3]));
+    };
+    p1a_prefix(0);
+    __syncthreads();
+    p1a_tables();
+    __syncthreads();
+
     const int nchunks = (T + L - 1) / L;
     for (int ch = 0; ch < nchunks; ++ch) {
         const int c0 = ch * L;
@@ -345,79 +429,7 @@ void chunked_kernel(ChunkArgs g) {
             sts<bf16x8>(smem + OFF_XS, xs_own, SoH);
             sts<bf16x8>(smem + OFF_XS, xs_own + 64 * 16, SoL);
         }
-
-        // ---------------- P1a: decay prefix down each key column ----------------
-        // Decay mode: running products of w, 2^-g as a reciprocal; log-decay mode:
-        // running sums of log2 w = -exp(x) log2(e), then exp2.
-        float pre[8];
-        {
-            float run = LOGW ? 0.f : 1.f;
-            #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = __uint_as_float(cw[e]);
-                const bool ok = c0 + 8 * pc + e < T;     // wave-uniform; w = 1 past the end
-                if constexpr (LOGW) run += ok ? -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e : 0.f;
-                else run *= ok ? x : 1.f;
-                pre[e] = run;
-            }
-            sts<float>(smem + OFF_TOT, (pc * 64 + jc) * 4, run);
-        }
-        __syncthreads();
-        {
-            float off = LOGW ? 0.f : 1.f, total = off;
-            #pragma unroll
-            for (int pp = 0; pp < 8; ++pp) {
-                const float tp = lds<float>(smem + OFF_TOT, (pp * 64 + jc) * 4);
-                if constexpr (LOGW) {
-                    off += pp < pc ? tp : 0.f;
-                    total += tp;
-                } else {
-                    off *= pp < pc ? tp : 1.f;
-                    total *= tp;
-                }
-            }
-            const float EL = LOGW ? __builtin_amdgcn_exp2f(total) : total;
-            if (pc == 0) sts<float>(smem + OFF_EL, jc * 4, EL);
-            uint32_t bh4[4], khh[4], khl[4], vh[4], vl[4];
-            #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                float Eh[2];
-                #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    float E, Ei;
-                    if constexpr (LOGW) {
-                        const float gv = pre[e + u] + off;
-                        E = __builtin_amdgcn_exp2f(gv);
-                        Ei = __builtin_amdgcn_exp2f(-gv);
-                    } else {
-                        E = pre[e + u] * off;
-                        Ei = __builtin_amdgcn_rcpf(E);
-                    }
-                    sts<float>(smem + OFF_E, ((8 * pc + e + u) * PE + jc) * 4, E);
-                    sts<float>(smem + OFF_EI, ((8 * pc + e + u) * PE + jc) * 4, Ei);
-                    Eh[u] = EL * Ei;
-                }
-                const float b0 = __uint_as_float(cb[e]), b1 = __uint_as_float(cb[e + 1]);
-                const float k0 = __uint_as_float(ck[e]), k1 = __uint_as_float(ck[e + 1]);
-                bh4[e / 2] = pack_bf16(b0 * Eh[0], b1 * Eh[1]);
-                split2(k0 * Eh[0], k1 * Eh[1], khh[e / 2], khl[e / 2]);
-                if constexpr (VSPLIT) {
-                    split2(__uint_as_float(cv[e]), __uint_as_float(cv[e + 1]), vh[e / 2], vl[e / 2]);
-                } else {
-                    vh[e / 2] = (cv[e] >> 16) | (cv[e + 1] & 0xffff0000u);   // bf16 bits as they are
-                }
-            }
-            const int o = (jc * P72 + 8 * pc) * 2;
-            sts<uint4>(smem + OFF_KHTH, o, make_uint4(khh[0], khh[1], khh[2], khh[3]));
-            sts<uint4>(smem + OFF_KHTL, o, make_uint4(khl[0], khl[1], khl[2], khl[3]));
-            sts<uint4>(smem + OFF_VT, o, make_uint4(vh[0], vh[1], vh[2], vh[3]));
-            if constexpr (VSPLIT) sts<uint4>(smem + OFF_VTL, o, make_uint4(vl[0], vl[1], vl[2], vl[3]));
-            // Bh^T on the pair-interleaved token axis: tokens 8 pc + (0..3) and 8 pc + (4..7).
-            const int ob = (jc * P72 + pairpos(8 * pc)) * 2;
-            sts<uint2>(smem + OFF_BHT, ob, make_uint2(bh4[0], bh4[1]));
-            sts<uint2>(smem + OFF_BHT, ob + 16, make_uint2(bh4[2], bh4[3]));
-        }
-        __syncthreads();
+        p1a_store();
 
         // ---------------- P1b: row-major scaled operands ----------------
         {
@@ -468,6 +480,8 @@ void chunked_kernel(ChunkArgs g) {
                 if (qr == 0) sts<float>(smem + OFF_BONUS, tr * 4, bonus_part);
             }
         }
+        // Next chunk's inputs: columns for its prefix during P5, rows for its P1b.
+        load_chunk(c0 + L);
         __syncthreads();
 
         // ---------------- P2: the four L x L matrices; inverses of the diagonal blocks ----------------
@@ -585,7 +599,7 @@ void chunked_kernel(ChunkArgs g) {
             const int tb = m ? 2 : 0, sb = tb + 1;
             sts<uint4>(smem + base, ((16 * tb + rw) * P72 + 16 * sb + 8 * half) * 2, make_uint4(0, 0, 0, 0));
         }
-        __syncthreads();   // everything P4..P7 read from LDS is in place; no barrier until the chunk ends
+        __syncthreads();   // everything P4..P7 read from LDS is in place
 
         // ---------------- P4: RHS = At S0^T + A_ak V (whole strip), Y's SA-free part ----------------
         // State operands: key pair hf from this wave's registers (own), pair 1 - hf from the partner.
@@ -650,6 +664,8 @@ void chunked_kernel(ChunkArgs g) {
             Yacc[u] = acc;
         }
 
+        p1a_prefix(c0 + L);
+
         // ---------------- P5: SA = (I - A_ab)^-1 RHS, blocked forward substitution ----------------
         s16x4 SAh[4], SAl[4];
         #pragma unroll
@@ -673,8 +689,8 @@ void chunked_kernel(ChunkArgs g) {
         const bf16x8 SPh[2] = {cat(SAh[0], SAh[1]), cat(SAh[2], SAh[3])};
         const bf16x8 SPl[2] = {cat(SAl[0], SAl[1]), cat(SAl[2], SAl[3])};
 
-        // Next chunk's inputs: in flight during P6, P7 and the start of the next chunk.
-        load_chunk(c0 + L);
+        __syncthreads();   // next chunk's column totals visible; every wave is past P4 (region 2 free)
+        p1a_tables();
 
         // ---------------- P6: Y += A_rb SA on token tiles ytile(hf, 0..1); epilogue; store ----------------
         {
