@@ -266,15 +266,16 @@ void chunked128_kernel(Args g) {
 
     uint32_t cw[8], cb[8], ck[8], cv[8];
     Row8<Tin> rr, ra, rb, rkv;
-    auto load_chunk = [&](int c0) {
+    // Columns of a chunk (for its P1a) and rows (for its P1b) load separately: the
+    // next chunk's columns are requested at the start of a chunk, its rows after P1b.
+    auto chunk_rsrc = [&](int c0, const char* base, uint32_t stride) {
         const int nv = max(0, min(T - c0, L));
         const int64_t t0 = nv > 0 ? tok0 + c0 : 0;
-        const rsrc_t Rr = make_rsrc(rp + t0 * stq, uint32_t(nv) * stq);
-        const rsrc_t Rw = make_rsrc(wp + t0 * stq, uint32_t(nv) * stq);
-        const rsrc_t Ra = make_rsrc(ap + t0 * stq, uint32_t(nv) * stq);
-        const rsrc_t Rb = make_rsrc(bp + t0 * stq, uint32_t(nv) * stq);
-        const rsrc_t Rk = make_rsrc(kp_ + t0 * stkv, uint32_t(nv) * stkv);
-        const rsrc_t Rv = make_rsrc(vp + t0 * stkv, uint32_t(nv) * stkv);
+        return make_rsrc(base + t0 * stride, uint32_t(nv) * stride);
+    };
+    auto load_cols = [&](int c0) {
+        const rsrc_t Rw = chunk_rsrc(c0, wp, stq), Rb = chunk_rsrc(c0, bp, stq);
+        const rsrc_t Rk = chunk_rsrc(c0, kp_, stkv), Rv = chunk_rsrc(c0, vp, stkv);
         #pragma unroll
         for (int e = 0; e < 8; ++e) {
             cw[e] = Buf<Tin>::load1(Rw, col_q[e]);
@@ -282,16 +283,101 @@ void chunked128_kernel(Args g) {
             ck[e] = Buf<Tin>::load1(Rk, col_kv[e]);
             cv[e] = Buf<Tin>::load1(Rv, col_v[e]);
         }
-        rr.load(Rr, row_q);
-        ra.load(Ra, row_q);
-        rb.load(Rb, row_q);
-        rkv.load(Rk, row_kv);
     };
-    load_chunk(0);
+    auto load_rows = [&](int c0) {
+        rr.load(chunk_rsrc(c0, rp, stq), row_q);
+        ra.load(chunk_rsrc(c0, ap, stq), row_q);
+        rb.load(chunk_rsrc(c0, bp, stq), row_q);
+        rkv.load(chunk_rsrc(c0, kp_, stkv), row_kv);
+    };
+    load_cols(0);
+    load_rows(0);
 
     const int opK = (lr * PK + 8 * lq) * 2;   // 32-deep operand: row lr, k = 8 lq .. 8 lq + 7 ([L][DK])
     const int opT = (lr * PT + 8 * lq) * 2;   // same on the [*][L] matrices
     const int xs_own = ((sg * 4 + kp) * 2 * 64 + l) * 16;
+
+    // ---------------- P1a: decay prefix down each key column ----------------
+    // Runs one chunk ahead: the prefix of chunk c + 1 during P2 of chunk c, its
+    // tables after P2's first barrier.  The 2^g / 2^-g tables and the segment
+    // totals have LDS of their own; the outputs P4..P7 of chunk c still read
+    // (Kh^T, V^T, Bh^T, 2^g_L) stay in registers (d_*) until chunk c + 1 begins.
+    float pre[8];
+    uint32_t d_bh4[4], d_khh[4], d_khl[4], d_vh[4], d_vl[4];
+    float d_EL = 0.f;
+    auto p1a_prefix = [&](int c0) {
+        float run = LOGW ? 0.f : 1.f;
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = __uint_as_float(cw[e]);
+            const bool ok = c0 + 8 * pc + e < T;     // wave-uniform; w = 1 past the end
+            if constexpr (LOGW) run += ok ? -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e : 0.f;
+            else run *= ok ? x : 1.f;
+            pre[e] = run;
+        }
+        sts<float>(smem + OFF_TOT, (pc * DK + jc) * 4, run);
+    };
+    auto p1a_tables = [&]() {
+        float off = LOGW ? 0.f : 1.f, total = off;
+        #pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+            const float tp = lds<float>(smem + OFF_TOT, (pp * DK + jc) * 4);
+            if constexpr (LOGW) {
+                off += pp < pc ? tp : 0.f;
+                total += tp;
+            } else {
+                off *= pp < pc ? tp : 1.f;
+                total *= tp;
+            }
+        }
+        const float EL = LOGW ? __builtin_amdgcn_exp2f(total) : total;
+        d_EL = EL;
+        #pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            float Eh[2];
+            #pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                float E, Ei;
+                if constexpr (LOGW) {
+                    const float gv = pre[e + u] + off;
+                    E = __builtin_amdgcn_exp2f(gv);
+                    Ei = __builtin_amdgcn_exp2f(-gv);
+                } else {
+                    E = pre[e + u] * off;
+                    Ei = __builtin_amdgcn_rcpf(E);
+                }
+                sts<float>(smem + OFF_E, ((8 * pc + e + u) * PE + jc) * 4, E);
+                sts<float>(smem + OFF_EI, ((8 * pc + e + u) * PE + jc) * 4, Ei);
+                Eh[u] = EL * Ei;
+            }
+            const float b0 = __uint_as_float(cb[e]), b1 = __uint_as_float(cb[e + 1]);
+            const float k0 = __uint_as_float(ck[e]), k1 = __uint_as_float(ck[e + 1]);
+            d_bh4[e / 2] = pack_bf16(b0 * Eh[0], b1 * Eh[1]);
+            split2(k0 * Eh[0], k1 * Eh[1], d_khh[e / 2], d_khl[e / 2]);
+            if constexpr (VSPLIT) {
+                split2(__uint_as_float(cv[e]), __uint_as_float(cv[e + 1]), d_vh[e / 2], d_vl[e / 2]);
+            } else {
+                d_vh[e / 2] = (cv[e] >> 16) | (cv[e + 1] & 0xffff0000u);
+            }
+        }
+    };
+    auto p1a_store = [&]() {
+        if (pc == 0) sts<float>(smem + OFF_EL, jc * 4, d_EL);
+        const int o = (jc * PT + 8 * pc) * 2;
+        sts<uint4>(smem + OFF_KHTH, o, make_uint4(d_khh[0], d_khh[1], d_khh[2], d_khh[3]));
+        sts<uint4>(smem + OFF_KHTL, o, make_uint4(d_khl[0], d_khl[1], d_khl[2], d_khl[3]));
+        const int ob = (jc * PT + pairpos(8 * pc)) * 2;
+        sts<uint2>(smem + OFF_BHT, ob, make_uint2(d_bh4[0], d_bh4[1]));
+        sts<uint2>(smem + OFF_BHT, ob + 16, make_uint2(d_bh4[2], d_bh4[3]));
+        if (jc < DV) {
+            sts<uint4>(smem + OFF_VT, o, make_uint4(d_vh[0], d_vh[1], d_vh[2], d_vh[3]));
+            if constexpr (VSPLIT) sts<uint4>(smem + OFF_VTL, o, make_uint4(d_vl[0], d_vl[1], d_vl[2], d_vl[3]));
+        }
+    };
+    p1a_prefix(0);
+    __syncthreads();
+    p1a_tables();
+    __syncthreads();
 
     const int nchunks = (T + L - 1) / L;
     for (int ch = 0; ch < nchunks; ++ch) {
@@ -303,78 +389,8 @@ void chunked128_kernel(Args g) {
             sts<bf16x8>(smem + OFF_XS, xs_own, cat(h0, h1));
             sts<bf16x8>(smem + OFF_XS, xs_own + 64 * 16, cat(l0, l1));
         }
-
-        // ---------------- P1a: decay prefix down each key column ----------------
-        float pre[8];
-        {
-            float run = LOGW ? 0.f : 1.f;
-            #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = __uint_as_float(cw[e]);
-                const bool ok = c0 + 8 * pc + e < T;     // wave-uniform; w = 1 past the end
-                if constexpr (LOGW) run += ok ? -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e : 0.f;
-                else run *= ok ? x : 1.f;
-                pre[e] = run;
-            }
-            sts<float>(smem + OFF_TOT, (pc * DK + jc) * 4, run);
-        }
-        __syncthreads();
-        {
-            float off = LOGW ? 0.f : 1.f, total = off;
-            #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                const float tp = lds<float>(smem + OFF_TOT, (pp * DK + jc) * 4);
-                if constexpr (LOGW) {
-                    off += pp < pc ? tp : 0.f;
-                    total += tp;
-                } else {
-                    off *= pp < pc ? tp : 1.f;
-                    total *= tp;
-                }
-            }
-            const float EL = LOGW ? __builtin_amdgcn_exp2f(total) : total;
-            if (pc == 0) sts<float>(smem + OFF_EL, jc * 4, EL);
-            uint32_t bh4[4], khh[4], khl[4], vh[4], vl[4];
-            #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                float Eh[2];
-                #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    float E, Ei;
-                    if constexpr (LOGW) {
-                        const float gv = pre[e + u] + off;
-                        E = __builtin_amdgcn_exp2f(gv);
-                        Ei = __builtin_amdgcn_exp2f(-gv);
-                    } else {
-                        E = pre[e + u] * off;
-                        Ei = __builtin_amdgcn_rcpf(E);
-                    }
-                    sts<float>(smem + OFF_E, ((8 * pc + e + u) * PE + jc) * 4, E);
-                    sts<float>(smem + OFF_EI, ((8 * pc + e + u) * PE + jc) * 4, Ei);
-                    Eh[u] = EL * Ei;
-                }
-                const float b0 = __uint_as_float(cb[e]), b1 = __uint_as_float(cb[e + 1]);
-                const float k0 = __uint_as_float(ck[e]), k1 = __uint_as_float(ck[e + 1]);
-                bh4[e / 2] = pack_bf16(b0 * Eh[0], b1 * Eh[1]);
-                split2(k0 * Eh[0], k1 * Eh[1], khh[e / 2], khl[e / 2]);
-                if constexpr (VSPLIT) {
-                    split2(__uint_as_float(cv[e]), __uint_as_float(cv[e + 1]), vh[e / 2], vl[e / 2]);
-                } else {
-                    vh[e / 2] = (cv[e] >> 16) | (cv[e + 1] & 0xffff0000u);
-                }
-            }
-            const int o = (jc * PT + 8 * pc) * 2;
-            sts<uint4>(smem + OFF_KHTH, o, make_uint4(khh[0], khh[1], khh[2], khh[3]));
-            sts<uint4>(smem + OFF_KHTL, o, make_uint4(khl[0], khl[1], khl[2], khl[3]));
-            const int ob = (jc * PT + pairpos(8 * pc)) * 2;
-            sts<uint2>(smem + OFF_BHT, ob, make_uint2(bh4[0], bh4[1]));
-            sts<uint2>(smem + OFF_BHT, ob + 16, make_uint2(bh4[2], bh4[3]));
-            if (jc < DV) {
-                sts<uint4>(smem + OFF_VT, o, make_uint4(vh[0], vh[1], vh[2], vh[3]));
-                if constexpr (VSPLIT) sts<uint4>(smem + OFF_VTL, o, make_uint4(vl[0], vl[1], vl[2], vl[3]));
-            }
-        }
-        __syncthreads();
+        p1a_store();
+        load_cols(c0 + L);
 
         // ---------------- P1b: row-major scaled operands ----------------
         {
@@ -425,6 +441,7 @@ void chunked128_kernel(Args g) {
                 if (qr == 0) sts<float>(smem + OFF_BONUS, tr * 4, bonus_part);
             }
         }
+        load_rows(c0 + L);
         __syncthreads();
 
         // ---------------- P2: the four L x L matrices; inverses of the diagonal blocks ----------------
@@ -505,7 +522,9 @@ void chunked128_kernel(Args g) {
                 }
             }
         }
-        __syncthreads();   // B~ / K~ (region 1) are dead now
+        p1a_prefix(c0 + L);
+        __syncthreads();   // B~ / K~ (region 1) are dead now; next chunk's column totals visible
+        p1a_tables();
         if (w < 6) {
             f32x4 c0v = acc0, c1v = acc1;
             if (ptb == psb) {
@@ -599,8 +618,6 @@ void chunked128_kernel(Args g) {
             to_operand(sa, SAh[ib], SAl[ib]);
         }
         const bf16x8 SPh = cat(SAh[0], SAh[1]), SPl = cat(SAl[0], SAl[1]);
-
-        load_chunk(c0 + L);
 
         // ---------------- P6: Y += A_rb SA on token tile kp (kp < 2); epilogue; store ----------------
         if (kp < 2) {
