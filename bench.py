@@ -115,9 +115,9 @@ def main(argv=None) -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE {world}); "
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE {world}); "
               "every (batch, head) pair is independent, so a multi-GPU run would shard the batch, "
-              "which this build does not do.", file=sys.stderr)
+              "which is not implemented.", file=sys.stderr)
         return 2
 
     import numpy as np  # noqa: F401
