@@ -300,16 +300,15 @@ void chunked_kernel(ChunkArgs g) {
 
     uint32_t cw[8], cb[8], ck[8], cv[8];
     Row8<Tin> rr, ra, rb, rkv;
-    auto load_chunk = [&](int c0) {
-        // Valid tokens of the chunk (0 past the end: every load reads zero).
-        const int nv = max(0, min(T - c0, L));
+    // Columns of a chunk (for its P1a) and rows (for its P1b) load separately.
+    auto chunk_rsrc = [&](int c0, const char* base, uint32_t stride) {
+        const int nv = max(0, min(T - c0, L));   // valid tokens (0 past the end: every load reads zero)
         const int64_t t0 = nv > 0 ? tok0 + c0 : 0;
-        const rsrc_t Rr = make_rsrc(rp + t0 * stq, uint32_t(nv) * stq);
-        const rsrc_t Rw = make_rsrc(wp + t0 * stq, uint32_t(nv) * stq);
-        const rsrc_t Ra = make_rsrc(ap + t0 * stq, uint32_t(nv) * stq);
-        const rsrc_t Rb = make_rsrc(bp + t0 * stq, uint32_t(nv) * stq);
-        const rsrc_t Rk = make_rsrc(kp + t0 * stkv, uint32_t(nv) * stkv);
-        const rsrc_t Rv = make_rsrc(vp + t0 * stkv, uint32_t(nv) * stkv);
+        return make_rsrc(base + t0 * stride, uint32_t(nv) * stride);
+    };
+    auto load_cols = [&](int c0) {
+        const rsrc_t Rw = chunk_rsrc(c0, wp, stq), Rb = chunk_rsrc(c0, bp, stq);
+        const rsrc_t Rk = chunk_rsrc(c0, kp, stkv), Rv = chunk_rsrc(c0, vp, stkv);
         #pragma unroll
         for (int e = 0; e < 8; ++e) {
             cw[e] = Buf<Tin>::load1(Rw, col_q[e]);
@@ -317,12 +316,15 @@ void chunked_kernel(ChunkArgs g) {
             ck[e] = Buf<Tin>::load1(Rk, col_kv[e]);
             cv[e] = Buf<Tin>::load1(Rv, col_kv[e]);
         }
-        rr.load(Rr, row_q);
-        ra.load(Ra, row_q);
-        rb.load(Rb, row_q);
-        rkv.load(Rk, row_kv);
     };
-    load_chunk(0);
+    auto load_rows = [&](int c0) {
+        rr.load(chunk_rsrc(c0, rp, stq), row_q);
+        ra.load(chunk_rsrc(c0, ap, stq), row_q);
+        rb.load(chunk_rsrc(c0, bp, stq), row_q);
+        rkv.load(chunk_rsrc(c0, kp, stkv), row_kv);
+    };
+    load_cols(0);
+    load_rows(0);
 
     // Lane offset of the 32-deep operand pattern inside a 64 x 64 bf16 matrix:
     // row lr, k = 8 lq .. 8 lq + 7.
@@ -480,8 +482,7 @@ void chunked_kernel(ChunkArgs g) {
                 if (qr == 0) sts<float>(smem + OFF_BONUS, tr * 4, bonus_part);
             }
         }
-        // Next chunk's inputs: columns for its prefix during P5, rows for its P1b.
-        load_chunk(c0 + L);
+        load_rows(c0 + L);   // next chunk's rows, for its P1b
         __syncthreads();
 
         // ---------------- P2: the four L x L matrices; inverses of the diagonal blocks ----------------
@@ -557,6 +558,9 @@ void chunked_kernel(ChunkArgs g) {
             sts<uint2>(smem + OFF_DINV, ((strip * 16 + lr) * PD + 4 * lq) * 2,
                        make_uint2(pack_bf16(Dt[0], Dt[1]), pack_bf16(Dt[2], Dt[3])));
         }
+        // Next chunk's columns (for its prefix after P4), issued here where waves 0..3
+        // wait for the block inverses of waves 4..7.
+        load_cols(c0 + L);
         __syncthreads();   // B~ / K~ (region 1) and the decay tables (region 2) are dead now
         #pragma unroll
         for (int n = 0; n < 2; ++n) {
