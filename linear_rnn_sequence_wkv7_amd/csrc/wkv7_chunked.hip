@@ -486,35 +486,35 @@ void chunked_kernel(ChunkArgs g) {
         __syncthreads();
 
         // ---------------- P2: the four L x L matrices; inverses of the diagonal blocks ----------------
-        // Tile ids 0..9 list (tb, sb), sb <= tb, in row order.  Waves 4..7 take the
-        // diagonal tile (strip, strip); waves 0..3 the off-diagonal tiles
-        // {1, 3}, {4, 6}, {7}, {8}; a wave computes all four matrices of its tiles,
-        // sharing the B~ / K~ reads.  Each tile is C'[s][t] = Y[s] . X[t], so a lane
-        // holds 4 consecutive s of one t: a row-major [t][s] store of 4 elements.
+        // Tile ids 0..9 list (tb, sb), sb <= tb, in row order.  Waves 0..3 take the
+        // off-diagonal tiles {1, 3}, {4, 6}, {7}, {8} (all four matrices, sharing the
+        // B~ / K~ reads) and A_ak, A_rb, A_rk of diagonal tile (strip, strip); waves
+        // 4..7 take only A_ab of that diagonal tile, whose block inverse is the serial
+        // part of this phase.  Each tile is C'[s][t] = Y[s] . X[t], so a lane holds 4
+        // consecutive s of one t: a row-major [t][s] store of 4 elements.
         auto tile_tb = [](int id) { return id >= 6 ? 3 : id >= 3 ? 2 : id >= 1 ? 1 : 0; };
         auto tile_id = [&](int n) {
             return hf ? (n == 0 ? strip * (strip + 3) / 2 : -1)
                       : (n == 0 ? min(1 + 3 * strip, 8) : (strip < 2 ? 3 + 3 * strip : -1));
         };
-        f32x4 Aab[2], Aak[2], Arb[2], Ark[2];
+        f32x4 Aab[3], Aak[3], Arb[3], Ark[3];
         f32x4 Nsw = {0.f, 0.f, 0.f, 0.f};   // diagonal block N of A_ab in C layout (waves 4..7)
         #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const int id = tile_id(n);
-            const int tb = tile_tb(id), sb = id - (tile_tb(id) * (tile_tb(id) + 1)) / 2;
-            Aab[n] = Aak[n] = Arb[n] = Ark[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (id >= 0) {
-                #pragma unroll
-                for (int kq = 0; kq < 2; ++kq) {
-                    const int ya = (16 * sb * P72 + 32 * kq) * 2 + op32;
-                    const int xb = (16 * tb * P72 + 32 * kq) * 2 + op32;
-                    const bf16x8 Bt8 = lds<bf16x8>(smem + OFF_BT, ya);
+        for (int n = 0; n < 3; ++n) Aab[n] = Aak[n] = Arb[n] = Ark[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto tile_products = [&](int n, int tb, int sb, bool ab, bool rest, bool swapped) {
+            #pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                const int ya = (16 * sb * P72 + 32 * kq) * 2 + op32;
+                const int xb = (16 * tb * P72 + 32 * kq) * 2 + op32;
+                const bf16x8 Bt8 = lds<bf16x8>(smem + OFF_BT, ya);
+                const bf16x8 At8 = lds<bf16x8>(smem + OFF_AT, xb);
+                if (ab) Aab[n] = mfma32(Bt8, At8, Aab[n]);
+                if (swapped) Nsw = mfma32(At8, Bt8, Nsw);   // same block, operands swapped
+                if (rest) {
                     const bf16x8 Kh8 = lds<bf16x8>(smem + OFF_KTH, ya);
                     const bf16x8 Kl8 = lds<bf16x8>(smem + OFF_KTL, ya);
-                    const bf16x8 At8 = lds<bf16x8>(smem + OFF_AT, xb);
                     const bf16x8 Rh8 = lds<bf16x8>(smem + OFF_RTH, xb);
                     const bf16x8 Rl8 = lds<bf16x8>(smem + OFF_RTL, xb);
-                    Aab[n] = mfma32(Bt8, At8, Aab[n]);
                     Aak[n] = mfma32(Kh8, At8, Aak[n]);
                     Aak[n] = mfma32(Kl8, At8, Aak[n]);
                     Arb[n] = mfma32(Bt8, Rh8, Arb[n]);
@@ -522,10 +522,23 @@ void chunked_kernel(ChunkArgs g) {
                     Ark[n] = mfma32(Kh8, Rh8, Ark[n]);
                     Ark[n] = mfma32(Kh8, Rl8, Ark[n]);
                     Ark[n] = mfma32(Kl8, Rh8, Ark[n]);
-                    if (hf) Nsw = mfma32(At8, Bt8, Nsw);   // same block, operands swapped
                 }
             }
+        };
+        if (!hf) {
+            #pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int id = tile_id(n);
+                const int tb = tile_tb(id), sb = id - (tile_tb(id) * (tile_tb(id) + 1)) / 2;
+                if (id >= 0) tile_products(n, tb, sb, true, true, false);
+            }
+            tile_products(2, strip, strip, false, true, false);
+        } else {
+            tile_products(0, strip, strip, true, false, true);
         }
+        // Next chunk's columns (for its prefix after P4); waves 4..7 issue them ahead
+        // of the inverse chain.
+        load_cols(c0 + L);
         if (hf) {
             // N = block `strip` of A_ab is strictly lower triangular, so N^16 = 0 and
             // (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8); the factors are
@@ -558,42 +571,44 @@ void chunked_kernel(ChunkArgs g) {
             sts<uint2>(smem + OFF_DINV, ((strip * 16 + lr) * PD + 4 * lq) * 2,
                        make_uint2(pack_bf16(Dt[0], Dt[1]), pack_bf16(Dt[2], Dt[3])));
         }
-        // Next chunk's columns (for its prefix after P4), issued here where waves 0..3
-        // wait for the block inverses of waves 4..7.
-        load_cols(c0 + L);
         __syncthreads();   // B~ / K~ (region 1) and the decay tables (region 2) are dead now
-        #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const int id = tile_id(n);
-            if (id >= 0) {
-                const int tb = tile_tb(id), sb = id - (tile_tb(id) * (tile_tb(id) + 1)) / 2;
-                f32x4 ab = Aab[n], ak = Aak[n], rb = Arb[n], rk = Ark[n];
-                if (tb == sb) {
-                    // A_ab, A_ak strictly lower (s < t); A_rb, A_rk lower with diagonal (s <= t).
-                    #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int sl = 4 * lq + r;
-                        ab[r] = sl >= lr ? 0.f : ab[r];
-                        ak[r] = sl >= lr ? 0.f : ak[r];
-                        rb[r] = sl > lr ? 0.f : rb[r];
-                        rk[r] = sl > lr ? 0.f : rk[r];
-                    }
+        // Row-major [t][s] stores of one tile: A_ab / A_rb bf16 on the pair-interleaved
+        // token axis, A_ak / A_rk hi / lo in natural order.
+        auto store_ab = [&](int tb, int sb, char* dst, f32x4 c) {
+            sts<uint2>(dst, ((16 * tb + lr) * P72 + pairpos(16 * sb + 4 * lq)) * 2,
+                       make_uint2(pack_bf16(c[0], c[1]), pack_bf16(c[2], c[3])));
+        };
+        auto store_hl = [&](int tb, int sb, int off_h, int off_l, f32x4 c) {
+            uint32_t h0, l0, h1, l1;
+            split2(c[0], c[1], h0, l0);
+            split2(c[2], c[3], h1, l1);
+            const int o = ((16 * tb + lr) * P72 + 16 * sb + 4 * lq) * 2;
+            sts<uint2>(smem + off_h, o, make_uint2(h0, h1));
+            sts<uint2>(smem + off_l, o, make_uint2(l0, l1));
+        };
+        // Diagonal tiles: A_ab, A_ak strictly lower (s < t); A_rb, A_rk lower with diagonal (s <= t).
+        auto mask = [&](f32x4 c, bool strict) {
+            #pragma unroll
+            for (int r = 0; r < 4; ++r) c[r] = 4 * lq + r >= lr + (strict ? 0 : 1) ? 0.f : c[r];
+            return c;
+        };
+        if (!hf) {
+            #pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int id = tile_id(n);
+                if (id >= 0) {   // off-diagonal
+                    const int tb = tile_tb(id), sb = id - (tile_tb(id) * (tile_tb(id) + 1)) / 2;
+                    store_ab(tb, sb, smem + OFF_AAB, Aab[n]);
+                    store_ab(tb, sb, smem + OFF_ARB, Arb[n]);
+                    store_hl(tb, sb, OFF_AKH, OFF_AKL, Aak[n]);
+                    store_hl(tb, sb, OFF_RKH, OFF_RKL, Ark[n]);
                 }
-                const int orow = (16 * tb + lr) * P72;
-                const int op = (orow + pairpos(16 * sb + 4 * lq)) * 2;
-                sts<uint2>(smem + OFF_AAB, op, make_uint2(pack_bf16(ab[0], ab[1]), pack_bf16(ab[2], ab[3])));
-                sts<uint2>(smem + OFF_ARB, op, make_uint2(pack_bf16(rb[0], rb[1]), pack_bf16(rb[2], rb[3])));
-                const int o = (orow + 16 * sb + 4 * lq) * 2;
-                uint32_t h0, l0, h1, l1;
-                split2(ak[0], ak[1], h0, l0);
-                split2(ak[2], ak[3], h1, l1);
-                sts<uint2>(smem + OFF_AKH, o, make_uint2(h0, h1));
-                sts<uint2>(smem + OFF_AKL, o, make_uint2(l0, l1));
-                split2(rk[0], rk[1], h0, l0);
-                split2(rk[2], rk[3], h1, l1);
-                sts<uint2>(smem + OFF_RKH, o, make_uint2(h0, h1));
-                sts<uint2>(smem + OFF_RKL, o, make_uint2(l0, l1));
             }
+            store_ab(strip, strip, smem + OFF_ARB, mask(Arb[2], false));
+            store_hl(strip, strip, OFF_AKH, OFF_AKL, mask(Aak[2], true));
+            store_hl(strip, strip, OFF_RKH, OFF_RKL, mask(Ark[2], false));
+        } else {
+            store_ab(strip, strip, smem + OFF_AAB, mask(Aab[0], true));
         }
         if (tid < 256) {
             // Zero the upper tiles (t-block 0, s-block 1) and (2, 3) of A_ak and A_rk,
