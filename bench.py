@@ -9,7 +9,10 @@ sides and timed with HIP events on the stream the kernels are launched on.
 Prints one JSON line with the throughput (head-tokens/s), the roofline of the
 dominant kernel and the fp64 CPU oracle timed on a bounded sample.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--algo auto|scan|chunked]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--algo auto|scan|chunked|two_pass]
+
+At D = 128 "auto" runs the two-pass form (two kernels per step, workspace
+allocated before the timed region); its roofline covers the whole step.
 """
 from __future__ import annotations
 
@@ -33,6 +36,7 @@ KERNEL_SOURCES = {
     "scan": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_scan.hip",
     "chunked": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_chunked.hip",
     "chunked128": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_chunked128.hip",
+    "twopass128": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_twopass128.hip",
     "decode": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_decode.hip",
 }
 
@@ -95,7 +99,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fwd_bf16_b8_t1024_h32_d64")
-    ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunked"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunked", "two_pass"])
     ap.add_argument("--cpu-pairs", type=int, default=256, help="sequences in the CPU-oracle sample (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (a reference for the "
@@ -157,17 +161,20 @@ def main(argv=None) -> int:
         nbytes = wl.B * wl.H * (2 * wl.D * wl.D * 4) + wl.B * wl.D * (wl.H * 5 + wl.H_kv * 2) * 2
         flops = 9 * wl.D * wl.D * wl.B * wl.H
     else:
-        algo = wkv7.wkv7_resolve_algo(wl.B, wl.T, wl.H, wl.D, H_kv=wl.H_kv, algo=a.algo if a.algo != "auto" else wl.algo,
-                                      in_dtype=wl.in_dtype, y_dtype=wl.y_dtype, w_mode=wl.w_mode)
-        kind = "chunked128" if algo == "chunked" and wl.D == 128 else algo
+        req = a.algo if a.algo != "auto" else wl.algo
+        kw = dict(H_kv=wl.H_kv, in_dtype=wl.in_dtype, y_dtype=wl.y_dtype, w_mode=wl.w_mode)
+        ws_bytes = wkv7.wkv7_workspace_bytes(wl.B, wl.T, wl.H, wl.D, algo=req, **kw)
+        algo = "two_pass" if ws_bytes > 0 else wkv7.wkv7_resolve_algo(wl.B, wl.T, wl.H, wl.D, algo=req, **kw)
+        kind = {"two_pass": "twopass128", "chunked": "chunked128" if wl.D == 128 else "chunked"}.get(algo, algo)
         y = torch.empty((wl.B, wl.T, wl.H, wl.D), dtype=torch.bfloat16 if wl.y_dtype == "bf16" else torch.float32,
                         device="cuda")
         s_out = torch.empty((wl.B, wl.H, wl.D, wl.D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes > 0 else None
 
         def one_step(i):
             wkv7.wkv7_forward(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state0"], w_mode=wl.w_mode,
                               y_dtype=wl.y_dtype, algo=algo, chunk_len=wl.chunk_len, y_scale=wl.y_scale,
-                              r_k=d["r_k"], y=y, state_out=s_out)
+                              r_k=d["r_k"], y=y, state_out=s_out, workspace=ws)
         head_tokens_per_step = wl.B * wl.T * wl.H
         nbytes = algorithmic_bytes(wl)
         flops = algorithmic_flops(wl)
@@ -184,7 +191,8 @@ def main(argv=None) -> int:
     ev1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms = ev0.elapsed_time(ev1) / a.steps      # one launch per step: the kernel's average duration
+    # One launch per step (two for the two-pass form, timed together): the step's average duration.
+    ms = ev0.elapsed_time(ev1) / a.steps
 
     value = head_tokens_per_step / (ms / 1e3)
     if kind == "scan":

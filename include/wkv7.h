@@ -28,9 +28,10 @@
  *
  * Ownership and memory: every pointer is DEVICE memory on the current HIP
  * device, owned by the caller.  The library never allocates, frees or keeps
- * a pointer after the call returns.  All data pointers must be 16-byte
- * aligned.  state_in == state_out (in place) is allowed; y must not overlap
- * any input.
+ * a pointer after the call returns; the two-pass form of wkv7_forward_ws
+ * works in a workspace the caller passes in.  All data pointers must be
+ * 16-byte aligned.  state_in == state_out (in place) is allowed; y must not
+ * overlap any input or the workspace.
  *
  * Streams: work is enqueued on `stream` (a hipStream_t; NULL = the legacy
  * default stream) and the call returns without synchronising.  A fault in a
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define WKV7_ABI_VERSION 1
+#define WKV7_ABI_VERSION 2
 
 enum wkv7_status {
     WKV7_OK = 0,
@@ -73,7 +74,10 @@ enum wkv7_w_mode {
 enum wkv7_algo {
     WKV7_ALGO_AUTO = 0,     /* library picks (see wkv7_resolve_algo) */
     WKV7_ALGO_SCAN = 1,     /* token-by-token scan, state in registers */
-    WKV7_ALGO_CHUNKED = 2   /* chunk-parallel form on bf16 matrix cores, fp32 accumulation */
+    WKV7_ALGO_CHUNKED = 2,  /* chunk-parallel form on bf16 matrix cores, fp32 accumulation */
+    WKV7_ALGO_TWO_PASS = 3  /* D = 128 only, wkv7_forward_ws only: the chunked form split in two
+                               kernels, the state-independent matrices of every chunk first (in
+                               parallel over chunks, into the workspace), then the recurrence */
 };
 
 typedef struct wkv7_desc {
@@ -104,6 +108,29 @@ int wkv7_forward(const wkv7_desc* desc,
                  const float* state_in, void* y, float* state_out,
                  void* stream);
 
+/* wkv7_forward with a caller-provided device workspace for the two-pass form.
+ *   workspace       : device memory, 16-byte aligned, at least
+ *                     wkv7_workspace_bytes(desc) bytes; may be NULL when that is 0.
+ *   workspace_bytes : its size.
+ * The algorithm is WKV7_ALGO_TWO_PASS when desc->algo asks for it, and for
+ * desc->algo == AUTO whenever wkv7_workspace_bytes(desc) > 0; otherwise the
+ * call is wkv7_forward.  The workspace contents are scratch: not read before
+ * they are written, undefined afterwards.  Calls that share a workspace must
+ * be ordered (same stream).  EINVAL if the workspace is NULL, misaligned or
+ * smaller than needed. */
+int wkv7_forward_ws(const wkv7_desc* desc,
+                    const void* r, const void* w, const void* k, const void* v,
+                    const void* a, const void* b,
+                    const float* state_in, void* y, float* state_out,
+                    void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes wkv7_forward_ws uses for this descriptor: for D = 128 with
+ * algo AUTO and T >= the chunk length, or algo TWO_PASS and T >= 1, it is
+ * B * H * ceil(T / 32) * 54272 (one 53 KiB record of operands per chunk);
+ * 0 otherwise.  A negative wkv7_status if the descriptor is invalid.  Host
+ * only: no HIP call. */
+int64_t wkv7_workspace_bytes(const wkv7_desc* desc);
+
 /* One decode token per sequence (desc->T must be 1): the same operation as
  * wkv7_forward with T = 1, run by a kernel that streams the B*H states
  * through HBM once (read state_in, write state_out).  state_in may be NULL
@@ -117,7 +144,8 @@ int wkv7_decode_step(const wkv7_desc* desc,
 /* Which algorithm wkv7_forward would run for this descriptor (WKV7_ALGO_SCAN or
  * WKV7_ALGO_CHUNKED), or a negative wkv7_status if the descriptor is invalid.
  * AUTO picks the chunked form once T covers one chunk (T >= chunk length),
- * the scan otherwise.  Host only: no HIP call. */
+ * the scan otherwise.  An explicit WKV7_ALGO_TWO_PASS is returned as is
+ * (wkv7_forward rejects it; wkv7_forward_ws runs it).  Host only: no HIP call. */
 int wkv7_resolve_algo(const wkv7_desc* desc);
 
 /* Static name of a status code. */

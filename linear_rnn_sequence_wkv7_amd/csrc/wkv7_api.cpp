@@ -67,8 +67,10 @@ int check_desc(const wkv7_desc* d, wkv7::Params* p) {
         return fail(WKV7_EINVAL, "y_dtype %d unknown", d->y_dtype);
     if (d->w_mode != WKV7_W_DECAY && d->w_mode != WKV7_W_LOGNEGLOG)
         return fail(WKV7_EINVAL, "w_mode %d unknown", d->w_mode);
-    if (d->algo < WKV7_ALGO_AUTO || d->algo > WKV7_ALGO_CHUNKED)
+    if (d->algo < WKV7_ALGO_AUTO || d->algo > WKV7_ALGO_TWO_PASS)
         return fail(WKV7_EINVAL, "algo %d unknown", d->algo);
+    if (d->algo == WKV7_ALGO_TWO_PASS && d->D != 128)
+        return fail(WKV7_EUNSUPPORTED, "the two-pass form needs D=128 (got %d)", d->D);
     // Each chunked kernel has one chunk length: 64 at D = 64, 32 at D = 128.
     const int L_native = d->D == 64 ? 64 : 32;
     int L = d->chunk_len == 0 ? L_native : d->chunk_len;
@@ -107,11 +109,16 @@ int check_ptrs(const wkv7::Params& p, const void* const* in6, const void* y,
 }
 
 // AUTO: the chunked matrix-core form once a sequence spans at least one full
-// chunk and the head size has a chunked kernel; the scan otherwise.
-int resolve_algo(const wkv7::Params& p, int requested) {
-    if (requested == WKV7_ALGO_SCAN) return WKV7_ALGO_SCAN;
-    if (requested == WKV7_ALGO_CHUNKED) return WKV7_ALGO_CHUNKED;
-    return p.T >= p.chunk_len ? WKV7_ALGO_CHUNKED : WKV7_ALGO_SCAN;
+// chunk; with a workspace at D = 128 its two-pass variant.  The scan otherwise.
+int resolve_algo(const wkv7::Params& p, int requested, bool with_workspace) {
+    if (requested != WKV7_ALGO_AUTO) return requested;
+    if (p.T < p.chunk_len) return WKV7_ALGO_SCAN;
+    return with_workspace && p.D == 128 ? WKV7_ALGO_TWO_PASS : WKV7_ALGO_CHUNKED;
+}
+
+int64_t workspace_bytes(const wkv7::Params& p, int algo) {
+    if (algo != WKV7_ALGO_TWO_PASS || p.T == 0) return 0;
+    return wkv7::twopass128_workspace_bytes(p.B, p.H, p.T);
 }
 
 int finish_launch(hipError_t e, const char* what) {
@@ -121,20 +128,28 @@ int finish_launch(hipError_t e, const char* what) {
     return WKV7_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+int forward_impl(const wkv7_desc* desc, const void* r, const void* w, const void* k,
                  const void* v, const void* a, const void* b, const float* state_in,
-                 void* y, float* state_out, void* stream) {
+                 void* y, float* state_out, void* workspace, int64_t workspace_bytes_given,
+                 bool ws_call, void* stream) {
     g_last_error[0] = '\0';
     wkv7::Params p{};
     int rc = check_desc(desc, &p);
     if (rc) return rc;
+    if (!ws_call && desc->algo == WKV7_ALGO_TWO_PASS)
+        return fail(WKV7_EINVAL, "algo TWO_PASS needs a workspace: call wkv7_forward_ws");
     const void* in6[6] = {r, w, k, v, a, b};
     if ((rc = check_ptrs(p, in6, y, state_in, state_out))) return rc;
-    int algo = resolve_algo(p, desc->algo);
+    const int algo = resolve_algo(p, desc->algo, ws_call);
+    const int64_t need = int64_t(p.B) * p.H > 0 ? workspace_bytes(p, algo) : 0;
+    if (need > 0) {
+        if (!workspace) return fail(WKV7_EINVAL, "workspace is NULL (%lld bytes needed)", (long long)need);
+        if (!aligned16(workspace)) return fail(WKV7_EINVAL, "workspace is not 16-byte aligned");
+        if (workspace_bytes_given < need)
+            return fail(WKV7_EINVAL, "workspace has %lld bytes, %lld needed",
+                        (long long)workspace_bytes_given, (long long)need);
+        if (workspace == y) return fail(WKV7_EINVAL, "y aliases the workspace");
+    }
     p.r = r; p.w = w; p.k = k; p.v = v; p.a = a; p.b = b;
     p.s0 = state_in; p.y = y; p.s1 = state_out;
     if (int64_t(p.B) * p.H == 0) return WKV7_OK;
@@ -144,10 +159,37 @@ int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void
         if (!state_out) return WKV7_OK;
         return finish_launch(wkv7::launch_state_copy(p, s), "state copy");
     }
+    if (algo == WKV7_ALGO_TWO_PASS) return finish_launch(wkv7::launch_twopass128(p, workspace, s), "two-pass (D=128)");
     if (algo == WKV7_ALGO_CHUNKED)
         return p.D == 64 ? finish_launch(wkv7::launch_chunked(p, s), "chunked")
                          : finish_launch(wkv7::launch_chunked128(p, s), "chunked (D=128)");
     return finish_launch(wkv7::launch_scan(p, s), "scan");
+}
+
+}  // namespace
+
+extern "C" {
+
+int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                 const void* v, const void* a, const void* b, const float* state_in,
+                 void* y, float* state_out, void* stream) {
+    return forward_impl(desc, r, w, k, v, a, b, state_in, y, state_out, nullptr, 0, false, stream);
+}
+
+int wkv7_forward_ws(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                    const void* v, const void* a, const void* b, const float* state_in,
+                    void* y, float* state_out, void* workspace, int64_t workspace_bytes_given,
+                    void* stream) {
+    return forward_impl(desc, r, w, k, v, a, b, state_in, y, state_out, workspace,
+                        workspace_bytes_given, true, stream);
+}
+
+int64_t wkv7_workspace_bytes(const wkv7_desc* desc) {
+    g_last_error[0] = '\0';
+    wkv7::Params p{};
+    int rc = check_desc(desc, &p);
+    if (rc) return -rc;
+    return workspace_bytes(p, resolve_algo(p, desc->algo, true));
 }
 
 int wkv7_decode_step(const wkv7_desc* desc, const void* r, const void* w, const void* k,
@@ -172,7 +214,7 @@ int wkv7_resolve_algo(const wkv7_desc* desc) {
     wkv7::Params p{};
     int rc = check_desc(desc, &p);
     if (rc) return -rc;
-    return resolve_algo(p, desc->algo);
+    return resolve_algo(p, desc->algo, false);
 }
 
 const char* wkv7_strerror(int code) {

@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI entry points (wkv7_api.cpp) and the
-// kernel launchers (wkv7_scan.hip, wkv7_chunked.hip, wkv7_decode.hip).
+// kernel launchers (wkv7_scan.hip, wkv7_chunked.hip, wkv7_chunked128.hip,
+// wkv7_twopass128.hip, wkv7_decode.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,6 +28,9 @@ struct Params {
 hipError_t launch_scan(const Params& p, hipStream_t stream);
 hipError_t launch_chunked(const Params& p, hipStream_t stream);      // D = 64, L = 64
 hipError_t launch_chunked128(const Params& p, hipStream_t stream);   // D = 128, L = 32
+// Two-pass form at D = 128: per-chunk matrices into `ws`, then the recurrence.
+int64_t twopass128_workspace_bytes(int B, int H, int T);
+hipError_t launch_twopass128(const Params& p, void* ws, hipStream_t stream);
 hipError_t launch_decode(const Params& p, hipStream_t stream);
 // state_out <- state_in (or zeros) for T == 0.
 hipError_t launch_state_copy(const Params& p, hipStream_t stream);

@@ -2,7 +2,8 @@
 
 Torch supplies device memory and the current HIP stream; every step of the
 computation runs in the library's HIP kernels.  The names mirror the C ABI in
-include/wkv7.h: wkv7_forward, wkv7_decode_step, wkv7_resolve_algo.
+include/wkv7.h: wkv7_forward (which calls wkv7_forward_ws when the two-pass
+form runs), wkv7_decode_step, wkv7_resolve_algo, wkv7_workspace_bytes.
 
 If the library is missing, every call raises: there is no fallback path.
 """
@@ -13,7 +14,8 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "wkv7_forward", "wkv7_decode_step", "wkv7_resolve_algo", "Wkv7Error", "lib_path", "load_library",
+    "wkv7_forward", "wkv7_decode_step", "wkv7_resolve_algo", "wkv7_workspace_bytes", "Wkv7Error",
+    "lib_path", "load_library",
     "WKV7_OK", "WKV7_EINVAL", "WKV7_EUNSUPPORTED", "WKV7_EDEVICE", "WKV7_ELAUNCH",
     "ALGOS", "W_MODES", "Desc", "EXPORTED_SYMBOLS",
 ]
@@ -21,9 +23,9 @@ __all__ = [
 WKV7_OK, WKV7_EINVAL, WKV7_EUNSUPPORTED, WKV7_EDEVICE, WKV7_ELAUNCH = 0, 1, 2, 3, 4
 _DTYPES = {"f32": 0, "bf16": 1}
 W_MODES = {"decay": 0, "logneglog": 1}
-ALGOS = {"auto": 0, "scan": 1, "chunked": 2}
-EXPORTED_SYMBOLS = ("wkv7_forward", "wkv7_decode_step", "wkv7_resolve_algo", "wkv7_strerror",
-                    "wkv7_last_error", "wkv7_abi_version")
+ALGOS = {"auto": 0, "scan": 1, "chunked": 2, "two_pass": 3}
+EXPORTED_SYMBOLS = ("wkv7_forward", "wkv7_forward_ws", "wkv7_workspace_bytes", "wkv7_decode_step",
+                    "wkv7_resolve_algo", "wkv7_strerror", "wkv7_last_error", "wkv7_abi_version")
 
 
 class Wkv7Error(RuntimeError):
@@ -64,6 +66,10 @@ def load_library():
         fn = getattr(lib, name)
         fn.argtypes = sig
         fn.restype = ctypes.c_int
+    lib.wkv7_forward_ws.argtypes = sig[:-1] + [vp, ctypes.c_int64, vp]
+    lib.wkv7_forward_ws.restype = ctypes.c_int
+    lib.wkv7_workspace_bytes.argtypes = [ctypes.POINTER(Desc)]
+    lib.wkv7_workspace_bytes.restype = ctypes.c_int64
     lib.wkv7_resolve_algo.argtypes = [ctypes.POINTER(Desc)]
     lib.wkv7_resolve_algo.restype = ctypes.c_int
     lib.wkv7_strerror.argtypes = [ctypes.c_int]
@@ -139,26 +145,40 @@ def _check_inputs(r, w, k, v, a, b, state, r_k):
     return B, T, H, int(k.shape[2]), D
 
 
-def _call(fn_name, desc, r, w, k, v, a, b, state, y, state_out):
+def _call(fn_name, desc, r, w, k, v, a, b, state, y, state_out, workspace=None):
     torch = _torch()
     lib = load_library()
     stream = torch.cuda.current_stream(r.device).cuda_stream
+    args = [ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+            _ptr(state), _ptr(y), _ptr(state_out)]
+    if fn_name == "wkv7_forward_ws":
+        args += [_ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size()]
     with torch.cuda.device(r.device):
-        rc = getattr(lib, fn_name)(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
-                                   _ptr(state), _ptr(y), _ptr(state_out), stream)
+        rc = getattr(lib, fn_name)(*args, stream)
     if rc != WKV7_OK:
         raise Wkv7Error(rc, fn_name, lib.wkv7_last_error().decode())
 
 
+def wkv7_workspace_bytes(B, T, H, D, *, H_kv=None, algo="auto", **kw) -> int:
+    """Workspace bytes wkv7_forward_ws uses for these sizes (0: none)."""
+    n = load_library().wkv7_workspace_bytes(ctypes.byref(make_desc(B, T, H, D, H_kv=H_kv, algo=algo, **kw)))
+    if n < 0:
+        raise Wkv7Error(int(-n), "wkv7_workspace_bytes", load_library().wkv7_last_error().decode())
+    return int(n)
+
+
 def wkv7_forward(r, w, k, v, a, b, state=None, *, w_mode: str = "decay", y_dtype: Optional[str] = None,
                  algo: str = "auto", chunk_len: int = 0, y_scale: float = 1.0, r_k=None,
-                 y=None, state_out=None, return_state: bool = True) -> Tuple[object, object]:
-    """Run wkv7_forward on torch GPU tensors.
+                 y=None, state_out=None, return_state: bool = True, workspace=None) -> Tuple[object, object]:
+    """Run the forward on torch GPU tensors.
 
     r, w, a, b: [B, T, H, D]; k, v: [B, T, H_kv, D]; all float32 or all bfloat16, contiguous.
     state: [B, H, D, D] float32 or None (zeros).  r_k: [H, D] float32 or None.
     y_dtype: "f32" | "bf16" (default: the input dtype).  Outputs are allocated
     unless `y` / `state_out` are given (state_out may equal state: in place).
+    algo "auto" and "two_pass" go through wkv7_forward_ws: when the library
+    reports a workspace size for the descriptor, `workspace` (a contiguous
+    device tensor of at least that many bytes) is used, or allocated here.
     Returns (y, state_out); state_out is None when return_state is False.
     """
     torch = _torch()
@@ -170,7 +190,17 @@ def wkv7_forward(r, w, k, v, a, b, state=None, *, w_mode: str = "decay", y_dtype
         state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=r.device)
     desc = make_desc(B, T, H, D, H_kv=H_kv, in_dtype=_dtype_name(r), y_dtype=ydt, w_mode=w_mode, algo=algo,
                      chunk_len=chunk_len, y_scale=y_scale, r_k_ptr=_ptr(r_k))
-    _call("wkv7_forward", desc, r, w, k, v, a, b, state, y, state_out)
+    if algo in ("auto", "two_pass"):
+        need = load_library().wkv7_workspace_bytes(ctypes.byref(desc))
+        if need < 0:
+            raise Wkv7Error(int(-need), "wkv7_workspace_bytes", load_library().wkv7_last_error().decode())
+        if need > 0 and workspace is None:
+            workspace = torch.empty(int(need), dtype=torch.uint8, device=r.device)
+        if workspace is not None and (workspace.device != r.device or not workspace.is_contiguous()):
+            raise ValueError(f"workspace must be a contiguous tensor on {r.device}")
+        _call("wkv7_forward_ws", desc, r, w, k, v, a, b, state, y, state_out, workspace)
+    else:
+        _call("wkv7_forward", desc, r, w, k, v, a, b, state, y, state_out)
     return y, state_out
 
 
@@ -193,8 +223,9 @@ def wkv7_decode_step(r, w, k, v, a, b, state, *, w_mode: str = "decay", y_dtype:
 
 
 def wkv7_resolve_algo(B, T, H, D, *, H_kv=None, algo="auto", **kw) -> str:
-    """Which algorithm wkv7_forward runs for these sizes ("scan" or "chunked")."""
+    """Which algorithm the C wkv7_forward runs for these sizes ("scan" or "chunked";
+    an explicit "two_pass" is returned as is)."""
     rc = load_library().wkv7_resolve_algo(ctypes.byref(make_desc(B, T, H, D, H_kv=H_kv, algo=algo, **kw)))
     if rc < 0:
         raise Wkv7Error(-rc, "wkv7_resolve_algo", load_library().wkv7_last_error().decode())
-    return {1: "scan", 2: "chunked"}[rc]
+    return {1: "scan", 2: "chunked", 3: "two_pass"}[rc]

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_strerror():
     lib = W.load_library()
-    assert lib.wkv7_abi_version() == 1
+    assert lib.wkv7_abi_version() == 2
     assert lib.wkv7_strerror(0) == b"ok"
     assert lib.wkv7_strerror(W.WKV7_EINVAL) == b"invalid argument"
     assert lib.wkv7_strerror(99) == b"unknown status"
@@ -47,8 +47,10 @@ def _call(desc, ptrs=None, fn="wkv7_forward"):
     lib = W.load_library()
     p = ptrs or {}
     args = [p.get(k, FAKE) for k in ("r", "w", "k", "v", "a", "b")] + \
-           [p.get("s0"), p.get("y", FAKE + 4096), p.get("s1"), None]
-    return getattr(lib, fn)(ctypes.byref(desc) if desc is not None else None, *args)
+           [p.get("s0"), p.get("y", FAKE + 4096), p.get("s1")]
+    if fn == "wkv7_forward_ws":
+        args += [p.get("ws"), p.get("ws_bytes", 0)]
+    return getattr(lib, fn)(ctypes.byref(desc) if desc is not None else None, *args, None)
 
 
 def good(**kw):
@@ -70,6 +72,7 @@ def good(**kw):
 ])
 def test_bad_descriptor_rejected(desc, code):
     assert _call(desc) == code
+    assert _call(desc, fn="wkv7_forward_ws") == code
     assert _call(desc, fn="wkv7_decode_step") == code
 
 
@@ -124,3 +127,38 @@ def test_resolve_algo():
         W.wkv7_resolve_algo(2, 8, 4, 128, chunk_len=64)
     with pytest.raises(W.Wkv7Error):
         W.wkv7_resolve_algo(2, 8, 4, 96)
+
+
+def test_workspace_bytes():
+    rec = 54272   # one record per (b, h, chunk of 32 tokens)
+    assert W.wkv7_workspace_bytes(2, 64, 4, 128) == 2 * 4 * 2 * rec
+    assert W.wkv7_workspace_bytes(2, 70, 4, 128) == 2 * 4 * 3 * rec     # ragged last chunk
+    assert W.wkv7_workspace_bytes(2, 31, 4, 128) == 0                  # AUTO: the scan below one chunk
+    assert W.wkv7_workspace_bytes(2, 31, 4, 128, algo="two_pass") == 2 * 4 * 1 * rec
+    assert W.wkv7_workspace_bytes(2, 0, 4, 128, algo="two_pass") == 0
+    assert W.wkv7_workspace_bytes(2, 64, 4, 128, algo="chunked") == 0
+    assert W.wkv7_workspace_bytes(2, 64, 4, 128, algo="scan") == 0
+    assert W.wkv7_workspace_bytes(2, 128, 4, 64) == 0                  # D = 64 has no two-pass form
+    assert W.wkv7_workspace_bytes(2, 16384, 32, 128, H_kv=8) == 2 * 32 * 512 * rec
+    with pytest.raises(W.Wkv7Error) as e:
+        W.wkv7_workspace_bytes(2, 64, 4, 64, algo="two_pass")
+    assert e.value.code == W.WKV7_EUNSUPPORTED
+
+
+def test_two_pass_argument_rules():
+    d = good(D=128, T=64)
+    need = W.wkv7_workspace_bytes(2, 64, 4, 128)
+    # wkv7_forward never runs the two-pass form; asked for it explicitly, it refuses.
+    assert _call(good(D=128, T=64, algo="two_pass")) == W.WKV7_EINVAL
+    assert b"wkv7_forward_ws" in W.load_library().wkv7_last_error()
+    # wkv7_forward_ws: the workspace must be present, aligned, large enough and not y.
+    assert _call(d, {}, fn="wkv7_forward_ws") == W.WKV7_EINVAL
+    assert _call(d, {"ws": FAKE + 65536 + 8, "ws_bytes": need}, fn="wkv7_forward_ws") == W.WKV7_EINVAL
+    assert _call(d, {"ws": FAKE + 65536, "ws_bytes": need - 1}, fn="wkv7_forward_ws") == W.WKV7_EINVAL
+    assert b"needed" in W.load_library().wkv7_last_error()
+    assert _call(d, {"ws": FAKE + 4096, "ws_bytes": need}, fn="wkv7_forward_ws") == W.WKV7_EINVAL
+    assert _call(good(D=128, T=64, algo="two_pass"), {}, fn="wkv7_forward_ws") == W.WKV7_EINVAL
+    # Without a two-pass algorithm the workspace is not needed.
+    assert _call(good(D=128, T=64, algo="scan", B=0), {}, fn="wkv7_forward_ws") == W.WKV7_OK
+    assert _call(good(D=128, T=64, B=0), {}, fn="wkv7_forward_ws") == W.WKV7_OK
+    assert W.wkv7_resolve_algo(2, 64, 4, 128, algo="two_pass") == "two_pass"

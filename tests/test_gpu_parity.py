@@ -14,8 +14,13 @@ from tests.gpu_util import announce, dev_inputs, to_dev, to_host, torch
 
 pytestmark = pytest.mark.gpu
 
-FWD_ALGOS = ["scan", "chunked"]
-TAU = {"scan": P.TAU_SCAN, "chunked": P.TAU_CHUNKED}
+FWD_ALGOS = ["scan", "chunked", "two_pass"]
+TAU = {"scan": P.TAU_SCAN, "chunked": P.TAU_CHUNKED, "two_pass": P.TAU_CHUNKED}
+
+
+def need_algo(algo, D):
+    if algo == "two_pass" and D != 128:
+        pytest.skip("the two-pass form exists for D = 128 only")
 
 
 @pytest.fixture(autouse=True)
@@ -71,6 +76,7 @@ SWEEP = [
 @pytest.mark.parametrize("algo", FWD_ALGOS)
 @pytest.mark.parametrize("case", SWEEP, ids=lambda c: "D{}_B{}_T{}_H{}_kv{}_{}_{}_{}_s{}_e{}".format(*c))
 def test_forward_sweep(case, algo):
+    need_algo(algo, case[0])
     wl = make_case(*case, seed=7 + case[2])
     x = G.make_inputs(wl)
     y_ref, s_ref = oracle_full(wl, x)
@@ -83,6 +89,7 @@ def test_forward_sweep(case, algo):
 @pytest.mark.parametrize("algo", FWD_ALGOS)
 def test_state_in_place_and_split(algo, D):
     """state_out may alias state_in; forward(T1) then forward(T2) from its state == forward(T1+T2)."""
+    need_algo(algo, D)
     wl = make_case(D, 2, 96, 2, 2, "bf16", "f32", "decay", 0.1, False, seed=3)
     x = G.make_inputs(wl)
     y_ref, s_ref = oracle_full(wl, x)
@@ -117,6 +124,7 @@ def test_zero_tokens_copies_state():
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("algo", FWD_ALGOS)
 def test_bitwise_deterministic(algo, D):
+    need_algo(algo, D)
     wl = make_case(D, 2, 150, 4, 4, "bf16", "bf16", "decay", 0.1, False, seed=9)
     x = G.make_inputs(wl)
     y1, s1 = run_forward(wl, x, algo)
@@ -183,6 +191,7 @@ def inputs_of(name):
 
 @pytest.mark.parametrize("algo", FWD_ALGOS)
 def test_workload_small_f32(algo):
+    need_algo(algo, 64)
     wl = G.WORKLOADS["fwd_f32_b1_t64_h2_d64"]
     x = inputs_of(wl.name)
     y_ref, s_ref = oracle_full(wl, x)
@@ -208,11 +217,13 @@ def _sampled(wl, algo, n_pairs, y_dtype=None):
 @pytest.mark.parametrize("y_dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("algo", FWD_ALGOS)
 def test_workload_fwd_bf16(algo, y_dtype):
+    need_algo(algo, 64)
     _sampled(G.WORKLOADS["fwd_bf16_b8_t1024_h32_d64"], algo, 16, y_dtype=y_dtype)
 
 
 @pytest.mark.parametrize("algo", FWD_ALGOS)
 def test_workload_prefill(algo):
+    need_algo(algo, 64)
     _sampled(G.WORKLOADS["prefill_bf16_b4_t4096_h40_d64_l64"], algo, 8)
 
 
