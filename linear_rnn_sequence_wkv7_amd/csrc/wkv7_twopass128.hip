@@ -802,22 +802,40 @@ void scan128_kernel(ScanArgs g) {
 
     // This wave finishes Y tile (token block ty, value strip sy) and X tile 2 ty + sy.
     const int ty = kp >> 1, sy = kp & 1;
-    auto load_ops = [&](int c, Ops& o) {
-        const char* rec = recs + int64_t(c) * WS_CHUNK;
-        const char* kb = rec + kp * WS_KP + l * 16;
+    // The next chunk's operands are requested in three groups spread over the
+    // chunk (when every wave of the chip issues them at once the memory pipeline
+    // backs up and the issuing waves stall): W and Q (first needed), Bh and E,
+    // then P, d and the bonus.
+    auto load_wq = [&](int c, Ops& o) {
+        const char* kb = recs + int64_t(c) * WS_CHUNK + kp * WS_KP + l * 16;
         #pragma unroll
         for (int i = 0; i < 2; ++i) {
             o.W[i] = *reinterpret_cast<const bf16x8*>(kb + (BLK_W + i) * WS_BLK);
             o.Qh[i] = *reinterpret_cast<const bf16x8*>(kb + (BLK_QH + i) * WS_BLK);
             o.Ql[i] = *reinterpret_cast<const bf16x8*>(kb + (BLK_QL + i) * WS_BLK);
+        }
+    };
+    auto load_be = [&](int c, Ops& o) {
+        const char* kb = recs + int64_t(c) * WS_CHUNK + kp * WS_KP + l * 16;
+        #pragma unroll
+        for (int i = 0; i < 2; ++i) {
             o.Bh[i] = *reinterpret_cast<const bf16x8*>(kb + (BLK_BH + i) * WS_BLK);
             o.Eh[i] = *reinterpret_cast<const bf16x8*>(kb + (BLK_EH + i) * WS_BLK);
             o.El[i] = *reinterpret_cast<const bf16x8*>(kb + (BLK_EL + i) * WS_BLK);
-            o.d[i] = ld_f32x4(rec + WS_D + (16 * (2 * kp + i) + 4 * lq) * 4);
         }
+    };
+    auto load_p = [&](int c, Ops& o) {   // P, d and the bonus
+        const char* rec = recs + int64_t(c) * WS_CHUNK;
         o.Ph = *reinterpret_cast<const bf16x8*>(rec + WS_P + ty * WS_BLK + l * 16);
         o.Pl = *reinterpret_cast<const bf16x8*>(rec + WS_P + (2 + ty) * WS_BLK + l * 16);
+        #pragma unroll
+        for (int i = 0; i < 2; ++i) o.d[i] = ld_f32x4(rec + WS_D + (16 * (2 * kp + i) + 4 * lq) * 4);
         if constexpr (EPI) o.bon = ld_f32x4(rec + WS_BON + (16 * ty + 4 * lq) * 4);
+    };
+    auto load_ops = [&](int c, Ops& o) {
+        load_wq(c, o);
+        load_be(c, o);
+        load_p(c, o);
     };
     // V of the slice: thread (vt, vg) loads token vt, values 32 q + 4 vg .. + 3.
     const char* vp = static_cast<const char*>(g.v);
@@ -846,12 +864,13 @@ void scan128_kernel(ScanArgs g) {
     for (int c = 0; c < nch; ++c) {
         const int c0 = c * L, buf = c & 1;
         cur = nxt;
-        // Next chunk: V rows first (their LDS store closes this iteration), then its
-        // workspace operands.
-        if (c + 1 < nch) {
-            load_v(c + 1);
-            load_ops(c + 1, nxt);
-        }
+        // Next chunk: V rows first (their LDS store closes this iteration), then W, Q.
+        // The last iteration loads its own chunk again (unused): unconditional loads
+        // keep the compiler's wait counts exact.
+        const int cn = min(c + 1, nch - 1);
+        load_v(cn);
+        load_wq(cn, nxt);
+        asm volatile("" ::: "memory");
         // X and Y over this wave's 32 keys: X^T (t x i) = W S^T, Y (t x i) = Q S^T.
         bf16x8 SBh[2], SBl[2];
         #pragma unroll
@@ -869,6 +888,8 @@ void scan128_kernel(ScanArgs g) {
                 sts<f32x4>(smem + S_PART, ((kp * 8 + 4 + 2 * tb + sg) * 64 + l) * 16, yq);
             }
         __syncthreads();   // partial tiles and V^T of this chunk visible
+        load_be(cn, nxt);
+        asm volatile("" ::: "memory");
 
         const char* vs = smem + S_VS + buf * VS_BYTES;
         bf16x8 VB[2], VBl[2];
@@ -928,6 +949,8 @@ void scan128_kernel(ScanArgs g) {
                 Buf<Ty>::store1(Ry, uint32_t(tl0 + r) * sty + uint32_t(h * DK + DV * q + i_loc) * SY, yv);
             }
         }
+        load_p(cn, nxt);
+        asm volatile("" ::: "memory");
         __syncthreads();   // reduced X tiles visible
 
         // S <- S + X Bh, X of strip sg as the B operand (k = token, n = value row).
@@ -943,10 +966,8 @@ void scan128_kernel(ScanArgs g) {
         }
         // V^T of chunk c + 1 into the other buffer (last read during chunk c - 1); the
         // barrier after the next chunk's partial products publishes it.
-        if (c + 1 < nch) {
-            store_v(buf ^ 1);
-            settle_ops(nxt);
-        }
+        store_v(buf ^ 1);
+        settle_ops(nxt);
     }
 
     if (g.s1) {
