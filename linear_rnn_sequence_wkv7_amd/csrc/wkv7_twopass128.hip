@@ -321,14 +321,21 @@ void prep128_kernel(PrepArgs g) {
         // ---------------- Q0: decay prefix and the scaled operands (row threads) ----------------
         {
             const bool ok = c0 + t < T;   // tokens past the end decay by 1 and carry zeros
-            float lw[8], gg[8], gl[8];
+            // Per key: E = 2^g_t, Ei = 2^-g_t; 2^g_(t-1) is E of the previous token
+            // (lane l - 1, 1 at t = 0); d = 2^g_L is E of token 31 (lane 31 / 63) and
+            // 2^(g_L - g_t) = d Ei.  Two exp2 per element besides the log-decay.
+            float Ex[8], Eix[8], Epx[8], dx[8];
             #pragma unroll
             for (int x = 0; x < 8; ++x) {
-                lw[x] = ok ? log2_decay(cur.w.get(x), LOGW) : 0.f;
-                gg[x] = scan32(lw[x]);
-                const float s31 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gg[x]), 31));
-                const float s63 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gg[x]), 63));
-                gl[x] = l < 32 ? s31 : s63;
+                const float lw = ok ? log2_decay(cur.w.get(x), LOGW) : 0.f;
+                const float gg = scan32(lw);
+                Ex[x] = __builtin_amdgcn_exp2f(gg);
+                Eix[x] = __builtin_amdgcn_exp2f(-gg);
+                const float prev = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(Ex[x]), 0x138, 0xF, 0xF, false));   // wave_shr:1
+                Epx[x] = t == 0 ? 1.f : prev;
+                const float d31 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ex[x]), 31));
+                const float d63 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ex[x]), 63));
+                dx[x] = l < 32 ? d31 : d63;
             }
             uint32_t at[4], rth[4], rtl[4], bt[4], kth[4], ktl[4], bhat[4];
             float bonus_part = 0.f;
@@ -337,10 +344,10 @@ void prep128_kernel(PrepArgs g) {
                 float Ep[2], E[2], Ei[2], Eh[2];
                 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    E[u] = __builtin_amdgcn_exp2f(gg[e + u]);
-                    Ep[u] = __builtin_amdgcn_exp2f(gg[e + u] - lw[e + u]);
-                    Ei[u] = __builtin_amdgcn_exp2f(-gg[e + u]);
-                    Eh[u] = __builtin_amdgcn_exp2f(gl[e + u] - gg[e + u]);
+                    E[u] = Ex[e + u];
+                    Ep[u] = Epx[e + u];
+                    Ei[u] = Eix[e + u];
+                    Eh[u] = dx[e + u] * Eix[e + u];
                 }
                 const float r0 = cur.r.get(e), r1 = cur.r.get(e + 1);
                 const float k0 = cur.k.get(e), k1 = cur.k.get(e + 1);
@@ -369,11 +376,8 @@ void prep128_kernel(PrepArgs g) {
             pair_col_store(smem + P_ATT, j0, t, at);
             pair_col_store(smem + P_BHT, j0, t, bhat);
             if (t == 0) {
-                float dv[8];
-                #pragma unroll
-                for (int x = 0; x < 8; ++x) dv[x] = __builtin_amdgcn_exp2f(gl[x]);
-                sts<float4>(smem + P_DL, j0 * 4, make_float4(dv[0], dv[1], dv[2], dv[3]));
-                sts<float4>(smem + P_DL, j0 * 4 + 16, make_float4(dv[4], dv[5], dv[6], dv[7]));
+                sts<float4>(smem + P_DL, j0 * 4, make_float4(dx[0], dx[1], dx[2], dx[3]));
+                sts<float4>(smem + P_DL, j0 * 4 + 16, make_float4(dx[4], dx[5], dx[6], dx[7]));
             }
             if constexpr (EPI) {
                 bonus_part += __shfl_xor(bonus_part, 32);
