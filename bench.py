@@ -195,16 +195,18 @@ def main(argv=None) -> int:
     ms = ev0.elapsed_time(ev1) / a.steps
 
     value = head_tokens_per_step / (ms / 1e3)
-    if kind == "scan":
+    if kind != "decode":
+        # Forward: the algorithmic work (9 D^2 flop per head-token) binds on the fp32
+        # vector ALU (intensity ~40 flop/B at D = 64, ~104 at D = 128).
         achieved = flops / (ms / 1e3) / 1e12
         roof = {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_FP32_VALU_TFLOPS}
-        dtype = "f32"
+        dtype = "f32" if kind == "scan" else "bf16"
     else:
         achieved = nbytes / (ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
-        dtype = "f32" if kind == "decode" else "bf16"
+        dtype = "f32"
     roof["traffic"] = traffic_from_profile(kind, wl.name)
     roof["kernel"] = kind
     roof["algorithmic_bytes"] = nbytes
