@@ -760,17 +760,6 @@ struct Ops {
     f32x4 d[2], bon;
 };
 
-// Wait for a prefetched operand set here: no load is then pending across the loop
-// back-edge, where the compiler's wait counting would also wait for the stores.
-__device__ __forceinline__ void settle_ops(Ops& o) {
-    #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        asm volatile("" : "+v"(o.W[i]), "+v"(o.Qh[i]), "+v"(o.Ql[i]), "+v"(o.Bh[i]), "+v"(o.Eh[i]), "+v"(o.El[i]));
-        asm volatile("" : "+v"(o.d[i]));
-    }
-    asm volatile("" : "+v"(o.Ph), "+v"(o.Pl), "+v"(o.bon));
-}
-
 template <typename Tin, typename Ty, bool EPI>
 __global__ __launch_bounds__(NTHR_SCAN)
 void scan128_kernel(ScanArgs g) {
@@ -859,15 +848,12 @@ void scan128_kernel(ScanArgs g) {
         if constexpr (VSPLIT) pair_col_store4(smem + S_VSL + buf * VS_BYTES, 4 * vg, vt, vl);
     };
 
-    Ops cur, nxt;
-    load_v(0);
-    load_ops(0, nxt);
-    store_v(0);
-    settle_ops(nxt);
     char* yp = static_cast<char*>(g.y);
-    for (int c = 0; c < nch; ++c) {
+    // One chunk: operands in `cur`, the next chunk's prefetched into `nxt`.  The
+    // loop below alternates two operand sets, so no prefetched register is copied
+    // (a copy would wait for the load); each load is waited for at its first use.
+    auto chunk = [&](const int c, Ops& cur, Ops& nxt) {
         const int c0 = c * L, buf = c & 1;
-        cur = nxt;
         // Next chunk: V rows first (their LDS store closes this iteration), then W, Q.
         // The last iteration loads its own chunk again (unused): unconditional loads
         // keep the compiler's wait counts exact.
@@ -894,6 +880,9 @@ void scan128_kernel(ScanArgs g) {
         __syncthreads();   // partial tiles and V^T of this chunk visible
         load_be(cn, nxt);
         asm volatile("" ::: "memory");
+        // Keep the S diag(d) update below this point (d is among the last operands to
+        // arrive; hoisted to the top of the chunk it would wait for them there).
+        asm volatile("" : "+v"(ST[0][0]), "+v"(ST[0][1]), "+v"(ST[1][0]), "+v"(ST[1][1]));
 
         const char* vs = smem + S_VS + buf * VS_BYTES;
         bf16x8 VB[2], VBl[2];
@@ -971,8 +960,25 @@ void scan128_kernel(ScanArgs g) {
         // V^T of chunk c + 1 into the other buffer (last read during chunk c - 1); the
         // barrier after the next chunk's partial products publishes it.
         store_v(buf ^ 1);
-        settle_ops(nxt);
+    };
+    Ops opa, opb;
+    load_v(0);
+    load_ops(0, opa);
+    store_v(0);
+    // The first operand set completes here: its load order would otherwise enter
+    // the compiler's wait counts of every loop iteration.
+    #pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        asm volatile("" : "+v"(opa.W[i]), "+v"(opa.Qh[i]), "+v"(opa.Ql[i]), "+v"(opa.Bh[i]), "+v"(opa.Eh[i]), "+v"(opa.El[i]));
+        asm volatile("" : "+v"(opa.d[i]));
     }
+    asm volatile("" : "+v"(opa.Ph), "+v"(opa.Pl), "+v"(opa.bon));
+    int c = 0;
+    for (; c + 1 < nch; c += 2) {
+        chunk(c, opa, opb);
+        chunk(c + 1, opb, opa);
+    }
+    if (c < nch) chunk(c, opa, opb);
 
     if (g.s1) {
         #pragma unroll
