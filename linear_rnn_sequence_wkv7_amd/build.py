@@ -34,6 +34,14 @@ COMMON = [
 ]
 
 
+# Per-source extras.  The two-pass kernels do VALU work on their MFMA
+# accumulators (state tiles, partial products); kept in VGPRs they need no
+# AGPR <-> VGPR copies.
+EXTRA = {
+    "wkv7_twopass128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -57,9 +65,10 @@ def build(asm: bool = False, verbose: bool = False) -> str:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        jobs.append([cc, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        extra = EXTRA.get(src, [])
+        jobs.append([cc, *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
         if asm and src.endswith(".hip"):
-            jobs.append([cc, *COMMON, "-x", "hip", "--cuda-device-only", "-S",
+            jobs.append([cc, *COMMON, *extra, "-x", "hip", "--cuda-device-only", "-S",
                          os.path.join(CSRC, src), "-o",
                          os.path.join(BUILD, os.path.splitext(src)[0] + f"-{ARCH}.s")])
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:

@@ -124,18 +124,21 @@ __device__ __forceinline__ f32x4 ld_f32x4(const char* p) {
 __device__ __forceinline__ uint32_t dpp_u32_xor1(uint32_t x) {
     return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), kDppQuadXor1, 0xF, 0xF, false));
 }
-// Inclusive prefix sum over lanes 0..31 and, separately, 32..63.
-__device__ __forceinline__ float scan32(float x) {
-    auto shr = [](float v, auto C) {
-        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(C)::value, 0xF, 0xF, false));
-    };
-    x += shr(x, std::integral_constant<int, 0x111>{});   // row_shr:1
-    x += shr(x, std::integral_constant<int, 0x112>{});   // row_shr:2
-    x += shr(x, std::integral_constant<int, 0x114>{});   // row_shr:4
-    x += shr(x, std::integral_constant<int, 0x118>{});   // row_shr:8
-    // row_bcast:15 into rows 1 and 3 only: lane 15 (47) of the row below.
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
-    return x;
+// Inclusive prefix sums over lanes 0..31 and, separately, 32..63, of 8 values per
+// lane, step by step across the 8 (a DPP read of a value written by the previous
+// instruction would need wait states).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_add8(float (&x)[8]) {
+    #pragma unroll
+    for (int i = 0; i < 8; ++i)
+        x[i] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[i]), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ void scan32x8(float (&x)[8]) {
+    dpp_add8<0x111, 0xF>(x);   // row_shr:1
+    dpp_add8<0x112, 0xF>(x);   // row_shr:2
+    dpp_add8<0x114, 0xF>(x);   // row_shr:4
+    dpp_add8<0x118, 0xF>(x);   // row_shr:8
+    dpp_add8<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3 only: lane 15 (47) of the row below
 }
 
 constexpr int kRsrcWord3 = 0x00020000;
@@ -324,11 +327,13 @@ void prep128_kernel(PrepArgs g) {
             // Per key: E = 2^g_t, Ei = 2^-g_t; 2^g_(t-1) is E of the previous token
             // (lane l - 1, 1 at t = 0); d = 2^g_L is E of token 31 (lane 31 / 63) and
             // 2^(g_L - g_t) = d Ei.  Two exp2 per element besides the log-decay.
-            float Ex[8], Eix[8], Epx[8], dx[8];
+            float Ex[8], Eix[8], Epx[8], dx[8], gs[8];
+            #pragma unroll
+            for (int x = 0; x < 8; ++x) gs[x] = ok ? log2_decay(cur.w.get(x), LOGW) : 0.f;
+            scan32x8(gs);
             #pragma unroll
             for (int x = 0; x < 8; ++x) {
-                const float lw = ok ? log2_decay(cur.w.get(x), LOGW) : 0.f;
-                const float gg = scan32(lw);
+                const float gg = gs[x];
                 Ex[x] = __builtin_amdgcn_exp2f(gg);
                 Eix[x] = __builtin_amdgcn_exp2f(-gg);
                 const float prev = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(Ex[x]), 0x138, 0xF, 0xF, false));   // wave_shr:1
