@@ -25,6 +25,15 @@ Options, all from the hxa07D article (forward listing):
     h // (H / H_kv), i.e. repeat_kv's contiguous repetition (section 6).
   * epilogue: y_t <- y_scale * y_t + (sum_j r_tj k_tj r_k[h, j]) v_t
     (section 9: scale by head_size^-1/2 plus the r*k*r_k term times v).
+  * kk_from_k: the kernel vectors are formed from k and the in-context rate
+    alpha, as the forward listing does right before the kernel call (section
+    8): kk = normalize(k) per head (L2, floor 1e-12), a = -kk, b = kk * alpha,
+    and k itself becomes k * (1 - w + alpha) with w the decay; that modified k
+    is also the k of the epilogue's r*k*r_k term.  alpha is passed in the a
+    argument.
+  * mask [B, T]: the listing passes an attention mask to the kernel without
+    defining it; here a masked token (mask == 0) leaves the state unchanged
+    and emits y = 0, so padding and variable lengths drop out.
 
 Every function here is pinned by tests/test_oracle_pins.py against things
 other than itself: a hand-worked example, closed forms of special cases
@@ -38,8 +47,8 @@ from typing import Optional, Tuple
 import numpy as np
 
 __all__ = [
-    "as_f64", "decay_from_logneglog", "wkv7_forward", "wkv7_brute", "wkv7_unrolled",
-    "wkv7_chunked",
+    "as_f64", "decay_from_logneglog", "kernel_vectors_from_k", "wkv7_forward", "wkv7_brute",
+    "wkv7_unrolled", "wkv7_chunked",
 ]
 
 
@@ -97,15 +106,34 @@ def _epilogue(y, r, k, v, rk, y_scale):
     return y
 
 
+def kernel_vectors_from_k(k, w, alpha):
+    """kk = normalize(k) (L2 over the head, floor 1e-12); returns the kernel's
+    (k * (1 - w + alpha), a = -kk, b = kk * alpha) for decay w (hxa07D article,
+    forward listing, section 8).  k, w, alpha: [..., D] float64."""
+    n = np.sqrt(np.sum(k * k, axis=-1, keepdims=True))
+    kk = k / np.maximum(n, 1e-12)
+    return k * (1.0 - w + alpha), -kk, kk * alpha
+
+
+def _masked(keep, S_old, S_new, y):
+    """keep [B] bool: a kept token takes the update and its output; a masked one
+    keeps the old state and outputs zero."""
+    return (np.where(keep[:, None, None, None], S_new, S_old),
+            np.where(keep[:, None, None], y, 0.0))
+
+
 def wkv7_forward(r, w, k, v, a, b, state0=None, *, w_mode: str = "decay",
-                 r_k=None, y_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
+                 r_k=None, y_scale: float = 1.0, kk_from_k: bool = False,
+                 mask=None) -> Tuple[np.ndarray, np.ndarray]:
     """The recurrence over T tokens, token by token, in float64.
 
     r, w, a, b: [B, T, H, D]; k, v: [B, T, H_kv, D] (uint16 = bf16 bits, or float).
     state0: [B, H, D, D] or None (zeros).  r_k: [H, D] or None.
+    kk_from_k: a holds alpha and b is ignored (see the module notes).
+    mask: [B, T] (nonzero = token kept) or None.
     Returns y [B, T, H, D] and the final state [B, H, D, D], both float64.
     """
-    r, w, k, v, a, b = (as_f64(x) for x in (r, w, k, v, a, b))
+    r, w, k, v, a = (as_f64(x) for x in (r, w, k, v, a))
     B, T, H, D = r.shape
     k = _expand_kv(k, H)
     v = _expand_kv(v, H)
@@ -113,12 +141,21 @@ def wkv7_forward(r, w, k, v, a, b, state0=None, *, w_mode: str = "decay",
         w = decay_from_logneglog(w)
     elif w_mode != "decay":
         raise ValueError(w_mode)
+    if kk_from_k:
+        k, a, b = kernel_vectors_from_k(k, w, a)
+    else:
+        b = as_f64(b)
+    keep = None if mask is None else (np.asarray(mask) != 0)
     S = np.zeros((B, H, D, D)) if state0 is None else as_f64(state0).copy()
     rk = None if r_k is None else as_f64(r_k)
     y = np.empty((B, T, H, D))
     for t in range(T):
-        S, yt = _step(S, r[:, t], w[:, t], k[:, t], v[:, t], a[:, t], b[:, t])
-        y[:, t] = _epilogue(yt, r[:, t], k[:, t], v[:, t], rk, y_scale)
+        S_new, yt = _step(S, r[:, t], w[:, t], k[:, t], v[:, t], a[:, t], b[:, t])
+        yt = _epilogue(yt, r[:, t], k[:, t], v[:, t], rk, y_scale)
+        if keep is None:
+            S, y[:, t] = S_new, yt
+        else:
+            S, y[:, t] = _masked(keep[:, t], S, S_new, yt)
     return y, S
 
 

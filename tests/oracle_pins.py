@@ -238,6 +238,93 @@ def pin_chunked_matches_sequential():
     _close(Sc, S, 1e-11, "chunked S")
 
 
+def _hand_kk():
+    with open(os.path.join(GOLDEN, "hand_example_kk_d2.json")) as f:
+        g = json.load(f)
+    arr = {k: np.array(g[k], dtype=float) for k in
+           ("state0", "w", "alpha", "k", "v", "r", "r_k", "expected_y", "expected_state",
+            "expected_y_epilogue")}
+    return g, arr
+
+
+def pin_hand_kk_mask():
+    """Hand-worked kernel vectors from k, with a masked middle token
+    (tests/golden/hand_example_kk_d2.json)."""
+    g, x = _hand_kk()
+    mask = np.array(g["mask"])
+    args = (x["r"], x["w"], x["k"], x["v"], x["alpha"], None, x["state0"])
+    y, S = O.wkv7_forward(*args, kk_from_k=True, mask=mask)
+    _close(y, x["expected_y"], 1e-14, "hand kk y")
+    _close(S, x["expected_state"], 1e-14, "hand kk state")
+    y, _ = O.wkv7_forward(*args, kk_from_k=True, mask=mask, r_k=x["r_k"], y_scale=g["y_scale"])
+    _close(y, x["expected_y_epilogue"], 1e-14, "hand kk epilogue")
+
+
+def pin_kk_overwrite_invariant():
+    """Kernel vectors from k with alpha = 1 and w = 1: k' = k and the update
+    replaces what the state returns for the unit key kk, so S_t kk_t = |k_t| v_t
+    (delta rule, wiki note; kk of the hxa07D article, section 8)."""
+    rng = np.random.default_rng(22)
+    B, T, H, D = 2, 7, 2, 5
+    r, _, k, v, _, _, S0 = _rand_problem(rng, B, T, H, D)
+    k *= rng.uniform(0.2, 3.0, (B, T, H, 1))
+    one = np.ones((B, T, H, D))
+    S = S0.copy()
+    for t in range(T):
+        sl = slice(t, t + 1)
+        _, S = O.wkv7_forward(r[:, sl], one[:, sl], k[:, sl], v[:, sl], one[:, sl], None, S,
+                              kk_from_k=True)
+        n = np.linalg.norm(k[:, t], axis=-1)
+        kk = k[:, t] / n[..., None]
+        _close(np.einsum("bhij,bhj->bhi", S, kk), n[..., None] * v[:, t], 1e-12, "kk overwrite")
+
+
+def pin_kk_key_scale():
+    """From a zero state, scaling every k by c > 0 scales y and S by c: kk does
+    not depend on the length of k and k' is linear in it.  A zero key row gives
+    kk = 0 (the 1e-12 floor) and leaves S diag(w) with no NaN."""
+    rng = np.random.default_rng(23)
+    B, T, H, D = 1, 6, 2, 4
+    r, w, k, v, _, _, _ = _rand_problem(rng, B, T, H, D, s0=False)
+    alpha = rng.uniform(0.0, 1.0, (B, T, H, D))
+    y1, S1 = O.wkv7_forward(r, w, k, v, alpha, None, None, kk_from_k=True)
+    y2, S2 = O.wkv7_forward(r, w, 2.5 * k, v, alpha, None, None, kk_from_k=True)
+    _close(y2, 2.5 * y1, 1e-12, "kk scale y")
+    _close(S2, 2.5 * S1, 1e-12, "kk scale S")
+    S0 = rng.standard_normal((B, H, D, D))
+    z = np.zeros((B, 1, H, D))
+    _, S = O.wkv7_forward(r[:, :1], w[:, :1], z, v[:, :1], alpha[:, :1], None, S0, kk_from_k=True)
+    assert np.all(np.isfinite(S))
+    _close(S, S0 * w[:, 0][:, :, None, :], 1e-15, "zero key")
+
+
+def pin_mask_drops_tokens():
+    """A masked token is as if it were not in the sequence: the kept tokens'
+    outputs and the final state equal those of the sequence with the masked
+    tokens removed, and masked positions output zero.  Covers both kernel-vector
+    modes, two batch rows with different masks and a fully masked row."""
+    rng = np.random.default_rng(24)
+    B, T, H, D = 3, 9, 2, 3
+    r, w, k, v, a, b, S0 = _rand_problem(rng, B, T, H, D)
+    mask = np.ones((B, T), dtype=np.uint8)
+    mask[0, [0, 3, 4, 8]] = 0
+    mask[1, [5]] = 0
+    mask[2, :] = 0
+    for kk in (False, True):
+        y, S = O.wkv7_forward(r, w, k, v, a, b, S0, kk_from_k=kk, mask=mask)
+        for bi in range(B):
+            keep = np.flatnonzero(mask[bi])
+            assert np.all(y[bi, mask[bi] == 0] == 0.0), "masked output"
+            one = lambda x: x[bi:bi + 1][:, keep]
+            if keep.size:
+                yk, Sk = O.wkv7_forward(one(r), one(w), one(k), one(v), one(a), one(b),
+                                        S0[bi:bi + 1], kk_from_k=kk)
+                _close(y[bi, keep], yk[0], 1e-13, "mask kept y")
+            else:
+                Sk = S0[bi:bi + 1]
+            _close(S[bi], Sk[0], 1e-13, "mask state")
+
+
 def pin_bf16_decode():
     """bf16 bit patterns widen exactly: 0x3F80 = 1, 0xC040 = -3, 0x3EAB = 0.333984375."""
     bits = np.array([0x3F80, 0xC040, 0x3EAB, 0x0000], dtype=np.uint16)

@@ -51,6 +51,21 @@ MUTATIONS = {
     # log-decay conversion
     "logneglog_sign": ("decay_from_logneglog", lambda x: np.exp(-np.exp(-x))),
     "logneglog_single_exp": ("decay_from_logneglog", lambda x: np.exp(x)),
+    # kernel vectors from k
+    "kk_unnormalised": ("kernel_vectors_from_k", lambda k, w, al: (k * (1 - w + al), -k, k * al)),
+    "kk_key_factor_dropped": ("kernel_vectors_from_k", lambda k, w, al: (
+        k, -k / np.linalg.norm(k, axis=-1, keepdims=True), al * k / np.linalg.norm(k, axis=-1, keepdims=True))),
+    "kk_key_factor_sign": ("kernel_vectors_from_k", lambda k, w, al: (
+        k * (1 + w - al), -k / np.linalg.norm(k, axis=-1, keepdims=True),
+        al * k / np.linalg.norm(k, axis=-1, keepdims=True))),
+    "kk_b_without_alpha": ("kernel_vectors_from_k", lambda k, w, al: (
+        k * (1 - w + al), -k / np.linalg.norm(k, axis=-1, keepdims=True), k / np.linalg.norm(k, axis=-1, keepdims=True))),
+    "kk_a_sign": ("kernel_vectors_from_k", lambda k, w, al: (
+        k * (1 - w + al), k / np.linalg.norm(k, axis=-1, keepdims=True),
+        al * k / np.linalg.norm(k, axis=-1, keepdims=True))),
+    # attention mask
+    "mask_state_ignored": ("_masked", lambda m, So, Sn, y: (Sn, np.where(m[:, None, None], y, 0.0))),
+    "mask_output_kept": ("_masked", lambda m, So, Sn, y: (np.where(m[:, None, None, None], Sn, So), y)),
     # grouped KV heads
     "gqa_interleaved": ("_expand_kv", lambda x, H: np.tile(x, (1,) * (x.ndim - 2) + (H // x.shape[-2], 1))),
 }
