@@ -10,13 +10,18 @@ Prints one JSON line with the throughput (head-tokens/s), the roofline of the
 dominant kernel and the fp64 CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--algo auto|scan|chunked|two_pass]
+                    [--ab-mode given|from_k] [--mask pad|holes]
 
 At D = 128 "auto" runs the two-pass form (two kernels per step, workspace
 allocated before the timed region); its roofline covers the whole step.
+--ab-mode from_k passes alpha in place of a and no b: the kernels form
+a = -kk, b = kk alpha and k (1 - decay + alpha) themselves.  --mask adds an
+attention mask drawn by the named recipe.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -55,10 +60,16 @@ def algorithmic_bytes(wl) -> int:
     sin = 2 if wl.in_dtype == "bf16" else 4
     sy = 2 if wl.y_dtype == "bf16" else 4
     ht = wl.B * wl.T * wl.H
-    per_tok = wl.H * wl.D * (4 * sin + sy) + wl.H_kv * wl.D * 2 * sin
+    n_q = 3 if wl.ab_mode == "from_k" else 4         # r, w, a (, b)
+    per_tok = wl.H * wl.D * (n_q * sin + sy) + wl.H_kv * wl.D * 2 * sin + (1 if wl.mask else 0)
     state = wl.B * wl.H * wl.D * wl.D * 4 * (2 if wl.s0_std > 0 else 1)
     rk = wl.H * wl.D * 4 if wl.rk_std > 0 else 0
     return wl.B * wl.T * per_tok + state + rk if ht else 0
+
+
+def workload_label(wl) -> str:
+    """The workload's name plus its input options (kernel vectors from k, mask recipe)."""
+    return wl.name + ("+from_k" if wl.ab_mode == "from_k" else "") + (f"+mask_{wl.mask}" if wl.mask else "")
 
 
 def algorithmic_flops(wl) -> int:
@@ -100,6 +111,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fwd_bf16_b8_t1024_h32_d64")
     ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunked", "two_pass"])
+    ap.add_argument("--ab-mode", default="given", choices=["given", "from_k"])
+    ap.add_argument("--mask", default="", choices=["", "pad", "holes"])
     ap.add_argument("--cpu-pairs", type=int, default=256, help="sequences in the CPU-oracle sample (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (a reference for the "
@@ -130,7 +143,8 @@ def main(argv=None) -> int:
     from linear_rnn_sequence_wkv7_amd import inputs as G
     from linear_rnn_sequence_wkv7_amd import wkv7
 
-    wl = G.WORKLOADS[a.workload]
+    wl = dataclasses.replace(G.WORKLOADS[a.workload], ab_mode=a.ab_mode, mask=a.mask)
+    label = workload_label(wl)
     torch.cuda.set_device(0)
     x = G.make_inputs(wl)
 
@@ -155,14 +169,16 @@ def main(argv=None) -> int:
         def one_step(i):
             s_in, s_out = bufs[i % 2], bufs[(i + 1) % 2]
             j = i % n_steps_avail
-            wkv7.wkv7_decode_step(*(d[k][j] for k in ("r", "w", "k", "v", "a", "b")), s_in,
-                                  w_mode=wl.w_mode, y_scale=wl.y_scale, r_k=d["r_k"], y=y, state_out=s_out)
+            wkv7.wkv7_decode_step(*(None if d[k] is None else d[k][j] for k in ("r", "w", "k", "v", "a", "b")),
+                                  s_in, w_mode=wl.w_mode, y_scale=wl.y_scale, r_k=d["r_k"], y=y, state_out=s_out,
+                                  ab_mode=wl.ab_mode, mask=None if d["mask"] is None else d["mask"][j])
         head_tokens_per_step = wl.B * wl.H
-        nbytes = wl.B * wl.H * (2 * wl.D * wl.D * 4) + wl.B * wl.D * (wl.H * 5 + wl.H_kv * 2) * 2
+        n_q = 4 if wl.ab_mode == "from_k" else 5          # r, w, a (, b) and y
+        nbytes = wl.B * wl.H * (2 * wl.D * wl.D * 4) + wl.B * wl.D * (wl.H * n_q + wl.H_kv * 2) * 2
         flops = 9 * wl.D * wl.D * wl.B * wl.H
     else:
         req = a.algo if a.algo != "auto" else wl.algo
-        kw = dict(H_kv=wl.H_kv, in_dtype=wl.in_dtype, y_dtype=wl.y_dtype, w_mode=wl.w_mode)
+        kw = dict(H_kv=wl.H_kv, in_dtype=wl.in_dtype, y_dtype=wl.y_dtype, w_mode=wl.w_mode, ab_mode=wl.ab_mode)
         ws_bytes = wkv7.wkv7_workspace_bytes(wl.B, wl.T, wl.H, wl.D, algo=req, **kw)
         algo = "two_pass" if ws_bytes > 0 else wkv7.wkv7_resolve_algo(wl.B, wl.T, wl.H, wl.D, algo=req, **kw)
         kind = {"two_pass": "twopass128", "chunked": "chunked128" if wl.D == 128 else "chunked"}.get(algo, algo)
@@ -174,7 +190,8 @@ def main(argv=None) -> int:
         def one_step(i):
             wkv7.wkv7_forward(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state0"], w_mode=wl.w_mode,
                               y_dtype=wl.y_dtype, algo=algo, chunk_len=wl.chunk_len, y_scale=wl.y_scale,
-                              r_k=d["r_k"], y=y, state_out=s_out, workspace=ws)
+                              r_k=d["r_k"], y=y, state_out=s_out, workspace=ws, ab_mode=wl.ab_mode,
+                              mask=d["mask"])
         head_tokens_per_step = wl.B * wl.T * wl.H
         nbytes = algorithmic_bytes(wl)
         flops = algorithmic_flops(wl)
@@ -207,7 +224,7 @@ def main(argv=None) -> int:
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
         dtype = "f32"
-    roof["traffic"] = traffic_from_profile(kind, wl.name)
+    roof["traffic"] = traffic_from_profile(kind, label)
     roof["kernel"] = kind
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
@@ -218,7 +235,7 @@ def main(argv=None) -> int:
         "metric": METRIC, "value": value, "unit": "head-tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype, "data": "synthetic",
-        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "H_kv": wl.H_kv, "D": wl.D,
+        "config": {"workload": label, "B": wl.B, "T": wl.T, "H": wl.H, "H_kv": wl.H_kv, "D": wl.D,
                    "io_dtype": wl.in_dtype, "y_dtype": wl.y_dtype, "kernel": kind},
         "roofline": roof,
         "wall_s_timed_region": t_wall,

@@ -18,11 +18,23 @@
  * epilogue (same article, section 9); the log-decay input mode is its
  * section 3 and grouped KV heads its section 6.
  *
+ * Kernel vectors from k (desc->ab_mode == WKV7_AB_FROM_K): the a input holds
+ * the in-context rate alpha, b is not read, and per token and head the kernel
+ * forms kk = k / max(|k|_2, 1e-12), a = -kk, b = kk * alpha and replaces k by
+ * k * (1 - decay + alpha) in the update and in the r_k term, which is the
+ * preparation the hxa07D forward listing does before its kernel call (same
+ * article, section 8).
+ *
+ * Attention mask (desc->mask): the same listing hands its kernel an attention
+ * mask.  A token whose mask byte is 0 leaves the state as it was and outputs
+ * y = 0; the other tokens run as if the masked ones were not there.
+ *
  * Layouts (row-major, contiguous, element strides implied by the sizes):
  *     r, w, a, b, y : [B, T, H, D]
  *     k, v          : [B, T, H_kv, D]      head h reads KV head h / (H / H_kv)
  *     state         : [B, H, D, D] fp32,  state[b][h][i][j] = S_ij
  *     r_k           : [H, D] fp32
+ *     mask          : [B, T] bytes
  * Element types: r, w, k, v, a, b all have desc->in_dtype (fp32 or bf16);
  * y has desc->y_dtype; the state is always fp32.
  *
@@ -53,7 +65,7 @@
 extern "C" {
 #endif
 
-#define WKV7_ABI_VERSION 2
+#define WKV7_ABI_VERSION 3
 
 enum wkv7_status {
     WKV7_OK = 0,
@@ -69,6 +81,15 @@ enum wkv7_dtype { WKV7_F32 = 0, WKV7_BF16 = 1 };
 enum wkv7_w_mode {
     WKV7_W_DECAY = 0,       /* w is the decay itself, in (0, 1] */
     WKV7_W_LOGNEGLOG = 1    /* w holds log(-log(decay)); decay = exp(-exp(w)) */
+};
+
+/* Where the kernel vectors a, b come from. */
+enum wkv7_ab_mode {
+    WKV7_AB_GIVEN = 0,      /* a and b are inputs */
+    WKV7_AB_FROM_K = 1      /* a holds alpha, b is unused (may be NULL); a, b and the scaled k
+                               are formed from k, alpha and the decay (see above).  Runs in the
+                               scan, the decode step and the two-pass form; ALGO_CHUNKED
+                               rejects it with EUNSUPPORTED. */
 };
 
 enum wkv7_algo {
@@ -93,8 +114,10 @@ typedef struct wkv7_desc {
     int32_t chunk_len;  /* chunk length of ALGO_CHUNKED, fixed per head size: 64 at D = 64,
                            32 at D = 128; 0 selects it, other values are EUNSUPPORTED */
     float   y_scale;    /* multiplies S_t r_t; 1.0f for the plain readout */
-    int32_t reserved;   /* must be 0 */
+    int32_t ab_mode;    /* wkv7_ab_mode */
     const float* r_k;   /* [H, D] fp32 device pointer, or NULL for no bonus term */
+    const uint8_t* mask;/* [B, T] device bytes, 0 = masked token; NULL = no token masked.
+                           No alignment needed.  Supported by every algorithm. */
 } wkv7_desc;
 
 /* Forward over T tokens for every (b, h).
@@ -113,8 +136,8 @@ int wkv7_forward(const wkv7_desc* desc,
  *                     wkv7_workspace_bytes(desc) bytes; may be NULL when that is 0.
  *   workspace_bytes : its size.
  * The algorithm is WKV7_ALGO_TWO_PASS when desc->algo asks for it, and for
- * desc->algo == AUTO whenever wkv7_workspace_bytes(desc) > 0; otherwise the
- * call is wkv7_forward.  The workspace contents are scratch: not read before
+ * desc->algo == AUTO whenever wkv7_workspace_bytes(desc) > 0 (ab_mode
+ * included); otherwise the call is wkv7_forward.  The workspace contents are scratch: not read before
  * they are written, undefined afterwards.  Calls that share a workspace must
  * be ordered (same stream).  EINVAL if the workspace is NULL, misaligned or
  * smaller than needed. */
@@ -144,8 +167,9 @@ int wkv7_decode_step(const wkv7_desc* desc,
 /* Which algorithm wkv7_forward would run for this descriptor (WKV7_ALGO_SCAN or
  * WKV7_ALGO_CHUNKED), or a negative wkv7_status if the descriptor is invalid.
  * AUTO picks the chunked form once T covers one chunk (T >= chunk length),
- * the scan otherwise.  An explicit WKV7_ALGO_TWO_PASS is returned as is
- * (wkv7_forward rejects it; wkv7_forward_ws runs it).  Host only: no HIP call. */
+ * the scan otherwise; with ab_mode FROM_K it picks the scan.  An explicit
+ * WKV7_ALGO_TWO_PASS is returned as is (wkv7_forward rejects it;
+ * wkv7_forward_ws runs it).  Host only: no HIP call. */
 int wkv7_resolve_algo(const wkv7_desc* desc);
 
 /* Static name of a status code. */

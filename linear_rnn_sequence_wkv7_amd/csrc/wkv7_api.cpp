@@ -53,7 +53,6 @@ int check_device() {
 // Validate the descriptor and fill the size/mode fields of Params.
 int check_desc(const wkv7_desc* d, wkv7::Params* p) {
     if (!d) return fail(WKV7_EINVAL, "desc is NULL");
-    if (d->reserved != 0) return fail(WKV7_EINVAL, "desc->reserved must be 0");
     if (d->B < 0 || d->T < 0 || d->H < 0 || d->H_kv < 0)
         return fail(WKV7_EINVAL, "negative size (B=%d T=%d H=%d H_kv=%d)", d->B, d->T, d->H, d->H_kv);
     if (d->D <= 0) return fail(WKV7_EINVAL, "D must be positive (got %d)", d->D);
@@ -69,6 +68,11 @@ int check_desc(const wkv7_desc* d, wkv7::Params* p) {
         return fail(WKV7_EINVAL, "w_mode %d unknown", d->w_mode);
     if (d->algo < WKV7_ALGO_AUTO || d->algo > WKV7_ALGO_TWO_PASS)
         return fail(WKV7_EINVAL, "algo %d unknown", d->algo);
+    if (d->ab_mode != WKV7_AB_GIVEN && d->ab_mode != WKV7_AB_FROM_K)
+        return fail(WKV7_EINVAL, "ab_mode %d unknown", d->ab_mode);
+    if (d->ab_mode == WKV7_AB_FROM_K && d->algo == WKV7_ALGO_CHUNKED)
+        return fail(WKV7_EUNSUPPORTED, "ab_mode FROM_K runs in the scan, the decode step and the two-pass form, "
+                    "not in algo CHUNKED");
     if (d->algo == WKV7_ALGO_TWO_PASS && d->D != 128)
         return fail(WKV7_EUNSUPPORTED, "the two-pass form needs D=128 (got %d)", d->D);
     // Each chunked kernel has one chunk length: 64 at D = 64, 32 at D = 128.
@@ -85,7 +89,8 @@ int check_desc(const wkv7_desc* d, wkv7::Params* p) {
     if (elems > (int64_t(1) << 46)) return fail(WKV7_EUNSUPPORTED, "B*T*H*D too large");
     p->B = d->B; p->T = d->T; p->H = d->H; p->H_kv = H_kv; p->D = d->D;
     p->in_dtype = d->in_dtype; p->y_dtype = d->y_dtype; p->w_mode = d->w_mode;
-    p->chunk_len = L; p->y_scale = d->y_scale; p->r_k = d->r_k;
+    p->chunk_len = L; p->ab_mode = d->ab_mode; p->y_scale = d->y_scale; p->r_k = d->r_k;
+    p->mask = d->mask;
     return WKV7_OK;
 }
 
@@ -94,7 +99,9 @@ int check_ptrs(const wkv7::Params& p, const void* const* in6, const void* y,
     static const char* names[6] = {"r", "w", "k", "v", "a", "b"};
     bool has_tokens = int64_t(p.B) * p.T * p.H > 0;
     if (has_tokens) {
-        for (int i = 0; i < 6; ++i) {
+        // b is not read when the kernel vectors come from k.
+        const int n_in = p.ab_mode == WKV7_AB_FROM_K ? 5 : 6;
+        for (int i = 0; i < n_in; ++i) {
             if (!in6[i]) return fail(WKV7_EINVAL, "%s is NULL", names[i]);
             if (!aligned16(in6[i])) return fail(WKV7_EINVAL, "%s is not 16-byte aligned", names[i]);
         }
@@ -109,11 +116,13 @@ int check_ptrs(const wkv7::Params& p, const void* const* in6, const void* y,
 }
 
 // AUTO: the chunked matrix-core form once a sequence spans at least one full
-// chunk; with a workspace at D = 128 its two-pass variant.  The scan otherwise.
+// chunk; with a workspace at D = 128 its two-pass variant.  The scan otherwise,
+// and for kernel vectors formed from k unless the two-pass form applies.
 int resolve_algo(const wkv7::Params& p, int requested, bool with_workspace) {
     if (requested != WKV7_ALGO_AUTO) return requested;
     if (p.T < p.chunk_len) return WKV7_ALGO_SCAN;
-    return with_workspace && p.D == 128 ? WKV7_ALGO_TWO_PASS : WKV7_ALGO_CHUNKED;
+    if (with_workspace && p.D == 128) return WKV7_ALGO_TWO_PASS;
+    return p.ab_mode == WKV7_AB_FROM_K ? WKV7_ALGO_SCAN : WKV7_ALGO_CHUNKED;
 }
 
 int64_t workspace_bytes(const wkv7::Params& p, int algo) {

@@ -120,6 +120,7 @@ struct ChunkArgs {
     const void *r, *w, *k, *v, *a, *b;
     const float* s0;
     const float* r_k;
+    const uint8_t* mask;
     void* y;
     float* s1;
     int T, H, H_kv;
@@ -203,6 +204,9 @@ template <> struct Row8<bf16_t> {
     __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
         x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
     }
+    __device__ __forceinline__ void keep_if(bool keep) {
+        x.x = keep ? x.x : 0u; x.y = keep ? x.y : 0u; x.z = keep ? x.z : 0u; x.w = keep ? x.w : 0u;
+    }
     __device__ __forceinline__ float get(int e) const {
         const uint32_t d = e < 2 ? x.x : e < 4 ? x.y : e < 6 ? x.z : x.w;
         return (e & 1) ? __uint_as_float(d & 0xffff0000u) : __uint_as_float(d << 16);
@@ -213,6 +217,13 @@ template <> struct Row8<float> {
     __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
         x[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
         x[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+    }
+    __device__ __forceinline__ void keep_if(bool keep) {
+        #pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            x[i].x = keep ? x[i].x : 0u; x[i].y = keep ? x[i].y : 0u;
+            x[i].z = keep ? x[i].z : 0u; x[i].w = keep ? x[i].w : 0u;
+        }
     }
     __device__ __forceinline__ float get(int e) const {
         const uint4& u = x[e >> 2];
@@ -300,6 +311,10 @@ void chunked_kernel(ChunkArgs g) {
 
     uint32_t cw[8], cb[8], ck[8], cv[8];
     Row8<Tin> rr, ra, rb, rkv;
+    // Mask bytes (1 without a mask): lane l of a column wave holds token 8 pc + (l & 7)'s,
+    // a row thread its token's.  Masked tokens become identity tokens (zeros, decay 1).
+    const char* mp = reinterpret_cast<const char*>(g.mask);
+    uint32_t cm = 1u, rm = 1u;
     // Columns of a chunk (for its P1a) and rows (for its P1b) load separately.
     auto chunk_rsrc = [&](int c0, const char* base, uint32_t stride) {
         const int nv = max(0, min(T - c0, L));   // valid tokens (0 past the end: every load reads zero)
@@ -309,6 +324,7 @@ void chunked_kernel(ChunkArgs g) {
     auto load_cols = [&](int c0) {
         const rsrc_t Rw = chunk_rsrc(c0, wp, stq), Rb = chunk_rsrc(c0, bp, stq);
         const rsrc_t Rk = chunk_rsrc(c0, kp, stkv), Rv = chunk_rsrc(c0, vp, stkv);
+        if (mp) cm = __builtin_amdgcn_raw_buffer_load_b8(chunk_rsrc(c0, mp, 1u), uint32_t(8 * pc + (l & 7)), 0, 0);
         #pragma unroll
         for (int e = 0; e < 8; ++e) {
             cw[e] = Buf<Tin>::load1(Rw, col_q[e]);
@@ -322,6 +338,7 @@ void chunked_kernel(ChunkArgs g) {
         ra.load(chunk_rsrc(c0, ap, stq), row_q);
         rb.load(chunk_rsrc(c0, bp, stq), row_q);
         rkv.load(chunk_rsrc(c0, kp, stkv), row_kv);
+        if (mp) rm = __builtin_amdgcn_raw_buffer_load_b8(chunk_rsrc(c0, mp, 1u), uint32_t(tr), 0, 0);
     };
     load_cols(0);
     load_rows(0);
@@ -349,9 +366,14 @@ void chunked_kernel(ChunkArgs g) {
         #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float x = __uint_as_float(cw[e]);
-            const bool ok = c0 + 8 * pc + e < T;     // wave-uniform; w = 1 past the end
+            // Wave-uniform; w = 1 past the end and for masked tokens, whose b and k are zeroed.
+            const bool ok = c0 + 8 * pc + e < T && (!mp || __builtin_amdgcn_readlane(int(cm), e) != 0);
             if constexpr (LOGW) run += ok ? -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e : 0.f;
             else run *= ok ? x : 1.f;
+            if (mp) {
+                cb[e] = ok ? cb[e] : 0u;
+                ck[e] = ok ? ck[e] : 0u;
+            }
             pre[e] = run;
         }
         sts<float>(smem + OFF_TOT, (pc * 64 + jc) * 4, run);
@@ -434,6 +456,10 @@ void chunked_kernel(ChunkArgs g) {
         p1a_store();
 
         // ---------------- P1b: row-major scaled operands ----------------
+        if (mp) {
+            const bool keep = rm != 0;
+            rr.keep_if(keep); ra.keep_if(keep); rb.keep_if(keep); rkv.keep_if(keep);
+        }
         {
             float E[8], Ei[8], Ep[8];
             const int oe = (tr * PE + 8 * qr) * 4;
@@ -793,7 +819,7 @@ void chunked_kernel(ChunkArgs g) {
 
 template <typename Tin, typename Ty, bool LOGW, bool EPI>
 hipError_t launch_t(const Params& p, hipStream_t stream) {
-    ChunkArgs g{p.r, p.w, p.k, p.v, p.a, p.b, p.s0, p.r_k, p.y, p.s1, p.T, p.H, p.H_kv, p.y_scale};
+    ChunkArgs g{p.r, p.w, p.k, p.v, p.a, p.b, p.s0, p.r_k, p.mask, p.y, p.s1, p.T, p.H, p.H_kv, p.y_scale};
     auto kern = chunked_kernel<Tin, Ty, LOGW, EPI>;
     constexpr int smem = sizeof(Tin) == 4 ? SMEM_F32 : SMEM_BF16;
     static bool attr_set = false;   // per template instance; idempotent if raced

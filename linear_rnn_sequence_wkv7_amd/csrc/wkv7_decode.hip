@@ -12,6 +12,10 @@
 // D = 128) of rows 4*it + rl.  Row sums (S a for the removal term, S r for the
 // readout) are a per-lane partial plus a 16-lane DPP all-reduce.  For D = 128
 // the rows are processed in four batches of 32 to bound register use.
+//
+// With the kernel vectors formed from k (KK), the key norm is one more 16-lane
+// sum; a masked token becomes the identity update (r, k, a, b = 0, decay 1),
+// which leaves the state bit for bit and gives y = 0.
 #include "wkv7_internal.h"
 #include "wkv7_device.h"
 
@@ -22,13 +26,14 @@ struct DecodeArgs {
     const void *r, *w, *k, *v, *a, *b;
     const float* s0;
     const float* r_k;
+    const uint8_t* mask;
     void* y;
     float* s1;
     int B, H, H_kv;
     float y_scale;
 };
 
-template <int D, typename Tin, typename Ty, bool LOGW, bool EPI>
+template <int D, typename Tin, typename Ty, bool LOGW, bool EPI, bool KK>
 __global__ __launch_bounds__(256)
 void decode_kernel(DecodeArgs g) {
     constexpr int CPL = D / 16;          // columns per lane (two groups of 4 for D = 128)
@@ -62,13 +67,31 @@ void decode_kernel(DecodeArgs g) {
         const int col = 64 * gi + 4 * cq;
         ld4(ap, oq + col, av + 4 * gi);
         ld4(wp, oq + col, wv + 4 * gi);
-        ld4(bp, oq + col, bv + 4 * gi);
+        if constexpr (!KK) ld4(bp, oq + col, bv + 4 * gi);
         ld4(kp, okv + col, kv + 4 * gi);
         ld4(rp, oq + col, rv + 4 * gi);
     }
     if constexpr (LOGW) {
         #pragma unroll
         for (int c = 0; c < CPL; ++c) wv[c] = decay_from_logneglog(wv[c]);
+    }
+    if constexpr (KK) {
+        // av holds alpha: kk = k / max(|k|, 1e-12), a = -kk, b = kk alpha, k <- k (1 - decay + alpha).
+        float ss = 0.f;
+        #pragma unroll
+        for (int c = 0; c < CPL; ++c) ss = fmaf(kv[c], kv[c], ss);
+        const float inv = inv_key_norm(sum16(ss));
+        #pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const float kk = kv[c] * inv, al = av[c];
+            av[c] = -kk;
+            bv[c] = kk * al;
+            kv[c] *= 1.f - wv[c] + al;
+        }
+    }
+    if (g.mask && g.mask[bb] == 0) {   // T == 1: mask[b][0]
+        #pragma unroll
+        for (int c = 0; c < CPL; ++c) { av[c] = 0.f; bv[c] = 0.f; kv[c] = 0.f; rv[c] = 0.f; wv[c] = 1.f; }
     }
     // v: lane j holds v_j (and v_{64+j}); rows fetch theirs with a lane shuffle.
     float vl[D / 64];
@@ -152,21 +175,26 @@ void decode_kernel(DecodeArgs g) {
     for (int m = 0; m < NIT / 16; ++m) st1(yp, oq + 4 * (cq + 16 * m) + rl, ykeep[m]);
 }
 
-template <int D, typename Tin, typename Ty, bool LOGW, bool EPI>
+template <int D, typename Tin, typename Ty, bool LOGW, bool EPI, bool KK>
 hipError_t launch_t(const Params& p, hipStream_t stream) {
-    DecodeArgs g{p.r, p.w, p.k, p.v, p.a, p.b, p.s0, p.r_k, p.y, p.s1, p.B, p.H, p.H_kv, p.y_scale};
+    DecodeArgs g{p.r, p.w, p.k, p.v, p.a, p.b, p.s0, p.r_k, p.mask, p.y, p.s1, p.B, p.H, p.H_kv, p.y_scale};
     const int64_t heads = int64_t(p.B) * p.H;
     dim3 grid(unsigned((heads + 3) / 4));
-    hipLaunchKernelGGL((decode_kernel<D, Tin, Ty, LOGW, EPI>), grid, dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((decode_kernel<D, Tin, Ty, LOGW, EPI, KK>), grid, dim3(256), 0, stream, g);
     return hipGetLastError();
+}
+
+template <int D, typename Tin, typename Ty, bool KK>
+hipError_t dispatch_epi(const Params& p, hipStream_t s) {
+    const bool logw = p.w_mode == WKV7_W_LOGNEGLOG;
+    const bool epi = p.r_k != nullptr;
+    if (logw) return epi ? launch_t<D, Tin, Ty, true, true, KK>(p, s) : launch_t<D, Tin, Ty, true, false, KK>(p, s);
+    return epi ? launch_t<D, Tin, Ty, false, true, KK>(p, s) : launch_t<D, Tin, Ty, false, false, KK>(p, s);
 }
 
 template <int D, typename Tin, typename Ty>
 hipError_t dispatch_modes(const Params& p, hipStream_t s) {
-    const bool logw = p.w_mode == WKV7_W_LOGNEGLOG;
-    const bool epi = p.r_k != nullptr;
-    if (logw) return epi ? launch_t<D, Tin, Ty, true, true>(p, s) : launch_t<D, Tin, Ty, true, false>(p, s);
-    return epi ? launch_t<D, Tin, Ty, false, true>(p, s) : launch_t<D, Tin, Ty, false, false>(p, s);
+    return p.ab_mode == WKV7_AB_FROM_K ? dispatch_epi<D, Tin, Ty, true>(p, s) : dispatch_epi<D, Tin, Ty, false>(p, s);
 }
 
 template <int D>

@@ -86,6 +86,12 @@ __device__ __forceinline__ float log2_decay(float x, bool logneglog) {
     return __builtin_amdgcn_logf(x);
 }
 
+// 1 / max(|k|, 1e-12) from the sum of squares |k|^2: the scale of the
+// normalised key kk = k / max(|k|, 1e-12) (L2 normalisation with a floor).
+__device__ __forceinline__ float inv_key_norm(float sumsq) {
+    return 1.f / fmaxf(__builtin_sqrtf(sumsq), 1e-12f);
+}
+
 // Make the compiler materialise x here (inserting any wait for the load
 // that produced it at this point rather than at a later first use).
 __device__ __forceinline__ void settle(float& x) { asm volatile("" : "+v"(x)); }

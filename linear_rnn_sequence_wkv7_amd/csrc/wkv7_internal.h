@@ -15,8 +15,10 @@ namespace wkv7 {
 struct Params {
     int B, T, H, H_kv, D;
     int in_dtype, y_dtype, w_mode, chunk_len;
+    int ab_mode;              // wkv7_ab_mode
     float y_scale;
     const float* r_k;
+    const uint8_t* mask;      // [B, T] or null
     const void *r, *w, *k, *v, *a, *b;
     const float* s0;   // may be null: zero initial state
     void* y;

@@ -18,6 +18,15 @@
 // partials of its rows.  Readout partials S r go to an LDS ring of TY tokens
 // and are reduced, scaled, given the hxa07D bonus term and stored (coalesced)
 // once every TY tokens.
+//
+// Kernel vectors from k (KK): the a slot carries alpha and b is not read.
+// With kk = k / n, n = max(|k|, 1e-12), the removal term is
+// (S a) b^T = -(S k)(k alpha)^T / n^2, so each wave reduces S k (not S a) and
+// the partial |k|^2 of its columns through the same LDS exchange, and the
+// update adds (-(S k) / n^2) (k alpha)_j and v (k (1 - decay + alpha))_j.
+// Masked tokens (mask byte 0) run as the identity update: r, k, a, b = 0 and
+// decay 1 leave the state bit for bit and give y = 0.  Lane i of a wave holds
+// the mask byte of token t0 + i of the current ring block.
 #include "wkv7_internal.h"
 #include "wkv7_device.h"
 
@@ -28,6 +37,7 @@ struct ScanArgs {
     const void *r, *w, *k, *v, *a, *b;
     const float* s0;
     const float* r_k;
+    const uint8_t* mask;
     void* y;
     float* s1;
     int B, T, H, H_kv;
@@ -43,15 +53,24 @@ template <> struct ScanShape<128> { static constexpr int CS = 8, TY = 4; };
 template <typename Tin> struct RawSlice;
 template <> struct RawSlice<bf16_t> {
     uint32_t a[4], w[4], b[4], k[4], r[4];
+    template <bool LOAD_B>
     __device__ __forceinline__ void load(cptr<bf16_t> ap, cptr<bf16_t> wp, cptr<bf16_t> bp,
                                          cptr<bf16_t> kp, cptr<bf16_t> rp, int64_t oq, int64_t okv) {
         #pragma unroll
         for (int c = 0; c < 4; ++c) {
             a[c] = ((cptr<uint32_t>)(ap + oq))[c];
             w[c] = ((cptr<uint32_t>)(wp + oq))[c];
-            b[c] = ((cptr<uint32_t>)(bp + oq))[c];
+            b[c] = LOAD_B ? ((cptr<uint32_t>)(bp + oq))[c] : 0u;
             k[c] = ((cptr<uint32_t>)(kp + okv))[c];
             r[c] = ((cptr<uint32_t>)(rp + oq))[c];
+        }
+    }
+    // The identity token: a, b, k, r = 0 and decay 1 (w = 1, or -inf in the log-decay mode).
+    template <bool LOGW> __device__ __forceinline__ void make_identity() {
+        #pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            a[c] = 0u; b[c] = 0u; k[c] = 0u; r[c] = 0u;
+            w[c] = LOGW ? 0xff80ff80u : 0x3f803f80u;
         }
     }
     static __device__ __forceinline__ float get(const uint32_t* x, int c) {
@@ -65,11 +84,20 @@ template <> struct RawSlice<bf16_t> {
 };
 template <> struct RawSlice<float> {
     float a[8], w[8], b[8], k[8], r[8];
+    template <bool LOAD_B>
     __device__ __forceinline__ void load(cptr<float> ap, cptr<float> wp, cptr<float> bp,
                                          cptr<float> kp, cptr<float> rp, int64_t oq, int64_t okv) {
         #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            a[c] = ap[oq + c]; w[c] = wp[oq + c]; b[c] = bp[oq + c]; k[c] = kp[okv + c]; r[c] = rp[oq + c];
+            a[c] = ap[oq + c]; w[c] = wp[oq + c]; b[c] = LOAD_B ? bp[oq + c] : 0.f;
+            k[c] = kp[okv + c]; r[c] = rp[oq + c];
+        }
+    }
+    template <bool LOGW> __device__ __forceinline__ void make_identity() {
+        #pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            a[c] = 0.f; b[c] = 0.f; k[c] = 0.f; r[c] = 0.f;
+            w[c] = LOGW ? -__builtin_inff() : 1.f;
         }
     }
     __device__ __forceinline__ float A(int c) const { return a[c]; }
@@ -79,7 +107,7 @@ template <> struct RawSlice<float> {
     __device__ __forceinline__ float R(int c) const { return r[c]; }
 };
 
-template <int D, typename Tin, typename Ty, bool LOGW, bool EPI>
+template <int D, typename Tin, typename Ty, bool LOGW, bool EPI, bool KK>
 __global__ __launch_bounds__((D / ScanShape<D>::CS) * 64)
 void scan_kernel(ScanArgs g) {
     constexpr int CS = ScanShape<D>::CS;
@@ -98,6 +126,7 @@ void scan_kernel(ScanArgs g) {
     __shared__ float ybuf[TY][NW][D];
     __shared__ float vbuf[TY][D];
     __shared__ float bonus_buf[TY][NW];
+    __shared__ float ksq_buf[2][NW];       // per-wave |k|^2 partials (KK)
 
     // Wave-uniform reads of the per-token vectors go through the scalar path.
     const cptr<Tin> rp = as_const(static_cast<const Tin*>(g.r));
@@ -165,7 +194,8 @@ void scan_kernel(ScanArgs g) {
         const int line = id % LINES_PER_VEC;
         const int vec = (id / LINES_PER_VEC) % 6;
         const int s_tok = id / (LINES_PER_VEC * 6);
-        const void* src = vec == 0 ? g.r : vec == 1 ? g.w : vec == 2 ? g.k : vec == 3 ? g.v : vec == 4 ? g.a : g.b;
+        // b is not read (and may be null) when the kernel vectors come from k: touch a again.
+        const void* src = vec == 0 ? g.r : vec == 1 ? g.w : vec == 2 ? g.k : vec == 3 ? g.v : vec == 4 || KK ? g.a : g.b;
         const bool kvv = (vec == 2 || vec == 3);
         pf_base = as_global(static_cast<const uint32_t*>(src));
         pf_step = kvv ? step_kv : step_q;
@@ -199,25 +229,42 @@ void scan_kernel(ScanArgs g) {
             if (e < TY * D) vbuf[e / D][e % D] = vstage[u];
         }
     };
+    // Mask bytes of a ring block: lane i holds token tb + i's (1 without a mask).
+    const int64_t mbase = int64_t(bb) * T;
+    auto load_mask = [&](int tb) -> uint32_t {
+        return g.mask ? uint32_t(g.mask[mbase + min(tb + lane, T - 1)]) : 1u;
+    };
+    uint32_t mnext = load_mask(0), mcur = 0;
     load_v(0);
     store_v();
+    mcur = mnext;
     __syncthreads();
 
     int t0 = 0;  // first token of the current ring block
     // One token.  `cur` holds this token's vector slice; the next token's is
     // loaded into `nxt` while this token's update runs.
-    auto step = [&](const int t, const RawSlice<Tin>& cur, RawSlice<Tin>& nxt) {
+    auto step = [&](const int t, const RawSlice<Tin>& in, RawSlice<Tin>& nxt) {
         const int buf = t & 1;
-        // Partial removal projection over this wave's columns.
+        RawSlice<Tin> cur = in;
+        if (__builtin_amdgcn_readlane(int(mcur), t - t0) == 0) cur.template make_identity<LOGW>();
+        // Partial removal projection over this wave's columns (S k for KK).
         #pragma unroll
         for (int p = 0; p < RPL; ++p) {
             float s0 = 0.f, s1 = 0.f;
             #pragma unroll
             for (int c = 0; c < CS; c += 2) {
-                s0 = fmaf(S[p][c], cur.A(c), s0);
-                s1 = fmaf(S[p][c + 1], cur.A(c + 1), s1);
+                s0 = fmaf(S[p][c], KK ? cur.K(c) : cur.A(c), s0);
+                s1 = fmaf(S[p][c + 1], KK ? cur.K(c + 1) : cur.A(c + 1), s1);
             }
             red[buf][q][lane + 64 * p] = s0 + s1;
+        }
+        if constexpr (KK) {
+            if (lane == 0) {
+                float ss = 0.f;
+                #pragma unroll
+                for (int c = 0; c < CS; ++c) ss = fmaf(cur.K(c), cur.K(c), ss);
+                ksq_buf[buf][q] = ss;
+            }
         }
         __syncthreads();
         float sa[RPL], vrow[RPL];
@@ -231,12 +278,22 @@ void scan_kernel(ScanArgs g) {
             settle(vrow[p]);
             settle(sa[p]);
         }
+        // KK: sa holds S k; the removal coefficient of (k alpha)_j is -(S k) / n^2.
+        if constexpr (KK) {
+            float ss = 0.f;
+            #pragma unroll
+            for (int qq = 0; qq < NW; ++qq) ss += ksq_buf[buf][qq];
+            const float inv = inv_key_norm(ss);
+            const float c2 = -inv * inv;
+            #pragma unroll
+            for (int p = 0; p < RPL; ++p) sa[p] *= c2;
+        }
         // Issue the next token's scalar loads only after the LDS reads above
         // have been waited on (SMEM and LDS share one wait counter), so they
         // stay in flight during this token's update.
         __builtin_amdgcn_sched_barrier(0);
         const int tn = (t + 1 < T) ? t + 1 : t;
-        nxt.load(ap, wp, bp, kp, rp, base_q + tn * step_q + c0, base_kv + tn * step_kv + c0);
+        nxt.template load<!KK>(ap, wp, bp, kp, rp, base_q + tn * step_q + c0, base_kv + tn * step_kv + c0);
 
         // State update (in place: S*w, then + sa*b, then + v*k) and partial readout.
         #pragma unroll
@@ -245,9 +302,12 @@ void scan_kernel(ScanArgs g) {
             #pragma unroll
             for (int c = 0; c < CS; ++c) {
                 const float wc = LOGW ? decay_from_logneglog(cur.W(c)) : cur.W(c);
+                // KK: b_j -> (k alpha)_j (sa already carries -1/n^2), k_j -> k_j (1 - w_j + alpha_j).
+                const float bc = KK ? cur.K(c) * cur.A(c) : cur.Bv(c);
+                const float kc = KK ? cur.K(c) * (1.f - wc + cur.A(c)) : cur.K(c);
                 float s = S[p][c] * wc;
-                s = fmaf(sa[p], cur.Bv(c), s);
-                s = fmaf(vrow[p], cur.K(c), s);
+                s = fmaf(sa[p], bc, s);
+                s = fmaf(vrow[p], kc, s);
                 S[p][c] = s;
                 if (c & 1) y1 = fmaf(s, cur.R(c), y1); else y0 = fmaf(s, cur.R(c), y0);
             }
@@ -257,7 +317,14 @@ void scan_kernel(ScanArgs g) {
             if (lane == 0) {
                 float bsum = 0.f;
                 #pragma unroll
-                for (int c = 0; c < CS; ++c) bsum = fmaf(cur.R(c) * cur.K(c), rk[c], bsum);
+                for (int c = 0; c < CS; ++c) {
+                    float kc = cur.K(c);
+                    if constexpr (KK) {
+                        const float wc = LOGW ? decay_from_logneglog(cur.W(c)) : cur.W(c);
+                        kc *= 1.f - wc + cur.A(c);
+                    }
+                    bsum = fmaf(cur.R(c) * kc, rk[c], bsum);
+                }
                 bonus_buf[t - t0][q] = bsum;
             }
         }
@@ -266,6 +333,7 @@ void scan_kernel(ScanArgs g) {
         if (t - t0 == TY - 1 || t == T - 1) {
             __syncthreads();
             load_v(t + 1);
+            mnext = load_mask(t + 1);
             const int nsteps = t - t0 + 1;
             for (int e = threadIdx.x; e < nsteps * D; e += NT) {
                 const int s = e / D, i = e - s * D;
@@ -285,6 +353,7 @@ void scan_kernel(ScanArgs g) {
             // epilogue reads of it are done; the next token's barrier publishes it.
             __syncthreads();
             store_v();
+            mcur = mnext;
             // Issued last so that no wait in the ring block below covers them.
             sink ^= pf;
             prefetch(t0 + 2 * TY);
@@ -294,7 +363,7 @@ void scan_kernel(ScanArgs g) {
 
     // Two tokens per iteration with the slices swapping roles (no SGPR copies).
     RawSlice<Tin> sl0, sl1;
-    sl0.load(ap, wp, bp, kp, rp, base_q + c0, base_kv + c0);
+    sl0.template load<!KK>(ap, wp, bp, kp, rp, base_q + c0, base_kv + c0);
     int t = 0;
     for (; t + 1 < T; t += 2) {
         step(t, sl0, sl1);
@@ -317,21 +386,26 @@ void scan_kernel(ScanArgs g) {
     if (g.s1 && t0 != T && sink == 0x9e3779b9u) g.s1[0] = 0.f;
 }
 
-template <int D, typename Tin, typename Ty, bool LOGW, bool EPI>
+template <int D, typename Tin, typename Ty, bool LOGW, bool EPI, bool KK>
 hipError_t launch_scan_t(const Params& p, hipStream_t stream) {
-    ScanArgs g{p.r, p.w, p.k, p.v, p.a, p.b, p.s0, p.r_k, p.y, p.s1, p.B, p.T, p.H, p.H_kv, p.y_scale};
+    ScanArgs g{p.r, p.w, p.k, p.v, p.a, p.b, p.s0, p.r_k, p.mask, p.y, p.s1, p.B, p.T, p.H, p.H_kv, p.y_scale};
     dim3 grid(unsigned(p.B) * unsigned(p.H));
     dim3 block((D / ScanShape<D>::CS) * 64);
-    hipLaunchKernelGGL((scan_kernel<D, Tin, Ty, LOGW, EPI>), grid, block, 0, stream, g);
+    hipLaunchKernelGGL((scan_kernel<D, Tin, Ty, LOGW, EPI, KK>), grid, block, 0, stream, g);
     return hipGetLastError();
+}
+
+template <int D, typename Tin, typename Ty, bool KK>
+hipError_t dispatch_epi(const Params& p, hipStream_t s) {
+    const bool logw = p.w_mode == WKV7_W_LOGNEGLOG;
+    const bool epi = p.r_k != nullptr;
+    if (logw) return epi ? launch_scan_t<D, Tin, Ty, true, true, KK>(p, s) : launch_scan_t<D, Tin, Ty, true, false, KK>(p, s);
+    return epi ? launch_scan_t<D, Tin, Ty, false, true, KK>(p, s) : launch_scan_t<D, Tin, Ty, false, false, KK>(p, s);
 }
 
 template <int D, typename Tin, typename Ty>
 hipError_t dispatch_modes(const Params& p, hipStream_t s) {
-    const bool logw = p.w_mode == WKV7_W_LOGNEGLOG;
-    const bool epi = p.r_k != nullptr;
-    if (logw) return epi ? launch_scan_t<D, Tin, Ty, true, true>(p, s) : launch_scan_t<D, Tin, Ty, true, false>(p, s);
-    return epi ? launch_scan_t<D, Tin, Ty, false, true>(p, s) : launch_scan_t<D, Tin, Ty, false, false>(p, s);
+    return p.ab_mode == WKV7_AB_FROM_K ? dispatch_epi<D, Tin, Ty, true>(p, s) : dispatch_epi<D, Tin, Ty, false>(p, s);
 }
 
 template <int D>

@@ -32,6 +32,14 @@
 // pair-interleaved (position 8 q + 4 e + r of a 32-block holds index
 // 16 e + 4 q + r), and every accumulator chain uses the single 16x16x32
 // opcode (never a result of one MFMA opcode as the accumulator of another).
+//
+// Only pass 1 reads r, w, k, a, b, so both input options live there.  A
+// masked token is the identity token (r, k, a, b = 0, decay 1): its rows and
+// columns of every per-chunk matrix vanish, so pass 2 adds nothing for it and
+// outputs y = 0.  Kernel vectors from k (KK): the a slot carries alpha; each
+// row thread reduces |k|^2 over its 8 keys, the 16 threads of a token meet in
+// LDS (one extra barrier inside the scaling step), and the operands take
+// a = -kk, b = kk alpha and k (1 - decay + alpha) in place of the inputs.
 #include "wkv7_internal.h"
 #include "wkv7_device.h"
 
@@ -169,6 +177,9 @@ template <> struct Row8<bf16_t> {
     __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
         x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
     }
+    __device__ __forceinline__ void keep_if(bool keep) {
+        x.x = keep ? x.x : 0u; x.y = keep ? x.y : 0u; x.z = keep ? x.z : 0u; x.w = keep ? x.w : 0u;
+    }
     __device__ __forceinline__ float get(int e) const {
         const uint32_t d = e < 2 ? x.x : e < 4 ? x.y : e < 6 ? x.z : x.w;
         return (e & 1) ? __uint_as_float(d & 0xffff0000u) : __uint_as_float(d << 16);
@@ -179,6 +190,13 @@ template <> struct Row8<float> {
     __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
         x[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
         x[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+    }
+    __device__ __forceinline__ void keep_if(bool keep) {
+        #pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            x[i].x = keep ? x[i].x : 0u; x[i].y = keep ? x[i].y : 0u;
+            x[i].z = keep ? x[i].z : 0u; x[i].w = keep ? x[i].w : 0u;
+        }
     }
     __device__ __forceinline__ float get(int e) const {
         const uint4& u = x[e >> 2];
@@ -242,7 +260,8 @@ constexpr int P_UTL = P_UTH + MATL;
 constexpr int P_D0T = P_UTL + MATL;              // D0^T hi / lo, [16][PD] each
 constexpr int P_DL = P_D0T + 2 * 16 * PD * 2;    // fp32 [DK] 2^g_L
 constexpr int P_BON = P_DL + DK * 4;             // fp32 [8 waves][L] bonus partials
-constexpr int SMEM_PREP = P_BON + 8 * L * 4;
+constexpr int P_KSQ = P_BON + 8 * L * 4;         // fp32 [L][8 waves] |k|^2 partials (KK)
+constexpr int SMEM_PREP = P_KSQ + L * 8 * 4;
 static_assert(SMEM_PREP <= 160 * 1024, "LDS budget");
 static_assert(P_ATT % 16 == 0 && P_ARB % 16 == 0 && P_D0T % 16 == 0 && P_DL % 16 == 0, "alignment");
 
@@ -252,6 +271,7 @@ constexpr int kPrepGrid = 256;   // one persistent workgroup per compute unit of
 struct PrepArgs {
     const void *r, *w, *k, *a, *b;
     const float* r_k;
+    const uint8_t* mask;
     char* ws;
     int T, H, H_kv, nch, items;
 };
@@ -259,12 +279,13 @@ struct PrepArgs {
 template <typename Tin> struct ItemRows {
     Row8<Tin> r, w, k, a, b;
     float rk[8];
+    uint32_t m;   // mask byte of the row's token (1 without a mask, 0 past the end)
 };
 // (One dword per load instruction suffices: the wait is per instruction.)
 __device__ __forceinline__ void settle_row(Row8<bf16_t>& x) { asm volatile("" : "+v"(x.x.x)); }
 __device__ __forceinline__ void settle_row(Row8<float>& x) { asm volatile("" : "+v"(x.x[0].x), "+v"(x.x[1].x)); }
 
-template <typename Tin, bool LOGW, bool EPI>
+template <typename Tin, bool LOGW, bool EPI, bool KK>
 __global__ __launch_bounds__(NTHR_PREP)
 void prep128_kernel(PrepArgs g) {
     constexpr uint32_t SI = sizeof(Tin);
@@ -287,8 +308,11 @@ void prep128_kernel(PrepArgs g) {
         x.r.load(chunk_rsrc(static_cast<const char*>(g.r), tok0, c0, T, stq), oq);
         x.w.load(chunk_rsrc(static_cast<const char*>(g.w), tok0, c0, T, stq), oq);
         x.a.load(chunk_rsrc(static_cast<const char*>(g.a), tok0, c0, T, stq), oq);
-        x.b.load(chunk_rsrc(static_cast<const char*>(g.b), tok0, c0, T, stq), oq);
+        if constexpr (!KK) x.b.load(chunk_rsrc(static_cast<const char*>(g.b), tok0, c0, T, stq), oq);
         x.k.load(chunk_rsrc(static_cast<const char*>(g.k), tok0, c0, T, stkv), okv);
+        x.m = g.mask ? uint32_t(__builtin_amdgcn_raw_buffer_load_b8(
+                           chunk_rsrc(reinterpret_cast<const char*>(g.mask), tok0, c0, T, 1u), uint32_t(t), 0, 0))
+                     : 1u;
         if constexpr (EPI) {
             const float4 u0 = *reinterpret_cast<const float4*>(g.r_k + h * DK + j0);
             const float4 u1 = *reinterpret_cast<const float4*>(g.r_k + h * DK + j0 + 4);
@@ -306,7 +330,9 @@ void prep128_kernel(PrepArgs g) {
 
     ItemRows<Tin> cur, nxt;
     auto settle_item = [&](ItemRows<Tin>& x) {
-        settle_row(x.r); settle_row(x.w); settle_row(x.k); settle_row(x.a); settle_row(x.b);
+        settle_row(x.r); settle_row(x.w); settle_row(x.k); settle_row(x.a);
+        if constexpr (!KK) settle_row(x.b);
+        asm volatile("" : "+v"(x.m));
         #pragma unroll
         for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(x.rk[e]));
     };
@@ -323,13 +349,30 @@ void prep128_kernel(PrepArgs g) {
 
         // ---------------- Q0: decay prefix and the scaled operands (row threads) ----------------
         {
-            const bool ok = c0 + t < T;   // tokens past the end decay by 1 and carry zeros
+            // Tokens past the end (and masked ones) decay by 1 and carry zeros.
+            const bool ok = c0 + t < T && cur.m != 0;
+            if (g.mask) {
+                cur.r.keep_if(ok); cur.k.keep_if(ok); cur.a.keep_if(ok);
+                if constexpr (!KK) cur.b.keep_if(ok);
+            }
+            if constexpr (KK) {
+                // |k|^2 partial over this thread's 8 keys and its partner lane's 8.
+                float ss = 0.f;
+                #pragma unroll
+                for (int x = 0; x < 8; ++x) ss = fmaf(cur.k.get(x), cur.k.get(x), ss);
+                ss += __shfl_xor(ss, 32);
+                if (l < 32) sts<float>(smem + P_KSQ, (t * 8 + w) * 4, ss);
+            }
             // Per key: E = 2^g_t, Ei = 2^-g_t; 2^g_(t-1) is E of the previous token
             // (lane l - 1, 1 at t = 0); d = 2^g_L is E of token 31 (lane 31 / 63) and
             // 2^(g_L - g_t) = d Ei.  Two exp2 per element besides the log-decay.
-            float Ex[8], Eix[8], Epx[8], dx[8], gs[8];
+            float Ex[8], Eix[8], Epx[8], dx[8], gs[8], dec[8];
             #pragma unroll
             for (int x = 0; x < 8; ++x) gs[x] = ok ? log2_decay(cur.w.get(x), LOGW) : 0.f;
+            if constexpr (KK) {
+                #pragma unroll
+                for (int x = 0; x < 8; ++x) dec[x] = LOGW ? __builtin_amdgcn_exp2f(gs[x]) : cur.w.get(x);
+            }
             scan32x8(gs);
             #pragma unroll
             for (int x = 0; x < 8; ++x) {
@@ -341,6 +384,13 @@ void prep128_kernel(PrepArgs g) {
                 const float d31 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ex[x]), 31));
                 const float d63 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ex[x]), 63));
                 dx[x] = l < 32 ? d31 : d63;
+            }
+            // KK: the token's |k|^2 from the 8 waves' partials.
+            float inv = 0.f;
+            if constexpr (KK) {
+                __syncthreads();
+                const float4 s0 = lds<float4>(smem + P_KSQ, t * 32), s1 = lds<float4>(smem + P_KSQ, t * 32 + 16);
+                inv = inv_key_norm(((s0.x + s0.y) + (s0.z + s0.w)) + ((s1.x + s1.y) + (s1.z + s1.w)));
             }
             uint32_t at[4], rth[4], rtl[4], bt[4], kth[4], ktl[4], bhat[4];
             float bonus_part = 0.f;
@@ -355,9 +405,19 @@ void prep128_kernel(PrepArgs g) {
                     Eh[u] = dx[e + u] * Eix[e + u];
                 }
                 const float r0 = cur.r.get(e), r1 = cur.r.get(e + 1);
-                const float k0 = cur.k.get(e), k1 = cur.k.get(e + 1);
-                const float b0 = cur.b.get(e), b1 = cur.b.get(e + 1);
-                at[e / 2] = pack_bf16(cur.a.get(e) * Ep[0], cur.a.get(e + 1) * Ep[1]);
+                float k0 = cur.k.get(e), k1 = cur.k.get(e + 1);
+                float a0 = cur.a.get(e), a1 = cur.a.get(e + 1);
+                float b0, b1;
+                if constexpr (KK) {
+                    // a holds alpha: b = kk alpha, a = -kk, k <- k (1 - decay + alpha).
+                    const float kk0 = k0 * inv, kk1 = k1 * inv;
+                    b0 = kk0 * a0; b1 = kk1 * a1;
+                    k0 *= 1.f - dec[e] + a0; k1 *= 1.f - dec[e + 1] + a1;
+                    a0 = -kk0; a1 = -kk1;
+                } else {
+                    b0 = cur.b.get(e); b1 = cur.b.get(e + 1);
+                }
+                at[e / 2] = pack_bf16(a0 * Ep[0], a1 * Ep[1]);
                 split2(r0 * E[0], r1 * E[1], rth[e / 2], rtl[e / 2]);
                 bt[e / 2] = pack_bf16(b0 * Ei[0], b1 * Ei[1]);
                 split2(k0 * Ei[0], k1 * Ei[1], kth[e / 2], ktl[e / 2]);
@@ -995,12 +1055,12 @@ void scan128_kernel(ScanArgs g) {
     }
 }
 
-template <typename Tin, typename Ty, bool LOGW, bool EPI>
+template <typename Tin, typename Ty, bool LOGW, bool EPI, bool KK>
 hipError_t launch_t(const Params& p, void* ws, hipStream_t stream) {
     const int bh = p.B * p.H, nch = (p.T + L - 1) / L;
     const int items = bh * nch;
-    PrepArgs pa{p.r, p.w, p.k, p.a, p.b, p.r_k, static_cast<char*>(ws), p.T, p.H, p.H_kv, nch, items};
-    auto prep = prep128_kernel<Tin, LOGW, EPI>;
+    PrepArgs pa{p.r, p.w, p.k, p.a, p.b, p.r_k, p.mask, static_cast<char*>(ws), p.T, p.H, p.H_kv, nch, items};
+    auto prep = prep128_kernel<Tin, LOGW, EPI, KK>;
     static bool attr_set = false;   // per template instance; idempotent if raced
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep),
@@ -1021,12 +1081,17 @@ hipError_t launch_t(const Params& p, void* ws, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename Tin, typename Ty>
-hipError_t dispatch_modes(const Params& p, void* ws, hipStream_t s) {
+template <typename Tin, typename Ty, bool KK>
+hipError_t dispatch_epi(const Params& p, void* ws, hipStream_t s) {
     const bool logw = p.w_mode == WKV7_W_LOGNEGLOG;
     const bool epi = p.r_k != nullptr;
-    if (logw) return epi ? launch_t<Tin, Ty, true, true>(p, ws, s) : launch_t<Tin, Ty, true, false>(p, ws, s);
-    return epi ? launch_t<Tin, Ty, false, true>(p, ws, s) : launch_t<Tin, Ty, false, false>(p, ws, s);
+    if (logw) return epi ? launch_t<Tin, Ty, true, true, KK>(p, ws, s) : launch_t<Tin, Ty, true, false, KK>(p, ws, s);
+    return epi ? launch_t<Tin, Ty, false, true, KK>(p, ws, s) : launch_t<Tin, Ty, false, false, KK>(p, ws, s);
+}
+
+template <typename Tin, typename Ty>
+hipError_t dispatch_modes(const Params& p, void* ws, hipStream_t s) {
+    return p.ab_mode == WKV7_AB_FROM_K ? dispatch_epi<Tin, Ty, true>(p, ws, s) : dispatch_epi<Tin, Ty, false>(p, ws, s);
 }
 
 }  // namespace

@@ -17,6 +17,7 @@ Layouts (all C-contiguous):
   k, v       : [B, T, H_kv, D]
   state      : [B, H, D, D] fp32, state[b, h, i, j] = S_ij (i value row, j key column)
   r_k        : [H, D] fp32
+  mask       : [B, T] uint8 (0 = masked token), or None
 Decode workloads carry a leading step axis: r..b are [steps, B, 1, H, D].
 
 bf16 tensors are returned as uint16 bit patterns (round-to-nearest-even from
@@ -68,6 +69,8 @@ class Workload:
     y_scale: float = 1.0
     rk_std: float = 0.0       # > 0 -> per-head/dim bonus weights r_k ~ N(0, rk_std^2)
     kk_from_k: bool = False   # removal key = normalise(repeated k) instead of an independent draw
+    ab_mode: str = "given"    # "from_k": a carries alpha, b is None (the kernel forms both from k)
+    mask: str = ""            # "": none; "pad": right padding; "holes": scattered masked tokens
     algo: str = "auto"
     note: str = ""
 
@@ -125,12 +128,17 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarra
     """Draw the workload's inputs.
 
     Draw order from one PCG64 stream (float64 normals, C order): r, k, v, z,
-    kappa_raw (skipped when kk_from_k), alpha_raw, state0 (when s0_std > 0),
-    r_k (when rk_std > 0).
+    kappa_raw (skipped when kk_from_k or ab_mode == "from_k"), alpha_raw,
+    state0 (when s0_std > 0), r_k (when rk_std > 0), then the mask draws.
 
     Returns a dict with keys r, w, k, v, a, b (encoded per in_dtype), state0
-    (fp32 or None), r_k (fp32 or None).  For decode workloads each per-token
-    tensor has a leading [steps] axis.
+    (fp32 or None), r_k (fp32 or None), mask (uint8 or None).  With ab_mode
+    "from_k", a holds alpha and b is None.  For decode workloads each per-token
+    tensor has a leading [steps] axis (the mask too: [steps, B, 1]).
+
+    Mask recipes: "pad" keeps a prefix of each sequence, its length uniform
+    on [ceil(T / 2), T] (sequence 0 keeps all T tokens); "holes" masks each
+    token independently with probability 1/8.
     """
     rng = np.random.Generator(np.random.PCG64(wl.seed if seed is None else seed))
     lead = (wl.steps,) if wl.kind == "decode" else ()
@@ -155,15 +163,24 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarra
     out["w"] = _encode(w, wl.in_dtype)
     del w
 
-    if wl.kk_from_k:
-        kk = _l2_normalize(np.repeat(k64, rep, axis=-2))
+    if wl.ab_mode == "from_k":
+        del k64
+        alpha = 1.0 / (1.0 + np.exp(-rng.standard_normal(shp_q)))
+        out["a"] = _encode(alpha, wl.in_dtype)
+        out["b"] = None
+        del alpha
+    elif wl.ab_mode == "given":
+        if wl.kk_from_k:
+            kk = _l2_normalize(np.repeat(k64, rep, axis=-2))
+        else:
+            kk = _l2_normalize(rng.standard_normal(shp_q))
+        del k64
+        alpha = 1.0 / (1.0 + np.exp(-rng.standard_normal(shp_q)))
+        out["a"] = _encode(-kk, wl.in_dtype)
+        out["b"] = _encode(kk * alpha, wl.in_dtype)
+        del kk, alpha
     else:
-        kk = _l2_normalize(rng.standard_normal(shp_q))
-    del k64
-    alpha = 1.0 / (1.0 + np.exp(-rng.standard_normal(shp_q)))
-    out["a"] = _encode(-kk, wl.in_dtype)
-    out["b"] = _encode(kk * alpha, wl.in_dtype)
-    del kk, alpha
+        raise ValueError(wl.ab_mode)
 
     if wl.s0_std > 0:
         out["state0"] = (rng.standard_normal((wl.B, wl.H, wl.D, wl.D)) * wl.s0_std).astype(np.float32)
@@ -173,4 +190,18 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarra
         out["r_k"] = (rng.standard_normal((wl.H, wl.D)) * wl.rk_std).astype(np.float32)
     else:
         out["r_k"] = None
+    out["mask"] = _mask(rng, wl, lead)
     return out
+
+
+def _mask(rng, wl: Workload, lead) -> Optional[np.ndarray]:
+    if not wl.mask:
+        return None
+    shp = lead + (wl.B, wl.T)
+    if wl.mask == "holes":
+        return (rng.random(shp) >= 0.125).astype(np.uint8)
+    if wl.mask == "pad":
+        lens = rng.integers((wl.T + 1) // 2, wl.T + 1, size=lead + (wl.B,))
+        lens[..., 0] = wl.T
+        return (np.arange(wl.T) < lens[..., None]).astype(np.uint8)
+    raise ValueError(wl.mask)

@@ -17,13 +17,14 @@ __all__ = [
     "wkv7_forward", "wkv7_decode_step", "wkv7_resolve_algo", "wkv7_workspace_bytes", "Wkv7Error",
     "lib_path", "load_library",
     "WKV7_OK", "WKV7_EINVAL", "WKV7_EUNSUPPORTED", "WKV7_EDEVICE", "WKV7_ELAUNCH",
-    "ALGOS", "W_MODES", "Desc", "EXPORTED_SYMBOLS",
+    "ALGOS", "W_MODES", "AB_MODES", "Desc", "EXPORTED_SYMBOLS",
 ]
 
 WKV7_OK, WKV7_EINVAL, WKV7_EUNSUPPORTED, WKV7_EDEVICE, WKV7_ELAUNCH = 0, 1, 2, 3, 4
 _DTYPES = {"f32": 0, "bf16": 1}
 W_MODES = {"decay": 0, "logneglog": 1}
 ALGOS = {"auto": 0, "scan": 1, "chunked": 2, "two_pass": 3}
+AB_MODES = {"given": 0, "from_k": 1}
 EXPORTED_SYMBOLS = ("wkv7_forward", "wkv7_forward_ws", "wkv7_workspace_bytes", "wkv7_decode_step",
                     "wkv7_resolve_algo", "wkv7_strerror", "wkv7_last_error", "wkv7_abi_version")
 
@@ -40,7 +41,8 @@ class Desc(ctypes.Structure):
         ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("H_kv", ctypes.c_int32),
         ("D", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32),
         ("w_mode", ctypes.c_int32), ("algo", ctypes.c_int32), ("chunk_len", ctypes.c_int32),
-        ("y_scale", ctypes.c_float), ("reserved", ctypes.c_int32), ("r_k", ctypes.c_void_p),
+        ("y_scale", ctypes.c_float), ("ab_mode", ctypes.c_int32), ("r_k", ctypes.c_void_p),
+        ("mask", ctypes.c_void_p),
     ]
 
 
@@ -90,11 +92,11 @@ def _status_name(code: int) -> str:
 
 
 def make_desc(B, T, H, D, *, H_kv=None, in_dtype="bf16", y_dtype="bf16", w_mode="decay",
-              algo="auto", chunk_len=0, y_scale=1.0, r_k_ptr=None) -> Desc:
+              algo="auto", chunk_len=0, y_scale=1.0, r_k_ptr=None, ab_mode="given", mask_ptr=None) -> Desc:
     return Desc(B=B, T=T, H=H, H_kv=H if H_kv is None else H_kv, D=D,
                 in_dtype=_DTYPES[in_dtype], y_dtype=_DTYPES[y_dtype], w_mode=W_MODES[w_mode],
-                algo=ALGOS[algo], chunk_len=chunk_len, y_scale=float(y_scale), reserved=0,
-                r_k=r_k_ptr)
+                algo=ALGOS[algo], chunk_len=chunk_len, y_scale=float(y_scale), ab_mode=AB_MODES[ab_mode],
+                r_k=r_k_ptr, mask=mask_ptr)
 
 
 def _torch():
@@ -115,7 +117,7 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _check_inputs(r, w, k, v, a, b, state, r_k):
+def _check_inputs(r, w, k, v, a, b, state, r_k, mask=None, ab_mode="given"):
     torch = _torch()
     if r.dim() != 4:
         raise ValueError("r must be [B, T, H, D]")
@@ -124,12 +126,20 @@ def _check_inputs(r, w, k, v, a, b, state, r_k):
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU device")
     dt = r.dtype
+    if ab_mode not in AB_MODES:
+        raise ValueError(f"ab_mode must be one of {sorted(AB_MODES)}")
+    if b is None and ab_mode != "from_k":
+        raise ValueError("b is required unless ab_mode='from_k'")
     for name, x in (("w", w), ("a", a), ("b", b)):
+        if x is None:
+            continue
         if tuple(x.shape) != (B, T, H, D):
             raise ValueError(f"{name} must have shape {(B, T, H, D)}, got {tuple(x.shape)}")
     if k.dim() != 4 or tuple(k.shape[:2]) != (B, T) or k.shape[3] != D or tuple(v.shape) != tuple(k.shape):
         raise ValueError("k and v must be [B, T, H_kv, D] with matching shapes")
     for name, x in (("r", r), ("w", w), ("k", k), ("v", v), ("a", a), ("b", b)):
+        if x is None:
+            continue
         if x.dtype != dt:
             raise TypeError(f"{name} has dtype {x.dtype}, expected {dt} like r")
         if x.device != dev or not x.is_contiguous():
@@ -142,6 +152,10 @@ def _check_inputs(r, w, k, v, a, b, state, r_k):
     if r_k is not None:
         if tuple(r_k.shape) != (H, D) or r_k.dtype != torch.float32 or r_k.device != dev or not r_k.is_contiguous():
             raise ValueError(f"r_k must be contiguous float32 [H, D] = {(H, D)} on {dev}")
+    if mask is not None:
+        if (tuple(mask.shape) != (B, T) or mask.dtype not in (torch.uint8, torch.bool)
+                or mask.device != dev or not mask.is_contiguous()):
+            raise ValueError(f"mask must be a contiguous uint8 or bool [B, T] = {(B, T)} tensor on {dev}")
     return B, T, H, int(k.shape[2]), D
 
 
@@ -169,11 +183,15 @@ def wkv7_workspace_bytes(B, T, H, D, *, H_kv=None, algo="auto", **kw) -> int:
 
 def wkv7_forward(r, w, k, v, a, b, state=None, *, w_mode: str = "decay", y_dtype: Optional[str] = None,
                  algo: str = "auto", chunk_len: int = 0, y_scale: float = 1.0, r_k=None,
+                 ab_mode: str = "given", mask=None,
                  y=None, state_out=None, return_state: bool = True, workspace=None) -> Tuple[object, object]:
     """Run the forward on torch GPU tensors.
 
     r, w, a, b: [B, T, H, D]; k, v: [B, T, H_kv, D]; all float32 or all bfloat16, contiguous.
     state: [B, H, D, D] float32 or None (zeros).  r_k: [H, D] float32 or None.
+    ab_mode "from_k": a holds alpha and b is unused (may be None); the kernel
+    forms kk = normalize(k), a = -kk, b = kk * alpha, k * (1 - decay + alpha).
+    mask: [B, T] uint8 / bool device tensor (0 = token masked) or None.
     y_dtype: "f32" | "bf16" (default: the input dtype).  Outputs are allocated
     unless `y` / `state_out` are given (state_out may equal state: in place).
     algo "auto" and "two_pass" go through wkv7_forward_ws: when the library
@@ -182,14 +200,15 @@ def wkv7_forward(r, w, k, v, a, b, state=None, *, w_mode: str = "decay", y_dtype
     Returns (y, state_out); state_out is None when return_state is False.
     """
     torch = _torch()
-    B, T, H, H_kv, D = _check_inputs(r, w, k, v, a, b, state, r_k)
+    B, T, H, H_kv, D = _check_inputs(r, w, k, v, a, b, state, r_k, mask, ab_mode)
     ydt = y_dtype or _dtype_name(r)
     if y is None:
         y = torch.empty((B, T, H, D), dtype=torch.float32 if ydt == "f32" else torch.bfloat16, device=r.device)
     if state_out is None and return_state:
         state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=r.device)
     desc = make_desc(B, T, H, D, H_kv=H_kv, in_dtype=_dtype_name(r), y_dtype=ydt, w_mode=w_mode, algo=algo,
-                     chunk_len=chunk_len, y_scale=y_scale, r_k_ptr=_ptr(r_k))
+                     chunk_len=chunk_len, y_scale=y_scale, r_k_ptr=_ptr(r_k), ab_mode=ab_mode,
+                     mask_ptr=_ptr(mask))
     if algo in ("auto", "two_pass"):
         need = load_library().wkv7_workspace_bytes(ctypes.byref(desc))
         if need < 0:
@@ -205,10 +224,12 @@ def wkv7_forward(r, w, k, v, a, b, state=None, *, w_mode: str = "decay", y_dtype
 
 
 def wkv7_decode_step(r, w, k, v, a, b, state, *, w_mode: str = "decay", y_dtype: Optional[str] = None,
-                     y_scale: float = 1.0, r_k=None, y=None, state_out=None) -> Tuple[object, object]:
-    """One token per sequence: inputs [B, 1, H, D] (k, v [B, 1, H_kv, D]); state [B, H, D, D] or None."""
+                     y_scale: float = 1.0, r_k=None, ab_mode: str = "given", mask=None,
+                     y=None, state_out=None) -> Tuple[object, object]:
+    """One token per sequence: inputs [B, 1, H, D] (k, v [B, 1, H_kv, D]); state [B, H, D, D] or None.
+    ab_mode and mask ([B, 1]) as in wkv7_forward."""
     torch = _torch()
-    B, T, H, H_kv, D = _check_inputs(r, w, k, v, a, b, state, r_k)
+    B, T, H, H_kv, D = _check_inputs(r, w, k, v, a, b, state, r_k, mask, ab_mode)
     if T != 1:
         raise ValueError("decode_step takes exactly one token per sequence (T == 1)")
     ydt = y_dtype or _dtype_name(r)
@@ -217,7 +238,7 @@ def wkv7_decode_step(r, w, k, v, a, b, state, *, w_mode: str = "decay", y_dtype:
     if state_out is None:
         state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=r.device)
     desc = make_desc(B, 1, H, D, H_kv=H_kv, in_dtype=_dtype_name(r), y_dtype=ydt, w_mode=w_mode,
-                     y_scale=y_scale, r_k_ptr=_ptr(r_k))
+                     y_scale=y_scale, r_k_ptr=_ptr(r_k), ab_mode=ab_mode, mask_ptr=_ptr(mask))
     _call("wkv7_decode_step", desc, r, w, k, v, a, b, state, y, state_out)
     return y, state_out
 

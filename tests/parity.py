@@ -45,6 +45,9 @@ def select_pairs(x, wl, pairs):
     hks = hs // rep
     out = {}
     for key in ("r", "w", "a", "b"):
+        if x.get(key) is None:
+            out[key] = None
+            continue
         out[key] = np.ascontiguousarray(np.moveaxis(x[key][bs, :, hs], 0, 1)[None])   # [1, T, n, D]
     for key in ("k", "v"):
         out[key] = np.ascontiguousarray(np.moveaxis(x[key][bs, :, hks], 0, 1)[None])
@@ -54,11 +57,23 @@ def select_pairs(x, wl, pairs):
 
 
 def oracle_pairs(x, wl, pairs):
-    """Oracle y [n, T, D] and final state [n, D, D] for the chosen (b, h) pairs."""
-    sel = select_pairs(x, wl, pairs)
-    y, S = O.wkv7_forward(sel["r"], sel["w"], sel["k"], sel["v"], sel["a"], sel["b"], sel["state0"],
-                          w_mode=wl.w_mode, y_scale=wl.y_scale, r_k=sel["r_k"])
-    return np.moveaxis(y[0], 1, 0), S[0]
+    """Oracle y [n, T, D] and final state [n, D, D] for the chosen (b, h) pairs.
+    With a mask, pairs of the same sequence run together under its mask row."""
+    kk = getattr(wl, "ab_mode", "given") == "from_k"
+    mask = x.get("mask")
+    groups = [list(range(len(pairs)))] if mask is None else \
+        [[i for i, p in enumerate(pairs) if p[0] == b] for b in sorted({p[0] for p in pairs})]
+    y_out = [None] * len(pairs)
+    s_out = [None] * len(pairs)
+    for idx in groups:
+        sel = select_pairs(x, wl, [pairs[i] for i in idx])
+        m = None if mask is None else mask[pairs[idx[0]][0]][None]
+        y, S = O.wkv7_forward(sel["r"], sel["w"], sel["k"], sel["v"], sel["a"], sel["b"], sel["state0"],
+                              w_mode=wl.w_mode, y_scale=wl.y_scale, r_k=sel["r_k"], kk_from_k=kk, mask=m)
+        for j, i in enumerate(idx):
+            y_out[i] = y[0, :, j]
+            s_out[i] = S[0, j]
+    return np.stack(y_out), np.stack(s_out)
 
 
 def sample_pairs(wl, n, seed=0):

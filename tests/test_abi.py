@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_strerror():
     lib = W.load_library()
-    assert lib.wkv7_abi_version() == 2
+    assert lib.wkv7_abi_version() == 3
     assert lib.wkv7_strerror(0) == b"ok"
     assert lib.wkv7_strerror(W.WKV7_EINVAL) == b"invalid argument"
     assert lib.wkv7_strerror(99) == b"unknown status"
@@ -76,15 +76,16 @@ def test_bad_descriptor_rejected(desc, code):
     assert _call(desc, fn="wkv7_decode_step") == code
 
 
-def test_bad_enum_and_reserved():
+def test_bad_enums():
     d = good(); d.in_dtype = 7
     assert _call(d) == W.WKV7_EINVAL
     d = good(); d.w_mode = 2
     assert _call(d) == W.WKV7_EINVAL
     d = good(); d.algo = 9
     assert _call(d) == W.WKV7_EINVAL
-    d = good(); d.reserved = 1
+    d = good(); d.ab_mode = 2
     assert _call(d) == W.WKV7_EINVAL
+    assert b"ab_mode" in W.load_library().wkv7_last_error()
     d = good(); d.y_scale = float("nan")
     assert _call(d) == W.WKV7_EINVAL
     assert b"y_scale" in W.load_library().wkv7_last_error()
@@ -162,3 +163,25 @@ def test_two_pass_argument_rules():
     assert _call(good(D=128, T=64, algo="scan", B=0), {}, fn="wkv7_forward_ws") == W.WKV7_OK
     assert _call(good(D=128, T=64, B=0), {}, fn="wkv7_forward_ws") == W.WKV7_OK
     assert W.wkv7_resolve_algo(2, 64, 4, 128, algo="two_pass") == "two_pass"
+
+
+def test_desc_layout():
+    # Field offsets of struct wkv7_desc on LP64 (the mask pointer follows r_k).
+    assert W.Desc.ab_mode.offset == 44 and W.Desc.r_k.offset == 48 and W.Desc.mask.offset == 56
+    assert ctypes.sizeof(W.Desc) == 64
+
+
+def test_ab_mode_from_k_rules():
+    # The one-pass chunked kernels do not form the kernel vectors from k.
+    assert _call(good(T=64, algo="chunked", ab_mode="from_k")) == W.WKV7_EUNSUPPORTED
+    assert _call(good(D=128, T=64, algo="chunked", ab_mode="from_k")) == W.WKV7_EUNSUPPORTED
+    # b is not read: NULL passes its check (the call then fails on the misaligned y).
+    assert _call(good(ab_mode="from_k"), {"b": None, "y": FAKE + 4096 + 8}) == W.WKV7_EINVAL
+    assert b"y is not" in W.load_library().wkv7_last_error()
+    assert _call(good(), {"b": None}) == W.WKV7_EINVAL
+    assert b"b is NULL" in W.load_library().wkv7_last_error()
+    # AUTO: the scan without a workspace, the two-pass form with one at D = 128.
+    assert W.wkv7_resolve_algo(2, 64, 4, 64, ab_mode="from_k") == "scan"
+    assert W.wkv7_resolve_algo(2, 64, 4, 128, ab_mode="from_k") == "scan"
+    assert W.wkv7_workspace_bytes(2, 64, 4, 128, ab_mode="from_k") == 2 * 4 * 2 * 54272
+    assert W.wkv7_workspace_bytes(2, 64, 4, 64, ab_mode="from_k") == 0

@@ -81,3 +81,23 @@ def test_logneglog_and_grouping():
         kk = kh / np.linalg.norm(kh, axis=-1, keepdims=True)
         assert np.allclose(-a[:, :, h], kk, atol=2e-2)
     assert x["r_k"].shape == (32, 128) and abs(x["r_k"].std() - 0.1) < 0.01
+
+
+def test_from_k_and_masks():
+    base = G.workload("hxa07d_bf16_b2_t16384_h32_kv8_d128", B=3, T=40)
+    x = G.make_inputs(G.workload(base.name, B=3, T=40, ab_mode="from_k"))
+    alpha = _f(x["a"]).astype(np.float64)
+    assert x["b"] is None and alpha.min() > 0.0 and alpha.max() < 1.0
+    assert x["mask"] is None
+    # The draws before alpha are the same as in the given-a/b mode.
+    y = G.make_inputs(base)
+    for key in ("r", "k", "v", "w"):
+        np.testing.assert_array_equal(x[key], y[key])
+    pad = G.make_inputs(G.workload(base.name, B=3, T=40, mask="pad"))["mask"]
+    assert pad.shape == (3, 40) and pad.dtype == np.uint8
+    assert np.all(pad[0] == 1)
+    for row in pad:                       # a kept prefix of at least half the tokens
+        n = int(row.sum())
+        assert n >= 20 and np.all(row[:n] == 1) and np.all(row[n:] == 0)
+    holes = G.make_inputs(G.workload(base.name, B=3, T=4000, H=1, H_kv=1, mask="holes"))["mask"]
+    assert abs(1.0 - holes.mean() - 0.125) < 0.01
