@@ -202,7 +202,7 @@ template <> struct Row8<float> {
 
 template <int V> struct IC { static constexpr int value = V; };
 
-template <typename Tin, typename Ty, bool LOGW, bool EPI>
+template <typename Tin, typename Ty, bool LOGW, bool EPI, bool MASK>
 __global__ __launch_bounds__(NTHR)
 void chunked128_kernel(Args g) {
     constexpr bool VSPLIT = sizeof(Tin) == 4;
@@ -291,7 +291,7 @@ void chunked128_kernel(Args g) {
     auto load_cols = [&](int c0) {
         const rsrc_t Rw = chunk_rsrc(c0, wp, stq), Rb = chunk_rsrc(c0, bp, stq);
         const rsrc_t Rk = chunk_rsrc(c0, kp_, stkv), Rv = chunk_rsrc(c0, vp, stkv);
-        if (mp) cm = __builtin_amdgcn_raw_buffer_load_b8(chunk_rsrc(c0, mp, 1u), uint32_t(8 * pc + (l & 7)), 0, 0);
+        if constexpr (MASK) cm = __builtin_amdgcn_raw_buffer_load_b8(chunk_rsrc(c0, mp, 1u), uint32_t(8 * pc + (l & 7)), 0, 0);
         #pragma unroll
         for (int e = 0; e < 8; ++e) {
             cw[e] = Buf<Tin>::load1(Rw, col_q[e]);
@@ -305,7 +305,7 @@ void chunked128_kernel(Args g) {
         ra.load(chunk_rsrc(c0, ap, stq), row_q);
         rb.load(chunk_rsrc(c0, bp, stq), row_q);
         rkv.load(chunk_rsrc(c0, kp_, stkv), row_kv);
-        if (mp) rm = __builtin_amdgcn_raw_buffer_load_b8(chunk_rsrc(c0, mp, 1u), uint32_t(tr), 0, 0);
+        if constexpr (MASK) rm = __builtin_amdgcn_raw_buffer_load_b8(chunk_rsrc(c0, mp, 1u), uint32_t(tr), 0, 0);
     };
     load_cols(0);
     load_rows(0);
@@ -328,10 +328,10 @@ void chunked128_kernel(Args g) {
         for (int e = 0; e < 8; ++e) {
             const float x = __uint_as_float(cw[e]);
             // Wave-uniform; w = 1 past the end and for masked tokens, whose b and k are zeroed.
-            const bool ok = c0 + 8 * pc + e < T && (!mp || __builtin_amdgcn_readlane(int(cm), e) != 0);
+            const bool ok = c0 + 8 * pc + e < T && (!MASK || __builtin_amdgcn_readlane(int(cm), e) != 0);
             if constexpr (LOGW) run += ok ? -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e : 0.f;
             else run *= ok ? x : 1.f;
-            if (mp) {
+            if constexpr (MASK) {
                 cb[e] = ok ? cb[e] : 0u;
                 ck[e] = ok ? ck[e] : 0u;
             }
@@ -415,7 +415,7 @@ void chunked128_kernel(Args g) {
         load_cols(c0 + L);
 
         // ---------------- P1b: row-major scaled operands ----------------
-        if (mp) {
+        if constexpr (MASK) {
             const bool keep = rm != 0;
             rr.keep_if(keep); ra.keep_if(keep); rb.keep_if(keep); rkv.keep_if(keep);
         }
@@ -710,11 +710,11 @@ void chunked128_kernel(Args g) {
     }
 }
 
-template <typename Tin, typename Ty, bool LOGW, bool EPI>
+template <typename Tin, typename Ty, bool LOGW, bool EPI, bool MASK>
 hipError_t launch_t(const Params& p, hipStream_t stream) {
     const int bh = p.B * p.H;
     Args g{p.r, p.w, p.k, p.v, p.a, p.b, p.s0, p.r_k, p.mask, p.y, p.s1, p.T, p.H, p.H_kv, bh, p.y_scale};
-    auto kern = chunked128_kernel<Tin, Ty, LOGW, EPI>;
+    auto kern = chunked128_kernel<Tin, Ty, LOGW, EPI, MASK>;
     constexpr int smem = sizeof(Tin) == 4 ? SMEM_F32 : SMEM_BF16;
     static bool attr_set = false;   // per template instance; idempotent if raced
     if (!attr_set) {
@@ -729,12 +729,17 @@ hipError_t launch_t(const Params& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename Tin, typename Ty>
-hipError_t dispatch_modes(const Params& p, hipStream_t s) {
+template <typename Tin, typename Ty, bool MASK>
+hipError_t dispatch_epi(const Params& p, hipStream_t s) {
     const bool logw = p.w_mode == WKV7_W_LOGNEGLOG;
     const bool epi = p.r_k != nullptr;
-    if (logw) return epi ? launch_t<Tin, Ty, true, true>(p, s) : launch_t<Tin, Ty, true, false>(p, s);
-    return epi ? launch_t<Tin, Ty, false, true>(p, s) : launch_t<Tin, Ty, false, false>(p, s);
+    if (logw) return epi ? launch_t<Tin, Ty, true, true, MASK>(p, s) : launch_t<Tin, Ty, true, false, MASK>(p, s);
+    return epi ? launch_t<Tin, Ty, false, true, MASK>(p, s) : launch_t<Tin, Ty, false, false, MASK>(p, s);
+}
+
+template <typename Tin, typename Ty>
+hipError_t dispatch_modes(const Params& p, hipStream_t s) {
+    return p.mask ? dispatch_epi<Tin, Ty, true>(p, s) : dispatch_epi<Tin, Ty, false>(p, s);
 }
 
 }  // namespace

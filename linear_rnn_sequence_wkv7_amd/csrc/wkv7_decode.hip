@@ -33,7 +33,7 @@ struct DecodeArgs {
     float y_scale;
 };
 
-template <int D, typename Tin, typename Ty, bool LOGW, bool EPI, bool KK>
+template <int D, typename Tin, typename Ty, bool LOGW, bool EPI, bool KK, bool MASK>
 __global__ __launch_bounds__(256)
 void decode_kernel(DecodeArgs g) {
     constexpr int CPL = D / 16;          // columns per lane (two groups of 4 for D = 128)
@@ -89,7 +89,7 @@ void decode_kernel(DecodeArgs g) {
             kv[c] *= 1.f - wv[c] + al;
         }
     }
-    if (g.mask && g.mask[bb] == 0) {   // T == 1: mask[b][0]
+    if (MASK && g.mask[bb] == 0) {   // T == 1: mask[b][0]
         #pragma unroll
         for (int c = 0; c < CPL; ++c) { av[c] = 0.f; bv[c] = 0.f; kv[c] = 0.f; rv[c] = 0.f; wv[c] = 1.f; }
     }
@@ -175,26 +175,31 @@ void decode_kernel(DecodeArgs g) {
     for (int m = 0; m < NIT / 16; ++m) st1(yp, oq + 4 * (cq + 16 * m) + rl, ykeep[m]);
 }
 
-template <int D, typename Tin, typename Ty, bool LOGW, bool EPI, bool KK>
+template <int D, typename Tin, typename Ty, bool LOGW, bool EPI, bool KK, bool MASK>
 hipError_t launch_t(const Params& p, hipStream_t stream) {
     DecodeArgs g{p.r, p.w, p.k, p.v, p.a, p.b, p.s0, p.r_k, p.mask, p.y, p.s1, p.B, p.H, p.H_kv, p.y_scale};
     const int64_t heads = int64_t(p.B) * p.H;
     dim3 grid(unsigned((heads + 3) / 4));
-    hipLaunchKernelGGL((decode_kernel<D, Tin, Ty, LOGW, EPI, KK>), grid, dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((decode_kernel<D, Tin, Ty, LOGW, EPI, KK, MASK>), grid, dim3(256), 0, stream, g);
     return hipGetLastError();
 }
 
-template <int D, typename Tin, typename Ty, bool KK>
+template <int D, typename Tin, typename Ty, bool KK, bool MASK>
 hipError_t dispatch_epi(const Params& p, hipStream_t s) {
     const bool logw = p.w_mode == WKV7_W_LOGNEGLOG;
     const bool epi = p.r_k != nullptr;
-    if (logw) return epi ? launch_t<D, Tin, Ty, true, true, KK>(p, s) : launch_t<D, Tin, Ty, true, false, KK>(p, s);
-    return epi ? launch_t<D, Tin, Ty, false, true, KK>(p, s) : launch_t<D, Tin, Ty, false, false, KK>(p, s);
+    if (logw) return epi ? launch_t<D, Tin, Ty, true, true, KK, MASK>(p, s) : launch_t<D, Tin, Ty, true, false, KK, MASK>(p, s);
+    return epi ? launch_t<D, Tin, Ty, false, true, KK, MASK>(p, s) : launch_t<D, Tin, Ty, false, false, KK, MASK>(p, s);
+}
+
+template <int D, typename Tin, typename Ty, bool KK>
+hipError_t dispatch_mask(const Params& p, hipStream_t s) {
+    return p.mask ? dispatch_epi<D, Tin, Ty, KK, true>(p, s) : dispatch_epi<D, Tin, Ty, KK, false>(p, s);
 }
 
 template <int D, typename Tin, typename Ty>
 hipError_t dispatch_modes(const Params& p, hipStream_t s) {
-    return p.ab_mode == WKV7_AB_FROM_K ? dispatch_epi<D, Tin, Ty, true>(p, s) : dispatch_epi<D, Tin, Ty, false>(p, s);
+    return p.ab_mode == WKV7_AB_FROM_K ? dispatch_mask<D, Tin, Ty, true>(p, s) : dispatch_mask<D, Tin, Ty, false>(p, s);
 }
 
 template <int D>

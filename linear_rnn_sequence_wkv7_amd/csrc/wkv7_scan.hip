@@ -107,7 +107,7 @@ template <> struct RawSlice<float> {
     __device__ __forceinline__ float R(int c) const { return r[c]; }
 };
 
-template <int D, typename Tin, typename Ty, bool LOGW, bool EPI, bool KK>
+template <int D, typename Tin, typename Ty, bool LOGW, bool EPI, bool KK, bool MASK>
 __global__ __launch_bounds__((D / ScanShape<D>::CS) * 64)
 void scan_kernel(ScanArgs g) {
     constexpr int CS = ScanShape<D>::CS;
@@ -232,7 +232,7 @@ void scan_kernel(ScanArgs g) {
     // Mask bytes of a ring block: lane i holds token tb + i's (1 without a mask).
     const int64_t mbase = int64_t(bb) * T;
     auto load_mask = [&](int tb) -> uint32_t {
-        return g.mask ? uint32_t(g.mask[mbase + min(tb + lane, T - 1)]) : 1u;
+        return MASK ? uint32_t(g.mask[mbase + min(tb + lane, T - 1)]) : 1u;
     };
     uint32_t mnext = load_mask(0), mcur = 0;
     load_v(0);
@@ -246,7 +246,9 @@ void scan_kernel(ScanArgs g) {
     auto step = [&](const int t, const RawSlice<Tin>& in, RawSlice<Tin>& nxt) {
         const int buf = t & 1;
         RawSlice<Tin> cur = in;
-        if (__builtin_amdgcn_readlane(int(mcur), t - t0) == 0) cur.template make_identity<LOGW>();
+        if constexpr (MASK) {
+            if (__builtin_amdgcn_readlane(int(mcur), t - t0) == 0) cur.template make_identity<LOGW>();
+        }
         // Partial removal projection over this wave's columns (S k for KK).
         #pragma unroll
         for (int p = 0; p < RPL; ++p) {
@@ -386,26 +388,31 @@ void scan_kernel(ScanArgs g) {
     if (g.s1 && t0 != T && sink == 0x9e3779b9u) g.s1[0] = 0.f;
 }
 
-template <int D, typename Tin, typename Ty, bool LOGW, bool EPI, bool KK>
+template <int D, typename Tin, typename Ty, bool LOGW, bool EPI, bool KK, bool MASK>
 hipError_t launch_scan_t(const Params& p, hipStream_t stream) {
     ScanArgs g{p.r, p.w, p.k, p.v, p.a, p.b, p.s0, p.r_k, p.mask, p.y, p.s1, p.B, p.T, p.H, p.H_kv, p.y_scale};
     dim3 grid(unsigned(p.B) * unsigned(p.H));
     dim3 block((D / ScanShape<D>::CS) * 64);
-    hipLaunchKernelGGL((scan_kernel<D, Tin, Ty, LOGW, EPI, KK>), grid, block, 0, stream, g);
+    hipLaunchKernelGGL((scan_kernel<D, Tin, Ty, LOGW, EPI, KK, MASK>), grid, block, 0, stream, g);
     return hipGetLastError();
 }
 
-template <int D, typename Tin, typename Ty, bool KK>
+template <int D, typename Tin, typename Ty, bool KK, bool MASK>
 hipError_t dispatch_epi(const Params& p, hipStream_t s) {
     const bool logw = p.w_mode == WKV7_W_LOGNEGLOG;
     const bool epi = p.r_k != nullptr;
-    if (logw) return epi ? launch_scan_t<D, Tin, Ty, true, true, KK>(p, s) : launch_scan_t<D, Tin, Ty, true, false, KK>(p, s);
-    return epi ? launch_scan_t<D, Tin, Ty, false, true, KK>(p, s) : launch_scan_t<D, Tin, Ty, false, false, KK>(p, s);
+    if (logw) return epi ? launch_scan_t<D, Tin, Ty, true, true, KK, MASK>(p, s) : launch_scan_t<D, Tin, Ty, true, false, KK, MASK>(p, s);
+    return epi ? launch_scan_t<D, Tin, Ty, false, true, KK, MASK>(p, s) : launch_scan_t<D, Tin, Ty, false, false, KK, MASK>(p, s);
+}
+
+template <int D, typename Tin, typename Ty, bool KK>
+hipError_t dispatch_mask(const Params& p, hipStream_t s) {
+    return p.mask ? dispatch_epi<D, Tin, Ty, KK, true>(p, s) : dispatch_epi<D, Tin, Ty, KK, false>(p, s);
 }
 
 template <int D, typename Tin, typename Ty>
 hipError_t dispatch_modes(const Params& p, hipStream_t s) {
-    return p.ab_mode == WKV7_AB_FROM_K ? dispatch_epi<D, Tin, Ty, true>(p, s) : dispatch_epi<D, Tin, Ty, false>(p, s);
+    return p.ab_mode == WKV7_AB_FROM_K ? dispatch_mask<D, Tin, Ty, true>(p, s) : dispatch_mask<D, Tin, Ty, false>(p, s);
 }
 
 template <int D>
