@@ -35,6 +35,21 @@ Options, all from the hxa07D article (forward listing):
     defining it; here a masked token (mask == 0) leaves the state unchanged
     and emits y = 0, so padding and variable lengths drop out.
 
+Backward (wkv7_backward): the gradients of L = <dy, y> + <dS_T, S_T> with
+respect to every input, by reverse-mode differentiation of (1), (2) and the
+epilogue written out token by token (no page gives these formulas).  With
+U_t = dL/dS_t, going from t = T down to 1:
+
+  U_t += dy_t r_t^T                               (readout (2) uses S_t)
+  dr_t = S_t^T dy_t,  dv_t = U_t k_t,  dk_t = U_t^T v_t
+  db_t = U_t^T (S_{t-1} a_t),  da_t = S_{t-1}^T (U_t b_t)
+  dw_t[j] = sum_i S_{t-1}[i, j] U_t[i, j]
+  U_{t-1} = U_t (diag(w_t) + b_t a_t^T)           (the transpose of the step)
+
+and dS_0 = U_0; dy is first scaled by y_scale, the r*k*r_k term adds its own
+direct terms, grouped KV heads sum dk and dv over their group, and in the
+log-decay mode dw is carried to x by d decay / dx = -exp(x) decay.
+
 Every function here is pinned by tests/test_oracle_pins.py against things
 other than itself: a hand-worked example, closed forms of special cases
 (diagonal decay, linear attention / prefix sum), the delta-rule overwrite
@@ -47,8 +62,8 @@ from typing import Optional, Tuple
 import numpy as np
 
 __all__ = [
-    "as_f64", "decay_from_logneglog", "kernel_vectors_from_k", "wkv7_forward", "wkv7_brute",
-    "wkv7_unrolled", "wkv7_chunked",
+    "as_f64", "decay_from_logneglog", "kernel_vectors_from_k", "wkv7_forward", "wkv7_backward",
+    "wkv7_brute", "wkv7_unrolled", "wkv7_chunked",
 ]
 
 
@@ -266,3 +281,103 @@ def wkv7_chunked(r, w, k, v, a, b, state0=None, *, chunk_len: int = 64):
                 S = S * np.exp(c[-1])[None, :] + SA.T @ (Bm * dec) + V.T @ (K * dec)
             S_T[bb, h] = S
     return y, S_T
+
+
+# ------------------------------------ backward ------------------------------------
+
+def _bwd_token(U, S_prev, S_cur, r, w, k, v, a, b, dyc):
+    """Reverse of one token (update (1), readout (2)).  U = dL/dS_t from the
+    later tokens; dyc = the gradient of this token's S_t r_t.  Returns
+    dL/dS_{t-1} and the token's (dr, dw, dk, dv, da, db)."""
+    U = U + dyc[..., :, None] * r[..., None, :]
+    dr = np.einsum("...ij,...i->...j", S_cur, dyc)
+    dv = np.einsum("...ij,...j->...i", U, k)
+    dk = np.einsum("...ij,...i->...j", U, v)
+    sa = np.einsum("...ij,...j->...i", S_prev, a)
+    db = np.einsum("...ij,...i->...j", U, sa)
+    Ub = np.einsum("...ij,...j->...i", U, b)
+    da = np.einsum("...ij,...i->...j", S_prev, Ub)
+    dw = np.sum(S_prev * U, axis=-2)
+    U_prev = U * w[..., None, :] + Ub[..., :, None] * a[..., None, :]
+    return U_prev, (dr, dw, dk, dv, da, db)
+
+
+def _bwd_epilogue(dy, r, k, v, rk):
+    """Direct terms of y += (sum_j r_j k_j rk_j) v: returns (dr, dk, dv, drk)."""
+    beta = np.sum(r * k * rk, axis=-1)[..., None]
+    dbeta = np.sum(dy * v, axis=-1)[..., None]
+    return dbeta * k * rk, dbeta * r * rk, beta * dy, dbeta * r * k
+
+
+def wkv7_backward(r, w, k, v, a, b, state0, dy, dstate=None, *, w_mode: str = "decay",
+                  r_k=None, y_scale: float = 1.0, mask=None, segment: int = 256):
+    """Gradients of L = <dy, y> + <dstate, S_T> for the forward wkv7_forward
+    computes with the same arguments (kernel vectors given as a, b).
+
+    dy: [B, T, H, D]; dstate: [B, H, D, D] or None (zero).  Returns a dict with
+    r, w, a, b [B, T, H, D], k, v [B, T, H_kv, D] (summed over each KV group),
+    state0 [B, H, D, D] and r_k [H, D] (None without r_k); dw is with respect to
+    the w input in its own mode.  States are kept at every `segment`-th token
+    and recomputed in between, so memory stays bounded on long sequences.
+    """
+    r, w_in, k_kv, v_kv, a, b = (as_f64(x) for x in (r, w, k, v, a, b))
+    dy = as_f64(dy)
+    B, T, H, D = r.shape
+    H_kv = k_kv.shape[-2]
+    k = _expand_kv(k_kv, H)
+    v = _expand_kv(v_kv, H)
+    if w_mode == "logneglog":
+        w = decay_from_logneglog(w_in)
+    elif w_mode == "decay":
+        w = w_in
+    else:
+        raise ValueError(w_mode)
+    keep = np.ones((B, T), dtype=bool) if mask is None else (np.asarray(mask) != 0)
+    rk = None if r_k is None else as_f64(r_k)
+    S0 = np.zeros((B, H, D, D)) if state0 is None else as_f64(state0).copy()
+
+    def advance(S, t):
+        S_new, _ = _step(S, r[:, t], w[:, t], k[:, t], v[:, t], a[:, t], b[:, t])
+        return np.where(keep[:, t][:, None, None, None], S_new, S)
+
+    # Forward: checkpoints at t = 0, segment, 2 segment, ...
+    ckpt = {}
+    S = S0
+    for t in range(T):
+        if t % segment == 0:
+            ckpt[t] = S
+        S = advance(S, t)
+    S_T = S
+
+    g = {name: np.zeros((B, T, H, D)) for name in ("r", "w", "k", "v", "a", "b")}
+    drk = None if rk is None else np.zeros((H, D))
+    U = np.zeros((B, H, D, D)) if dstate is None else as_f64(dstate).copy()
+    for t0 in reversed(range(0, T, segment)):
+        t1 = min(t0 + segment, T)
+        states = [ckpt[t0]]                      # states[i] = S_{t0 + i} (before token t0 + i)
+        for t in range(t0, t1):
+            states.append(advance(states[-1], t))
+        for t in reversed(range(t0, t1)):
+            m = keep[:, t]
+            dyt = np.where(m[:, None, None], dy[:, t], 0.0)
+            U_prev, grads = _bwd_token(U, states[t - t0], states[t - t0 + 1], r[:, t], w[:, t], k[:, t],
+                                       v[:, t], a[:, t], b[:, t], dyt * y_scale)
+            U = np.where(m[:, None, None, None], U_prev, U)
+            for name, x in zip(("r", "w", "k", "v", "a", "b"), grads):
+                g[name][:, t] = np.where(m[:, None, None], x, 0.0)
+            if rk is not None:
+                er, ek, ev, erk = _bwd_epilogue(dyt, r[:, t], k[:, t], v[:, t], rk)
+                g["r"][:, t] += er
+                g["k"][:, t] += ek
+                g["v"][:, t] += ev
+                drk += erk.sum(axis=0)
+    if w_mode == "logneglog":
+        g["w"] = g["w"] * w * -np.exp(w_in)
+    rep = H // H_kv
+    out = {name: g[name] for name in ("r", "w", "a", "b")}
+    out["k"] = g["k"].reshape(B, T, H_kv, rep, D).sum(axis=3)
+    out["v"] = g["v"].reshape(B, T, H_kv, rep, D).sum(axis=3)
+    out["state0"] = U
+    out["r_k"] = drk
+    out["S_T"] = S_T
+    return out

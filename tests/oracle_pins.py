@@ -325,6 +325,112 @@ def pin_mask_drops_tokens():
             _close(S[bi], Sk[0], 1e-13, "mask state")
 
 
+# ------------------------------- backward -------------------------------
+
+def _bwd_problem(seed, B=2, T=5, H=2, H_kv=1, D=3, logneglog=False):
+    rng = np.random.default_rng(seed)
+    r, w, k, v, a, b, S0 = _rand_problem(rng, B, T, H, D, H_kv=H_kv)
+    if logneglog:
+        w = np.log(-np.log(w))
+    rk = rng.standard_normal((H, D))
+    dy = rng.standard_normal((B, T, H, D))
+    dS = rng.standard_normal((B, H, D, D))
+    return dict(r=r, w=w, k=k, v=v, a=a, b=b, state0=S0, r_k=rk), dy, dS
+
+
+_ORDER = ("r", "w", "k", "v", "a", "b", "state0", "r_k")
+
+
+def _loss(args, dy, dS, **kw):
+    y, S = O.wkv7_forward(*(args[n] for n in _ORDER[:7]), r_k=args["r_k"], **kw)
+    return float(np.sum(y * dy) + np.sum(S * dS))
+
+
+def pin_bwd_finite_differences():
+    """Every gradient against central differences of the forward oracle's loss
+    <dy, y> + <dS, S_T> (fp64, step 1e-6), in both decay modes, with grouped KV
+    heads, the epilogue, a masked token and states recomputed from checkpoints."""
+    for mode, seed in (("decay", 30), ("logneglog", 31)):
+        args, dy, dS = _bwd_problem(seed, logneglog=mode == "logneglog")
+        mask = np.ones((2, 5), dtype=np.uint8)
+        mask[1, 2] = 0
+        kw = dict(w_mode=mode, y_scale=0.7, mask=mask)
+        g = O.wkv7_backward(*(args[n] for n in _ORDER[:7]), dy, dS, r_k=args["r_k"], segment=2, **kw)
+        h = 1e-6
+        for name in _ORDER:
+            arr = args[name]
+            fd = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                old = arr[idx]
+                arr[idx] = old + h
+                lp = _loss(args, dy, dS, **kw)
+                arr[idx] = old - h
+                lm = _loss(args, dy, dS, **kw)
+                arr[idx] = old
+                fd[idx] = (lp - lm) / (2 * h)
+            _close(g[name], fd, 1e-7, f"d{name} vs finite differences ({mode})")
+
+
+def pin_bwd_linear_attention():
+    """a = b = 0, w = 1, S0 = 0: y = tril(R K^T) V and S_T = V^T K, whose gradients
+    are dR = tril(dY V^T) K, dK = tril(dY V^T)^T R + V dS, dV = tril(R K^T)^T dY
+    + K dS^T and dS0 = dY^T R + dS (linear attention, Goose analysis)."""
+    rng = np.random.default_rng(32)
+    B, T, H, D = 1, 7, 2, 4
+    r, _, k, v, _, _, _ = _rand_problem(rng, B, T, H, D, s0=False)
+    z = np.zeros((B, T, H, D))
+    one = np.ones((B, T, H, D))
+    dy = rng.standard_normal((B, T, H, D))
+    dS = rng.standard_normal((B, H, D, D))
+    g = O.wkv7_backward(r, one, k, v, z, z, None, dy, dS)
+    for h in range(H):
+        R, K, V, dY = r[0, :, h], k[0, :, h], v[0, :, h], dy[0, :, h]
+        M = np.tril(dY @ V.T)
+        _close(g["r"][0, :, h], M @ K, 1e-12, "linear attention dr")
+        _close(g["k"][0, :, h], M.T @ R + V @ dS[0, h], 1e-12, "linear attention dk")
+        _close(g["v"][0, :, h], np.tril(R @ K.T).T @ dY + K @ dS[0, h].T, 1e-12, "linear attention dv")
+        _close(g["state0"][0, h], dY.T @ R + dS[0, h], 1e-12, "linear attention dS0")
+
+
+def pin_bwd_adjoint():
+    """y and S_T are jointly linear in (S0, v), so <dy, y> + <dS, S_T> =
+    <dS0, S0> + <dv, v> exactly (with the epilogue, grouped heads and a mask)."""
+    args, dy, dS = _bwd_problem(33, T=6, D=4)
+    mask = np.ones((2, 6), dtype=np.uint8)
+    mask[0, 1] = 0
+    kw = dict(w_mode="decay", y_scale=1.3, mask=mask)
+    g = O.wkv7_backward(*(args[n] for n in _ORDER[:7]), dy, dS, r_k=args["r_k"], **kw)
+    lhs = _loss(args, dy, dS, **kw)
+    rhs = np.sum(g["state0"] * args["state0"]) + np.sum(g["v"] * args["v"])
+    _close(rhs, lhs, 1e-12, "adjoint identity")
+
+
+def pin_bwd_homogeneity():
+    """y is linear in r, so <dr, r> = <dy, y>; G = diag(w) + a b^T is unchanged by
+    a -> c a, b -> b / c, so <da, a> = <db, b>."""
+    args, dy, dS = _bwd_problem(34, T=6, D=4)
+    g = O.wkv7_backward(*(args[n] for n in _ORDER[:7]), dy, None, r_k=args["r_k"], y_scale=0.6)
+    y, _ = O.wkv7_forward(*(args[n] for n in _ORDER[:7]), r_k=args["r_k"], y_scale=0.6)
+    _close(np.sum(g["r"] * args["r"]), np.sum(y * dy), 1e-12, "r homogeneity")
+    _close(np.sum(g["a"] * args["a"]), np.sum(g["b"] * args["b"]), 1e-12, "a/b rescaling")
+
+
+def pin_bwd_log_decay_identity():
+    """Writing the recurrence with r_t 2^g_t, a_t 2^g_(t-1), b_t 2^-g_t, k_t 2^-g_t
+    (g the cumulative log-decay) and S_T = (...) diag(2^g_T), the gradient of each
+    log-decay is a suffix sum: dL/dlog w_s = sum_(t>=s) [r dr + a_(t+1) da_(t+1)
+    - b db - k dk]_t + diag(S_T^T dS) (one KV head per head, no epilogue)."""
+    args, dy, dS = _bwd_problem(35, B=1, T=7, H=2, H_kv=2, D=4)
+    g = O.wkv7_backward(*(args[n] for n in _ORDER[:7]), dy, dS, y_scale=0.9)
+    r, w, k, a, b = (args[n] for n in ("r", "w", "k", "a", "b"))
+    per_t = r * g["r"] - b * g["b"] - k * g["k"]
+    per_t[:, :-1] += a[:, 1:] * g["a"][:, 1:]
+    S_T = g["S_T"]
+    per_t[:, -1] += np.sum(S_T * dS, axis=-2)
+    suffix = np.cumsum(per_t[:, ::-1], axis=1)[:, ::-1]
+    _close(g["w"] * w, suffix, 1e-12, "log-decay suffix sums")
+
+
 def pin_bf16_decode():
     """bf16 bit patterns widen exactly: 0x3F80 = 1, 0xC040 = -3, 0x3EAB = 0.333984375."""
     bits = np.array([0x3F80, 0xC040, 0x3EAB, 0x0000], dtype=np.uint16)

@@ -66,9 +66,48 @@ MUTATIONS = {
     # attention mask
     "mask_state_ignored": ("_masked", lambda m, So, Sn, y: (Sn, np.where(m[:, None, None], y, 0.0))),
     "mask_output_kept": ("_masked", lambda m, So, Sn, y: (np.where(m[:, None, None, None], Sn, So), y)),
+    # backward
+    "bwd_dr_from_previous_state": ("_bwd_token", lambda U, Sp, Sc, r, w, k, v, a, b, dyc: _patch(
+        _ORIG_BWD(U, Sp, Sc, r, w, k, v, a, b, dyc), 0, np.einsum("...ij,...i->...j", Sp, dyc))),
+    "bwd_dw_dropped": ("_bwd_token", lambda U, Sp, Sc, r, w, k, v, a, b, dyc: _patch(
+        _ORIG_BWD(U, Sp, Sc, r, w, k, v, a, b, dyc), 1, np.zeros_like(w))),
+    "bwd_dk_transposed": ("_bwd_token", lambda U, Sp, Sc, r, w, k, v, a, b, dyc: _patch(
+        _ORIG_BWD(U, Sp, Sc, r, w, k, v, a, b, dyc), 2,
+        np.einsum("...ij,...j->...i", U + dyc[..., :, None] * r[..., None, :], v))),
+    "bwd_db_from_updated_state": ("_bwd_token", lambda U, Sp, Sc, r, w, k, v, a, b, dyc: _patch(
+        _ORIG_BWD(U, Sp, Sc, r, w, k, v, a, b, dyc), 5,
+        np.einsum("...ij,...i->...j", U + dyc[..., :, None] * r[..., None, :],
+                  np.einsum("...ij,...j->...i", Sc, a)))),
+    "bwd_state_through_G_not_transpose": ("_bwd_token", lambda U, Sp, Sc, r, w, k, v, a, b, dyc: (
+        _with_U(_ORIG_BWD(U, Sp, Sc, r, w, k, v, a, b, dyc), U + dyc[..., :, None] * r[..., None, :], w, a, b))),
+    "bwd_readout_before_update": ("_bwd_token", lambda U, Sp, Sc, r, w, k, v, a, b, dyc: (
+        _ORIG_BWD(U, Sp, Sc, r, w, k, v, a, b, np.zeros_like(dyc))[0] + dyc[..., :, None] * r[..., None, :],
+        _ORIG_BWD(U, Sp, Sc, r, w, k, v, a, b, dyc)[1])),
+    "bwd_epilogue_dbeta_on_r": ("_bwd_epilogue", lambda dy, r, k, v, rk: (
+        np.sum(dy * r, axis=-1)[..., None] * k * rk, np.sum(dy * v, axis=-1)[..., None] * r * rk,
+        np.sum(r * k * rk, axis=-1)[..., None] * dy, np.sum(dy * v, axis=-1)[..., None] * r * k)),
+    "bwd_epilogue_dv_dropped": ("_bwd_epilogue", lambda dy, r, k, v, rk: (
+        np.sum(dy * v, axis=-1)[..., None] * k * rk, np.sum(dy * v, axis=-1)[..., None] * r * rk,
+        0.0 * dy, np.sum(dy * v, axis=-1)[..., None] * r * k)),
     # grouped KV heads
     "gqa_interleaved": ("_expand_kv", lambda x, H: np.tile(x, (1,) * (x.ndim - 2) + (H // x.shape[-2], 1))),
 }
+
+
+_ORIG_BWD = O._bwd_token
+
+
+def _patch(res, i, value):
+    U_prev, grads = res
+    grads = list(grads)
+    grads[i] = value
+    return U_prev, tuple(grads)
+
+
+def _with_U(res, U, w, a, b):
+    """Replace U_prev by U (diag(w) + a b^T), the step's own matrix instead of its transpose."""
+    Ua = np.einsum("...ij,...j->...i", U, a)
+    return U * w[..., None, :] + Ua[..., :, None] * b[..., None, :], res[1]
 
 
 def _any_pin_fails():
