@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define WKV7_ABI_VERSION 3
+#define WKV7_ABI_VERSION 4
 
 enum wkv7_status {
     WKV7_OK = 0,
@@ -163,6 +163,39 @@ int wkv7_decode_step(const wkv7_desc* desc,
                      const void* a, const void* b,
                      const float* state_in, void* y, float* state_out,
                      void* stream);
+
+/* Backward of wkv7_forward: the gradients of L = <dy, y> + <dstate_out, state_out>
+ * for the forward this descriptor describes (same inputs, same state_in).  No
+ * page gives these formulas: they are the reverse-mode derivative of the update,
+ * the readout and the epilogue (the update of the wiki note "RWKV-7 Goose",
+ * generalised delta rule; readout and epilogue as in wkv7_forward).
+ *   dy          : [B, T, H, D] of desc->y_dtype (required when B*T*H > 0).
+ *   dstate_out  : [B, H, D, D] fp32 gradient of the final state, or NULL (zero).
+ *   dr, dw, da, db : [B, T, H, D] fp32;  dk, dv : [B, T, H_kv, D] fp32 (summed over
+ *                 each KV group).  dw is with respect to the w input in its own
+ *                 mode (decay, or log(-log decay)).  Masked tokens get zeros.
+ *   dstate_in   : [B, H, D, D] fp32 gradient of state_in, or NULL to skip it.
+ *   dr_k        : [H, D] fp32, summed over the batch; required exactly when
+ *                 desc->r_k is given.
+ *   workspace   : device memory of at least wkv7_backward_workspace_bytes(desc)
+ *                 bytes, 16-byte aligned (scratch: not read before it is written).
+ * desc->algo and desc->chunk_len are ignored; ab_mode FROM_K is EUNSUPPORTED.
+ * Every pointer is device memory, 16-byte aligned, owned by the caller; outputs
+ * must not overlap inputs or the workspace.  Runs one forward sweep that keeps
+ * the state at every 32-token boundary in the workspace, then the backward. */
+int wkv7_backward(const wkv7_desc* desc,
+                  const void* r, const void* w, const void* k, const void* v,
+                  const void* a, const void* b, const float* state_in,
+                  const void* dy, const float* dstate_out,
+                  float* dr, float* dw, float* dk, float* dv, float* da, float* db,
+                  float* dstate_in, float* dr_k,
+                  void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes of wkv7_backward: B H (ceil(T / 32) + 2) D^2 4 for the state
+ * checkpoints and dL/dS, plus 2 B T H D 4 for grouped KV heads (H_kv < H) and
+ * B H D 4 with r_k, each rounded up to 256; 0 when B H T == 0.  A negative
+ * wkv7_status if the descriptor is invalid.  Host only: no HIP call. */
+int64_t wkv7_backward_workspace_bytes(const wkv7_desc* desc);
 
 /* Which algorithm wkv7_forward would run for this descriptor (WKV7_ALGO_SCAN or
  * WKV7_ALGO_CHUNKED), or a negative wkv7_status if the descriptor is invalid.

@@ -219,6 +219,59 @@ int wkv7_decode_step(const wkv7_desc* desc, const void* r, const void* w, const 
     return finish_launch(wkv7::launch_decode(p, reinterpret_cast<hipStream_t>(stream)), "decode");
 }
 
+int64_t wkv7_backward_workspace_bytes(const wkv7_desc* desc) {
+    g_last_error[0] = '\0';
+    wkv7::Params p{};
+    int rc = check_desc(desc, &p);
+    if (rc) return -rc;
+    return wkv7::backward_workspace_bytes(p);
+}
+
+int wkv7_backward(const wkv7_desc* desc, const void* r, const void* w, const void* k, const void* v,
+                  const void* a, const void* b, const float* state_in, const void* dy,
+                  const float* dstate_out, float* dr, float* dw, float* dk, float* dv, float* da,
+                  float* db, float* dstate_in, float* dr_k, void* workspace,
+                  int64_t workspace_bytes_given, void* stream) {
+    g_last_error[0] = '\0';
+    wkv7::Params p{};
+    int rc = check_desc(desc, &p);
+    if (rc) return rc;
+    if (p.ab_mode != WKV7_AB_GIVEN)
+        return fail(WKV7_EUNSUPPORTED, "wkv7_backward takes the kernel vectors as inputs (ab_mode GIVEN)");
+    const void* in6[6] = {r, w, k, v, a, b};
+    if (int64_t(p.B) * p.T * p.H > 0 && !dy) return fail(WKV7_EINVAL, "dy is NULL");
+    // dy plays the role of y in the input checks (aligned, not an input).
+    if ((rc = check_ptrs(p, in6, dy, state_in, nullptr))) return rc;
+    if (dstate_out && !aligned16(dstate_out)) return fail(WKV7_EINVAL, "dstate_out is not 16-byte aligned");
+    const bool has_tokens = int64_t(p.B) * p.T * p.H > 0;
+    float* outs[6] = {dr, dw, dk, dv, da, db};
+    static const char* onames[6] = {"dr", "dw", "dk", "dv", "da", "db"};
+    for (int i = 0; i < 6; ++i) {
+        if (has_tokens && !outs[i]) return fail(WKV7_EINVAL, "%s is NULL", onames[i]);
+        if (outs[i] && !aligned16(outs[i])) return fail(WKV7_EINVAL, "%s is not 16-byte aligned", onames[i]);
+        for (int j = 0; j < 6; ++j)
+            if (outs[i] && outs[i] == in6[j]) return fail(WKV7_EINVAL, "%s aliases input", onames[i]);
+    }
+    if (dstate_in && !aligned16(dstate_in)) return fail(WKV7_EINVAL, "dstate_in is not 16-byte aligned");
+    if (p.r_k && p.H > 0 && !dr_k) return fail(WKV7_EINVAL, "dr_k is NULL but r_k is given");
+    if (!p.r_k && dr_k) return fail(WKV7_EINVAL, "dr_k is given but r_k is NULL");
+    if (dr_k && !aligned16(dr_k)) return fail(WKV7_EINVAL, "dr_k is not 16-byte aligned");
+    const int64_t need = wkv7::backward_workspace_bytes(p);
+    if (need > 0) {
+        if (!workspace) return fail(WKV7_EINVAL, "workspace is NULL (%lld bytes needed)", (long long)need);
+        if (!aligned16(workspace)) return fail(WKV7_EINVAL, "workspace is not 16-byte aligned");
+        if (workspace_bytes_given < need)
+            return fail(WKV7_EINVAL, "workspace has %lld bytes, %lld needed",
+                        (long long)workspace_bytes_given, (long long)need);
+    }
+    p.r = r; p.w = w; p.k = k; p.v = v; p.a = a; p.b = b;
+    p.s0 = state_in; p.y = nullptr; p.s1 = nullptr;
+    if (int64_t(p.B) * p.H == 0) return WKV7_OK;
+    if ((rc = check_device())) return rc;
+    wkv7::BwdIo io{dy, dstate_out, dr, dw, da, db, dk, dv, dstate_in, dr_k};
+    return finish_launch(wkv7::launch_backward(p, io, workspace, reinterpret_cast<hipStream_t>(stream)), "backward");
+}
+
 int wkv7_resolve_algo(const wkv7_desc* desc) {
     wkv7::Params p{};
     int rc = check_desc(desc, &p);

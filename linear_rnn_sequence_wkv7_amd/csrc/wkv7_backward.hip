@@ -1,0 +1,645 @@
+// Backward of the WKV-7 recurrence on gfx950: the gradients of
+// L = <dy, y> + <dS_T, S_T> with respect to r, w, k, v, a, b, the initial
+// state and the epilogue's r_k.
+//
+// No page gives these formulas.  They are the reverse-mode derivative of the
+// chunk form the forward kernels use (unrolling S_t = S_{t-1}(diag(w_t) +
+// a_t b_t^T) + v_t k_t^T over a chunk of L tokens from S0; wiki note "RWKV-7
+// Goose", generalised delta rule).  With g_t the chunk-local cumulative
+// log2-decay per key column, Rt = r 2^g, At = a 2^g_(t-1), Bt = b 2^-g,
+// Kt = k 2^-g, d = 2^g_L and
+//
+//   A_ab = stril(At Bt^T), A_ak = stril(At Kt^T), A_rb = tril(Rt Bt^T), A_rk = tril(Rt Kt^T)
+//   SA  = Dinv (At S0^T + A_ak V),   Dinv = (I - A_ab)^-1
+//   Y   = Rt S0^T + A_rb SA + A_rk V
+//   S_L = (S0 + SA^T Bt + V^T Kt) diag(d)
+//
+// the chunk's backward, given dY and U = dL/dS_L, is (dM = U diag(d))
+//
+//   dSA = Bt dM^T + A_rb^T dY,   dZ = Dinv^T dSA
+//   dS0 = dM + dY^T Rt + dZ^T At                        (carried to the previous chunk)
+//   dV  = Kt dM^T + A_rk^T dY + A_ak^T dZ
+//   dA_rb = tril(dY SA^T), dA_rk = tril(dY V^T), dA_ab = stril(dZ SA^T), dA_ak = stril(dZ V^T)
+//   dRt = dY S0 + dA_rb Bt + dA_rk Kt        dAt = dZ S0 + dA_ab Bt + dA_ak Kt
+//   dBt = SA dM + dA_ab^T At + dA_rb^T Rt    dKt = V dM + dA_ak^T At + dA_rk^T Rt
+//
+// and dr = dRt 2^g, da = dAt 2^g_(t-1), db = dBt 2^-g, dk = dKt 2^-g.  The
+// decay enters only through the 2^(+-g) factors and the final diag(d), so the
+// gradient of each log-decay is a suffix sum within the chunk:
+// dL/dlog w_s = sum_(t >= s) [Rt dRt + At_(t+1) dAt_(t+1) - Bt dBt - Kt dKt]_t
+// + diag(S_L^T U) (at the chunk's last token).
+//
+// Every row of the state (value index) evolves on its own, so the value axis
+// is processed in slices of 32 rows: the key-axis matrices of a chunk are
+// built once and each slice adds its share to the key-axis gradients.
+//
+// Mapping: one 512-thread workgroup per (b, h).  A forward sweep over the
+// chunks stores the state at every chunk boundary (fp32, in the workspace);
+// the backward sweep walks the chunks in reverse with U = dL/dS in the
+// workspace too, one 32-row slice at a time.  All
+// products run on v_mfma_f32_16x16x4f32 with fp32 operands staged in LDS
+// (lane l: A[l & 15][l >> 4], B[l >> 4][l & 15], C[4 (l >> 4) + r][l & 15]).
+// Masked tokens and tokens past the end are identity tokens (r, k, a, b, v,
+// dy = 0, decay 1); their gradients are written as zero.
+#include "wkv7_internal.h"
+#include "wkv7_device.h"
+
+namespace wkv7 {
+namespace {
+
+constexpr int BL = 32;        // chunk length
+constexpr int BSL = 32;       // value rows per slice
+constexpr int BNT = 512;      // threads per workgroup
+constexpr int PL = BL + 1;    // LDS row pitch of [*][32] matrices (floats)
+
+struct BwdArgs {
+    const void *r, *w, *k, *v, *a, *b;
+    const float* s0;
+    const float* r_k;
+    const uint8_t* mask;
+    const void* dy;
+    const float* ds1;
+    float *dr, *dw, *dk, *dv, *da, *db;   // dk, dv per query head: [B, T, H, D]
+    float* ds0;
+    float* drk;                            // [B, H, D] partial sums (EPI)
+    float* ckpt;                           // [B H][nch + 1][D][D] states at the chunk boundaries
+    float* ubuf;                           // [B H][D][D] dL/dS during the backward sweep
+    int B, T, H, H_kv, nch;
+    float y_scale;
+};
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// acc += op(A)[m0 .. m0 + 16, k0 .. k1) x op(B)[k0 .. k1, n0 .. n0 + 16) on LDS matrices.
+// TA: A is stored [k][m]; TB: B is stored [n][k].
+template <bool TA, bool TB>
+__device__ __forceinline__ f32x4 mm(const float* A, int lda, const float* B, int ldb, int m0, int n0,
+                                    int k0, int k1, f32x4 acc) {
+    const int lane = threadIdx.x & 63, i = lane & 15, q = lane >> 4;
+    #pragma unroll 2
+    for (int k = k0; k < k1; k += 4) {
+        const float a = TA ? A[(k + q) * lda + m0 + i] : A[(m0 + i) * lda + k + q];
+        const float b = TB ? B[(n0 + i) * ldb + k + q] : B[(k + q) * ldb + n0 + i];
+        acc = mfma4(a, b, acc);
+    }
+    return acc;
+}
+
+// Store a C tile to an LDS matrix [row][ld]; `keep(row, col)` masks elements to zero.
+template <typename F>
+__device__ __forceinline__ void st_tile(float* C, int ld, int m0, int n0, f32x4 acc, F keep) {
+    const int lane = threadIdx.x & 63, i = lane & 15, q = lane >> 4;
+    #pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        const int row = m0 + 4 * q + rr, col = n0 + i;
+        C[row * ld + col] = keep(row, col) ? acc[rr] : 0.f;
+    }
+}
+
+constexpr f32x4 kZero4 = {0.f, 0.f, 0.f, 0.f};
+
+template <int D, typename Tin, typename Tdy, bool LOGW, bool EPI>
+__global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
+    constexpr int PD = D + 1;            // LDS row pitch of [*][D] matrices
+    constexpr int NS = D / BSL;          // value slices
+    constexpr int TC = D / 16;           // column tiles of a [*][D] matrix
+    constexpr int NU = TC / 4;           // tiles per wave of one slice: (2 row tiles x TC) / 8 waves
+    constexpr int NA = (2 * TC) / 8;     // tiles per wave of one [32][D] matrix
+    constexpr int UNI = (2 * BSL * PD > 4 * BL * PL) ? 2 * BSL * PD : 4 * BL * PL;
+    static_assert(BSL == BL, "slice and chunk share the 32-wide LDS pitch");
+
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+    float* RT = sm;
+    float* AT = RT + BL * PD;
+    float* BT = AT + BL * PD;
+    float* KT = BT + BL * PD;
+    float* GG = KT + BL * PD;            // cumulative log2-decay g_t per key column
+    float* AAB = GG + BL * PD;
+    float* AAK = AAB + BL * PL;
+    float* ARB = AAK + BL * PL;
+    float* ARK = ARB + BL * PL;
+    float* DINV = ARK + BL * PL;
+    float* UN = DINV + BL * PL;          // per slice: S0 | dM;  then dA x 4;  then QP | QA
+    float* S0S = UN;
+    float* DMS = UN + BSL * PD;
+    float* QP = UN;
+    float* QA = UN + BL * PD;
+    float* VS = UN + UNI;
+    float* DYS = VS + BL * PL;
+    float* SAS = DYS + BL * PL;
+    float* DZS = SAS + BL * PL;
+    float* ZS = DZS + BL * PL;
+    float* DSAS = ZS + BL * PL;
+    float* DD = DSAS + BL * PL;          // [D] diag(S_L^T U)
+    float* DEC = DD + D;                 // [D] d = 2^g_L
+    float* BETA = DEC + D;               // [BL] r k r_k per token
+    float* DBETA = BETA + BL;            // [BL] dy . v per token
+    float* DRK = DBETA + BL;             // [D] r_k gradient of this (b, h)
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, li = lane & 15, lq = lane >> 4;
+    const int bh = blockIdx.x;
+    const int H = g.H, T = g.T, H_kv = g.H_kv;
+    const int bb = bh / H, h = bh - bb * H, hk = h / (H / H_kv);
+    const Tin* rp = static_cast<const Tin*>(g.r);
+    const Tin* wp = static_cast<const Tin*>(g.w);
+    const Tin* kp = static_cast<const Tin*>(g.k);
+    const Tin* vp = static_cast<const Tin*>(g.v);
+    const Tin* ap = static_cast<const Tin*>(g.a);
+    const Tin* bp = static_cast<const Tin*>(g.b);
+    const Tdy* dyp = static_cast<const Tdy*>(g.dy);
+    float* ck = g.ckpt + int64_t(bh) * (g.nch + 1) * D * D;
+
+    auto qidx = [&](int t, int j) { return ((int64_t(bb) * T + t) * H + h) * D + j; };
+    auto kvidx = [&](int t, int j) { return ((int64_t(bb) * T + t) * H_kv + hk) * D + j; };
+    const uint8_t* mrow = g.mask ? g.mask + int64_t(bb) * T : nullptr;
+    auto valid = [&](int t) {   // t: absolute token
+        return t < T && (!mrow || mrow[t] != 0);
+    };
+
+    // Chunk c: g_t, the scaled key-axis operands and d.  With `with_r`, Rt and the
+    // epilogue's r k r_k as well.
+    auto load_chunk = [&](int c, bool with_r) {
+        const int c0 = c * BL;
+        for (int e = tid; e < BL * D; e += BNT) {
+            const int t = e / D, j = e - t * D;
+            const bool ok = valid(c0 + t);
+            float lw = 0.f;
+            if (ok) lw = log2_decay(ld1(wp, qidx(c0 + t, j)), LOGW);
+            GG[t * PD + j] = lw;
+        }
+        if (EPI && with_r && tid < BL) BETA[tid] = 0.f;
+        __syncthreads();
+        if (tid < D) {
+            float run = 0.f;
+            for (int t = 0; t < BL; ++t) {
+                run += GG[t * PD + tid];
+                GG[t * PD + tid] = run;
+            }
+            DEC[tid] = __builtin_amdgcn_exp2f(run);
+        }
+        __syncthreads();
+        for (int e = tid; e < BL * D; e += BNT) {
+            const int t = e / D, j = e - t * D;
+            const bool ok = valid(c0 + t);
+            const float gt = GG[t * PD + j], gp = t > 0 ? GG[(t - 1) * PD + j] : 0.f;
+            float av = 0.f, bv = 0.f, kv = 0.f, rv = 0.f;
+            if (ok) {
+                av = ld1(ap, qidx(c0 + t, j));
+                bv = ld1(bp, qidx(c0 + t, j));
+                kv = ld1(kp, kvidx(c0 + t, j));
+                if (with_r) rv = ld1(rp, qidx(c0 + t, j));
+            }
+            const float ep = __builtin_amdgcn_exp2f(gt), em = __builtin_amdgcn_exp2f(-gt);
+            AT[t * PD + j] = av * __builtin_amdgcn_exp2f(gp);
+            BT[t * PD + j] = bv * em;
+            KT[t * PD + j] = kv * em;
+            if (with_r) {
+                RT[t * PD + j] = rv * ep;
+                if constexpr (EPI) {
+                    const float x = rv * kv * g.r_k[h * D + j];
+                    if (ok) atomicAdd(&BETA[t], x);
+                }
+            }
+        }
+        __syncthreads();
+    };
+
+    // L x L matrices: A_ab, A_ak (and A_rb, A_rk); then Dinv = (I - A_ab)^-1 by wave 0.
+    auto build_LL = [&](bool with_r) {
+        const int nmat = with_r ? 4 : 2;
+        for (int n = w; n < 4 * nmat; n += 8) {
+            const int mat = n >> 2, tile = n & 3, m0 = 16 * (tile >> 1), n0 = 16 * (tile & 1);
+            const float* A = mat < 2 ? AT : RT;
+            const float* B = (mat & 1) ? KT : BT;
+            float* C = mat == 0 ? AAB : mat == 1 ? AAK : mat == 2 ? ARB : ARK;
+            f32x4 acc = mm<false, true>(A, PD, B, PD, m0, n0, 0, D, kZero4);
+            if (mat < 2) st_tile(C, PL, m0, n0, acc, [](int r, int c) { return c < r; });
+            else st_tile(C, PL, m0, n0, acc, [](int r, int c) { return c <= r; });
+        }
+        __syncthreads();
+        if (w == 0 && lane < BL) {
+            // Column `lane` of X = (I - A_ab)^-1: x_t = [t == lane] + sum_(s<t) A_ab[t][s] x_s.
+            float x[BL];
+            #pragma unroll
+            for (int t = 0; t < BL; ++t) x[t] = t == lane ? 1.f : 0.f;
+            #pragma unroll
+            for (int s = 0; s < BL; ++s) {
+                #pragma unroll
+                for (int t = s + 1; t < BL; ++t) x[t] = fmaf(AAB[t * PL + s], x[s], x[t]);
+            }
+            #pragma unroll
+            for (int t = 0; t < BL; ++t) DINV[t * PL + lane] = x[t];
+        }
+        __syncthreads();
+    };
+
+    // Tiles of one slice (32 rows x D) of a D x D matrix: this wave's u-th, at local
+    // rows ml and columns n0 (tile n = w + 8 u of the slice's 2 x TC tiles).
+    auto slice_tile = [&](int u, int& ml, int& n0) {
+        const int n = w + 8 * u;
+        ml = 16 * (n / TC);
+        n0 = 16 * (n % TC);
+    };
+    float* ub = g.ubuf + int64_t(bh) * D * D;   // U = dL/dS of the backward sweep
+
+    // ------------------------------- forward sweep: checkpoints -------------------------------
+    for (int e = tid; e < D * D; e += BNT) ck[e] = g.s0 ? g.s0[int64_t(bh) * D * D + e] : 0.f;
+    __syncthreads();
+    for (int c = 0; c < g.nch; ++c) {
+        const int c0 = c * BL;
+        const float* sc = ck + int64_t(c) * D * D;
+        float* sn = ck + int64_t(c + 1) * D * D;
+        load_chunk(c, false);
+        build_LL(false);
+        #pragma unroll 1
+        for (int s = 0; s < NS; ++s) {
+            for (int e = tid; e < BSL * D; e += BNT) {
+                const int i = e / D, j = e - i * D;
+                S0S[i * PD + j] = sc[(BSL * s + i) * D + j];
+            }
+            for (int e = tid; e < BL * BSL; e += BNT) {
+                const int t = e / BSL, i = e - t * BSL;
+                VS[t * PL + i] = valid(c0 + t) ? ld1(vp, kvidx(c0 + t, BSL * s + i)) : 0.f;
+            }
+            __syncthreads();
+            if (w < 4) {   // Z = At S0s^T + A_ak Vs
+                const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);
+                f32x4 acc = mm<false, true>(AT, PD, S0S, PD, m0, n0, 0, D, kZero4);
+                acc = mm<false, false>(AAK, PL, VS, PL, m0, n0, 0, BL, acc);
+                st_tile(ZS, PL, m0, n0, acc, [](int, int) { return true; });
+            }
+            __syncthreads();
+            if (w < 4) {   // SA = Dinv Z
+                const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);
+                f32x4 acc = mm<false, false>(DINV, PL, ZS, PL, m0, n0, 0, BL, kZero4);
+                st_tile(SAS, PL, m0, n0, acc, [](int, int) { return true; });
+            }
+            __syncthreads();
+            #pragma unroll
+            for (int u = 0; u < NU; ++u) {   // S_next = (S + SA^T Bt + V^T Kt) diag(d)
+                int ml, n0;
+                slice_tile(u, ml, n0);
+                f32x4 acc;
+                #pragma unroll
+                for (int rr = 0; rr < 4; ++rr) acc[rr] = S0S[(ml + 4 * lq + rr) * PD + n0 + li];
+                acc = mm<true, false>(SAS, PL, BT, PD, ml, n0, 0, BL, acc);
+                acc = mm<true, false>(VS, PL, KT, PD, ml, n0, 0, BL, acc);
+                const float dc = DEC[n0 + li];
+                #pragma unroll
+                for (int rr = 0; rr < 4; ++rr) sn[(BSL * s + ml + 4 * lq + rr) * D + n0 + li] = acc[rr] * dc;
+            }
+            __syncthreads();
+        }
+    }
+
+    // ------------------------------- backward sweep -------------------------------
+    for (int e = tid; e < D * D; e += BNT) ub[e] = g.ds1 ? g.ds1[int64_t(bh) * D * D + e] : 0.f;
+    if (EPI && tid < D) DRK[tid] = 0.f;
+    __syncthreads();
+    for (int c = g.nch - 1; c >= 0; --c) {
+        const int c0 = c * BL;
+        if (tid < D) DD[tid] = 0.f;
+        if (EPI && tid < BL) DBETA[tid] = 0.f;
+        load_chunk(c, true);
+        build_LL(true);
+
+        f32x4 accR[NA], accA[NA], accB[NA], accK[NA], accDA[2];
+        #pragma unroll
+        for (int u = 0; u < NA; ++u) accR[u] = accA[u] = accB[u] = accK[u] = kZero4;
+        accDA[0] = accDA[1] = kZero4;
+        // dA tiles of this wave: matrix w >> 1 (rb, rk, ab, ak), tiles 2 (w & 1) + {0, 1}.
+        const int dmat = w >> 1;
+
+        #pragma unroll 1
+        for (int s = 0; s < NS; ++s) {
+            // S0 slice, dM = U diag(d), V and y_scale dy slices; diag(S_L^T U) and dy . v shares.
+            for (int e = tid; e < BSL * D; e += BNT) {
+                const int i = e / D, j = e - i * D;
+                const int o = (BSL * s + i) * D + j;
+                S0S[i * PD + j] = ck[int64_t(c) * D * D + o];
+                const float uv = ub[o];
+                DMS[i * PD + j] = uv * DEC[j];
+                atomicAdd(&DD[j], ck[int64_t(c + 1) * D * D + o] * uv);
+            }
+            for (int e = tid; e < BL * BSL; e += BNT) {
+                const int t = e / BSL, i = e - t * BSL;
+                const bool ok = valid(c0 + t);
+                const float vv = ok ? ld1(vp, kvidx(c0 + t, BSL * s + i)) : 0.f;
+                const float dyv = ok ? ld1(dyp, qidx(c0 + t, BSL * s + i)) : 0.f;
+                VS[t * PL + i] = vv;
+                DYS[t * PL + i] = dyv * g.y_scale;
+                if constexpr (EPI) {
+                    if (ok) atomicAdd(&DBETA[t], dyv * vv);
+                }
+            }
+            __syncthreads();
+            if (w < 4) {   // Z = At S0s^T + A_ak Vs
+                const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);
+                f32x4 acc = mm<false, true>(AT, PD, S0S, PD, m0, n0, 0, D, kZero4);
+                acc = mm<false, false>(AAK, PL, VS, PL, m0, n0, 0, BL, acc);
+                st_tile(ZS, PL, m0, n0, acc, [](int, int) { return true; });
+            } else {       // dSA = Bt dM^T + A_rb^T dY
+                const int m0 = 16 * ((w - 4) >> 1), n0 = 16 * (w & 1);
+                f32x4 acc = mm<false, true>(BT, PD, DMS, PD, m0, n0, 0, D, kZero4);
+                acc = mm<true, false>(ARB, PL, DYS, PL, m0, n0, 0, BL, acc);
+                st_tile(DSAS, PL, m0, n0, acc, [](int, int) { return true; });
+            }
+            __syncthreads();
+            if (w < 4) {   // SA = Dinv Z
+                const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);
+                f32x4 acc = mm<false, false>(DINV, PL, ZS, PL, m0, n0, 0, BL, kZero4);
+                st_tile(SAS, PL, m0, n0, acc, [](int, int) { return true; });
+            } else {       // dZ = Dinv^T dSA
+                const int m0 = 16 * ((w - 4) >> 1), n0 = 16 * (w & 1);
+                f32x4 acc = mm<true, false>(DINV, PL, DSAS, PL, m0, n0, 0, BL, kZero4);
+                st_tile(DZS, PL, m0, n0, acc, [](int, int) { return true; });
+            }
+            __syncthreads();
+            // U <- dM + dY^T Rt + dZ^T At for this slice's rows.
+            #pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                int ml, n0;
+                slice_tile(u, ml, n0);
+                f32x4 acc;
+                #pragma unroll
+                for (int rr = 0; rr < 4; ++rr) acc[rr] = DMS[(ml + 4 * lq + rr) * PD + n0 + li];
+                acc = mm<true, false>(DYS, PL, RT, PD, ml, n0, 0, BL, acc);
+                acc = mm<true, false>(DZS, PL, AT, PD, ml, n0, 0, BL, acc);
+                #pragma unroll
+                for (int rr = 0; rr < 4; ++rr) ub[(BSL * s + ml + 4 * lq + rr) * D + n0 + li] = acc[rr];
+            }
+            // dV = Kt dM^T + A_rk^T dY + A_ak^T dZ (+ the epilogue's beta dy), this slice's columns.
+            if (w < 4) {
+                const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);
+                f32x4 acc = mm<false, true>(KT, PD, DMS, PD, m0, n0, 0, D, kZero4);
+                acc = mm<true, false>(ARK, PL, DYS, PL, m0, n0, 0, BL, acc);
+                acc = mm<true, false>(AAK, PL, DZS, PL, m0, n0, 0, BL, acc);
+                #pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int t = m0 + 4 * lq + rr, i = BSL * s + n0 + li;
+                    if (c0 + t < T) {
+                        float x = acc[rr];
+                        if (!valid(c0 + t)) x = 0.f;
+                        else if constexpr (EPI) x = fmaf(BETA[t], ld1(dyp, qidx(c0 + t, i)), x);
+                        g.dv[qidx(c0 + t, i)] = x;
+                    }
+                }
+            }
+            // dA shares: tril(dY SA^T), tril(dY V^T), stril(dZ SA^T), stril(dZ V^T).
+            #pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int tile = 2 * (w & 1) + u, m0 = 16 * (tile >> 1), n0 = 16 * (tile & 1);
+                const float* A = dmat < 2 ? DYS : DZS;
+                const float* B = (dmat & 1) ? VS : SAS;
+                accDA[u] = mm<false, true>(A, PL, B, PL, m0, n0, 0, BSL, accDA[u]);
+            }
+            // dRt += dY S0, dAt += dZ S0, dBt += SA dM, dKt += V dM.
+            #pragma unroll
+            for (int u = 0; u < NA; ++u) {
+                const int n = w + 8 * u, m0 = 16 * (n / TC), n0 = 16 * (n % TC);
+                accR[u] = mm<false, false>(DYS, PL, S0S, PD, m0, n0, 0, BSL, accR[u]);
+                accA[u] = mm<false, false>(DZS, PL, S0S, PD, m0, n0, 0, BSL, accA[u]);
+                accB[u] = mm<false, false>(SAS, PL, DMS, PD, m0, n0, 0, BSL, accB[u]);
+                accK[u] = mm<false, false>(VS, PL, DMS, PD, m0, n0, 0, BSL, accK[u]);
+            }
+            __syncthreads();
+        }
+        // dA matrices (masked) to LDS.
+        {
+            float* C = UN + dmat * BL * PL;
+            #pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int tile = 2 * (w & 1) + u, m0 = 16 * (tile >> 1), n0 = 16 * (tile & 1);
+                if (dmat < 2) st_tile(C, PL, m0, n0, accDA[u], [](int r, int c) { return c <= r; });
+                else st_tile(C, PL, m0, n0, accDA[u], [](int r, int c) { return c < r; });
+            }
+        }
+        __syncthreads();
+        {
+            const float* DRB = UN;
+            const float* DRKm = UN + BL * PL;
+            const float* DAB = UN + 2 * BL * PL;
+            const float* DAK = UN + 3 * BL * PL;
+            #pragma unroll
+            for (int u = 0; u < NA; ++u) {
+                const int n = w + 8 * u, m0 = 16 * (n / TC), n0 = 16 * (n % TC);
+                accR[u] = mm<false, false>(DRB, PL, BT, PD, m0, n0, 0, BL, accR[u]);
+                accR[u] = mm<false, false>(DRKm, PL, KT, PD, m0, n0, 0, BL, accR[u]);
+                accA[u] = mm<false, false>(DAB, PL, BT, PD, m0, n0, 0, BL, accA[u]);
+                accA[u] = mm<false, false>(DAK, PL, KT, PD, m0, n0, 0, BL, accA[u]);
+                accB[u] = mm<true, false>(DAB, PL, AT, PD, m0, n0, 0, BL, accB[u]);
+                accB[u] = mm<true, false>(DRB, PL, RT, PD, m0, n0, 0, BL, accB[u]);
+                accK[u] = mm<true, false>(DAK, PL, AT, PD, m0, n0, 0, BL, accK[u]);
+                accK[u] = mm<true, false>(DRKm, PL, RT, PD, m0, n0, 0, BL, accK[u]);
+            }
+        }
+        __syncthreads();
+        // Gradients of r, a, b, k; the log-decay suffix-sum terms.
+        #pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int n = w + 8 * u, m0 = 16 * (n / TC), n0 = 16 * (n % TC);
+            const int j = n0 + li;
+            #pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int t = m0 + 4 * lq + rr;
+                const int o = t * PD + j;
+                QP[o] = RT[o] * accR[u][rr] - BT[o] * accB[u][rr] - KT[o] * accK[u][rr];
+                QA[o] = AT[o] * accA[u][rr];
+                if (c0 + t < T) {
+                    const bool ok = valid(c0 + t);
+                    const float gt = GG[o], gp = t > 0 ? GG[o - PD] : 0.f;
+                    float dr = accR[u][rr] * __builtin_amdgcn_exp2f(gt);
+                    const float da = accA[u][rr] * __builtin_amdgcn_exp2f(gp);
+                    const float db = accB[u][rr] * __builtin_amdgcn_exp2f(-gt);
+                    float dk = accK[u][rr] * __builtin_amdgcn_exp2f(-gt);
+                    if constexpr (EPI) {
+                        if (ok) {
+                            const float rv = ld1(rp, qidx(c0 + t, j)), kv = ld1(kp, kvidx(c0 + t, j));
+                            const float rkj = g.r_k[h * D + j], dbt = DBETA[t];
+                            dr = fmaf(dbt * kv, rkj, dr);
+                            dk = fmaf(dbt * rv, rkj, dk);
+                            atomicAdd(&DRK[j], dbt * rv * kv);
+                        }
+                    }
+                    const int64_t gi = qidx(c0 + t, j);
+                    g.dr[gi] = ok ? dr : 0.f;
+                    g.da[gi] = ok ? da : 0.f;
+                    g.db[gi] = ok ? db : 0.f;
+                    g.dk[gi] = ok ? dk : 0.f;
+                }
+            }
+        }
+        __syncthreads();
+        if (tid < D) {   // dL/dlog w: suffix sums within the chunk, carried to the w input
+            const int j = tid;
+            float run = DD[j];
+            for (int t = BL - 1; t >= 0; --t) {
+                run += QP[t * PD + j] + (t + 1 < BL ? QA[(t + 1) * PD + j] : 0.f);
+                if (c0 + t < T) {
+                    const int64_t gi = qidx(c0 + t, j);
+                    float dwv = 0.f;
+                    if (valid(c0 + t)) {
+                        const float x = ld1(wp, gi);
+                        dwv = LOGW ? run * -__builtin_amdgcn_exp2f(x * kLog2e) : run / x;
+                    }
+                    g.dw[gi] = dwv;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (g.ds0) {
+        for (int e = tid; e < D * D; e += BNT) g.ds0[int64_t(bh) * D * D + e] = ub[e];
+    }
+    if constexpr (EPI) {
+        if (tid < D) g.drk[int64_t(bh) * D + tid] = DRK[tid];
+    }
+}
+
+template <int D>
+constexpr int bwd_smem_bytes() {
+    constexpr int PD = D + 1;
+    constexpr int UNI = (2 * BSL * PD > 4 * BL * PL) ? 2 * BSL * PD : 4 * BL * PL;
+    return 4 * (5 * BL * PD + 5 * BL * PL + UNI + 6 * BL * PL + 2 * D + 2 * BL + D);
+}
+static_assert(bwd_smem_bytes<128>() <= 160 * 1024, "LDS budget at D = 128");
+
+// dk, dv of the KV heads: sums over each group of query heads.  dr_k: sum over the batch.
+__global__ __launch_bounds__(256) void group_sum_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                        int64_t n_out, int D, int H, int H_kv) {
+    const int rep = H / H_kv;
+    for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < n_out; e += int64_t(gridDim.x) * 256) {
+        const int64_t j = e % D, bthk = e / D;
+        const int64_t hk = bthk % H_kv, bt = bthk / H_kv;
+        float acc = 0.f;
+        for (int u = 0; u < rep; ++u) acc += src[(bt * H + hk * rep + u) * D + j];
+        dst[e] = acc;
+    }
+}
+__global__ __launch_bounds__(256) void batch_sum_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                        int B, int HD) {
+    for (int e = blockIdx.x * 256 + threadIdx.x; e < HD; e += gridDim.x * 256) {
+        float acc = 0.f;
+        for (int bb = 0; bb < B; ++bb) acc += src[int64_t(bb) * HD + e];
+        dst[e] = acc;
+    }
+}
+
+struct BwdLayout {
+    int64_t ckpt, ubuf, dkq, dvq, drk, total;
+};
+
+BwdLayout bwd_layout(const Params& p) {
+    auto al = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+    const int nch = (p.T + BL - 1) / BL;
+    BwdLayout o{};
+    const int64_t bh = int64_t(p.B) * p.H;
+    o.ckpt = 0;
+    int64_t off = al(bh * (nch + 1) * p.D * p.D * 4);
+    o.ubuf = off;
+    off += al(bh * p.D * p.D * 4);
+    const bool grouped = p.H_kv != p.H;
+    o.dkq = off;
+    if (grouped) off += al(int64_t(p.B) * p.T * p.H * p.D * 4);
+    o.dvq = off;
+    if (grouped) off += al(int64_t(p.B) * p.T * p.H * p.D * 4);
+    o.drk = off;
+    if (p.r_k) off += al(bh * p.D * 4);
+    o.total = off;
+    return o;
+}
+
+template <int D, typename Tin, typename Tdy, bool LOGW, bool EPI>
+hipError_t launch_bwd_t(const Params& p, const BwdIo& io, char* ws, hipStream_t stream) {
+    const BwdLayout lay = bwd_layout(p);
+    const bool grouped = p.H_kv != p.H;
+    BwdArgs g{};
+    g.r = p.r; g.w = p.w; g.k = p.k; g.v = p.v; g.a = p.a; g.b = p.b;
+    g.s0 = p.s0; g.r_k = p.r_k; g.mask = p.mask; g.dy = io.dy; g.ds1 = io.ds1;
+    g.dr = io.dr; g.dw = io.dw; g.da = io.da; g.db = io.db;
+    g.dk = grouped ? reinterpret_cast<float*>(ws + lay.dkq) : io.dk;
+    g.dv = grouped ? reinterpret_cast<float*>(ws + lay.dvq) : io.dv;
+    g.ds0 = io.ds0;
+    g.drk = p.r_k ? reinterpret_cast<float*>(ws + lay.drk) : nullptr;
+    g.ckpt = reinterpret_cast<float*>(ws + lay.ckpt);
+    g.ubuf = reinterpret_cast<float*>(ws + lay.ubuf);
+    g.B = p.B; g.T = p.T; g.H = p.H; g.H_kv = p.H_kv; g.nch = (p.T + BL - 1) / BL;
+    g.y_scale = p.y_scale;
+    auto kern = bwd_kernel<D, Tin, Tdy, LOGW, EPI>;
+    constexpr int smem = bwd_smem_bytes<D>();
+    static bool attr_set = false;   // per template instance; idempotent if raced
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(unsigned(p.B) * unsigned(p.H)), dim3(BNT), smem, stream, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (grouped) {
+        const int64_t n_out = int64_t(p.B) * p.T * p.H_kv * D;
+        const int64_t blocks = (n_out + 255) / 256;
+        const dim3 grid(unsigned(blocks < 65536 ? blocks : 65536));
+        hipLaunchKernelGGL(group_sum_kernel, grid, dim3(256), 0, stream, g.dk, io.dk, n_out, D, p.H, p.H_kv);
+        hipLaunchKernelGGL(group_sum_kernel, grid, dim3(256), 0, stream, g.dv, io.dv, n_out, D, p.H, p.H_kv);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (p.r_k) {
+        const int HD = p.H * D;
+        hipLaunchKernelGGL(batch_sum_kernel, dim3(unsigned((HD + 255) / 256)), dim3(256), 0, stream,
+                           g.drk, io.drk, p.B, HD);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+template <int D, typename Tin, typename Tdy>
+hipError_t dispatch_modes(const Params& p, const BwdIo& io, char* ws, hipStream_t s) {
+    const bool logw = p.w_mode == WKV7_W_LOGNEGLOG;
+    const bool epi = p.r_k != nullptr;
+    if (logw) return epi ? launch_bwd_t<D, Tin, Tdy, true, true>(p, io, ws, s) : launch_bwd_t<D, Tin, Tdy, true, false>(p, io, ws, s);
+    return epi ? launch_bwd_t<D, Tin, Tdy, false, true>(p, io, ws, s) : launch_bwd_t<D, Tin, Tdy, false, false>(p, io, ws, s);
+}
+
+template <int D>
+hipError_t dispatch_types(const Params& p, const BwdIo& io, char* ws, hipStream_t s) {
+    if (p.in_dtype == WKV7_BF16)
+        return p.y_dtype == WKV7_BF16 ? dispatch_modes<D, bf16_t, bf16_t>(p, io, ws, s) : dispatch_modes<D, bf16_t, float>(p, io, ws, s);
+    return p.y_dtype == WKV7_BF16 ? dispatch_modes<D, float, bf16_t>(p, io, ws, s) : dispatch_modes<D, float, float>(p, io, ws, s);
+}
+
+}  // namespace
+
+int64_t backward_workspace_bytes(const Params& p) {
+    if (int64_t(p.B) * p.H == 0 || p.T == 0) return 0;
+    return bwd_layout(p).total;
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ dst, const float* __restrict__ src, int64_t n) {
+    for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < n; e += int64_t(gridDim.x) * 256)
+        dst[e] = src ? src[e] : 0.f;
+}
+
+hipError_t launch_backward(const Params& p, const BwdIo& io, void* ws, hipStream_t stream) {
+    if (p.T == 0) {   // dS0 = dS_T, dr_k = 0
+        const int64_t n = int64_t(p.B) * p.H * p.D * p.D;
+        if (io.ds0 && n > 0) {
+            const int64_t blocks = (n + 255) / 256;
+            hipLaunchKernelGGL(fill_kernel, dim3(unsigned(blocks < 65536 ? blocks : 65536)), dim3(256), 0, stream,
+                               io.ds0, io.ds1, n);
+        }
+        if (p.r_k && p.H > 0)
+            hipLaunchKernelGGL(fill_kernel, dim3(unsigned((p.H * p.D + 255) / 256)), dim3(256), 0, stream,
+                               io.drk, static_cast<const float*>(nullptr), int64_t(p.H) * p.D);
+        return hipGetLastError();
+    }
+    char* w = static_cast<char*>(ws);
+    return p.D == 64 ? dispatch_types<64>(p, io, w, stream) : dispatch_types<128>(p, io, w, stream);
+}
+
+}  // namespace wkv7

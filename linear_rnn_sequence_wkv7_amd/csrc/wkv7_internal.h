@@ -1,6 +1,6 @@
 // Internal interface between the C-ABI entry points (wkv7_api.cpp) and the
 // kernel launchers (wkv7_scan.hip, wkv7_chunked.hip, wkv7_chunked128.hip,
-// wkv7_twopass128.hip, wkv7_decode.hip).
+// wkv7_twopass128.hip, wkv7_decode.hip, wkv7_backward.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -36,5 +36,17 @@ hipError_t launch_twopass128(const Params& p, void* ws, hipStream_t stream);
 hipError_t launch_decode(const Params& p, hipStream_t stream);
 // state_out <- state_in (or zeros) for T == 0.
 hipError_t launch_state_copy(const Params& p, hipStream_t stream);
+
+// Backward: the arrays beyond the forward's inputs.
+struct BwdIo {
+    const void* dy;        // [B, T, H, D] of y_dtype
+    const float* ds1;      // dL/dS_T or null (zero)
+    float *dr, *dw, *da, *db;   // [B, T, H, D]
+    float *dk, *dv;        // [B, T, H_kv, D]
+    float* ds0;            // dL/dS_0 or null (not written)
+    float* drk;            // [H, D] when r_k is given
+};
+int64_t backward_workspace_bytes(const Params& p);
+hipError_t launch_backward(const Params& p, const BwdIo& io, void* ws, hipStream_t stream);
 
 }  // namespace wkv7

@@ -31,7 +31,7 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "make_inputs", "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "Workload", "WORKLOADS", "make_inputs", "make_grad_inputs", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "workload",
 ]
 
@@ -205,3 +205,14 @@ def _mask(rng, wl: Workload, lead) -> Optional[np.ndarray]:
         lens[..., 0] = wl.T
         return (np.arange(wl.T) < lens[..., None]).astype(np.uint8)
     raise ValueError(wl.mask)
+
+
+def make_grad_inputs(wl: Workload, seed: Optional[int] = None, dstate: bool = True) -> Dict[str, np.ndarray]:
+    """Upstream gradients for the backward: dy ~ N(0, 1) [B, T, H, D] encoded per
+    y_dtype, and dstate ~ N(0, 1) [B, H, D, D] fp32 (or None).  Own PCG64 stream,
+    seeded with the workload seed + 500 unless given."""
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 500 if seed is None else seed))
+    out: Dict[str, Optional[np.ndarray]] = {}
+    out["dy"] = _encode(rng.standard_normal((wl.B, wl.T, wl.H, wl.D)), wl.y_dtype)
+    out["dstate"] = rng.standard_normal((wl.B, wl.H, wl.D, wl.D)).astype(np.float32) if dstate else None
+    return out

@@ -14,7 +14,8 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "wkv7_forward", "wkv7_decode_step", "wkv7_resolve_algo", "wkv7_workspace_bytes", "Wkv7Error",
+    "wkv7_forward", "wkv7_backward", "wkv7_decode_step", "wkv7_resolve_algo", "wkv7_workspace_bytes",
+    "wkv7_backward_workspace_bytes", "Wkv7Error",
     "lib_path", "load_library",
     "WKV7_OK", "WKV7_EINVAL", "WKV7_EUNSUPPORTED", "WKV7_EDEVICE", "WKV7_ELAUNCH",
     "ALGOS", "W_MODES", "AB_MODES", "Desc", "EXPORTED_SYMBOLS",
@@ -26,6 +27,7 @@ W_MODES = {"decay": 0, "logneglog": 1}
 ALGOS = {"auto": 0, "scan": 1, "chunked": 2, "two_pass": 3}
 AB_MODES = {"given": 0, "from_k": 1}
 EXPORTED_SYMBOLS = ("wkv7_forward", "wkv7_forward_ws", "wkv7_workspace_bytes", "wkv7_decode_step",
+                    "wkv7_backward", "wkv7_backward_workspace_bytes",
                     "wkv7_resolve_algo", "wkv7_strerror", "wkv7_last_error", "wkv7_abi_version")
 
 
@@ -72,6 +74,10 @@ def load_library():
     lib.wkv7_forward_ws.restype = ctypes.c_int
     lib.wkv7_workspace_bytes.argtypes = [ctypes.POINTER(Desc)]
     lib.wkv7_workspace_bytes.restype = ctypes.c_int64
+    lib.wkv7_backward.argtypes = [ctypes.POINTER(Desc)] + [vp] * 18 + [ctypes.c_int64, vp]
+    lib.wkv7_backward.restype = ctypes.c_int
+    lib.wkv7_backward_workspace_bytes.argtypes = [ctypes.POINTER(Desc)]
+    lib.wkv7_backward_workspace_bytes.restype = ctypes.c_int64
     lib.wkv7_resolve_algo.argtypes = [ctypes.POINTER(Desc)]
     lib.wkv7_resolve_algo.restype = ctypes.c_int
     lib.wkv7_strerror.argtypes = [ctypes.c_int]
@@ -250,3 +256,60 @@ def wkv7_resolve_algo(B, T, H, D, *, H_kv=None, algo="auto", **kw) -> str:
     if rc < 0:
         raise Wkv7Error(-rc, "wkv7_resolve_algo", load_library().wkv7_last_error().decode())
     return {1: "scan", 2: "chunked", 3: "two_pass"}[rc]
+
+
+def wkv7_backward_workspace_bytes(B, T, H, D, *, H_kv=None, **kw) -> int:
+    """Workspace bytes wkv7_backward uses for these sizes."""
+    n = load_library().wkv7_backward_workspace_bytes(ctypes.byref(make_desc(B, T, H, D, H_kv=H_kv, **kw)))
+    if n < 0:
+        raise Wkv7Error(int(-n), "wkv7_backward_workspace_bytes", load_library().wkv7_last_error().decode())
+    return int(n)
+
+
+def wkv7_backward(r, w, k, v, a, b, dy, state=None, dstate=None, *, w_mode: str = "decay",
+                  y_scale: float = 1.0, r_k=None, mask=None, workspace=None, grads=None,
+                  return_dstate: bool = True) -> dict:
+    """Gradients of <dy, y> + <dstate, state_out> for wkv7_forward with the same arguments.
+
+    dy: [B, T, H, D] float32 or bfloat16 (the y dtype); dstate: [B, H, D, D] float32 or None.
+    Returns a dict of float32 tensors: r, w, a, b [B, T, H, D], k, v [B, T, H_kv, D],
+    state [B, H, D, D] (None when return_dstate is False) and r_k [H, D] (None without r_k).
+    `grads` may supply preallocated output tensors under the same keys.
+    """
+    torch = _torch()
+    B, T, H, H_kv, D = _check_inputs(r, w, k, v, a, b, state, r_k, mask)
+    dev = r.device
+    if tuple(dy.shape) != (B, T, H, D) or dy.device != dev or not dy.is_contiguous():
+        raise ValueError(f"dy must be a contiguous [B, T, H, D] = {(B, T, H, D)} tensor on {dev}")
+    if dstate is not None:
+        if tuple(dstate.shape) != (B, H, D, D) or dstate.dtype != torch.float32 or dstate.device != dev \
+                or not dstate.is_contiguous():
+            raise ValueError(f"dstate must be contiguous float32 [B, H, D, D] = {(B, H, D, D)} on {dev}")
+    out = dict(grads or {})
+    f32 = dict(dtype=torch.float32, device=dev)
+    for key in ("r", "w", "a", "b"):
+        out.setdefault(key, torch.empty((B, T, H, D), **f32))
+    for key in ("k", "v"):
+        out.setdefault(key, torch.empty((B, T, H_kv, D), **f32))
+    if return_dstate:
+        out.setdefault("state", torch.empty((B, H, D, D), **f32))
+    else:
+        out["state"] = None
+    out["r_k"] = out.get("r_k", torch.empty((H, D), **f32)) if r_k is not None else None
+    desc = make_desc(B, T, H, D, H_kv=H_kv, in_dtype=_dtype_name(r), y_dtype=_dtype_name(dy), w_mode=w_mode,
+                     y_scale=y_scale, r_k_ptr=_ptr(r_k), mask_ptr=_ptr(mask))
+    lib = load_library()
+    need = lib.wkv7_backward_workspace_bytes(ctypes.byref(desc))
+    if need < 0:
+        raise Wkv7Error(int(-need), "wkv7_backward_workspace_bytes", lib.wkv7_last_error().decode())
+    if need > 0 and workspace is None:
+        workspace = torch.empty(int(need), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    args = [ctypes.byref(desc)] + [_ptr(x) for x in (r, w, k, v, a, b, state, dy, dstate)] + \
+           [_ptr(out[n]) for n in ("r", "w", "k", "v", "a", "b", "state", "r_k")] + [_ptr(workspace), ws_bytes, stream]
+    with torch.cuda.device(dev):
+        rc = lib.wkv7_backward(*args)
+    if rc != WKV7_OK:
+        raise Wkv7Error(rc, "wkv7_backward", lib.wkv7_last_error().decode())
+    return out

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_strerror():
     lib = W.load_library()
-    assert lib.wkv7_abi_version() == 3
+    assert lib.wkv7_abi_version() == 4
     assert lib.wkv7_strerror(0) == b"ok"
     assert lib.wkv7_strerror(W.WKV7_EINVAL) == b"invalid argument"
     assert lib.wkv7_strerror(99) == b"unknown status"
@@ -185,3 +185,46 @@ def test_ab_mode_from_k_rules():
     assert W.wkv7_resolve_algo(2, 64, 4, 128, ab_mode="from_k") == "scan"
     assert W.wkv7_workspace_bytes(2, 64, 4, 128, ab_mode="from_k") == 2 * 4 * 2 * 54272
     assert W.wkv7_workspace_bytes(2, 64, 4, 64, ab_mode="from_k") == 0
+
+
+def _bwd(desc, **over):
+    """wkv7_backward with fake aligned pointers (every case fails validation first)."""
+    lib = W.load_library()
+    names = ("r", "w", "k", "v", "a", "b", "s0", "dy", "ds1", "dr", "dw", "dk", "dv", "da", "db", "ds0",
+             "drk", "ws")
+    vals = {n: FAKE + 4096 * (i + 1) for i, n in enumerate(names)}
+    vals.update(s0=None, ds1=None, ds0=None, drk=None)
+    vals.update(over)
+    ws_bytes = over.get("ws_bytes", 1 << 40)
+    args = [vals[n] for n in names[:-1]] + [vals["ws"], ws_bytes, None]
+    return lib.wkv7_backward(ctypes.byref(desc), *args)
+
+
+def test_backward_workspace_bytes():
+    # B H (ceil(T/32) + 2) D^2 4, rounded to 256, plus grouped-head and r_k terms.
+    assert W.wkv7_backward_workspace_bytes(2, 64, 4, 64) == 2 * 4 * (2 + 2) * 64 * 64 * 4
+    assert W.wkv7_backward_workspace_bytes(2, 65, 4, 64) == 2 * 4 * (3 + 2) * 64 * 64 * 4
+    assert W.wkv7_backward_workspace_bytes(1, 32, 4, 128, H_kv=2) == \
+        1 * 4 * 3 * 128 * 128 * 4 + 2 * (1 * 32 * 4 * 128 * 4)
+    assert W.wkv7_backward_workspace_bytes(2, 0, 4, 64) == 0
+    assert W.wkv7_backward_workspace_bytes(0, 8, 4, 64) == 0
+
+
+def test_backward_argument_rules():
+    lib = W.load_library()
+    assert _bwd(good(ab_mode="from_k")) == W.WKV7_EUNSUPPORTED
+    assert _bwd(good(), dy=None) == W.WKV7_EINVAL
+    assert b"dy is NULL" in lib.wkv7_last_error()
+    for name in ("dr", "dw", "dk", "dv", "da", "db"):
+        assert _bwd(good(), **{name: None}) == W.WKV7_EINVAL
+        assert f"{name} is NULL".encode() in lib.wkv7_last_error()
+        assert _bwd(good(), **{name: FAKE + 4}) == W.WKV7_EINVAL
+    assert _bwd(good(), dr=FAKE + 4096) == W.WKV7_EINVAL          # aliases r
+    assert _bwd(good(r_k_ptr=FAKE)) == W.WKV7_EINVAL                # r_k without dr_k
+    assert b"dr_k" in lib.wkv7_last_error()
+    assert _bwd(good(), drk=FAKE + 8192 * 64) == W.WKV7_EINVAL      # dr_k without r_k
+    assert _bwd(good(), ds1=FAKE + 8) == W.WKV7_EINVAL
+    assert _bwd(good(), ws=None) == W.WKV7_EINVAL
+    assert _bwd(good(), ws_bytes=100) == W.WKV7_EINVAL
+    assert b"needed" in lib.wkv7_last_error()
+    assert _bwd(good(B=0), ws=None, ws_bytes=0) == W.WKV7_OK         # empty: no device call

@@ -1,0 +1,167 @@
+"""GPU parity of the backward (wkv7_backward, through the C ABI) against the
+fp64 oracle's wkv7_backward: every gradient, on small cases element by
+element and on the full-size workloads on sampled (batch, head) sequences."""
+import numpy as np
+import pytest
+
+from linear_rnn_sequence_wkv7_amd import inputs as G
+from oracle import wkv7_oracle as O
+from tests import parity as P
+from tests.gpu_util import announce, dev_inputs, to_dev, to_host, torch
+
+pytestmark = pytest.mark.gpu
+
+# The backward runs in fp32 throughout (fp32 matrix cores): the scan's bound.
+TAU = P.TAU_SCAN
+NAMES = ("r", "w", "k", "v", "a", "b")
+
+
+@pytest.fixture(autouse=True)
+def _gpu_and_name(request):
+    if not torch().cuda.is_available():
+        pytest.skip("no GPU")
+    announce(request.node.nodeid)
+    yield
+
+
+def W():
+    from linear_rnn_sequence_wkv7_amd import wkv7
+    return wkv7
+
+
+def make_case(D, B, T, H, H_kv, in_dtype, y_dtype, w_mode, s0, epi, mask, seed):
+    return G.workload("hxa07d_bf16_b2_t16384_h32_kv8_d128", B=B, T=T, H=H, H_kv=H_kv, D=D, in_dtype=in_dtype,
+                      y_dtype=y_dtype, w_mode=w_mode, s0_std=s0, rk_std=0.1 if epi else 0.0,
+                      y_scale=D ** -0.5 if epi else 1.0, kk_from_k=False, mask=mask, seed=seed)
+
+
+def run_bwd(wl, x, gi):
+    d = dev_inputs(x)
+    dy = to_dev(gi["dy"])
+    ds = to_dev(gi["dstate"])
+    out = W().wkv7_backward(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], dy, d["state0"], ds,
+                            w_mode=wl.w_mode, y_scale=wl.y_scale, r_k=d["r_k"], mask=d["mask"])
+    torch().cuda.synchronize()
+    return {n: (None if t is None else to_host(t)) for n, t in out.items()}
+
+
+def oracle_bwd(wl, x, gi):
+    return O.wkv7_backward(x["r"], x["w"], x["k"], x["v"], x["a"], x["b"], x["state0"], gi["dy"],
+                           gi["dstate"], w_mode=wl.w_mode, r_k=x["r_k"], y_scale=wl.y_scale, mask=x["mask"])
+
+
+def check_all(got, ref, names=NAMES + ("state0", "r_k")):
+    errs = {}
+    for n in names:
+        key = "state" if n == "state0" else n
+        if ref.get(n) is None:
+            continue
+        errs[n] = P.check(f"d{n}", got[key], ref[n], TAU)
+    return errs
+
+
+SWEEP = [
+    # D, B, T, H, H_kv, in, dy, w_mode, s0_std, epilogue, mask, dstate
+    (64, 2, 1, 2, 2, "bf16", "f32", "decay", 0.1, False, "", True),
+    (64, 2, 31, 3, 3, "f32", "f32", "decay", 0.0, False, "", False),
+    (64, 2, 70, 2, 1, "bf16", "bf16", "logneglog", 0.1, True, "", True),
+    (64, 3, 100, 2, 2, "bf16", "f32", "decay", 0.1, True, "holes", True),
+    (64, 2, 160, 4, 2, "f32", "bf16", "logneglog", 0.0, False, "pad", False),
+    (128, 1, 33, 2, 2, "bf16", "f32", "logneglog", 0.1, True, "", True),
+    (128, 2, 64, 4, 1, "bf16", "bf16", "decay", 0.0, False, "holes", True),
+    (128, 3, 75, 2, 2, "f32", "f32", "logneglog", 0.1, True, "pad", False),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: "D{}_B{}_T{}_H{}_kv{}_{}_{}_{}_s{}_e{}_m{}_ds{}".format(*c))
+def test_backward_sweep(case):
+    *shape, dstate = case
+    wl = make_case(*shape, seed=51 + case[2])
+    x = G.make_inputs(wl)
+    gi = G.make_grad_inputs(wl, dstate=dstate)
+    ref = oracle_bwd(wl, x, gi)
+    got = run_bwd(wl, x, gi)
+    errs = check_all(got, ref)
+    announce("  " + " ".join(f"d{n} {e:.1e}" for n, e in errs.items()))
+    if x["mask"] is not None:
+        m = x["mask"] == 0
+        for n in ("r", "w", "a", "b"):
+            assert np.all(got[n][m] == 0.0), f"d{n} of masked tokens"
+
+
+def test_backward_zero_tokens():
+    wl = make_case(64, 2, 0, 3, 3, "bf16", "f32", "decay", 0.1, True, "", seed=3)
+    x = G.make_inputs(wl)
+    gi = G.make_grad_inputs(wl)
+    got = run_bwd(wl, x, gi)
+    np.testing.assert_array_equal(got["state"], gi["dstate"].astype(np.float64))
+    assert np.all(got["r_k"] == 0.0)
+
+
+def test_backward_deterministic():
+    wl = make_case(128, 2, 70, 4, 2, "bf16", "bf16", "logneglog", 0.1, True, "holes", seed=5)
+    x = G.make_inputs(wl)
+    gi = G.make_grad_inputs(wl)
+    g1 = run_bwd(wl, x, gi)
+    g2 = run_bwd(wl, x, gi)
+    # LDS float atomics sum in a varying order: equal to rounding, not bit for bit.
+    for n in g1:
+        if g1[n] is not None:
+            P.check(f"repeat d{n}", g1[n], g2[n], 1e-5)
+
+
+def _bwd_pairs(x, gi, wl, pairs):
+    """Oracle gradients of whole (b, h) sequences; pairs must cover whole KV groups."""
+    sel = P.select_pairs(x, wl, pairs)
+    bs = np.array([p[0] for p in pairs])
+    hs = np.array([p[1] for p in pairs])
+    dy = np.ascontiguousarray(np.moveaxis(gi["dy"][bs, :, hs], 0, 1)[None])
+    ds = None if gi["dstate"] is None else gi["dstate"][bs, hs][None]
+    return O.wkv7_backward(sel["r"], sel["w"], sel["k"], sel["v"], sel["a"], sel["b"], sel["state0"], dy, ds,
+                           w_mode=wl.w_mode, r_k=sel["r_k"], y_scale=wl.y_scale)
+
+
+@pytest.mark.parametrize("name,n_pairs", [("fwd_bf16_b8_t1024_h32_d64", 8),
+                                          ("prefill_bf16_b4_t4096_h40_d64_l64", 3)])
+def test_backward_workload(name, n_pairs):
+    """Full-size D = 64 workloads; sampled whole sequences (one KV head per head)."""
+    wl = G.WORKLOADS[name]
+    x = G.make_inputs(wl)
+    gi = G.make_grad_inputs(wl)
+    pairs = P.sample_pairs(wl, n_pairs, seed=wl.seed)
+    got = run_bwd(wl, x, gi)
+    ref = _bwd_pairs(x, gi, wl, pairs)
+    bs = [p[0] for p in pairs]
+    hs = [p[1] for p in pairs]
+    errs = {}
+    for n in NAMES:
+        errs[n] = P.check(f"d{n}", got[n][bs, :, hs], np.moveaxis(ref[n][0], 1, 0), TAU)
+    errs["state0"] = P.check("dS0", got["state"][bs, hs], ref["state0"][0], TAU)
+    announce("  " + " ".join(f"d{n} {e:.1e}" for n, e in errs.items()))
+
+
+def test_backward_workload_hxa07d():
+    """hxa07D shapes (GQA x4, log-decay, epilogue): one KV group of both sequences,
+    so dk, dv and dr_k are complete sums."""
+    wl = G.workload("hxa07d_bf16_b2_t16384_h32_kv8_d128", T=4096)
+    x = G.make_inputs(wl)
+    gi = G.make_grad_inputs(wl)
+    got = run_bwd(wl, x, gi)
+    grp = 5
+    pairs = [(b, 4 * grp + u) for b in range(wl.B) for u in range(4)]
+    # The group's heads as one oracle batch per sequence, KV head kept grouped.
+    errs = {}
+    drk = np.zeros((4, wl.D))
+    for b in range(wl.B):
+        sl = slice(4 * grp, 4 * grp + 4)
+        ref = O.wkv7_backward(*(x[n][b:b + 1, :, sl] if n not in ("k", "v") else x[n][b:b + 1, :, grp:grp + 1]
+                                for n in NAMES), None, gi["dy"][b:b + 1, :, sl], gi["dstate"][b:b + 1, sl],
+                              w_mode=wl.w_mode, r_k=x["r_k"][sl], y_scale=wl.y_scale)
+        for n in ("r", "w", "a", "b"):
+            errs[f"{n}{b}"] = P.check(f"d{n} b{b}", got[n][b, :, sl], ref[n][0], TAU)
+        for n in ("k", "v"):
+            errs[f"{n}{b}"] = P.check(f"d{n} b{b}", got[n][b, :, grp], ref[n][0, :, 0], TAU)
+        errs[f"S{b}"] = P.check(f"dS0 b{b}", got["state"][b, sl], ref["state0"][0], TAU)
+        drk += ref["r_k"]
+    errs["r_k"] = P.check("dr_k", got["r_k"][4 * grp:4 * grp + 4], drk, TAU)
+    announce("  " + " ".join(f"{n} {e:.1e}" for n, e in errs.items()))
