@@ -10,13 +10,15 @@ Prints one JSON line with the throughput (head-tokens/s), the roofline of the
 dominant kernel and the fp64 CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--algo auto|scan|chunked|two_pass]
-                    [--ab-mode given|from_k] [--mask pad|holes]
+                    [--ab-mode given|from_k] [--mask pad|holes] [--backward]
 
 At D = 128 "auto" runs the two-pass form (two kernels per step, workspace
 allocated before the timed region); its roofline covers the whole step.
 --ab-mode from_k passes alpha in place of a and no b: the kernels form
 a = -kk, b = kk alpha and k (1 - decay + alpha) themselves.  --mask adds an
-attention mask drawn by the named recipe.
+attention mask drawn by the named recipe.  --backward times wkv7_backward
+(every input gradient, dS0 and dr_k) for the workload, with seeded upstream
+gradients dy and dS_T resident before the timed region.
 """
 from __future__ import annotations
 
@@ -43,6 +45,7 @@ KERNEL_SOURCES = {
     "chunked128": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_chunked128.hip",
     "twopass128": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_twopass128.hip",
     "decode": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_decode.hip",
+    "backward": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_backward.hip",
 }
 
 
@@ -77,6 +80,23 @@ def algorithmic_flops(wl) -> int:
     return 9 * wl.D * wl.D * wl.B * wl.T * wl.H
 
 
+def backward_flops(wl) -> int:
+    """28 D^2 per head-token: the token-level reverse step (U += dy r^T, S^T dy, U k,
+    U^T v, S a, U^T sa, U b, S^T Ub, sum S * U: 2 D^2 each; U diag(w) + Ub a^T: 3 D^2)
+    plus recomputing the state (7 D^2)."""
+    return 28 * wl.D * wl.D * wl.B * wl.T * wl.H
+
+
+def backward_bytes(wl) -> int:
+    """Inputs and dy read once, the seven gradients written once (fp32), dS_T read
+    and dS0 written."""
+    sin = 2 if wl.in_dtype == "bf16" else 4
+    sy = 2 if wl.y_dtype == "bf16" else 4
+    per_tok = wl.H * wl.D * (4 * sin + sy + 4 * 4) + wl.H_kv * wl.D * 2 * (sin + 4)
+    state = wl.B * wl.H * wl.D * wl.D * 4 * (3 if wl.s0_std > 0 else 2)
+    return wl.B * wl.T * per_tok + state
+
+
 def traffic_from_profile(kind: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs (FETCH_SIZE
     plus WRITE_SIZE, each scaled by what the counter reads for a plain copy of
@@ -104,6 +124,27 @@ def cpu_baseline(wl, x, n_pairs: int):
                       f"fp64 numpy, single thread, {dt:.1f} s"}
 
 
+def cpu_baseline_backward(wl, x, gi, n_pairs: int):
+    """The fp64 oracle's backward, as it stands, on n_pairs whole sequences (one KV
+    head each, so only workloads with H_kv == H)."""
+    import numpy as np
+    from oracle import wkv7_oracle as O
+    from tests import parity as P
+    pairs = P.sample_pairs(wl, n_pairs, seed=wl.seed)[:n_pairs]
+    sel = P.select_pairs(x, wl, pairs)
+    bs = np.array([p[0] for p in pairs])
+    hs = np.array([p[1] for p in pairs])
+    dy = np.ascontiguousarray(np.moveaxis(gi["dy"][bs, :, hs], 0, 1)[None])
+    ds = gi["dstate"][bs, hs][None]
+    t0 = time.perf_counter()
+    O.wkv7_backward(sel["r"], sel["w"], sel["k"], sel["v"], sel["a"], sel["b"], sel["state0"], dy, ds,
+                    w_mode=wl.w_mode, r_k=sel["r_k"], y_scale=wl.y_scale)
+    dt = time.perf_counter() - t0
+    return {"value": len(pairs) * wl.T / dt, "unit": "head-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"backward of {len(pairs)} of {wl.B * wl.H} (batch, head) sequences x all {wl.T} tokens, "
+                      f"fp64 numpy, single thread, {dt:.1f} s"}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +154,7 @@ def main(argv=None) -> int:
     ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunked", "two_pass"])
     ap.add_argument("--ab-mode", default="given", choices=["given", "from_k"])
     ap.add_argument("--mask", default="", choices=["", "pad", "holes"])
+    ap.add_argument("--backward", action="store_true", help="time wkv7_backward instead of the forward")
     ap.add_argument("--cpu-pairs", type=int, default=256, help="sequences in the CPU-oracle sample (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (a reference for the "
@@ -158,7 +200,32 @@ def main(argv=None) -> int:
     d = {k: dev(v) for k, v in x.items()}
     stream = torch.cuda.current_stream()
 
-    if wl.kind == "decode":
+    if a.backward:
+        if wl.kind != "forward":
+            print("--backward needs a forward workload", file=sys.stderr)
+            return 2
+        kind = "backward"
+        gi = G.make_grad_inputs(wl)
+        dy, dst = dev(gi["dy"]), dev(gi["dstate"])
+        ws_bytes = wkv7.wkv7_backward_workspace_bytes(
+            wl.B, wl.T, wl.H, wl.D, H_kv=wl.H_kv, in_dtype=wl.in_dtype, y_dtype=wl.y_dtype, w_mode=wl.w_mode,
+            r_k_ptr=None if d["r_k"] is None else d["r_k"].data_ptr())
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        f32 = dict(dtype=torch.float32, device="cuda")
+        grads = {n: torch.empty((wl.B, wl.T, wl.H, wl.D), **f32) for n in ("r", "w", "a", "b")}
+        grads.update({n: torch.empty((wl.B, wl.T, wl.H_kv, wl.D), **f32) for n in ("k", "v")})
+        grads["state"] = torch.empty((wl.B, wl.H, wl.D, wl.D), **f32)
+        if d["r_k"] is not None:
+            grads["r_k"] = torch.empty((wl.H, wl.D), **f32)
+
+        def one_step(i):
+            wkv7.wkv7_backward(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], dy, d["state0"], dst,
+                               w_mode=wl.w_mode, y_scale=wl.y_scale, r_k=d["r_k"], mask=d["mask"],
+                               workspace=ws, grads=grads)
+        head_tokens_per_step = wl.B * wl.T * wl.H
+        nbytes = backward_bytes(wl)
+        flops = backward_flops(wl)
+    elif wl.kind == "decode":
         kind = "decode"
         sa = d["state0"]
         sb = torch.empty_like(sa)
@@ -212,7 +279,13 @@ def main(argv=None) -> int:
     ms = ev0.elapsed_time(ev1) / a.steps
 
     value = head_tokens_per_step / (ms / 1e3)
-    if kind != "decode":
+    if kind == "backward":
+        # fp32 throughout, on fp32 matrix cores: the fp32 peak (157.3 TFLOP/s, the same for VALU and MFMA).
+        achieved = flops / (ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_FP32_VALU_TFLOPS}
+        dtype = "f32"
+    elif kind != "decode":
         # Forward: the algorithmic work (9 D^2 flop per head-token) binds on the fp32
         # vector ALU (intensity ~40 flop/B at D = 64, ~104 at D = 128).
         achieved = flops / (ms / 1e3) / 1e12
@@ -240,7 +313,9 @@ def main(argv=None) -> int:
         "roofline": roof,
         "wall_s_timed_region": t_wall,
     }
-    if a.cpu_pairs > 0 and wl.kind == "forward":
+    if a.cpu_pairs > 0 and a.backward and wl.H_kv == wl.H:
+        out["cpu_baseline"] = cpu_baseline_backward(wl, x, gi, min(a.cpu_pairs, 16))
+    elif a.cpu_pairs > 0 and wl.kind == "forward" and not a.backward:
         out["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_pairs)
     else:
         out["cpu_baseline"] = None

@@ -109,6 +109,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     constexpr int NA = (2 * TC) / 8;     // tiles per wave of one [32][D] matrix
     constexpr int UNI = (2 * BSL * PD > 4 * BL * PL) ? 2 * BSL * PD : 4 * BL * PL;
     static_assert(BSL == BL, "slice and chunk share the 32-wide LDS pitch");
+    static_assert(BL * D <= 6 * BL * PL, "the w-derivative table fits the slice buffers");
 
     extern __shared__ __attribute__((aligned(16))) float sm[];
     float* RT = sm;
@@ -132,6 +133,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     float* DZS = SAS + BL * PL;
     float* ZS = DZS + BL * PL;
     float* DSAS = ZS + BL * PL;
+    float* FAC = VS;                     // [BL][D] after the slices: d log w / d(w input)
     float* DD = DSAS + BL * PL;          // [D] diag(S_L^T U)
     float* DEC = DD + D;                 // [D] d = 2^g_L
     float* BETA = DEC + D;               // [BL] r k r_k per token
@@ -156,14 +158,20 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     auto qidx = [&](int t, int j) { return ((int64_t(bb) * T + t) * H + h) * D + j; };
     auto kvidx = [&](int t, int j) { return ((int64_t(bb) * T + t) * H_kv + hk) * D + j; };
     const uint8_t* mrow = g.mask ? g.mask + int64_t(bb) * T : nullptr;
-    auto valid = [&](int t) {   // t: absolute token
-        return t < T && (!mrow || mrow[t] != 0);
+    // Bit t of `vbits`: token c0 + t of the current chunk is kept (in range, not masked).
+    uint32_t vbits = 0;
+    auto set_chunk_bits = [&](int c0) {
+        const int t = c0 + (lane & 31);
+        const bool ok = t < T && (!mrow || mrow[t] != 0);
+        vbits = uint32_t(__builtin_amdgcn_ballot_w64(ok && lane < BL));
     };
+    auto valid = [&](int t_abs) { return ((vbits >> (t_abs & (BL - 1))) & 1u) != 0; };
 
     // Chunk c: g_t, the scaled key-axis operands and d.  With `with_r`, Rt and the
     // epilogue's r k r_k as well.
     auto load_chunk = [&](int c, bool with_r) {
         const int c0 = c * BL;
+        set_chunk_bits(c0);
         for (int e = tid; e < BL * D; e += BNT) {
             const int t = e / D, j = e - t * D;
             const bool ok = valid(c0 + t);
@@ -438,6 +446,16 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
             }
         }
         __syncthreads();
+        // d log w / d(w input) of every kept token (0 for the others), for the suffix sums.
+        for (int e = tid; e < BL * D; e += BNT) {
+            const int t = e / D, j = e - t * D;
+            float f = 0.f;
+            if (valid(c0 + t)) {
+                const float x = ld1(wp, qidx(c0 + t, j));
+                f = LOGW ? -__builtin_amdgcn_exp2f(x * kLog2e) : 1.f / x;
+            }
+            FAC[e] = f;
+        }
         // Gradients of r, a, b, k; the log-decay suffix-sum terms.
         #pragma unroll
         for (int u = 0; u < NA; ++u) {
@@ -479,15 +497,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
             float run = DD[j];
             for (int t = BL - 1; t >= 0; --t) {
                 run += QP[t * PD + j] + (t + 1 < BL ? QA[(t + 1) * PD + j] : 0.f);
-                if (c0 + t < T) {
-                    const int64_t gi = qidx(c0 + t, j);
-                    float dwv = 0.f;
-                    if (valid(c0 + t)) {
-                        const float x = ld1(wp, gi);
-                        dwv = LOGW ? run * -__builtin_amdgcn_exp2f(x * kLog2e) : run / x;
-                    }
-                    g.dw[gi] = dwv;
-                }
+                if (c0 + t < T) g.dw[qidx(c0 + t, j)] = run * FAC[t * D + j];
             }
         }
         __syncthreads();
