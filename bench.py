@@ -46,6 +46,7 @@ KERNEL_SOURCES = {
     "twopass128": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_twopass128.hip",
     "decode": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_decode.hip",
     "backward": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_backward.hip",
+    "wkv4": "linear_rnn_sequence_wkv7_amd/csrc/wkv4.hip",
 }
 
 
@@ -145,6 +146,72 @@ def cpu_baseline_backward(wl, x, gi, n_pairs: int):
                       f"fp64 numpy, single thread, {dt:.1f} s"}
 
 
+def run_wkv4(a, wl, G, wkv7, torch, np):
+    """RWKV-4 WKV workload: one step = one wkv4_forward over the batch."""
+    x = G.make_wkv4_inputs(wl)
+
+    def dev(arr):
+        if arr is None:
+            return None
+        if arr.dtype == np.uint16:
+            return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(arr).cuda()
+
+    d = {k: dev(v) for k, v in x.items()}
+    y = torch.empty((wl.B, wl.T, wl.C), dtype=torch.bfloat16 if wl.y_dtype == "bf16" else torch.float32, device="cuda")
+    s_out = torch.empty((wl.B, 3, wl.C), dtype=torch.float32, device="cuda")
+    ws = torch.empty(wkv7.wkv4_workspace_bytes(wl.B, wl.T, wl.C, in_dtype=wl.in_dtype, y_dtype=wl.y_dtype),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def one_step():
+        wkv7.wkv4_forward(d["w"], d["u"], d["k"], d["v"], d["state"], y_dtype=wl.y_dtype, y=y, state_out=s_out,
+                          workspace=ws)
+    for _ in range(a.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(a.steps):
+        one_step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1) / a.steps
+    sin = 2 if wl.in_dtype == "bf16" else 4
+    sy = 2 if wl.y_dtype == "bf16" else 4
+    # Algorithmic bytes: k, v read once, y written once, w and u, the final state written.
+    nbytes = wl.B * wl.T * wl.C * (2 * sin + sy) + 2 * wl.C * 4 + wl.B * 3 * wl.C * 4 * (2 if wl.state else 1)
+    ht = wl.B * wl.T * wl.C
+    achieved = nbytes / (ms / 1e3) / 1e9
+    out = {
+        "metric": "rwkv4 wkv channel-tokens/sec + % of HBM roofline, 1xMI355X", "value": ht / (ms / 1e3),
+        "unit": "channel-tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "C": wl.C, "io_dtype": wl.in_dtype,
+                   "y_dtype": wl.y_dtype, "kernel": "wkv4"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profile("wkv4", wl.name),
+                     "kernel": "wkv4", "algorithmic_bytes": nbytes},
+        "wall_s_timed_region": t_wall,
+    }
+    if a.cpu_pairs > 0:
+        from oracle import wkv4_oracle as O4
+        n = min(a.cpu_pairs, 8)
+        t0 = time.perf_counter()
+        O4.wkv4_forward(x["w"][:n], x["u"][:n], x["k"][:1, :, :n], x["v"][:1, :, :n])
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": n * wl.T / dt, "unit": "channel-tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} channels of batch 0 x all {wl.T} tokens (the oracle evaluates "
+                                         f"the sum definition, O(T^2) per channel), fp64 numpy, {dt:.1f} s"}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +252,9 @@ def main(argv=None) -> int:
     from linear_rnn_sequence_wkv7_amd import inputs as G
     from linear_rnn_sequence_wkv7_amd import wkv7
 
+    if a.workload in G.WKV4_WORKLOADS:
+        torch.cuda.set_device(0)
+        return run_wkv4(a, G.WKV4_WORKLOADS[a.workload], G, wkv7, torch, np)
     wl = dataclasses.replace(G.WORKLOADS[a.workload], ab_mode=a.ab_mode, mask=a.mask)
     label = workload_label(wl)
     torch.cuda.set_device(0)

@@ -272,6 +272,77 @@ int wkv7_backward(const wkv7_desc* desc, const void* r, const void* w, const voi
     return finish_launch(wkv7::launch_backward(p, io, workspace, reinterpret_cast<hipStream_t>(stream)), "backward");
 }
 
+}  // extern "C"
+
+namespace {
+
+int check_wkv4(const wkv4_desc* d) {
+    if (!d) return fail(WKV7_EINVAL, "desc is NULL");
+    if (d->reserved != 0) return fail(WKV7_EINVAL, "desc->reserved must be 0");
+    if (d->B < 0 || d->T < 0 || d->C < 0)
+        return fail(WKV7_EINVAL, "negative size (B=%d T=%d C=%d)", d->B, d->T, d->C);
+    if (d->in_dtype != WKV7_F32 && d->in_dtype != WKV7_BF16)
+        return fail(WKV7_EINVAL, "in_dtype %d unknown", d->in_dtype);
+    if (d->y_dtype != WKV7_F32 && d->y_dtype != WKV7_BF16)
+        return fail(WKV7_EINVAL, "y_dtype %d unknown", d->y_dtype);
+    if (int64_t(d->B) * d->T * d->C > (int64_t(1) << 46)) return fail(WKV7_EUNSUPPORTED, "B*T*C too large");
+    if (d->B > 65535 || (int64_t(d->T) + 63) / 64 > 65535)
+        return fail(WKV7_EUNSUPPORTED, "B=%d or T=%d beyond the grid limits", d->B, d->T);
+    // Byte offsets inside one 64-token chunk are 32-bit.
+    if (int64_t(d->C) * 64 * 4 >= (int64_t(1) << 31)) return fail(WKV7_EUNSUPPORTED, "C=%d too large", d->C);
+    return WKV7_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t wkv4_workspace_bytes(const wkv4_desc* desc) {
+    g_last_error[0] = '\0';
+    int rc = check_wkv4(desc);
+    if (rc) return -rc;
+    return wkv7::wkv4_workspace_bytes_internal(desc->B, desc->T, desc->C);
+}
+
+int wkv4_forward(const wkv4_desc* desc, const float* w, const float* u, const void* k, const void* v,
+                 const float* state_in, void* y, float* state_out, void* workspace,
+                 int64_t workspace_bytes_given, void* stream) {
+    g_last_error[0] = '\0';
+    int rc = check_wkv4(desc);
+    if (rc) return rc;
+    const int64_t bc = int64_t(desc->B) * desc->C;
+    const bool has_tokens = bc * desc->T > 0;
+    if (bc > 0) {
+        if (!w || !u) return fail(WKV7_EINVAL, "w or u is NULL");
+        if (!aligned16(w) || !aligned16(u)) return fail(WKV7_EINVAL, "w or u is not 16-byte aligned");
+    }
+    if (has_tokens) {
+        const void* ptrs[3] = {k, v, y};
+        static const char* names[3] = {"k", "v", "y"};
+        for (int i = 0; i < 3; ++i) {
+            if (!ptrs[i]) return fail(WKV7_EINVAL, "%s is NULL", names[i]);
+            if (!aligned16(ptrs[i])) return fail(WKV7_EINVAL, "%s is not 16-byte aligned", names[i]);
+        }
+        if (y == k || y == v) return fail(WKV7_EINVAL, "y aliases an input");
+    }
+    if (state_in && !aligned16(state_in)) return fail(WKV7_EINVAL, "state_in is not 16-byte aligned");
+    if (state_out && !aligned16(state_out)) return fail(WKV7_EINVAL, "state_out is not 16-byte aligned");
+    const int64_t need = has_tokens ? wkv7::wkv4_workspace_bytes_internal(desc->B, desc->T, desc->C) : 0;
+    if (need > 0) {
+        if (!workspace) return fail(WKV7_EINVAL, "workspace is NULL (%lld bytes needed)", (long long)need);
+        if (!aligned16(workspace)) return fail(WKV7_EINVAL, "workspace is not 16-byte aligned");
+        if (workspace_bytes_given < need)
+            return fail(WKV7_EINVAL, "workspace has %lld bytes, %lld needed",
+                        (long long)workspace_bytes_given, (long long)need);
+    }
+    if (bc == 0) return WKV7_OK;
+    if (!has_tokens && !state_out) return WKV7_OK;
+    if ((rc = check_device())) return rc;
+    wkv7::Wkv4Params p{desc->B, desc->T, desc->C, desc->in_dtype, desc->y_dtype, w, u, k, v, y,
+                       state_in, state_out, workspace};
+    return finish_launch(wkv7::launch_wkv4(p, reinterpret_cast<hipStream_t>(stream)), "wkv4");
+}
+
 int wkv7_resolve_algo(const wkv7_desc* desc) {
     wkv7::Params p{};
     int rc = check_desc(desc, &p);

@@ -1,12 +1,13 @@
 // Internal interface between the C-ABI entry points (wkv7_api.cpp) and the
 // kernel launchers (wkv7_scan.hip, wkv7_chunked.hip, wkv7_chunked128.hip,
-// wkv7_twopass128.hip, wkv7_decode.hip, wkv7_backward.hip).
+// wkv7_twopass128.hip, wkv7_decode.hip, wkv7_backward.hip, wkv4.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
 #include "../../include/wkv7.h"
+#include "../../include/wkv4.h"
 
 namespace wkv7 {
 
@@ -47,6 +48,19 @@ struct BwdIo {
     float* drk;            // [H, D] when r_k is given
 };
 int64_t backward_workspace_bytes(const Params& p);
+
+// RWKV-4 WKV (wkv4.hip).
+struct Wkv4Params {
+    int B, T, C, in_dtype, y_dtype;
+    const float *w, *u;
+    const void *k, *v;
+    void* y;
+    const float* s0;
+    float* s1;
+    void* ws;
+};
+int64_t wkv4_workspace_bytes_internal(int B, int T, int C);
+hipError_t launch_wkv4(const Wkv4Params& p, hipStream_t stream);
 hipError_t launch_backward(const Params& p, const BwdIo& io, void* ws, hipStream_t stream);
 
 }  // namespace wkv7

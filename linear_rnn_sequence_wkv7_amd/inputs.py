@@ -32,7 +32,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "make_inputs", "make_grad_inputs", "f32_to_bf16_bits", "bf16_bits_to_f32",
-    "workload",
+    "workload", "Wkv4Workload", "WKV4_WORKLOADS", "make_wkv4_inputs",
 ]
 
 
@@ -215,4 +215,49 @@ def make_grad_inputs(wl: Workload, seed: Optional[int] = None, dstate: bool = Tr
     out: Dict[str, Optional[np.ndarray]] = {}
     out["dy"] = _encode(rng.standard_normal((wl.B, wl.T, wl.H, wl.D)), wl.y_dtype)
     out["dstate"] = rng.standard_normal((wl.B, wl.H, wl.D, wl.D)).astype(np.float32) if dstate else None
+    return out
+
+
+# ------------------------------- RWKV-4 WKV -------------------------------
+
+@dataclass(frozen=True)
+class Wkv4Workload:
+    """RWKV-4 WKV inputs: k, v [B, T, C], per-channel w, u."""
+    name: str
+    B: int
+    T: int
+    C: int
+    in_dtype: str
+    y_dtype: str
+    seed: int
+    state: bool = False       # random initial state (A, Bs, P) instead of zero
+    k_offset: float = 0.0     # added to every k (exercises the exponent scaling)
+
+
+WKV4_WORKLOADS: Dict[str, Wkv4Workload] = {w.name: w for w in [
+    Wkv4Workload("rwkv4_bf16_b8_t4096_c4096", B=8, T=4096, C=4096, in_dtype="bf16", y_dtype="bf16", seed=1101),
+]}
+
+
+def make_wkv4_inputs(wl: Wkv4Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Draw order from one PCG64 stream: z (decay), u, k, v, then the state.
+
+    w = exp(z), z ~ U(-5, 1) per channel (a spread of slow and fast decays);
+    u ~ N(0, 1); k, v ~ N(0, 1) with k_offset added to k.  The optional state is
+    (A, Bs, P) per (b, c): A ~ N(0, 1), Bs ~ U(0.5, 2), P ~ N(0, 1) (a = A e^P,
+    b = Bs e^P).  k, v encoded per in_dtype; w, u, state fp32."""
+    rng = np.random.Generator(np.random.PCG64(wl.seed if seed is None else seed))
+    out: Dict[str, Optional[np.ndarray]] = {}
+    out["w"] = np.exp(rng.uniform(-5.0, 1.0, wl.C)).astype(np.float32)
+    out["u"] = rng.standard_normal(wl.C).astype(np.float32)
+    out["k"] = _encode(rng.standard_normal((wl.B, wl.T, wl.C)) + wl.k_offset, wl.in_dtype)
+    out["v"] = _encode(rng.standard_normal((wl.B, wl.T, wl.C)), wl.in_dtype)
+    if wl.state:
+        st = np.empty((wl.B, 3, wl.C), dtype=np.float32)
+        st[:, 0] = rng.standard_normal((wl.B, wl.C))
+        st[:, 1] = rng.uniform(0.5, 2.0, (wl.B, wl.C))
+        st[:, 2] = rng.standard_normal((wl.B, wl.C))
+        out["state"] = st
+    else:
+        out["state"] = None
     return out

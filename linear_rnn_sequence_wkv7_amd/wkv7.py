@@ -15,7 +15,7 @@ from typing import Optional, Tuple
 
 __all__ = [
     "wkv7_forward", "wkv7_backward", "wkv7_decode_step", "wkv7_resolve_algo", "wkv7_workspace_bytes",
-    "wkv7_backward_workspace_bytes", "Wkv7Error",
+    "wkv7_backward_workspace_bytes", "wkv4_forward", "wkv4_workspace_bytes", "Wkv7Error",
     "lib_path", "load_library",
     "WKV7_OK", "WKV7_EINVAL", "WKV7_EUNSUPPORTED", "WKV7_EDEVICE", "WKV7_ELAUNCH",
     "ALGOS", "W_MODES", "AB_MODES", "Desc", "EXPORTED_SYMBOLS",
@@ -27,7 +27,7 @@ W_MODES = {"decay": 0, "logneglog": 1}
 ALGOS = {"auto": 0, "scan": 1, "chunked": 2, "two_pass": 3}
 AB_MODES = {"given": 0, "from_k": 1}
 EXPORTED_SYMBOLS = ("wkv7_forward", "wkv7_forward_ws", "wkv7_workspace_bytes", "wkv7_decode_step",
-                    "wkv7_backward", "wkv7_backward_workspace_bytes",
+                    "wkv7_backward", "wkv7_backward_workspace_bytes", "wkv4_forward", "wkv4_workspace_bytes",
                     "wkv7_resolve_algo", "wkv7_strerror", "wkv7_last_error", "wkv7_abi_version")
 
 
@@ -46,6 +46,12 @@ class Desc(ctypes.Structure):
         ("y_scale", ctypes.c_float), ("ab_mode", ctypes.c_int32), ("r_k", ctypes.c_void_p),
         ("mask", ctypes.c_void_p),
     ]
+
+
+class Wkv4Desc(ctypes.Structure):
+    """Mirror of struct wkv4_desc."""
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 def lib_path() -> str:
@@ -78,6 +84,10 @@ def load_library():
     lib.wkv7_backward.restype = ctypes.c_int
     lib.wkv7_backward_workspace_bytes.argtypes = [ctypes.POINTER(Desc)]
     lib.wkv7_backward_workspace_bytes.restype = ctypes.c_int64
+    lib.wkv4_forward.argtypes = [ctypes.POINTER(Wkv4Desc)] + [vp] * 8 + [ctypes.c_int64, vp]
+    lib.wkv4_forward.restype = ctypes.c_int
+    lib.wkv4_workspace_bytes.argtypes = [ctypes.POINTER(Wkv4Desc)]
+    lib.wkv4_workspace_bytes.restype = ctypes.c_int64
     lib.wkv7_resolve_algo.argtypes = [ctypes.POINTER(Desc)]
     lib.wkv7_resolve_algo.restype = ctypes.c_int
     lib.wkv7_strerror.argtypes = [ctypes.c_int]
@@ -313,3 +323,51 @@ def wkv7_backward(r, w, k, v, a, b, dy, state=None, dstate=None, *, w_mode: str 
     if rc != WKV7_OK:
         raise Wkv7Error(rc, "wkv7_backward", lib.wkv7_last_error().decode())
     return out
+
+
+def wkv4_workspace_bytes(B, T, C, *, in_dtype="bf16", y_dtype="bf16") -> int:
+    """Workspace bytes of wkv4_forward for these sizes."""
+    d = Wkv4Desc(B=B, T=T, C=C, in_dtype=_DTYPES[in_dtype], y_dtype=_DTYPES[y_dtype], reserved=0)
+    n = load_library().wkv4_workspace_bytes(ctypes.byref(d))
+    if n < 0:
+        raise Wkv7Error(int(-n), "wkv4_workspace_bytes", load_library().wkv7_last_error().decode())
+    return int(n)
+
+
+def wkv4_forward(w, u, k, v, state=None, *, y_dtype: Optional[str] = None, y=None, state_out=None,
+                 return_state: bool = True, workspace=None) -> Tuple[object, object]:
+    """RWKV-4 WKV on torch GPU tensors: w, u [C] float32; k, v [B, T, C] float32 or bfloat16;
+    state [B, 3, C] float32 (A, Bs, P with a = A e^P, b = Bs e^P) or None.  Returns (y, state_out)."""
+    torch = _torch()
+    if k.dim() != 3 or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, T, C] with the same shape")
+    B, T, C = k.shape
+    dev = k.device
+    for name, x in (("w", w), ("u", u)):
+        if tuple(x.shape) != (C,) or x.dtype != torch.float32 or x.device != dev or not x.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 [C] = {(C,)} tensor on {dev}")
+    if v.dtype != k.dtype or not k.is_contiguous() or not v.is_contiguous() or v.device != dev:
+        raise ValueError("k and v must be contiguous, on one device, with one dtype")
+    if state is not None and (tuple(state.shape) != (B, 3, C) or state.dtype != torch.float32 or
+                              state.device != dev or not state.is_contiguous()):
+        raise ValueError(f"state must be contiguous float32 [B, 3, C] = {(B, 3, C)} on {dev}")
+    ydt = y_dtype or _dtype_name(k)
+    if y is None:
+        y = torch.empty((B, T, C), dtype=torch.float32 if ydt == "f32" else torch.bfloat16, device=dev)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, 3, C), dtype=torch.float32, device=dev)
+    d = Wkv4Desc(B=B, T=T, C=C, in_dtype=_DTYPES[_dtype_name(k)], y_dtype=_DTYPES[ydt], reserved=0)
+    lib = load_library()
+    need = lib.wkv4_workspace_bytes(ctypes.byref(d))
+    if need < 0:
+        raise Wkv7Error(int(-need), "wkv4_workspace_bytes", lib.wkv7_last_error().decode())
+    if need > 0 and workspace is None:
+        workspace = torch.empty(int(need), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = lib.wkv4_forward(ctypes.byref(d), _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state), _ptr(y),
+                              _ptr(state_out), _ptr(workspace), ws_bytes, stream)
+    if rc != WKV7_OK:
+        raise Wkv7Error(rc, "wkv4_forward", lib.wkv7_last_error().decode())
+    return y, state_out

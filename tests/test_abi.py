@@ -19,7 +19,7 @@ def declared_functions():
         if fn.endswith(".h"):
             src = open(os.path.join(ROOT, "include", fn)).read()
             src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-            names += re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(wkv7_\w+)\s*\(", src, flags=re.M)
+            names += re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(wkv[47]_\w+)\s*\(", src, flags=re.M)
     return sorted(set(names))
 
 
@@ -228,3 +228,33 @@ def test_backward_argument_rules():
     assert _bwd(good(), ws_bytes=100) == W.WKV7_EINVAL
     assert b"needed" in lib.wkv7_last_error()
     assert _bwd(good(B=0), ws=None, ws_bytes=0) == W.WKV7_OK         # empty: no device call
+
+
+def _wkv4(desc, **over):
+    lib = W.load_library()
+    names = ("w", "u", "k", "v", "s0", "y", "s1", "ws")
+    vals = {n: FAKE + 4096 * (i + 1) for i, n in enumerate(names)}
+    vals.update(s0=None, s1=None)
+    vals.update(over)
+    d = ctypes.byref(desc) if desc is not None else None
+    return lib.wkv4_forward(d, *(vals[n] for n in names), over.get("ws_bytes", 1 << 40), None)
+
+
+def test_wkv4_argument_rules():
+    lib = W.load_library()
+    good4 = lambda **kw: W.Wkv4Desc(**{**dict(B=2, T=100, C=64, in_dtype=1, y_dtype=1, reserved=0), **kw})
+    assert W.wkv4_workspace_bytes(2, 100, 64) == 2 * 2 * 3 * 64 * 4
+    assert W.wkv4_workspace_bytes(2, 0, 64) == 0
+    assert _wkv4(None) == W.WKV7_EINVAL
+    assert _wkv4(good4(reserved=1)) == W.WKV7_EINVAL
+    assert _wkv4(good4(T=-1)) == W.WKV7_EINVAL
+    assert _wkv4(good4(in_dtype=5)) == W.WKV7_EINVAL
+    assert _wkv4(good4(C=1 << 24)) == W.WKV7_EUNSUPPORTED
+    for name in ("w", "u", "k", "v", "y"):
+        assert _wkv4(good4(), **{name: None}) == W.WKV7_EINVAL
+        assert _wkv4(good4(), **{name: FAKE + 2}) == W.WKV7_EINVAL
+    assert _wkv4(good4(), y=FAKE + 4096 * 3) == W.WKV7_EINVAL      # y aliases k
+    assert _wkv4(good4(), ws=None) == W.WKV7_EINVAL
+    assert _wkv4(good4(), ws_bytes=10) == W.WKV7_EINVAL
+    assert b"needed" in lib.wkv7_last_error()
+    assert _wkv4(good4(B=0)) == W.WKV7_OK                          # empty: no device call
