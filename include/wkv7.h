@@ -192,8 +192,9 @@ int wkv7_backward(const wkv7_desc* desc,
                   void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Workspace bytes of wkv7_backward: B H (ceil(T / 32) + 2) D^2 4 for the state
- * checkpoints and dL/dS, plus 2 B T H D 4 for grouped KV heads (H_kv < H) and
- * B H D 4 with r_k, each rounded up to 256; 0 when B H T == 0.  A negative
+ * checkpoints and dL/dS, B H ceil(T / 32) 32^2 4 for each chunk's triangular
+ * inverse, plus 2 B T H D 4 for grouped KV heads (H_kv < H) and B H D 4 with
+ * r_k, each rounded up to 256; 0 when B H T == 0.  A negative
  * wkv7_status if the descriptor is invalid.  Host only: no HIP call. */
 int64_t wkv7_backward_workspace_bytes(const wkv7_desc* desc);
 

@@ -10,7 +10,9 @@ from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -56,6 +58,27 @@ def _run(cmd):
     return r.stdout
 
 
+# Per-kernel resource remarks of the device compile (scratch bytes per lane).
+# Register spills to scratch are avoided: the compiler has placed a spill store at
+# a loop exit before the execution mask was restored, losing the value.
+RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+SCRATCH_JSON = os.path.join(BUILD, "scratch_bytes.json")
+
+
+def _scratch_of(output: str) -> dict:
+    out, name = {}, None
+    for line in output.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name:
+            out[name] = int(m.group(1))
+            name = None
+    return out
+
+
 def build(asm: bool = False, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
@@ -66,15 +89,20 @@ def build(asm: bool = False, verbose: bool = False) -> str:
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         extra = EXTRA.get(src, [])
-        jobs.append([cc, *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        remarks = RESOURCE_REMARKS if src.endswith(".hip") else []
+        jobs.append([cc, *COMMON, *extra, *remarks, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
         if asm and src.endswith(".hip"):
             jobs.append([cc, *COMMON, *extra, "-x", "hip", "--cuda-device-only", "-S",
                          os.path.join(CSRC, src), "-o",
                          os.path.join(BUILD, os.path.splitext(src)[0] + f"-{ARCH}.s")])
+    scratch = {}
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         for out in ex.map(_run, jobs):
+            scratch.update(_scratch_of(out))
             if verbose and out.strip():
-                print(out)
+                print("\n".join(l for l in out.splitlines() if "remark:" not in l))
+    with open(SCRATCH_JSON, "w") as f:
+        json.dump(scratch, f, indent=0, sort_keys=True)
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)

@@ -64,6 +64,7 @@ struct BwdArgs {
     float* drk;                            // [B, H, D] partial sums (EPI)
     float* ckpt;                           // [B H][nch + 1][D][D] states at the chunk boundaries
     float* ubuf;                           // [B H][D][D] dL/dS during the backward sweep
+    float* dinv;                           // [B H][nch][BL][BL] (I - A_ab)^-1 of every chunk
     int B, T, H, H_kv, nch;
     float y_scale;
 };
@@ -72,12 +73,20 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// This lane's position in a 16 x 16 tile: column i = lane & 15, row group q = lane >> 4.
+// The kernel hides these values from the optimiser at the top of every chunk, so
+// the LDS addresses built from them are recomputed per chunk instead of being
+// kept in registers across the whole sweep.
+struct LanePos {
+    int i, q;
+};
+
 // acc += op(A)[m0 .. m0 + 16, k0 .. k1) x op(B)[k0 .. k1, n0 .. n0 + 16) on LDS matrices.
 // TA: A is stored [k][m]; TB: B is stored [n][k].
 template <bool TA, bool TB>
 __device__ __forceinline__ f32x4 mm(const float* A, int lda, const float* B, int ldb, int m0, int n0,
-                                    int k0, int k1, f32x4 acc) {
-    const int lane = threadIdx.x & 63, i = lane & 15, q = lane >> 4;
+                                    int k0, int k1, f32x4 acc, LanePos lp) {
+    const int i = lp.i, q = lp.q;
     #pragma unroll 2
     for (int k = k0; k < k1; k += 4) {
         const float a = TA ? A[(k + q) * lda + m0 + i] : A[(m0 + i) * lda + k + q];
@@ -89,8 +98,8 @@ __device__ __forceinline__ f32x4 mm(const float* A, int lda, const float* B, int
 
 // Store a C tile to an LDS matrix [row][ld]; `keep(row, col)` masks elements to zero.
 template <typename F>
-__device__ __forceinline__ void st_tile(float* C, int ld, int m0, int n0, f32x4 acc, F keep) {
-    const int lane = threadIdx.x & 63, i = lane & 15, q = lane >> 4;
+__device__ __forceinline__ void st_tile(float* C, int ld, int m0, int n0, f32x4 acc, LanePos lp, F keep) {
+    const int i = lp.i, q = lp.q;
     #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
         const int row = m0 + 4 * q + rr, col = n0 + i;
@@ -140,9 +149,12 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     float* DBETA = BETA + BL;            // [BL] dy . v per token
     float* DRK = DBETA + BL;             // [D] r_k gradient of this (b, h)
 
-    const int tid = threadIdx.x;
+    int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, li = lane & 15, lq = lane >> 4;
+    const int lane = tid & 63;
+    LanePos lp{lane & 15, lane >> 4};
+    // Hide the thread's position from the optimiser (see LanePos).
+    auto opaque_pos = [&]() { asm volatile("" : "+v"(tid), "+v"(lp.i), "+v"(lp.q)); };
     const int bh = blockIdx.x;
     const int H = g.H, T = g.T, H_kv = g.H_kv;
     const int bb = bh / H, h = bh - bb * H, hk = h / (H / H_kv);
@@ -168,67 +180,91 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     auto valid = [&](int t_abs) { return ((vbits >> (t_abs & (BL - 1))) & 1u) != 0; };
 
     // Chunk c: g_t, the scaled key-axis operands and d.  With `with_r`, Rt and the
-    // epilogue's r k r_k as well.
+    // epilogue's r k r_k as well (the backward sweep), the stored Dinv of the chunk
+    // and d log w / d(w input) per element (fac).  Every global load of the chunk
+    // is issued before the first use.
+    constexpr int NE = BL * D / BNT;      // elements of a [BL][D] matrix per thread
+    float fac[NE];
     auto load_chunk = [&](int c, bool with_r) {
         const int c0 = c * BL;
         set_chunk_bits(c0);
-        for (int e = tid; e < BL * D; e += BNT) {
-            const int t = e / D, j = e - t * D;
+        float wv[NE], av[NE], bv[NE], kv[NE], rv[NE], dv2[2];
+        #pragma unroll
+        for (int u = 0; u < NE; ++u) {
+            const int e = tid + BNT * u, t = e / D, j = e - t * D;
+            const int tt = min(c0 + t, T - 1);   // tokens past the end read the last one (unused)
+            wv[u] = ld1(wp, qidx(tt, j));
+            av[u] = ld1(ap, qidx(tt, j));
+            bv[u] = ld1(bp, qidx(tt, j));
+            kv[u] = ld1(kp, kvidx(tt, j));
+            rv[u] = with_r ? ld1(rp, qidx(tt, j)) : 0.f;
+        }
+        if (with_r) {
+            #pragma unroll
+            for (int u = 0; u < 2; ++u) dv2[u] = g.dinv[(int64_t(bh) * g.nch + c) * BL * BL + tid + BNT * u];
+        }
+        #pragma unroll
+        for (int u = 0; u < NE; ++u) {
+            const int e = tid + BNT * u, t = e / D, j = e - t * D;
             const bool ok = valid(c0 + t);
-            float lw = 0.f;
-            if (ok) lw = log2_decay(ld1(wp, qidx(c0 + t, j)), LOGW);
-            GG[t * PD + j] = lw;
+            GG[t * PD + j] = ok ? log2_decay(wv[u], LOGW) : 0.f;
+            fac[u] = ok ? (LOGW ? -__builtin_amdgcn_exp2f(wv[u] * kLog2e) : 1.f / wv[u]) : 0.f;
+        }
+        if (with_r) {
+            #pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int e = tid + BNT * u;
+                DINV[(e / BL) * PL + (e % BL)] = dv2[u];
+            }
         }
         if (EPI && with_r && tid < BL) BETA[tid] = 0.f;
         __syncthreads();
         if (tid < D) {
+            float col[BL];
+            #pragma unroll
+            for (int t = 0; t < BL; ++t) col[t] = GG[t * PD + tid];
             float run = 0.f;
+            #pragma unroll
             for (int t = 0; t < BL; ++t) {
-                run += GG[t * PD + tid];
+                run += col[t];
                 GG[t * PD + tid] = run;
             }
             DEC[tid] = __builtin_amdgcn_exp2f(run);
         }
         __syncthreads();
-        for (int e = tid; e < BL * D; e += BNT) {
-            const int t = e / D, j = e - t * D;
+        #pragma unroll
+        for (int u = 0; u < NE; ++u) {
+            const int e = tid + BNT * u, t = e / D, j = e - t * D;
             const bool ok = valid(c0 + t);
             const float gt = GG[t * PD + j], gp = t > 0 ? GG[(t - 1) * PD + j] : 0.f;
-            float av = 0.f, bv = 0.f, kv = 0.f, rv = 0.f;
-            if (ok) {
-                av = ld1(ap, qidx(c0 + t, j));
-                bv = ld1(bp, qidx(c0 + t, j));
-                kv = ld1(kp, kvidx(c0 + t, j));
-                if (with_r) rv = ld1(rp, qidx(c0 + t, j));
-            }
             const float ep = __builtin_amdgcn_exp2f(gt), em = __builtin_amdgcn_exp2f(-gt);
-            AT[t * PD + j] = av * __builtin_amdgcn_exp2f(gp);
-            BT[t * PD + j] = bv * em;
-            KT[t * PD + j] = kv * em;
+            AT[t * PD + j] = ok ? av[u] * __builtin_amdgcn_exp2f(gp) : 0.f;
+            BT[t * PD + j] = ok ? bv[u] * em : 0.f;
+            KT[t * PD + j] = ok ? kv[u] * em : 0.f;
             if (with_r) {
-                RT[t * PD + j] = rv * ep;
+                RT[t * PD + j] = ok ? rv[u] * ep : 0.f;
                 if constexpr (EPI) {
-                    const float x = rv * kv * g.r_k[h * D + j];
-                    if (ok) atomicAdd(&BETA[t], x);
+                    if (ok) atomicAdd(&BETA[t], rv[u] * kv[u] * g.r_k[h * D + j]);
                 }
             }
         }
         __syncthreads();
     };
 
-    // L x L matrices: A_ab, A_ak (and A_rb, A_rk); then Dinv = (I - A_ab)^-1 by wave 0.
-    auto build_LL = [&](bool with_r) {
-        const int nmat = with_r ? 4 : 2;
-        for (int n = w; n < 4 * nmat; n += 8) {
-            const int mat = n >> 2, tile = n & 3, m0 = 16 * (tile >> 1), n0 = 16 * (tile & 1);
+    // L x L matrices.  Forward sweep: A_ab, A_ak and Dinv = (I - A_ab)^-1 (wave 0),
+    // stored for the backward sweep.  Backward sweep: A_ak, A_rb, A_rk (Dinv loaded).
+    auto build_LL = [&](int c, bool bwd) {
+        for (int n = w; n < (bwd ? 12 : 8); n += 8) {
+            const int mat = (n >> 2) + (bwd ? 1 : 0), tile = n & 3, m0 = 16 * (tile >> 1), n0 = 16 * (tile & 1);
             const float* A = mat < 2 ? AT : RT;
             const float* B = (mat & 1) ? KT : BT;
             float* C = mat == 0 ? AAB : mat == 1 ? AAK : mat == 2 ? ARB : ARK;
-            f32x4 acc = mm<false, true>(A, PD, B, PD, m0, n0, 0, D, kZero4);
-            if (mat < 2) st_tile(C, PL, m0, n0, acc, [](int r, int c) { return c < r; });
-            else st_tile(C, PL, m0, n0, acc, [](int r, int c) { return c <= r; });
+            f32x4 acc = mm<false, true>(A, PD, B, PD, m0, n0, 0, D, kZero4, lp);
+            if (mat < 2) st_tile(C, PL, m0, n0, acc, lp, [](int r, int c) { return c < r; });
+            else st_tile(C, PL, m0, n0, acc, lp, [](int r, int c) { return c <= r; });
         }
         __syncthreads();
+        if (bwd) return;
         if (w == 0 && lane < BL) {
             // Column `lane` of X = (I - A_ab)^-1: x_t = [t == lane] + sum_(s<t) A_ab[t][s] x_s.
             float x[BL];
@@ -239,8 +275,12 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
                 #pragma unroll
                 for (int t = s + 1; t < BL; ++t) x[t] = fmaf(AAB[t * PL + s], x[s], x[t]);
             }
+            float* dg = g.dinv + (int64_t(bh) * g.nch + c) * BL * BL;
             #pragma unroll
-            for (int t = 0; t < BL; ++t) DINV[t * PL + lane] = x[t];
+            for (int t = 0; t < BL; ++t) {
+                DINV[t * PL + lane] = x[t];
+                dg[t * BL + lane] = x[t];
+            }
         }
         __syncthreads();
     };
@@ -257,34 +297,60 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     // ------------------------------- forward sweep: checkpoints -------------------------------
     for (int e = tid; e < D * D; e += BNT) ck[e] = g.s0 ? g.s0[int64_t(bh) * D * D + e] : 0.f;
     __syncthreads();
-    for (int c = 0; c < g.nch; ++c) {
+    // A slice's rows of a D x D matrix and its [BL][32] value columns, element e = tid + BNT u.
+    constexpr int NSE = BSL * D / BNT, NVE = BL * BSL / BNT;
+    float ps0[NSE], puu[NSE], psl[NSE], pvv[NVE], pdy[NVE];   // one slice's loads, issued together
+    auto fetch_slice = [&](int c, int s, bool bwd) {
         const int c0 = c * BL;
-        const float* sc = ck + int64_t(c) * D * D;
+        const float* sc = ck + int64_t(c) * D * D + BSL * s * D;
+        #pragma unroll
+        for (int u = 0; u < NSE; ++u) {
+            const int e = tid + BNT * u;
+            ps0[u] = sc[e];
+            if (bwd) {
+                puu[u] = ub[BSL * s * D + e];
+                psl[u] = sc[D * D + e];   // the next boundary: S_L of this chunk
+            }
+        }
+        #pragma unroll
+        for (int u = 0; u < NVE; ++u) {
+            const int e = tid + BNT * u, t = e / BSL, i = e - t * BSL;
+            const int tt = min(c0 + t, T - 1);
+            pvv[u] = ld1(vp, kvidx(tt, BSL * s + i));
+            if (bwd) pdy[u] = ld1(dyp, qidx(tt, BSL * s + i));
+        }
+    };
+    for (int c = 0; c < g.nch; ++c) {
+        opaque_pos();
+        const int c0 = c * BL;
         float* sn = ck + int64_t(c + 1) * D * D;
         load_chunk(c, false);
-        build_LL(false);
+        build_LL(c, false);
         #pragma unroll 1
         for (int s = 0; s < NS; ++s) {
-            for (int e = tid; e < BSL * D; e += BNT) {
-                const int i = e / D, j = e - i * D;
-                S0S[i * PD + j] = sc[(BSL * s + i) * D + j];
+            fetch_slice(c, s, false);
+            #pragma unroll
+            for (int u = 0; u < NSE; ++u) {
+                const int e = tid + BNT * u;
+                S0S[(e / D) * PD + (e % D)] = ps0[u];
             }
-            for (int e = tid; e < BL * BSL; e += BNT) {
-                const int t = e / BSL, i = e - t * BSL;
-                VS[t * PL + i] = valid(c0 + t) ? ld1(vp, kvidx(c0 + t, BSL * s + i)) : 0.f;
+            #pragma unroll
+            for (int u = 0; u < NVE; ++u) {
+                const int e = tid + BNT * u, t = e / BSL, i = e - t * BSL;
+                VS[t * PL + i] = valid(c0 + t) ? pvv[u] : 0.f;
             }
             __syncthreads();
             if (w < 4) {   // Z = At S0s^T + A_ak Vs
                 const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);
-                f32x4 acc = mm<false, true>(AT, PD, S0S, PD, m0, n0, 0, D, kZero4);
-                acc = mm<false, false>(AAK, PL, VS, PL, m0, n0, 0, BL, acc);
-                st_tile(ZS, PL, m0, n0, acc, [](int, int) { return true; });
+                f32x4 acc = mm<false, true>(AT, PD, S0S, PD, m0, n0, 0, D, kZero4, lp);
+                acc = mm<false, false>(AAK, PL, VS, PL, m0, n0, 0, BL, acc, lp);
+                st_tile(ZS, PL, m0, n0, acc, lp, [](int, int) { return true; });
             }
             __syncthreads();
             if (w < 4) {   // SA = Dinv Z
                 const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);
-                f32x4 acc = mm<false, false>(DINV, PL, ZS, PL, m0, n0, 0, BL, kZero4);
-                st_tile(SAS, PL, m0, n0, acc, [](int, int) { return true; });
+                f32x4 acc = mm<false, false>(DINV, PL, ZS, PL, m0, n0, 0, BL, kZero4, lp);
+                st_tile(SAS, PL, m0, n0, acc, lp, [](int, int) { return true; });
             }
             __syncthreads();
             #pragma unroll
@@ -293,12 +359,12 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
                 slice_tile(u, ml, n0);
                 f32x4 acc;
                 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) acc[rr] = S0S[(ml + 4 * lq + rr) * PD + n0 + li];
-                acc = mm<true, false>(SAS, PL, BT, PD, ml, n0, 0, BL, acc);
-                acc = mm<true, false>(VS, PL, KT, PD, ml, n0, 0, BL, acc);
-                const float dc = DEC[n0 + li];
+                for (int rr = 0; rr < 4; ++rr) acc[rr] = S0S[(ml + 4 * lp.q + rr) * PD + n0 + lp.i];
+                acc = mm<true, false>(SAS, PL, BT, PD, ml, n0, 0, BL, acc, lp);
+                acc = mm<true, false>(VS, PL, KT, PD, ml, n0, 0, BL, acc, lp);
+                const float dc = DEC[n0 + lp.i];
                 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) sn[(BSL * s + ml + 4 * lq + rr) * D + n0 + li] = acc[rr] * dc;
+                for (int rr = 0; rr < 4; ++rr) sn[(BSL * s + ml + 4 * lp.q + rr) * D + n0 + lp.i] = acc[rr] * dc;
             }
             __syncthreads();
         }
@@ -309,11 +375,12 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     if (EPI && tid < D) DRK[tid] = 0.f;
     __syncthreads();
     for (int c = g.nch - 1; c >= 0; --c) {
+        opaque_pos();
         const int c0 = c * BL;
         if (tid < D) DD[tid] = 0.f;
         if (EPI && tid < BL) DBETA[tid] = 0.f;
         load_chunk(c, true);
-        build_LL(true);
+        build_LL(c, true);
 
         f32x4 accR[NA], accA[NA], accB[NA], accK[NA], accDA[2];
         #pragma unroll
@@ -324,20 +391,20 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
 
         #pragma unroll 1
         for (int s = 0; s < NS; ++s) {
+            fetch_slice(c, s, true);
             // S0 slice, dM = U diag(d), V and y_scale dy slices; diag(S_L^T U) and dy . v shares.
-            for (int e = tid; e < BSL * D; e += BNT) {
-                const int i = e / D, j = e - i * D;
-                const int o = (BSL * s + i) * D + j;
-                S0S[i * PD + j] = ck[int64_t(c) * D * D + o];
-                const float uv = ub[o];
-                DMS[i * PD + j] = uv * DEC[j];
-                atomicAdd(&DD[j], ck[int64_t(c + 1) * D * D + o] * uv);
+            #pragma unroll
+            for (int u = 0; u < NSE; ++u) {
+                const int e = tid + BNT * u, i = e / D, j = e - i * D;
+                S0S[i * PD + j] = ps0[u];
+                DMS[i * PD + j] = puu[u] * DEC[j];
+                atomicAdd(&DD[j], psl[u] * puu[u]);
             }
-            for (int e = tid; e < BL * BSL; e += BNT) {
-                const int t = e / BSL, i = e - t * BSL;
+            #pragma unroll
+            for (int u = 0; u < NVE; ++u) {
+                const int e = tid + BNT * u, t = e / BSL, i = e - t * BSL;
                 const bool ok = valid(c0 + t);
-                const float vv = ok ? ld1(vp, kvidx(c0 + t, BSL * s + i)) : 0.f;
-                const float dyv = ok ? ld1(dyp, qidx(c0 + t, BSL * s + i)) : 0.f;
+                const float vv = ok ? pvv[u] : 0.f, dyv = ok ? pdy[u] : 0.f;
                 VS[t * PL + i] = vv;
                 DYS[t * PL + i] = dyv * g.y_scale;
                 if constexpr (EPI) {
@@ -347,24 +414,24 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
             __syncthreads();
             if (w < 4) {   // Z = At S0s^T + A_ak Vs
                 const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);
-                f32x4 acc = mm<false, true>(AT, PD, S0S, PD, m0, n0, 0, D, kZero4);
-                acc = mm<false, false>(AAK, PL, VS, PL, m0, n0, 0, BL, acc);
-                st_tile(ZS, PL, m0, n0, acc, [](int, int) { return true; });
+                f32x4 acc = mm<false, true>(AT, PD, S0S, PD, m0, n0, 0, D, kZero4, lp);
+                acc = mm<false, false>(AAK, PL, VS, PL, m0, n0, 0, BL, acc, lp);
+                st_tile(ZS, PL, m0, n0, acc, lp, [](int, int) { return true; });
             } else {       // dSA = Bt dM^T + A_rb^T dY
                 const int m0 = 16 * ((w - 4) >> 1), n0 = 16 * (w & 1);
-                f32x4 acc = mm<false, true>(BT, PD, DMS, PD, m0, n0, 0, D, kZero4);
-                acc = mm<true, false>(ARB, PL, DYS, PL, m0, n0, 0, BL, acc);
-                st_tile(DSAS, PL, m0, n0, acc, [](int, int) { return true; });
+                f32x4 acc = mm<false, true>(BT, PD, DMS, PD, m0, n0, 0, D, kZero4, lp);
+                acc = mm<true, false>(ARB, PL, DYS, PL, m0, n0, 0, BL, acc, lp);
+                st_tile(DSAS, PL, m0, n0, acc, lp, [](int, int) { return true; });
             }
             __syncthreads();
             if (w < 4) {   // SA = Dinv Z
                 const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);
-                f32x4 acc = mm<false, false>(DINV, PL, ZS, PL, m0, n0, 0, BL, kZero4);
-                st_tile(SAS, PL, m0, n0, acc, [](int, int) { return true; });
+                f32x4 acc = mm<false, false>(DINV, PL, ZS, PL, m0, n0, 0, BL, kZero4, lp);
+                st_tile(SAS, PL, m0, n0, acc, lp, [](int, int) { return true; });
             } else {       // dZ = Dinv^T dSA
                 const int m0 = 16 * ((w - 4) >> 1), n0 = 16 * (w & 1);
-                f32x4 acc = mm<true, false>(DINV, PL, DSAS, PL, m0, n0, 0, BL, kZero4);
-                st_tile(DZS, PL, m0, n0, acc, [](int, int) { return true; });
+                f32x4 acc = mm<true, false>(DINV, PL, DSAS, PL, m0, n0, 0, BL, kZero4, lp);
+                st_tile(DZS, PL, m0, n0, acc, lp, [](int, int) { return true; });
             }
             __syncthreads();
             // U <- dM + dY^T Rt + dZ^T At for this slice's rows.
@@ -374,21 +441,21 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
                 slice_tile(u, ml, n0);
                 f32x4 acc;
                 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) acc[rr] = DMS[(ml + 4 * lq + rr) * PD + n0 + li];
-                acc = mm<true, false>(DYS, PL, RT, PD, ml, n0, 0, BL, acc);
-                acc = mm<true, false>(DZS, PL, AT, PD, ml, n0, 0, BL, acc);
+                for (int rr = 0; rr < 4; ++rr) acc[rr] = DMS[(ml + 4 * lp.q + rr) * PD + n0 + lp.i];
+                acc = mm<true, false>(DYS, PL, RT, PD, ml, n0, 0, BL, acc, lp);
+                acc = mm<true, false>(DZS, PL, AT, PD, ml, n0, 0, BL, acc, lp);
                 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) ub[(BSL * s + ml + 4 * lq + rr) * D + n0 + li] = acc[rr];
+                for (int rr = 0; rr < 4; ++rr) ub[(BSL * s + ml + 4 * lp.q + rr) * D + n0 + lp.i] = acc[rr];
             }
             // dV = Kt dM^T + A_rk^T dY + A_ak^T dZ (+ the epilogue's beta dy), this slice's columns.
             if (w < 4) {
                 const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);
-                f32x4 acc = mm<false, true>(KT, PD, DMS, PD, m0, n0, 0, D, kZero4);
-                acc = mm<true, false>(ARK, PL, DYS, PL, m0, n0, 0, BL, acc);
-                acc = mm<true, false>(AAK, PL, DZS, PL, m0, n0, 0, BL, acc);
+                f32x4 acc = mm<false, true>(KT, PD, DMS, PD, m0, n0, 0, D, kZero4, lp);
+                acc = mm<true, false>(ARK, PL, DYS, PL, m0, n0, 0, BL, acc, lp);
+                acc = mm<true, false>(AAK, PL, DZS, PL, m0, n0, 0, BL, acc, lp);
                 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const int t = m0 + 4 * lq + rr, i = BSL * s + n0 + li;
+                    const int t = m0 + 4 * lp.q + rr, i = BSL * s + n0 + lp.i;
                     if (c0 + t < T) {
                         float x = acc[rr];
                         if (!valid(c0 + t)) x = 0.f;
@@ -403,16 +470,16 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
                 const int tile = 2 * (w & 1) + u, m0 = 16 * (tile >> 1), n0 = 16 * (tile & 1);
                 const float* A = dmat < 2 ? DYS : DZS;
                 const float* B = (dmat & 1) ? VS : SAS;
-                accDA[u] = mm<false, true>(A, PL, B, PL, m0, n0, 0, BSL, accDA[u]);
+                accDA[u] = mm<false, true>(A, PL, B, PL, m0, n0, 0, BSL, accDA[u], lp);
             }
             // dRt += dY S0, dAt += dZ S0, dBt += SA dM, dKt += V dM.
             #pragma unroll
             for (int u = 0; u < NA; ++u) {
                 const int n = w + 8 * u, m0 = 16 * (n / TC), n0 = 16 * (n % TC);
-                accR[u] = mm<false, false>(DYS, PL, S0S, PD, m0, n0, 0, BSL, accR[u]);
-                accA[u] = mm<false, false>(DZS, PL, S0S, PD, m0, n0, 0, BSL, accA[u]);
-                accB[u] = mm<false, false>(SAS, PL, DMS, PD, m0, n0, 0, BSL, accB[u]);
-                accK[u] = mm<false, false>(VS, PL, DMS, PD, m0, n0, 0, BSL, accK[u]);
+                accR[u] = mm<false, false>(DYS, PL, S0S, PD, m0, n0, 0, BSL, accR[u], lp);
+                accA[u] = mm<false, false>(DZS, PL, S0S, PD, m0, n0, 0, BSL, accA[u], lp);
+                accB[u] = mm<false, false>(SAS, PL, DMS, PD, m0, n0, 0, BSL, accB[u], lp);
+                accK[u] = mm<false, false>(VS, PL, DMS, PD, m0, n0, 0, BSL, accK[u], lp);
             }
             __syncthreads();
         }
@@ -422,8 +489,8 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
             #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int tile = 2 * (w & 1) + u, m0 = 16 * (tile >> 1), n0 = 16 * (tile & 1);
-                if (dmat < 2) st_tile(C, PL, m0, n0, accDA[u], [](int r, int c) { return c <= r; });
-                else st_tile(C, PL, m0, n0, accDA[u], [](int r, int c) { return c < r; });
+                if (dmat < 2) st_tile(C, PL, m0, n0, accDA[u], lp, [](int r, int c) { return c <= r; });
+                else st_tile(C, PL, m0, n0, accDA[u], lp, [](int r, int c) { return c < r; });
             }
         }
         __syncthreads();
@@ -435,35 +502,28 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
             #pragma unroll
             for (int u = 0; u < NA; ++u) {
                 const int n = w + 8 * u, m0 = 16 * (n / TC), n0 = 16 * (n % TC);
-                accR[u] = mm<false, false>(DRB, PL, BT, PD, m0, n0, 0, BL, accR[u]);
-                accR[u] = mm<false, false>(DRKm, PL, KT, PD, m0, n0, 0, BL, accR[u]);
-                accA[u] = mm<false, false>(DAB, PL, BT, PD, m0, n0, 0, BL, accA[u]);
-                accA[u] = mm<false, false>(DAK, PL, KT, PD, m0, n0, 0, BL, accA[u]);
-                accB[u] = mm<true, false>(DAB, PL, AT, PD, m0, n0, 0, BL, accB[u]);
-                accB[u] = mm<true, false>(DRB, PL, RT, PD, m0, n0, 0, BL, accB[u]);
-                accK[u] = mm<true, false>(DAK, PL, AT, PD, m0, n0, 0, BL, accK[u]);
-                accK[u] = mm<true, false>(DRKm, PL, RT, PD, m0, n0, 0, BL, accK[u]);
+                accR[u] = mm<false, false>(DRB, PL, BT, PD, m0, n0, 0, BL, accR[u], lp);
+                accR[u] = mm<false, false>(DRKm, PL, KT, PD, m0, n0, 0, BL, accR[u], lp);
+                accA[u] = mm<false, false>(DAB, PL, BT, PD, m0, n0, 0, BL, accA[u], lp);
+                accA[u] = mm<false, false>(DAK, PL, KT, PD, m0, n0, 0, BL, accA[u], lp);
+                accB[u] = mm<true, false>(DAB, PL, AT, PD, m0, n0, 0, BL, accB[u], lp);
+                accB[u] = mm<true, false>(DRB, PL, RT, PD, m0, n0, 0, BL, accB[u], lp);
+                accK[u] = mm<true, false>(DAK, PL, AT, PD, m0, n0, 0, BL, accK[u], lp);
+                accK[u] = mm<true, false>(DRKm, PL, RT, PD, m0, n0, 0, BL, accK[u], lp);
             }
         }
         __syncthreads();
         // d log w / d(w input) of every kept token (0 for the others), for the suffix sums.
-        for (int e = tid; e < BL * D; e += BNT) {
-            const int t = e / D, j = e - t * D;
-            float f = 0.f;
-            if (valid(c0 + t)) {
-                const float x = ld1(wp, qidx(c0 + t, j));
-                f = LOGW ? -__builtin_amdgcn_exp2f(x * kLog2e) : 1.f / x;
-            }
-            FAC[e] = f;
-        }
+        #pragma unroll
+        for (int u = 0; u < NE; ++u) FAC[tid + BNT * u] = fac[u];
         // Gradients of r, a, b, k; the log-decay suffix-sum terms.
         #pragma unroll
         for (int u = 0; u < NA; ++u) {
             const int n = w + 8 * u, m0 = 16 * (n / TC), n0 = 16 * (n % TC);
-            const int j = n0 + li;
+            const int j = n0 + lp.i;
             #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int t = m0 + 4 * lq + rr;
+                const int t = m0 + 4 * lp.q + rr;
                 const int o = t * PD + j;
                 QP[o] = RT[o] * accR[u][rr] - BT[o] * accB[u][rr] - KT[o] * accK[u][rr];
                 QA[o] = AT[o] * accA[u][rr];
@@ -494,9 +554,13 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
         __syncthreads();
         if (tid < D) {   // dL/dlog w: suffix sums within the chunk, carried to the w input
             const int j = tid;
+            float q[BL];
+            #pragma unroll
+            for (int t = 0; t < BL; ++t) q[t] = QP[t * PD + j] + (t + 1 < BL ? QA[(t + 1) * PD + j] : 0.f);
             float run = DD[j];
+            #pragma unroll
             for (int t = BL - 1; t >= 0; --t) {
-                run += QP[t * PD + j] + (t + 1 < BL ? QA[(t + 1) * PD + j] : 0.f);
+                run += q[t];
                 if (c0 + t < T) g.dw[qidx(c0 + t, j)] = run * FAC[t * D + j];
             }
         }
@@ -540,7 +604,7 @@ __global__ __launch_bounds__(256) void batch_sum_kernel(const float* __restrict_
 }
 
 struct BwdLayout {
-    int64_t ckpt, ubuf, dkq, dvq, drk, total;
+    int64_t ckpt, ubuf, dinv, dkq, dvq, drk, total;
 };
 
 BwdLayout bwd_layout(const Params& p) {
@@ -552,6 +616,8 @@ BwdLayout bwd_layout(const Params& p) {
     int64_t off = al(bh * (nch + 1) * p.D * p.D * 4);
     o.ubuf = off;
     off += al(bh * p.D * p.D * 4);
+    o.dinv = off;
+    off += al(bh * nch * BL * BL * 4);
     const bool grouped = p.H_kv != p.H;
     o.dkq = off;
     if (grouped) off += al(int64_t(p.B) * p.T * p.H * p.D * 4);
@@ -577,6 +643,7 @@ hipError_t launch_bwd_t(const Params& p, const BwdIo& io, char* ws, hipStream_t 
     g.drk = p.r_k ? reinterpret_cast<float*>(ws + lay.drk) : nullptr;
     g.ckpt = reinterpret_cast<float*>(ws + lay.ckpt);
     g.ubuf = reinterpret_cast<float*>(ws + lay.ubuf);
+    g.dinv = reinterpret_cast<float*>(ws + lay.dinv);
     g.B = p.B; g.T = p.T; g.H = p.H; g.H_kv = p.H_kv; g.nch = (p.T + BL - 1) / BL;
     g.y_scale = p.y_scale;
     auto kern = bwd_kernel<D, Tin, Tdy, LOGW, EPI>;

@@ -202,10 +202,11 @@ def _bwd(desc, **over):
 
 def test_backward_workspace_bytes():
     # B H (ceil(T/32) + 2) D^2 4, rounded to 256, plus grouped-head and r_k terms.
-    assert W.wkv7_backward_workspace_bytes(2, 64, 4, 64) == 2 * 4 * (2 + 2) * 64 * 64 * 4
-    assert W.wkv7_backward_workspace_bytes(2, 65, 4, 64) == 2 * 4 * (3 + 2) * 64 * 64 * 4
+    dinv = lambda B, H, T: B * H * ((T + 31) // 32) * 32 * 32 * 4
+    assert W.wkv7_backward_workspace_bytes(2, 64, 4, 64) == 2 * 4 * (2 + 2) * 64 * 64 * 4 + dinv(2, 4, 64)
+    assert W.wkv7_backward_workspace_bytes(2, 65, 4, 64) == 2 * 4 * (3 + 2) * 64 * 64 * 4 + dinv(2, 4, 65)
     assert W.wkv7_backward_workspace_bytes(1, 32, 4, 128, H_kv=2) == \
-        1 * 4 * 3 * 128 * 128 * 4 + 2 * (1 * 32 * 4 * 128 * 4)
+        1 * 4 * 3 * 128 * 128 * 4 + dinv(1, 4, 32) + 2 * (1 * 32 * 4 * 128 * 4)
     assert W.wkv7_backward_workspace_bytes(2, 0, 4, 64) == 0
     assert W.wkv7_backward_workspace_bytes(0, 8, 4, 64) == 0
 
@@ -258,3 +259,19 @@ def test_wkv4_argument_rules():
     assert _wkv4(good4(), ws_bytes=10) == W.WKV7_EINVAL
     assert b"needed" in lib.wkv7_last_error()
     assert _wkv4(good4(B=0)) == W.WKV7_OK                          # empty: no device call
+
+
+def test_no_kernel_spills_to_scratch():
+    """The build records each kernel's scratch bytes per lane.  Register spills are
+    kept out of the backward, RWKV-4 and two-pass kernels: a spill store has been
+    placed at a loop exit before the execution mask was restored, dropping the
+    value.  (Known: the one-pass D = 64 chunked kernel's fp32-input epilogue
+    instances spill 32-40 bytes.)"""
+    import json
+    path = os.path.join(ROOT, "_build", "scratch_bytes.json")
+    if not os.path.exists(path):
+        pytest.skip("no build record")
+    usage = json.load(open(path))
+    assert usage, "empty build record"
+    bad = {k: v for k, v in usage.items() if v and "chunked_kernel" not in k}
+    assert not bad, f"kernels using scratch: {bad}"
