@@ -373,12 +373,21 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     // ------------------------------- backward sweep -------------------------------
     for (int e = tid; e < D * D; e += BNT) ub[e] = g.ds1 ? g.ds1[int64_t(bh) * D * D + e] : 0.f;
     if (EPI && tid < D) DRK[tid] = 0.f;
+    // r_k gradient: per-thread partials over all chunks (column j of tile w + 8 u is
+    // fixed), added to DRK once at the end.
+    float drkp[NA];
+    #pragma unroll
+    for (int u = 0; u < NA; ++u) drkp[u] = 0.f;
     __syncthreads();
     for (int c = g.nch - 1; c >= 0; --c) {
         opaque_pos();
         const int c0 = c * BL;
-        if (tid < D) DD[tid] = 0.f;
-        if (EPI && tid < BL) DBETA[tid] = 0.f;
+        // diag(S_L^T U) and dy . v: per-thread partials over the slices, reduced once per
+        // chunk (LDS atomics on a few addresses would serialise).  A thread's column
+        // j = tid mod D and its tokens t = (tid + BNT u) / 32 are the same in every slice.
+        float ddp = 0.f, dbp[NVE];
+        #pragma unroll
+        for (int u = 0; u < NVE; ++u) dbp[u] = 0.f;
         load_chunk(c, true);
         build_LL(c, true);
 
@@ -398,7 +407,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
                 const int e = tid + BNT * u, i = e / D, j = e - i * D;
                 S0S[i * PD + j] = ps0[u];
                 DMS[i * PD + j] = puu[u] * DEC[j];
-                atomicAdd(&DD[j], psl[u] * puu[u]);
+                ddp = fmaf(psl[u], puu[u], ddp);
             }
             #pragma unroll
             for (int u = 0; u < NVE; ++u) {
@@ -407,9 +416,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
                 const float vv = ok ? pvv[u] : 0.f, dyv = ok ? pdy[u] : 0.f;
                 VS[t * PL + i] = vv;
                 DYS[t * PL + i] = dyv * g.y_scale;
-                if constexpr (EPI) {
-                    if (ok) atomicAdd(&DBETA[t], dyv * vv);
-                }
+                if constexpr (EPI) dbp[u] = fmaf(dyv, vv, dbp[u]);
             }
             __syncthreads();
             if (w < 4) {   // Z = At S0s^T + A_ak Vs
@@ -483,6 +490,12 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
             }
             __syncthreads();
         }
+        // The partials to the slice buffers ZS and DSAS (free until the next chunk).
+        ZS[tid] = ddp;
+        if constexpr (EPI) {
+            #pragma unroll
+            for (int u = 0; u < NVE; ++u) DSAS[tid + BNT * u] = dbp[u];
+        }
         // dA matrices (masked) to LDS.
         {
             float* C = UN + dmat * BL * PL;
@@ -495,6 +508,23 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
         }
         __syncthreads();
         {
+            // Reduce the per-thread partials: DD[j] over the threads of column j, DBETA[t]
+            // over the 32 entries of token t (read in a rotated order to spread the banks).
+            if (tid < D) {
+                float sdd = 0.f;
+                #pragma unroll
+                for (int k = 0; k < BNT / D; ++k) sdd += ZS[tid + D * k];
+                DD[tid] = sdd;
+            }
+            if constexpr (EPI) {
+                if (tid >= D && tid < D + BL) {
+                    const int t = tid - D;
+                    float sb = 0.f;
+                    #pragma unroll
+                    for (int i = 0; i < BSL; ++i) sb += DSAS[t * BSL + ((i + t) & (BSL - 1))];
+                    DBETA[t] = sb;
+                }
+            }
             const float* DRB = UN;
             const float* DRKm = UN + BL * PL;
             const float* DAB = UN + 2 * BL * PL;
@@ -540,7 +570,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
                             const float rkj = g.r_k[h * D + j], dbt = DBETA[t];
                             dr = fmaf(dbt * kv, rkj, dr);
                             dk = fmaf(dbt * rv, rkj, dk);
-                            atomicAdd(&DRK[j], dbt * rv * kv);
+                            drkp[u] = fmaf(dbt * rv, kv, drkp[u]);
                         }
                     }
                     const int64_t gi = qidx(c0 + t, j);
@@ -570,6 +600,9 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
         for (int e = tid; e < D * D; e += BNT) g.ds0[int64_t(bh) * D * D + e] = ub[e];
     }
     if constexpr (EPI) {
+        #pragma unroll
+        for (int u = 0; u < NA; ++u) atomicAdd(&DRK[16 * ((w + 8 * u) % TC) + lp.i], drkp[u]);
+        __syncthreads();
         if (tid < D) g.drk[int64_t(bh) * D + tid] = DRK[tid];
     }
 }
