@@ -81,18 +81,23 @@ struct LanePos {
     int i, q;
 };
 
+// This lane's operands of the k-step k .. k + 4 of a product with tiles at rows m0 / columns n0.
+// TA: A is stored [k][m] (else [m][k]); TB: B is stored [n][k] (else [k][n]).
+template <bool TA>
+__device__ __forceinline__ float opA(const float* A, int lda, int m0, int k, LanePos lp) {
+    return TA ? A[(k + lp.q) * lda + m0 + lp.i] : A[(m0 + lp.i) * lda + k + lp.q];
+}
+template <bool TB>
+__device__ __forceinline__ float opB(const float* B, int ldb, int n0, int k, LanePos lp) {
+    return TB ? B[(n0 + lp.i) * ldb + k + lp.q] : B[(k + lp.q) * ldb + n0 + lp.i];
+}
+
 // acc += op(A)[m0 .. m0 + 16, k0 .. k1) x op(B)[k0 .. k1, n0 .. n0 + 16) on LDS matrices.
-// TA: A is stored [k][m]; TB: B is stored [n][k].
 template <bool TA, bool TB>
 __device__ __forceinline__ f32x4 mm(const float* A, int lda, const float* B, int ldb, int m0, int n0,
                                     int k0, int k1, f32x4 acc, LanePos lp) {
-    const int i = lp.i, q = lp.q;
     #pragma unroll 2
-    for (int k = k0; k < k1; k += 4) {
-        const float a = TA ? A[(k + q) * lda + m0 + i] : A[(m0 + i) * lda + k + q];
-        const float b = TB ? B[(n0 + i) * ldb + k + q] : B[(k + q) * ldb + n0 + i];
-        acc = mfma4(a, b, acc);
-    }
+    for (int k = k0; k < k1; k += 4) acc = mfma4(opA<TA>(A, lda, m0, k, lp), opB<TB>(B, ldb, n0, k, lp), acc);
     return acc;
 }
 
@@ -117,6 +122,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     constexpr int NU = TC / 4;           // tiles per wave of one slice: (2 row tiles x TC) / 8 waves
     constexpr int NA = (2 * TC) / 8;     // tiles per wave of one [32][D] matrix
     constexpr int UNI = (2 * BSL * PD > 4 * BL * PL) ? 2 * BSL * PD : 4 * BL * PL;
+    constexpr int FU = D == 64 ? 2 : 1;   // unroll of the fused k-loops
     static_assert(BSL == BL, "slice and chunk share the 32-wide LDS pitch");
     static_assert(BL * D <= 6 * BL * PL, "the w-derivative table fits the slice buffers");
 
@@ -441,25 +447,39 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
                 st_tile(DZS, PL, m0, n0, acc, lp, [](int, int) { return true; });
             }
             __syncthreads();
-            // U <- dM + dY^T Rt + dZ^T At for this slice's rows.
+            // U <- dM + dY^T Rt + dZ^T At for this slice's rows (the two products in
+            // independent chains, so that consecutive matrix-core ops do not wait on each other).
             #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 int ml, n0;
                 slice_tile(u, ml, n0);
-                f32x4 acc;
+                f32x4 acc, acc2 = kZero4;
                 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) acc[rr] = DMS[(ml + 4 * lp.q + rr) * PD + n0 + lp.i];
-                acc = mm<true, false>(DYS, PL, RT, PD, ml, n0, 0, BL, acc, lp);
-                acc = mm<true, false>(DZS, PL, AT, PD, ml, n0, 0, BL, acc, lp);
+                #pragma unroll FU
+                for (int k = 0; k < BL; k += 4) {
+                    acc = mfma4(opA<true>(DYS, PL, ml, k, lp), opB<false>(RT, PD, n0, k, lp), acc);
+                    acc2 = mfma4(opA<true>(DZS, PL, ml, k, lp), opB<false>(AT, PD, n0, k, lp), acc2);
+                }
                 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) ub[(BSL * s + ml + 4 * lp.q + rr) * D + n0 + lp.i] = acc[rr];
+                for (int rr = 0; rr < 4; ++rr) ub[(BSL * s + ml + 4 * lp.q + rr) * D + n0 + lp.i] = acc[rr] + acc2[rr];
             }
             // dV = Kt dM^T + A_rk^T dY + A_ak^T dZ (+ the epilogue's beta dy), this slice's columns.
             if (w < 4) {
                 const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);
-                f32x4 acc = mm<false, true>(KT, PD, DMS, PD, m0, n0, 0, D, kZero4, lp);
-                acc = mm<true, false>(ARK, PL, DYS, PL, m0, n0, 0, BL, acc, lp);
-                acc = mm<true, false>(AAK, PL, DZS, PL, m0, n0, 0, BL, acc, lp);
+                f32x4 acc = kZero4, acc2 = kZero4;
+                #pragma unroll FU
+                for (int k = 0; k < D; k += 8) {
+                    acc = mfma4(opA<false>(KT, PD, m0, k, lp), opB<true>(DMS, PD, n0, k, lp), acc);
+                    acc2 = mfma4(opA<false>(KT, PD, m0, k + 4, lp), opB<true>(DMS, PD, n0, k + 4, lp), acc2);
+                }
+                #pragma unroll FU
+                for (int k = 0; k < BL; k += 4) {
+                    acc = mfma4(opA<true>(ARK, PL, m0, k, lp), opB<false>(DYS, PL, n0, k, lp), acc);
+                    acc2 = mfma4(opA<true>(AAK, PL, m0, k, lp), opB<false>(DZS, PL, n0, k, lp), acc2);
+                }
+                #pragma unroll
+                for (int rr = 0; rr < 4; ++rr) acc[rr] += acc2[rr];
                 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const int t = m0 + 4 * lp.q + rr, i = BSL * s + n0 + lp.i;
@@ -471,22 +491,29 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
                     }
                 }
             }
-            // dA shares: tril(dY SA^T), tril(dY V^T), stril(dZ SA^T), stril(dZ V^T).
-            #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int tile = 2 * (w & 1) + u, m0 = 16 * (tile >> 1), n0 = 16 * (tile & 1);
-                const float* A = dmat < 2 ? DYS : DZS;
-                const float* B = (dmat & 1) ? VS : SAS;
-                accDA[u] = mm<false, true>(A, PL, B, PL, m0, n0, 0, BSL, accDA[u], lp);
-            }
-            // dRt += dY S0, dAt += dZ S0, dBt += SA dM, dKt += V dM.
-            #pragma unroll
-            for (int u = 0; u < NA; ++u) {
-                const int n = w + 8 * u, m0 = 16 * (n / TC), n0 = 16 * (n % TC);
-                accR[u] = mm<false, false>(DYS, PL, S0S, PD, m0, n0, 0, BSL, accR[u], lp);
-                accA[u] = mm<false, false>(DZS, PL, S0S, PD, m0, n0, 0, BSL, accA[u], lp);
-                accB[u] = mm<false, false>(SAS, PL, DMS, PD, m0, n0, 0, BSL, accB[u], lp);
-                accK[u] = mm<false, false>(VS, PL, DMS, PD, m0, n0, 0, BSL, accK[u], lp);
+            // One k-loop over the slice rows for the dA shares (tril(dY SA^T), tril(dY V^T),
+            // stril(dZ SA^T), stril(dZ V^T): matrix dmat, tiles at rows 16 (w & 1), columns 0
+            // and 16) and for dRt += dY S0, dAt += dZ S0, dBt += SA dM, dKt += V dM, so the
+            // matrix-core ops of a step are independent and share their operand reads.
+            {
+                const float* XA = dmat < 2 ? DYS : DZS;
+                const float* XB = (dmat & 1) ? VS : SAS;
+                const int ma = 16 * (w & 1);
+                #pragma unroll FU
+                for (int k = 0; k < BSL; k += 4) {
+                    const float xa = opA<false>(XA, PL, ma, k, lp);
+                    accDA[0] = mfma4(xa, opB<true>(XB, PL, 0, k, lp), accDA[0]);
+                    accDA[1] = mfma4(xa, opB<true>(XB, PL, 16, k, lp), accDA[1]);
+                    #pragma unroll
+                    for (int u = 0; u < NA; ++u) {
+                        const int n = w + 8 * u, m0 = 16 * (n / TC), n0 = 16 * (n % TC);
+                        const float s0 = opB<false>(S0S, PD, n0, k, lp), dm = opB<false>(DMS, PD, n0, k, lp);
+                        accR[u] = mfma4(opA<false>(DYS, PL, m0, k, lp), s0, accR[u]);
+                        accA[u] = mfma4(opA<false>(DZS, PL, m0, k, lp), s0, accA[u]);
+                        accB[u] = mfma4(opA<false>(SAS, PL, m0, k, lp), dm, accB[u]);
+                        accK[u] = mfma4(opA<false>(VS, PL, m0, k, lp), dm, accK[u]);
+                    }
+                }
             }
             __syncthreads();
         }
@@ -529,17 +556,36 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
             const float* DRKm = UN + BL * PL;
             const float* DAB = UN + 2 * BL * PL;
             const float* DAK = UN + 3 * BL * PL;
+            // dRt += dA_rb Bt + dA_rk Kt, dAt += dA_ab Bt + dA_ak Kt, dBt += dA_ab^T At +
+            // dA_rb^T Rt, dKt += dA_ak^T At + dA_rk^T Rt.  At D = 64 in one k-loop with four
+            // independent chains; at D = 128 the separate products measured faster.
             #pragma unroll
             for (int u = 0; u < NA; ++u) {
                 const int n = w + 8 * u, m0 = 16 * (n / TC), n0 = 16 * (n % TC);
-                accR[u] = mm<false, false>(DRB, PL, BT, PD, m0, n0, 0, BL, accR[u], lp);
-                accR[u] = mm<false, false>(DRKm, PL, KT, PD, m0, n0, 0, BL, accR[u], lp);
-                accA[u] = mm<false, false>(DAB, PL, BT, PD, m0, n0, 0, BL, accA[u], lp);
-                accA[u] = mm<false, false>(DAK, PL, KT, PD, m0, n0, 0, BL, accA[u], lp);
-                accB[u] = mm<true, false>(DAB, PL, AT, PD, m0, n0, 0, BL, accB[u], lp);
-                accB[u] = mm<true, false>(DRB, PL, RT, PD, m0, n0, 0, BL, accB[u], lp);
-                accK[u] = mm<true, false>(DAK, PL, AT, PD, m0, n0, 0, BL, accK[u], lp);
-                accK[u] = mm<true, false>(DRKm, PL, RT, PD, m0, n0, 0, BL, accK[u], lp);
+                if constexpr (D == 64) {
+                    #pragma unroll 2
+                    for (int k = 0; k < BL; k += 4) {
+                        const float bt = opB<false>(BT, PD, n0, k, lp), kt = opB<false>(KT, PD, n0, k, lp);
+                        const float at = opB<false>(AT, PD, n0, k, lp), rt = opB<false>(RT, PD, n0, k, lp);
+                        accR[u] = mfma4(opA<false>(DRB, PL, m0, k, lp), bt, accR[u]);
+                        accA[u] = mfma4(opA<false>(DAB, PL, m0, k, lp), bt, accA[u]);
+                        accB[u] = mfma4(opA<true>(DAB, PL, m0, k, lp), at, accB[u]);
+                        accK[u] = mfma4(opA<true>(DAK, PL, m0, k, lp), at, accK[u]);
+                        accR[u] = mfma4(opA<false>(DRKm, PL, m0, k, lp), kt, accR[u]);
+                        accA[u] = mfma4(opA<false>(DAK, PL, m0, k, lp), kt, accA[u]);
+                        accB[u] = mfma4(opA<true>(DRB, PL, m0, k, lp), rt, accB[u]);
+                        accK[u] = mfma4(opA<true>(DRKm, PL, m0, k, lp), rt, accK[u]);
+                    }
+                } else {
+                    accR[u] = mm<false, false>(DRB, PL, BT, PD, m0, n0, 0, BL, accR[u], lp);
+                    accR[u] = mm<false, false>(DRKm, PL, KT, PD, m0, n0, 0, BL, accR[u], lp);
+                    accA[u] = mm<false, false>(DAB, PL, BT, PD, m0, n0, 0, BL, accA[u], lp);
+                    accA[u] = mm<false, false>(DAK, PL, KT, PD, m0, n0, 0, BL, accA[u], lp);
+                    accB[u] = mm<true, false>(DAB, PL, AT, PD, m0, n0, 0, BL, accB[u], lp);
+                    accB[u] = mm<true, false>(DRB, PL, RT, PD, m0, n0, 0, BL, accB[u], lp);
+                    accK[u] = mm<true, false>(DAK, PL, AT, PD, m0, n0, 0, BL, accK[u], lp);
+                    accK[u] = mm<true, false>(DRKm, PL, RT, PD, m0, n0, 0, BL, accK[u], lp);
+                }
             }
         }
         __syncthreads();
