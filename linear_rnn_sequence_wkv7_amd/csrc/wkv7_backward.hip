@@ -114,6 +114,22 @@ __device__ __forceinline__ void st_tile(float* C, int ld, int m0, int n0, f32x4 
 
 constexpr f32x4 kZero4 = {0.f, 0.f, 0.f, 0.f};
 
+// Raw bits of one input element (a bf16 pattern zero-extended, or fp32 bits): loads
+// issued ahead of their use stay unconverted, so nothing waits for them until then.
+__device__ __forceinline__ uint32_t ld_raw(const bf16_t* p, int64_t i) { return uint32_t(p[i]); }
+__device__ __forceinline__ uint32_t ld_raw(const float* p, int64_t i) { return __float_as_uint(p[i]); }
+__device__ __forceinline__ float from_raw(uint32_t x, const bf16_t*) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float from_raw(uint32_t x, const float*) { return __uint_as_float(x); }
+
+// Sum over the 64 lanes of the wave (every lane gets it).
+__device__ __forceinline__ float wave_sum(float x) {
+    x = sum16(x);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+}
+
 template <int D, typename Tin, typename Tdy, bool LOGW, bool EPI>
 __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     constexpr int PD = D + 1;            // LDS row pitch of [*][D] matrices
@@ -124,7 +140,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     constexpr int UNI = (2 * BSL * PD > 4 * BL * PL) ? 2 * BSL * PD : 4 * BL * PL;
     constexpr int FU = D == 64 ? 2 : 1;   // unroll of the fused k-loops
     static_assert(BSL == BL, "slice and chunk share the 32-wide LDS pitch");
-    static_assert(BL * D <= 6 * BL * PL, "the w-derivative table fits the slice buffers");
+    static_assert(BL * D <= 4 * BL * PL, "the w-derivative table fits VS .. DZS (ZS holds the suffix-sum partials)");
 
     extern __shared__ __attribute__((aligned(16))) float sm[];
     float* RT = sm;
@@ -178,36 +194,52 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     const uint8_t* mrow = g.mask ? g.mask + int64_t(bb) * T : nullptr;
     // Bit t of `vbits`: token c0 + t of the current chunk is kept (in range, not masked).
     uint32_t vbits = 0;
-    auto set_chunk_bits = [&](int c0) {
+    auto set_chunk_bits = [&](int c0, uint32_t mbyte) {
         const int t = c0 + (lane & 31);
-        const bool ok = t < T && (!mrow || mrow[t] != 0);
+        const bool ok = t < T && mbyte != 0;
         vbits = uint32_t(__builtin_amdgcn_ballot_w64(ok && lane < BL));
     };
     auto valid = [&](int t_abs) { return ((vbits >> (t_abs & (BL - 1))) & 1u) != 0; };
 
     // Chunk c: g_t, the scaled key-axis operands and d.  With `with_r`, Rt and the
     // epilogue's r k r_k as well (the backward sweep), the stored Dinv of the chunk
-    // and d log w / d(w input) per element (fac).  Every global load of the chunk
-    // is issued before the first use.
+    // and d log w / d(w input) per element (fac).  issue_chunk issues all of the
+    // chunk's global loads (raw, into registers); load_chunk then consumes them.
+    // (Issuing them one chunk ahead measured no faster: the issue cost about what
+    // the hidden latency saved.)
     constexpr int NE = BL * D / BNT;      // elements of a [BL][D] matrix per thread
     float fac[NE];
-    auto load_chunk = [&](int c, bool with_r) {
+    uint32_t wr[NE], ar[NE], br[NE], kr[NE], rr_[NE], mraw;
+    float dv2[2];
+    auto issue_chunk = [&](int c, bool with_r) {
         const int c0 = c * BL;
-        set_chunk_bits(c0);
-        float wv[NE], av[NE], bv[NE], kv[NE], rv[NE], dv2[2];
+        mraw = mrow ? uint32_t(mrow[min(c0 + (lane & 31), T - 1)]) : 1u;
         #pragma unroll
         for (int u = 0; u < NE; ++u) {
             const int e = tid + BNT * u, t = e / D, j = e - t * D;
             const int tt = min(c0 + t, T - 1);   // tokens past the end read the last one (unused)
-            wv[u] = ld1(wp, qidx(tt, j));
-            av[u] = ld1(ap, qidx(tt, j));
-            bv[u] = ld1(bp, qidx(tt, j));
-            kv[u] = ld1(kp, kvidx(tt, j));
-            rv[u] = with_r ? ld1(rp, qidx(tt, j)) : 0.f;
+            wr[u] = ld_raw(wp, qidx(tt, j));
+            ar[u] = ld_raw(ap, qidx(tt, j));
+            br[u] = ld_raw(bp, qidx(tt, j));
+            kr[u] = ld_raw(kp, kvidx(tt, j));
+            if (with_r) rr_[u] = ld_raw(rp, qidx(tt, j));
         }
         if (with_r) {
             #pragma unroll
             for (int u = 0; u < 2; ++u) dv2[u] = g.dinv[(int64_t(bh) * g.nch + c) * BL * BL + tid + BNT * u];
+        }
+    };
+    auto load_chunk = [&](int c, bool with_r) {
+        const int c0 = c * BL;
+        set_chunk_bits(c0, mraw);
+        float wv[NE], av[NE], bv[NE], kv[NE], rv[NE];
+        #pragma unroll
+        for (int u = 0; u < NE; ++u) {
+            wv[u] = from_raw(wr[u], wp);
+            av[u] = from_raw(ar[u], ap);
+            bv[u] = from_raw(br[u], bp);
+            kv[u] = from_raw(kr[u], kp);
+            rv[u] = with_r ? from_raw(rr_[u], rp) : 0.f;
         }
         #pragma unroll
         for (int u = 0; u < NE; ++u) {
@@ -250,7 +282,9 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
             if (with_r) {
                 RT[t * PD + j] = ok ? rv[u] * ep : 0.f;
                 if constexpr (EPI) {
-                    if (ok) atomicAdd(&BETA[t], rv[u] * kv[u] * g.r_k[h * D + j]);
+                    // The wave's 64 lanes share the token t: one add per wave.
+                    const float x = wave_sum(ok ? rv[u] * kv[u] * g.r_k[h * D + j] : 0.f);
+                    if (lane == 0) atomicAdd(&BETA[t], x);
                 }
             }
         }
@@ -305,7 +339,8 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     __syncthreads();
     // A slice's rows of a D x D matrix and its [BL][32] value columns, element e = tid + BNT u.
     constexpr int NSE = BSL * D / BNT, NVE = BL * BSL / BNT;
-    float ps0[NSE], puu[NSE], psl[NSE], pvv[NVE], pdy[NVE];   // one slice's loads, issued together
+    float ps0[NSE], puu[NSE], psl[NSE];   // one slice's loads, issued together
+    uint32_t pvv[NVE], pdy[NVE];          // (raw: converted where used)
     auto fetch_slice = [&](int c, int s, bool bwd) {
         const int c0 = c * BL;
         const float* sc = ck + int64_t(c) * D * D + BSL * s * D;
@@ -322,14 +357,15 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
         for (int u = 0; u < NVE; ++u) {
             const int e = tid + BNT * u, t = e / BSL, i = e - t * BSL;
             const int tt = min(c0 + t, T - 1);
-            pvv[u] = ld1(vp, kvidx(tt, BSL * s + i));
-            if (bwd) pdy[u] = ld1(dyp, qidx(tt, BSL * s + i));
+            pvv[u] = ld_raw(vp, kvidx(tt, BSL * s + i));
+            if (bwd) pdy[u] = ld_raw(dyp, qidx(tt, BSL * s + i));
         }
     };
     for (int c = 0; c < g.nch; ++c) {
         opaque_pos();
         const int c0 = c * BL;
         float* sn = ck + int64_t(c + 1) * D * D;
+        issue_chunk(c, false);
         load_chunk(c, false);
         build_LL(c, false);
         #pragma unroll 1
@@ -343,7 +379,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
             #pragma unroll
             for (int u = 0; u < NVE; ++u) {
                 const int e = tid + BNT * u, t = e / BSL, i = e - t * BSL;
-                VS[t * PL + i] = valid(c0 + t) ? pvv[u] : 0.f;
+                VS[t * PL + i] = valid(c0 + t) ? from_raw(pvv[u], vp) : 0.f;
             }
             __syncthreads();
             if (w < 4) {   // Z = At S0s^T + A_ak Vs
@@ -394,6 +430,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
         float ddp = 0.f, dbp[NVE];
         #pragma unroll
         for (int u = 0; u < NVE; ++u) dbp[u] = 0.f;
+        issue_chunk(c, true);
         load_chunk(c, true);
         build_LL(c, true);
 
@@ -419,7 +456,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
             for (int u = 0; u < NVE; ++u) {
                 const int e = tid + BNT * u, t = e / BSL, i = e - t * BSL;
                 const bool ok = valid(c0 + t);
-                const float vv = ok ? pvv[u] : 0.f, dyv = ok ? pdy[u] : 0.f;
+                const float vv = ok ? from_raw(pvv[u], vp) : 0.f, dyv = ok ? from_raw(pdy[u], dyp) : 0.f;
                 VS[t * PL + i] = vv;
                 DYS[t * PL + i] = dyv * g.y_scale;
                 if constexpr (EPI) dbp[u] = fmaf(dyv, vv, dbp[u]);
@@ -628,16 +665,27 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
             }
         }
         __syncthreads();
-        if (tid < D) {   // dL/dlog w: suffix sums within the chunk, carried to the w input
-            const int j = tid;
-            float q[BL];
+        {   // dL/dlog w: suffix sums within the chunk, carried to the w input.  Thread
+            // (seg, j) takes tokens [SEG seg, SEG seg + SEG) of column j: the segment sums
+            // go through LDS (ZS), then each thread adds the later segments' sums.
+            constexpr int NSEG = BNT / D, SEG = BL / NSEG;
+            const int j = tid % D, seg = tid / D, t0 = SEG * seg;
+            float q[SEG], part = 0.f;
             #pragma unroll
-            for (int t = 0; t < BL; ++t) q[t] = QP[t * PD + j] + (t + 1 < BL ? QA[(t + 1) * PD + j] : 0.f);
+            for (int t = 0; t < SEG; ++t) {
+                const int tt = t0 + t;
+                q[t] = QP[tt * PD + j] + (tt + 1 < BL ? QA[(tt + 1) * PD + j] : 0.f);
+                part += q[t];
+            }
+            ZS[seg * D + j] = part;
+            __syncthreads();
             float run = DD[j];
+            for (int s2 = seg + 1; s2 < NSEG; ++s2) run += ZS[s2 * D + j];
             #pragma unroll
-            for (int t = BL - 1; t >= 0; --t) {
+            for (int t = SEG - 1; t >= 0; --t) {
                 run += q[t];
-                if (c0 + t < T) g.dw[qidx(c0 + t, j)] = run * FAC[t * D + j];
+                const int tt = t0 + t;
+                if (c0 + tt < T) g.dw[qidx(c0 + tt, j)] = run * FAC[tt * D + j];
             }
         }
         __syncthreads();
