@@ -191,10 +191,13 @@ int wkv7_backward(const wkv7_desc* desc,
                   float* dstate_in, float* dr_k,
                   void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Workspace bytes of wkv7_backward: B H (ceil(T / 32) + 2) D^2 4 for the state
- * checkpoints and dL/dS, B H ceil(T / 32) 32^2 4 for each chunk's triangular
- * inverse, plus 2 B T H D 4 for grouped KV heads (H_kv < H) and B H D 4 with
- * r_k, each rounded up to 256; 0 when B H T == 0.  A negative
+/* Workspace bytes of wkv7_backward.  With P the number of value-slice groups
+ * per (b, h) (the largest power of two with P <= D / 32 and B H P <= 256; each
+ * group is one workgroup), the parts are: B H (ceil(T / 32) + 1) D^2 4 for the
+ * state checkpoints, B H D^2 4 for dL/dS, P B H ceil(T / 32) 32^2 4 for each
+ * chunk's triangular inverse, 2 B T H D 4 for grouped KV heads (H_kv < H),
+ * P B H D 4 with r_k, and (P - 1) 5 B T H D 4 for the key-axis gradients of
+ * groups 1 .. P - 1; each rounded up to 256.  0 when B H T == 0.  A negative
  * wkv7_status if the descriptor is invalid.  Host only: no HIP call. */
 int64_t wkv7_backward_workspace_bytes(const wkv7_desc* desc);
 

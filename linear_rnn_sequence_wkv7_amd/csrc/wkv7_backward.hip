@@ -64,8 +64,11 @@ struct BwdArgs {
     float* drk;                            // [B, H, D] partial sums (EPI)
     float* ckpt;                           // [B H][nch + 1][D][D] states at the chunk boundaries
     float* ubuf;                           // [B H][D][D] dL/dS during the backward sweep
-    float* dinv;                           // [B H][nch][BL][BL] (I - A_ab)^-1 of every chunk
+    float* dinv;                           // [P][B H][nch][BL][BL] (I - A_ab)^-1 of every chunk
+    float* part;                           // [P - 1][5][B T H D] key-axis gradients of groups 1 ..
+    int64_t nq;                            // B T H D
     int B, T, H, H_kv, nch;
+    int split;                             // P: value-slice groups (workgroups) per (b, h)
     float y_scale;
 };
 
@@ -178,6 +181,20 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     // Hide the thread's position from the optimiser (see LanePos).
     auto opaque_pos = [&]() { asm volatile("" : "+v"(tid), "+v"(lp.i), "+v"(lp.q)); };
     const int bh = blockIdx.x;
+    // Value-slice group sg of P = g.split: slices [s_begin, s_end) of this (b, h).  The
+    // rows of S, U, dS0 and the columns of dV split with no overlap; the key-axis
+    // gradients are this group's share (group 0 writes the outputs, the others their
+    // slots in g.part, summed afterwards).
+    const int sg = blockIdx.y;
+    const int s_begin = sg * (NS / g.split), s_end = s_begin + NS / g.split;
+    const int e_begin = s_begin * BSL * D, e_end = s_end * BSL * D;   // this group's state elements
+    const int64_t BH = int64_t(g.B) * g.H;
+    float* const o_dr = sg == 0 ? g.dr : g.part + (int64_t(sg - 1) * 5 + 0) * g.nq;
+    float* const o_da = sg == 0 ? g.da : g.part + (int64_t(sg - 1) * 5 + 1) * g.nq;
+    float* const o_db = sg == 0 ? g.db : g.part + (int64_t(sg - 1) * 5 + 2) * g.nq;
+    float* const o_dk = sg == 0 ? g.dk : g.part + (int64_t(sg - 1) * 5 + 3) * g.nq;
+    float* const o_dw = sg == 0 ? g.dw : g.part + (int64_t(sg - 1) * 5 + 4) * g.nq;
+    float* const dinv_g = g.dinv + (int64_t(sg) * BH + bh) * g.nch * BL * BL;
     const int H = g.H, T = g.T, H_kv = g.H_kv;
     const int bb = bh / H, h = bh - bb * H, hk = h / (H / H_kv);
     const Tin* rp = static_cast<const Tin*>(g.r);
@@ -226,7 +243,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
         }
         if (with_r) {
             #pragma unroll
-            for (int u = 0; u < 2; ++u) dv2[u] = g.dinv[(int64_t(bh) * g.nch + c) * BL * BL + tid + BNT * u];
+            for (int u = 0; u < 2; ++u) dv2[u] = dinv_g[int64_t(c) * BL * BL + tid + BNT * u];
         }
     };
     auto load_chunk = [&](int c, bool with_r) {
@@ -315,7 +332,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
                 #pragma unroll
                 for (int t = s + 1; t < BL; ++t) x[t] = fmaf(AAB[t * PL + s], x[s], x[t]);
             }
-            float* dg = g.dinv + (int64_t(bh) * g.nch + c) * BL * BL;
+            float* dg = dinv_g + int64_t(c) * BL * BL;
             #pragma unroll
             for (int t = 0; t < BL; ++t) {
                 DINV[t * PL + lane] = x[t];
@@ -335,7 +352,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     float* ub = g.ubuf + int64_t(bh) * D * D;   // U = dL/dS of the backward sweep
 
     // ------------------------------- forward sweep: checkpoints -------------------------------
-    for (int e = tid; e < D * D; e += BNT) ck[e] = g.s0 ? g.s0[int64_t(bh) * D * D + e] : 0.f;
+    for (int e = e_begin + tid; e < e_end; e += BNT) ck[e] = g.s0 ? g.s0[int64_t(bh) * D * D + e] : 0.f;
     __syncthreads();
     // A slice's rows of a D x D matrix and its [BL][32] value columns, element e = tid + BNT u.
     constexpr int NSE = BSL * D / BNT, NVE = BL * BSL / BNT;
@@ -369,7 +386,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
         load_chunk(c, false);
         build_LL(c, false);
         #pragma unroll 1
-        for (int s = 0; s < NS; ++s) {
+        for (int s = s_begin; s < s_end; ++s) {
             fetch_slice(c, s, false);
             #pragma unroll
             for (int u = 0; u < NSE; ++u) {
@@ -413,7 +430,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     }
 
     // ------------------------------- backward sweep -------------------------------
-    for (int e = tid; e < D * D; e += BNT) ub[e] = g.ds1 ? g.ds1[int64_t(bh) * D * D + e] : 0.f;
+    for (int e = e_begin + tid; e < e_end; e += BNT) ub[e] = g.ds1 ? g.ds1[int64_t(bh) * D * D + e] : 0.f;
     if (EPI && tid < D) DRK[tid] = 0.f;
     // r_k gradient: per-thread partials over all chunks (column j of tile w + 8 u is
     // fixed), added to DRK once at the end.
@@ -442,7 +459,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
         const int dmat = w >> 1;
 
         #pragma unroll 1
-        for (int s = 0; s < NS; ++s) {
+        for (int s = s_begin; s < s_end; ++s) {
             fetch_slice(c, s, true);
             // S0 slice, dM = U diag(d), V and y_scale dy slices; diag(S_L^T U) and dy . v shares.
             #pragma unroll
@@ -657,10 +674,10 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
                         }
                     }
                     const int64_t gi = qidx(c0 + t, j);
-                    g.dr[gi] = ok ? dr : 0.f;
-                    g.da[gi] = ok ? da : 0.f;
-                    g.db[gi] = ok ? db : 0.f;
-                    g.dk[gi] = ok ? dk : 0.f;
+                    o_dr[gi] = ok ? dr : 0.f;
+                    o_da[gi] = ok ? da : 0.f;
+                    o_db[gi] = ok ? db : 0.f;
+                    o_dk[gi] = ok ? dk : 0.f;
                 }
             }
         }
@@ -685,19 +702,19 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
             for (int t = SEG - 1; t >= 0; --t) {
                 run += q[t];
                 const int tt = t0 + t;
-                if (c0 + tt < T) g.dw[qidx(c0 + tt, j)] = run * FAC[tt * D + j];
+                if (c0 + tt < T) o_dw[qidx(c0 + tt, j)] = run * FAC[tt * D + j];
             }
         }
         __syncthreads();
     }
     if (g.ds0) {
-        for (int e = tid; e < D * D; e += BNT) g.ds0[int64_t(bh) * D * D + e] = ub[e];
+        for (int e = e_begin + tid; e < e_end; e += BNT) g.ds0[int64_t(bh) * D * D + e] = ub[e];
     }
     if constexpr (EPI) {
         #pragma unroll
         for (int u = 0; u < NA; ++u) atomicAdd(&DRK[16 * ((w + 8 * u) % TC) + lp.i], drkp[u]);
         __syncthreads();
-        if (tid < D) g.drk[int64_t(bh) * D + tid] = DRK[tid];
+        if (tid < D) g.drk[(int64_t(sg) * BH + bh) * D + tid] = DRK[tid];
     }
 }
 
@@ -730,28 +747,56 @@ __global__ __launch_bounds__(256) void batch_sum_kernel(const float* __restrict_
     }
 }
 
-struct BwdLayout {
-    int64_t ckpt, ubuf, dinv, dkq, dvq, drk, total;
+// Key-axis gradients of value-slice groups 1 .. P - 1 added to group 0's, in group order.
+struct PartSum {
+    float* out[5];   // dr, da, db, dk (per query head), dw
 };
+__global__ __launch_bounds__(256) void part_sum_kernel(PartSum o, const float* __restrict__ part, int64_t nq,
+                                                       int P) {
+    float* dst = o.out[blockIdx.y];
+    for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < nq; e += int64_t(gridDim.x) * 256) {
+        float acc = dst[e];
+        for (int sg = 1; sg < P; ++sg) acc += part[(int64_t(sg - 1) * 5 + blockIdx.y) * nq + e];
+        dst[e] = acc;
+    }
+}
+
+struct BwdLayout {
+    int64_t ckpt, ubuf, dinv, dkq, dvq, drk, part, total;
+    int split;
+};
+
+// Value-slice groups per (b, h): enough workgroups for the chip's 256 compute units
+// when B H is small, at most one per 32-row slice, a power of two.
+int bwd_split(const Params& p) {
+    const int64_t bh = int64_t(p.B) * p.H;
+    int P = 1;
+    while (2 * P <= p.D / BSL && bh * 2 * P <= 256) P *= 2;
+    return P;
+}
 
 BwdLayout bwd_layout(const Params& p) {
     auto al = [](int64_t x) { return (x + 255) & ~int64_t(255); };
     const int nch = (p.T + BL - 1) / BL;
     BwdLayout o{};
     const int64_t bh = int64_t(p.B) * p.H;
+    o.split = bwd_split(p);
     o.ckpt = 0;
     int64_t off = al(bh * (nch + 1) * p.D * p.D * 4);
     o.ubuf = off;
     off += al(bh * p.D * p.D * 4);
     o.dinv = off;
-    off += al(bh * nch * BL * BL * 4);
+    off += al(o.split * bh * nch * BL * BL * 4);
     const bool grouped = p.H_kv != p.H;
+    const int64_t nq = int64_t(p.B) * p.T * p.H * p.D;
     o.dkq = off;
-    if (grouped) off += al(int64_t(p.B) * p.T * p.H * p.D * 4);
+    if (grouped) off += al(nq * 4);
     o.dvq = off;
-    if (grouped) off += al(int64_t(p.B) * p.T * p.H * p.D * 4);
+    if (grouped) off += al(nq * 4);
     o.drk = off;
-    if (p.r_k) off += al(bh * p.D * 4);
+    if (p.r_k) off += al(o.split * bh * p.D * 4);
+    o.part = off;
+    off += al((o.split - 1) * 5 * nq * 4);
     o.total = off;
     return o;
 }
@@ -771,7 +816,10 @@ hipError_t launch_bwd_t(const Params& p, const BwdIo& io, char* ws, hipStream_t 
     g.ckpt = reinterpret_cast<float*>(ws + lay.ckpt);
     g.ubuf = reinterpret_cast<float*>(ws + lay.ubuf);
     g.dinv = reinterpret_cast<float*>(ws + lay.dinv);
+    g.part = reinterpret_cast<float*>(ws + lay.part);
+    g.nq = int64_t(p.B) * p.T * p.H * D;
     g.B = p.B; g.T = p.T; g.H = p.H; g.H_kv = p.H_kv; g.nch = (p.T + BL - 1) / BL;
+    g.split = lay.split;
     g.y_scale = p.y_scale;
     auto kern = bwd_kernel<D, Tin, Tdy, LOGW, EPI>;
     constexpr int smem = bwd_smem_bytes<D>();
@@ -782,9 +830,16 @@ hipError_t launch_bwd_t(const Params& p, const BwdIo& io, char* ws, hipStream_t 
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3(unsigned(p.B) * unsigned(p.H)), dim3(BNT), smem, stream, g);
+    hipLaunchKernelGGL(kern, dim3(unsigned(p.B) * unsigned(p.H), unsigned(lay.split)), dim3(BNT), smem, stream, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (lay.split > 1) {
+        const PartSum o{{g.dr, g.da, g.db, g.dk, g.dw}};
+        const int64_t blocks = (g.nq + 255) / 256;
+        hipLaunchKernelGGL(part_sum_kernel, dim3(unsigned(blocks < 16384 ? blocks : 16384), 5), dim3(256), 0,
+                           stream, o, g.part, g.nq, lay.split);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (grouped) {
         const int64_t n_out = int64_t(p.B) * p.T * p.H_kv * D;
         const int64_t blocks = (n_out + 255) / 256;
@@ -796,7 +851,7 @@ hipError_t launch_bwd_t(const Params& p, const BwdIo& io, char* ws, hipStream_t 
     if (p.r_k) {
         const int HD = p.H * D;
         hipLaunchKernelGGL(batch_sum_kernel, dim3(unsigned((HD + 255) / 256)), dim3(256), 0, stream,
-                           g.drk, io.drk, p.B, HD);
+                           g.drk, io.drk, p.B * lay.split, HD);
         e = hipGetLastError();
     }
     return e;

@@ -201,12 +201,31 @@ def _bwd(desc, **over):
 
 
 def test_backward_workspace_bytes():
-    # B H (ceil(T/32) + 2) D^2 4, rounded to 256, plus grouped-head and r_k terms.
-    dinv = lambda B, H, T: B * H * ((T + 31) // 32) * 32 * 32 * 4
-    assert W.wkv7_backward_workspace_bytes(2, 64, 4, 64) == 2 * 4 * (2 + 2) * 64 * 64 * 4 + dinv(2, 4, 64)
-    assert W.wkv7_backward_workspace_bytes(2, 65, 4, 64) == 2 * 4 * (3 + 2) * 64 * 64 * 4 + dinv(2, 4, 65)
-    assert W.wkv7_backward_workspace_bytes(1, 32, 4, 128, H_kv=2) == \
-        1 * 4 * 3 * 128 * 128 * 4 + dinv(1, 4, 32) + 2 * (1 * 32 * 4 * 128 * 4)
+    # Checkpoints, dL/dS, triangular inverses per value-slice group, grouped-head
+    # buffers, r_k partials and the key-axis gradients of groups 1 .. P - 1.
+    al = lambda x: (x + 255) // 256 * 256
+
+    def groups(B, H, D):
+        P = 1
+        while 2 * P <= D // 32 and B * H * 2 * P <= 256:
+            P *= 2
+        return P
+
+    def expect(B, T, H, D, H_kv=None, r_k=False):
+        H_kv = H if H_kv is None else H_kv
+        nch, P, nq = (T + 31) // 32, groups(B, H, D), B * T * H * D
+        n = al(B * H * (nch + 1) * D * D * 4) + al(B * H * D * D * 4) + al(P * B * H * nch * 32 * 32 * 4)
+        if H_kv != H:
+            n += 2 * al(nq * 4)
+        if r_k:
+            n += al(P * B * H * D * 4)
+        return n + al((P - 1) * 5 * nq * 4)
+
+    assert groups(2, 4, 64) == 2 and groups(2, 32, 128) == 4 and groups(8, 32, 64) == 1 and groups(1, 200, 128) == 1
+    assert W.wkv7_backward_workspace_bytes(2, 64, 4, 64) == expect(2, 64, 4, 64)
+    assert W.wkv7_backward_workspace_bytes(2, 65, 4, 64) == expect(2, 65, 4, 64)
+    assert W.wkv7_backward_workspace_bytes(1, 32, 4, 128, H_kv=2) == expect(1, 32, 4, 128, H_kv=2)
+    assert W.wkv7_backward_workspace_bytes(8, 1024, 32, 64) == expect(8, 1024, 32, 64)
     assert W.wkv7_backward_workspace_bytes(2, 0, 4, 64) == 0
     assert W.wkv7_backward_workspace_bytes(0, 8, 4, 64) == 0
 
