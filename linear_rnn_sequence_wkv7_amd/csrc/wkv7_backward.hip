@@ -124,14 +124,33 @@ __device__ __forceinline__ uint32_t ld_raw(const float* p, int64_t i) { return _
 __device__ __forceinline__ float from_raw(uint32_t x, const bf16_t*) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float from_raw(uint32_t x, const float*) { return __uint_as_float(x); }
 
-// Sum over the 64 lanes of the wave (every lane gets it).
-__device__ __forceinline__ float wave_sum(float x) {
-    x = sum16(x);
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
-           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16)) +
-           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)) +
-           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+// N consecutive input elements starting at p (N * sizeof(T) a multiple of 8 bytes and
+// p aligned to it) as raw 32-bit words: bf16 pairs packed, fp32 one per word.
+template <int N, typename T>
+__device__ __forceinline__ void ld_vec_raw(const T* p, uint32_t* o) {
+    constexpr int NW = N * int(sizeof(T)) / 4;
+    static_assert(NW % 2 == 0, "whole 8-byte loads");
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    if constexpr (NW % 4 == 0) {
+        #pragma unroll
+        for (int i = 0; i < NW; i += 4) {
+            const uint4 x = *reinterpret_cast<const uint4*>(q + i);
+            o[i] = x.x; o[i + 1] = x.y; o[i + 2] = x.z; o[i + 3] = x.w;
+        }
+    } else {
+        #pragma unroll
+        for (int i = 0; i < NW; i += 2) {
+            const uint2 x = *reinterpret_cast<const uint2*>(q + i);
+            o[i] = x.x; o[i + 1] = x.y;
+        }
+    }
 }
+// Element e of such a word array.
+__device__ __forceinline__ float vec_elem(const uint32_t* o, int e, const bf16_t*) {
+    const uint32_t x = o[e >> 1];
+    return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
+}
+__device__ __forceinline__ float vec_elem(const uint32_t* o, int e, const float*) { return __uint_as_float(o[e]); }
 
 template <int D, typename Tin, typename Tdy, bool LOGW, bool EPI>
 __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
@@ -222,87 +241,79 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     // epilogue's r k r_k as well (the backward sweep), the stored Dinv of the chunk
     // and d log w / d(w input) per element (fac).  issue_chunk issues all of the
     // chunk's global loads (raw, into registers); load_chunk then consumes them.
-    // (Issuing them one chunk ahead measured no faster: the issue cost about what
-    // the hidden latency saved.)
+    // Thread tid takes NE consecutive elements of one token row: t = tid / 16,
+    // j0 = NE (tid mod 16), one vector load per input.  (Issuing the loads one
+    // chunk ahead measured no faster: the issue cost about what the hidden latency
+    // saved.)
     constexpr int NE = BL * D / BNT;      // elements of a [BL][D] matrix per thread
+    constexpr int NW = NE * int(sizeof(Tin)) / 4;
+    static_assert(D / NE == 16, "16 threads per token row");
+    const int et = tid >> 4, ej0 = NE * (tid & 15);
     float fac[NE];
-    uint32_t wr[NE], ar[NE], br[NE], kr[NE], rr_[NE], mraw;
-    float dv2[2];
+    uint32_t wr[NW], ar[NW], br[NW], kr[NW], rr_[NW], mraw;
+    float2 dv2;
     auto issue_chunk = [&](int c, bool with_r) {
         const int c0 = c * BL;
         mraw = mrow ? uint32_t(mrow[min(c0 + (lane & 31), T - 1)]) : 1u;
-        #pragma unroll
-        for (int u = 0; u < NE; ++u) {
-            const int e = tid + BNT * u, t = e / D, j = e - t * D;
-            const int tt = min(c0 + t, T - 1);   // tokens past the end read the last one (unused)
-            wr[u] = ld_raw(wp, qidx(tt, j));
-            ar[u] = ld_raw(ap, qidx(tt, j));
-            br[u] = ld_raw(bp, qidx(tt, j));
-            kr[u] = ld_raw(kp, kvidx(tt, j));
-            if (with_r) rr_[u] = ld_raw(rp, qidx(tt, j));
-        }
+        const int tt = min(c0 + et, T - 1);   // tokens past the end read the last one (unused)
+        ld_vec_raw<NE>(wp + qidx(tt, ej0), wr);
+        ld_vec_raw<NE>(ap + qidx(tt, ej0), ar);
+        ld_vec_raw<NE>(bp + qidx(tt, ej0), br);
+        ld_vec_raw<NE>(kp + kvidx(tt, ej0), kr);
         if (with_r) {
-            #pragma unroll
-            for (int u = 0; u < 2; ++u) dv2[u] = dinv_g[int64_t(c) * BL * BL + tid + BNT * u];
+            ld_vec_raw<NE>(rp + qidx(tt, ej0), rr_);
+            dv2 = *reinterpret_cast<const float2*>(dinv_g + int64_t(c) * BL * BL + 2 * tid);
         }
     };
     auto load_chunk = [&](int c, bool with_r) {
         const int c0 = c * BL;
         set_chunk_bits(c0, mraw);
-        float wv[NE], av[NE], bv[NE], kv[NE], rv[NE];
+        const int t = et, o0 = t * PD + ej0;
+        const bool ok = valid(c0 + t);
         #pragma unroll
-        for (int u = 0; u < NE; ++u) {
-            wv[u] = from_raw(wr[u], wp);
-            av[u] = from_raw(ar[u], ap);
-            bv[u] = from_raw(br[u], bp);
-            kv[u] = from_raw(kr[u], kp);
-            rv[u] = with_r ? from_raw(rr_[u], rp) : 0.f;
+        for (int q = 0; q < NE; ++q) {
+            const float wv = vec_elem(wr, q, wp);
+            GG[o0 + q] = ok ? log2_decay(wv, LOGW) : 0.f;
+            fac[q] = ok ? (LOGW ? -__builtin_amdgcn_exp2f(wv * kLog2e) : 1.f / wv) : 0.f;
         }
-        #pragma unroll
-        for (int u = 0; u < NE; ++u) {
-            const int e = tid + BNT * u, t = e / D, j = e - t * D;
-            const bool ok = valid(c0 + t);
-            GG[t * PD + j] = ok ? log2_decay(wv[u], LOGW) : 0.f;
-            fac[u] = ok ? (LOGW ? -__builtin_amdgcn_exp2f(wv[u] * kLog2e) : 1.f / wv[u]) : 0.f;
+        if (with_r) {   // Dinv row 2 tid / 32, columns 2 tid mod 32 and the next
+            DINV[(tid >> 4) * PL + 2 * (tid & 15)] = dv2.x;
+            DINV[(tid >> 4) * PL + 2 * (tid & 15) + 1] = dv2.y;
         }
-        if (with_r) {
-            #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int e = tid + BNT * u;
-                DINV[(e / BL) * PL + (e % BL)] = dv2[u];
-            }
-        }
-        if (EPI && with_r && tid < BL) BETA[tid] = 0.f;
         __syncthreads();
         if (tid < D) {
             float col[BL];
             #pragma unroll
-            for (int t = 0; t < BL; ++t) col[t] = GG[t * PD + tid];
+            for (int tq = 0; tq < BL; ++tq) col[tq] = GG[tq * PD + tid];
             float run = 0.f;
             #pragma unroll
-            for (int t = 0; t < BL; ++t) {
-                run += col[t];
-                GG[t * PD + tid] = run;
+            for (int tq = 0; tq < BL; ++tq) {
+                run += col[tq];
+                GG[tq * PD + tid] = run;
             }
             DEC[tid] = __builtin_amdgcn_exp2f(run);
         }
         __syncthreads();
+        float rkk = 0.f;   // this thread's share of r . (k r_k) for token t
         #pragma unroll
-        for (int u = 0; u < NE; ++u) {
-            const int e = tid + BNT * u, t = e / D, j = e - t * D;
-            const bool ok = valid(c0 + t);
-            const float gt = GG[t * PD + j], gp = t > 0 ? GG[(t - 1) * PD + j] : 0.f;
+        for (int q = 0; q < NE; ++q) {
+            const int o = o0 + q;
+            const float gt = GG[o], gp = t > 0 ? GG[o - PD] : 0.f;
             const float ep = __builtin_amdgcn_exp2f(gt), em = __builtin_amdgcn_exp2f(-gt);
-            AT[t * PD + j] = ok ? av[u] * __builtin_amdgcn_exp2f(gp) : 0.f;
-            BT[t * PD + j] = ok ? bv[u] * em : 0.f;
-            KT[t * PD + j] = ok ? kv[u] * em : 0.f;
+            const float kv = vec_elem(kr, q, kp);
+            AT[o] = ok ? vec_elem(ar, q, ap) * __builtin_amdgcn_exp2f(gp) : 0.f;
+            BT[o] = ok ? vec_elem(br, q, bp) * em : 0.f;
+            KT[o] = ok ? kv * em : 0.f;
             if (with_r) {
-                RT[t * PD + j] = ok ? rv[u] * ep : 0.f;
-                if constexpr (EPI) {
-                    // The wave's 64 lanes share the token t: one add per wave.
-                    const float x = wave_sum(ok ? rv[u] * kv[u] * g.r_k[h * D + j] : 0.f);
-                    if (lane == 0) atomicAdd(&BETA[t], x);
-                }
+                const float rv = vec_elem(rr_, q, rp);
+                RT[o] = ok ? rv * ep : 0.f;
+                if constexpr (EPI) rkk = fmaf(rv * kv, g.r_k[h * D + ej0 + q], rkk);
+            }
+        }
+        if constexpr (EPI) {
+            if (with_r) {   // the row's 16 threads are an aligned group of 16 lanes
+                rkk = sum16(rkk);
+                if ((tid & 15) == 0) BETA[t] = ok ? rkk : 0.f;
             }
         }
         __syncthreads();
@@ -645,7 +656,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
         __syncthreads();
         // d log w / d(w input) of every kept token (0 for the others), for the suffix sums.
         #pragma unroll
-        for (int u = 0; u < NE; ++u) FAC[tid + BNT * u] = fac[u];
+        for (int q = 0; q < NE; ++q) FAC[et * D + ej0 + q] = fac[q];
         // Gradients of r, a, b, k; the log-decay suffix-sum terms.
         #pragma unroll
         for (int u = 0; u < NA; ++u) {
