@@ -333,21 +333,37 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
         }
         __syncthreads();
         if (bwd) return;
-        if (w == 0 && lane < BL) {
-            // Column `lane` of X = (I - A_ab)^-1: x_t = [t == lane] + sum_(s<t) A_ab[t][s] x_s.
-            float x[BL];
-            #pragma unroll
-            for (int t = 0; t < BL; ++t) x[t] = t == lane ? 1.f : 0.f;
-            #pragma unroll
-            for (int s = 0; s < BL; ++s) {
+        if (w == 0) {
+            // X = (I - A_ab)^-1 in 16 x 16 blocks.  The diagonal blocks by forward
+            // substitution, both at once (lanes 0-15: columns of X11, lanes 16-31: of
+            // X22): x_t = [t == col] + sum_(s<t) A_ab[t][s] x_s within the block.  Then
+            // X21 = X22 A21 X11 on the matrix cores (the block of I - A_ab below the
+            // diagonal is -A21); X12 = 0.
+            if (lane < BL) {
+                const int r0 = 16 * (lane >> 4), col = lane & 15;
+                float x[16];
                 #pragma unroll
-                for (int t = s + 1; t < BL; ++t) x[t] = fmaf(AAB[t * PL + s], x[s], x[t]);
+                for (int t = 0; t < 16; ++t) x[t] = t == col ? 1.f : 0.f;
+                #pragma unroll
+                for (int s2 = 0; s2 < 16; ++s2) {
+                    #pragma unroll
+                    for (int t = s2 + 1; t < 16; ++t) x[t] = fmaf(AAB[(r0 + t) * PL + r0 + s2], x[s2], x[t]);
+                }
+                #pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    DINV[(r0 + t) * PL + r0 + col] = x[t];
+                    if (r0 == 0) DINV[t * PL + 16 + col] = 0.f;   // X12 (by the X11 lanes)
+                }
             }
-            float* dg = dinv_g + int64_t(c) * BL * BL;
-            #pragma unroll
-            for (int t = 0; t < BL; ++t) {
-                DINV[t * PL + lane] = x[t];
-                dg[t * BL + lane] = x[t];
+            // One wave: its LDS accesses take effect in order, no barrier needed.
+            const f32x4 tmp = mm<false, false>(AAB, PL, DINV, PL, 16, 0, 0, 16, kZero4, lp);   // A21 X11
+            st_tile(DINV, PL, 16, 0, tmp, lp, [](int, int) { return true; });
+            const f32x4 x21 = mm<false, false>(DINV, PL, DINV, PL, 16, 0, 16, 32, kZero4, lp);   // X22 (A21 X11)
+            st_tile(DINV, PL, 16, 0, x21, lp, [](int, int) { return true; });
+            if (lane < BL) {
+                float* dg = dinv_g + int64_t(c) * BL * BL;
+                #pragma unroll
+                for (int t = 0; t < BL; ++t) dg[t * BL + lane] = DINV[t * PL + lane];
             }
         }
         __syncthreads();
