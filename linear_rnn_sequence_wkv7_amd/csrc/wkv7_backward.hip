@@ -778,12 +778,21 @@ __global__ __launch_bounds__(256) void batch_sum_kernel(const float* __restrict_
 struct PartSum {
     float* out[5];   // dr, da, db, dk (per query head), dw
 };
+// Four elements per thread (nq is a multiple of 4, every array 16-byte aligned).
 __global__ __launch_bounds__(256) void part_sum_kernel(PartSum o, const float* __restrict__ part, int64_t nq,
                                                        int P) {
-    float* dst = o.out[blockIdx.y];
-    for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < nq; e += int64_t(gridDim.x) * 256) {
-        float acc = dst[e];
-        for (int sg = 1; sg < P; ++sg) acc += part[(int64_t(sg - 1) * 5 + blockIdx.y) * nq + e];
+    float4* dst = reinterpret_cast<float4*>(o.out[blockIdx.y]);
+    const float4* src = reinterpret_cast<const float4*>(part);
+    const int64_t n4 = nq / 4;
+    for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < n4; e += int64_t(gridDim.x) * 256) {
+        float4 acc = dst[e];
+        for (int sg = 1; sg < P; ++sg) {
+            const float4 x = src[(int64_t(sg - 1) * 5 + blockIdx.y) * n4 + e];
+            acc.x += x.x;
+            acc.y += x.y;
+            acc.z += x.z;
+            acc.w += x.w;
+        }
         dst[e] = acc;
     }
 }
@@ -862,8 +871,8 @@ hipError_t launch_bwd_t(const Params& p, const BwdIo& io, char* ws, hipStream_t 
     if (e != hipSuccess) return e;
     if (lay.split > 1) {
         const PartSum o{{g.dr, g.da, g.db, g.dk, g.dw}};
-        const int64_t blocks = (g.nq + 255) / 256;
-        hipLaunchKernelGGL(part_sum_kernel, dim3(unsigned(blocks < 16384 ? blocks : 16384), 5), dim3(256), 0,
+        const int64_t blocks = (g.nq / 4 + 255) / 256;
+        hipLaunchKernelGGL(part_sum_kernel, dim3(unsigned(blocks < 8192 ? blocks : 8192), 5), dim3(256), 0,
                            stream, o, g.part, g.nq, lay.split);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
