@@ -103,7 +103,8 @@ constexpr int OFF_BONUS = OFF_EL + 256;    // fp32 [64] hxa07D bonus coefficient
 constexpr int OFF_XS = OFF_BONUS + 256;    // state halves exchanged by the two waves of a strip
 constexpr int XS_BYTES = 4 * 2 * 2 * 64 * 16;   // [strip][half][hi/lo][lane] 16 B
 constexpr int OFF_TOT = OFF_XS + XS_BYTES; // fp32 [8][64] column-segment totals (own slot: written during P5)
-constexpr int OFF_VTL = OFF_TOT + 8 * 64 * 4; // V^T lo part (fp32 inputs only)
+constexpr int OFF_RK = OFF_TOT + 8 * 64 * 4;  // fp32 [64] r_k of this head (epilogue)
+constexpr int OFF_VTL = OFF_RK + 64 * 4;      // V^T lo part (fp32 inputs only)
 constexpr int SMEM_BF16 = OFF_VTL;
 constexpr int SMEM_F32 = OFF_VTL + MAT;
 static_assert(2 * 64 * PE * 4 <= 4 * MAT, "decay tables fit");
@@ -282,17 +283,20 @@ void chunked_kernel(ChunkArgs g) {
     // Row threads (P1b): token tr = tid / 8, key columns [8 qr, 8 qr + 8).
     const int jc = l, pc = w;
     const int tr = tid >> 3, qr = tid & 7;
-    float rk8[8];
+    // The epilogue's r_k row goes to LDS (read where used: in registers for the
+    // whole kernel it would push the fp32-input variants past the register file).
     if constexpr (EPI) {
-        #pragma unroll
-        for (int e = 0; e < 8; ++e) rk8[e] = g.r_k[h * DH + 8 * qr + e];
+        if (tid < DH) reinterpret_cast<float*>(smem + OFF_RK)[tid] = g.r_k[h * DH + tid];
     }
     // Chunk-relative byte offsets (the descriptors move with the chunk), kept as
-    // per-lane values in VGPRs: the column threads' 8 tokens, the row threads'
-    // token, and the 4 x 2 y elements of a lane.
-    uint32_t col_q[8], col_kv[8], y_off[2][4];
+    // per-lane values in VGPRs: the column threads' 8 tokens (fp32 inputs, whose
+    // rows take twice the registers, keep the first and add the token stride at
+    // each load), the row threads' token, and the first of each 4-token group of
+    // a lane's y elements (the others added where stored).
+    constexpr int NCO = VSPLIT ? 1 : 8;
+    uint32_t col_q[NCO], col_kv[NCO], y_off[2];
     #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < NCO; ++e) {
         col_q[e] = uint32_t(8 * pc + e) * stq + uint32_t(h * DH + jc) * SI;
         col_kv[e] = uint32_t(8 * pc + e) * stkv + uint32_t(hk * DH + jc) * SI;
         asm volatile("" : "+v"(col_q[e]));
@@ -300,11 +304,8 @@ void chunked_kernel(ChunkArgs g) {
     }
     #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            y_off[u][r] = uint32_t(16 * ytile(hf, u) + 4 * lq + r) * sty + uint32_t(h * DH + i_row) * SY;
-            asm volatile("" : "+v"(y_off[u][r]));
-        }
+        y_off[u] = uint32_t(16 * ytile(hf, u) + 4 * lq) * sty + uint32_t(h * DH + i_row) * SY;
+        asm volatile("" : "+v"(y_off[u]));
     }
     const uint32_t row_q = uint32_t(tr) * stq + uint32_t(h * DH + 8 * qr) * SI;
     const uint32_t row_kv = uint32_t(tr) * stkv + uint32_t(hk * DH + 8 * qr) * SI;
@@ -325,12 +326,28 @@ void chunked_kernel(ChunkArgs g) {
         const rsrc_t Rw = chunk_rsrc(c0, wp, stq), Rb = chunk_rsrc(c0, bp, stq);
         const rsrc_t Rk = chunk_rsrc(c0, kp, stkv), Rv = chunk_rsrc(c0, vp, stkv);
         if constexpr (MASK) cm = __builtin_amdgcn_raw_buffer_load_b8(chunk_rsrc(c0, mp, 1u), uint32_t(8 * pc + (l & 7)), 0, 0);
+        uint32_t oq[8], okv[8];
+        if constexpr (VSPLIT) {
+            uint32_t q0 = col_q[0], kv0 = col_kv[0];
+            asm volatile("" : "+v"(q0), "+v"(kv0));   // formed here, not kept per token
+            #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                oq[e] = q0 + uint32_t(e) * stq;
+                okv[e] = kv0 + uint32_t(e) * stkv;
+            }
+        } else {
+            #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                oq[e] = col_q[e];
+                okv[e] = col_kv[e];
+            }
+        }
         #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            cw[e] = Buf<Tin>::load1(Rw, col_q[e]);
-            cb[e] = Buf<Tin>::load1(Rb, col_q[e]);
-            ck[e] = Buf<Tin>::load1(Rk, col_kv[e]);
-            cv[e] = Buf<Tin>::load1(Rv, col_kv[e]);
+            cw[e] = Buf<Tin>::load1(Rw, oq[e]);
+            cb[e] = Buf<Tin>::load1(Rb, oq[e]);
+            ck[e] = Buf<Tin>::load1(Rk, okv[e]);
+            cv[e] = Buf<Tin>::load1(Rv, okv[e]);
         }
     };
     auto load_rows = [&](int c0) {
@@ -476,6 +493,12 @@ void chunked_kernel(ChunkArgs g) {
             }
             uint32_t at[4], rth[4], rtl[4], bt[4], kth[4], ktl[4];
             float bonus_part = 0.f;
+            float rk8[8];
+            if constexpr (EPI) {
+                const float4 q0 = lds<float4>(smem + OFF_RK, 32 * qr), q1 = lds<float4>(smem + OFF_RK, 32 * qr + 16);
+                rk8[0] = q0.x; rk8[1] = q0.y; rk8[2] = q0.z; rk8[3] = q0.w;
+                rk8[4] = q1.x; rk8[5] = q1.y; rk8[6] = q1.z; rk8[7] = q1.w;
+            }
             #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 const float r0 = rr.get(e), r1 = rr.get(e + 1);
@@ -772,11 +795,13 @@ void chunked_kernel(ChunkArgs g) {
                         const float4 bq = lds<float4>(smem + OFF_BONUS, tl0 * 4);
                         bon[0] = bq.x; bon[1] = bq.y; bon[2] = bq.z; bon[3] = bq.w;
                     }
+                    uint32_t yo = y_off[u];
+                    asm volatile("" : "+v"(yo));   // formed here, not kept per element for the whole loop
                     #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         float yv = acc[r] * g.y_scale;
                         if constexpr (EPI) yv = fmaf(bon[r], vtr[r], yv);
-                        Buf<Ty>::store1(Ry, y_off[u][r], yv);
+                        Buf<Ty>::store1(Ry, yo + uint32_t(r) * sty, yv);
                     }
                 }
             };

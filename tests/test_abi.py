@@ -281,16 +281,14 @@ def test_wkv4_argument_rules():
 
 
 def test_no_kernel_spills_to_scratch():
-    """The build records each kernel's scratch bytes per lane.  Register spills are
-    kept out of the backward, RWKV-4 and two-pass kernels: a spill store has been
-    placed at a loop exit before the execution mask was restored, dropping the
-    value.  (Known: the one-pass D = 64 chunked kernel's fp32-input epilogue
-    instances spill 32-40 bytes.)"""
+    """The build records each kernel's scratch bytes per lane: no kernel may spill
+    registers.  (A spill store has been placed at a loop exit before the
+    execution mask was restored, dropping the value.)"""
     import json
     path = os.path.join(ROOT, "_build", "scratch_bytes.json")
     if not os.path.exists(path):
         pytest.skip("no build record")
     usage = json.load(open(path))
     assert usage, "empty build record"
-    bad = {k: v for k, v in usage.items() if v and "chunked_kernel" not in k}
+    bad = {k: v for k, v in usage.items() if v}
     assert not bad, f"kernels using scratch: {bad}"
