@@ -104,10 +104,15 @@ def test_backward_deterministic():
     gi = G.make_grad_inputs(wl)
     g1 = run_bwd(wl, x, gi)
     g2 = run_bwd(wl, x, gi)
-    # LDS float atomics sum in a varying order: equal to rounding, not bit for bit.
+    # Every sum runs in a fixed order (value-slice groups added in group order),
+    # except dr_k's per-thread partials, added to LDS by atomics: equal to rounding.
     for n in g1:
-        if g1[n] is not None:
+        if g1[n] is None:
+            continue
+        if n == "r_k":
             P.check(f"repeat d{n}", g1[n], g2[n], 1e-5)
+        else:
+            np.testing.assert_array_equal(g1[n], g2[n], err_msg=f"repeat d{n}")
 
 
 def _bwd_pairs(x, gi, wl, pairs):
