@@ -39,8 +39,11 @@ typedef struct wkv4_desc {
     int32_t reserved;   /* must be 0 */
 } wkv4_desc;
 
-/* Workspace bytes of wkv4_forward: B * ceil(T / 64) * 3 * C * 4 (the per-chunk
- * states); a negative wkv7_status if the descriptor is invalid.  Host only. */
+/* Workspace bytes of wkv4_forward: 2 * B * ceil(T / 64) * 3 * C * 4 (each
+ * 64-token chunk's local and inclusive states) rounded up to 256, plus 256 for
+ * a ticket counter; 0 when B T C == 0; a negative wkv7_status if the descriptor
+ * is invalid.  Host only.  Calls that share a workspace must be ordered (same
+ * stream). */
 int64_t wkv4_workspace_bytes(const wkv4_desc* desc);
 
 /* y <- wkv over T tokens from state_in (or zero); state_out (may be NULL) gets

@@ -12,14 +12,26 @@
 // from scaled terms that never exceed 1.
 //
 // The recurrence is linear in (a, b) with a scalar decay per channel, so it
-// runs chunk-parallel in three launches over chunks of 64 tokens:
-//   1. every (b, chunk, c) reduces its chunk from a zero state (local state);
-//   2. one thread per (b, c) scans the chunks: incoming state of chunk j =
-//      the previous incoming state decayed by the chunk length, merged with the
-//      previous chunk's local state; the last merge is the final state;
-//   3. every (b, chunk, c) reruns its chunk from its incoming state and writes y.
-// Inputs are read twice (steps 1 and 3), y once; one thread per channel, so
-// each wave's loads of a token row are 64 consecutive channels.
+// runs chunk-parallel over chunks of 64 tokens in a single pass with a
+// look-back: every workgroup takes one (batch, chunk, 256-channel block),
+// loads its k and v once into registers and
+//   1. reduces its chunk from a zero state and publishes that local state;
+//   2. per channel, walks back over the preceding chunks: one that has
+//      published its inclusive state (everything up to its end) ends the walk,
+//      one that has only published its local state is merged in and the walk
+//      goes on; the merged sum, decayed to this chunk's start (plus state_in
+//      when the walk passes the first chunk), is the incoming state;
+//   3. publishes its inclusive state and reruns its chunk from the incoming
+//      state, writing y from the registers.
+// k and v are read once, y written once.  No fences: every published value is
+// written and read with a device-scope atomic (kept out of the XCD-private L2
+// caches) and is ready when it no longer holds the not-ready pattern that a
+// first small kernel writes over the whole state area; a release/acquire pair
+// per chunk would write back or invalidate an XCD's whole L2 each time.
+// Workgroups take their chunk from a ticket counter in the order they start,
+// chunk-major, so a thread only waits for chunks whose workgroups are already
+// running; each wait is also bounded.  One thread per channel, so each wave's
+// loads of a token row are 64 consecutive channels.
 #include "wkv7_internal.h"
 #include "wkv7_device.h"
 
@@ -37,7 +49,8 @@ struct Wkv4Args {
     void* y;             // [B, T, C]
     const float* s0;     // [B, 3, C] (A, B, P natural-log units) or null
     float* s1;           // [B, 3, C] or null
-    float* ws;           // [B, nch, 3, C]
+    float* ws;           // [B, nch, 3, C] local states, then the inclusive ones likewise
+    int* ticket;         // chunk ticket counter
     int B, T, C, nch;
 };
 
@@ -82,108 +95,74 @@ __device__ __forceinline__ void load_chunk_row(const Tin* p, int64_t elem0, int 
     for (int i = 0; i < CL; ++i) out[i] = buf_ld(r, uint32_t((i * C + c) * int(sizeof(Tin))), p);
 }
 
-// Step 1: local state of chunk j from zero.
-template <typename Tin>
-__global__ __launch_bounds__(NT4) void wkv4_local_kernel(Wkv4Args g) {
-    const int c = blockIdx.x * NT4 + threadIdx.x;
-    const int j = blockIdx.y, bb = blockIdx.z;
+// With no tokens: the final state is the initial state (or the zero state).
+__global__ __launch_bounds__(NT4) void wkv4_copy_state_kernel(Wkv4Args g) {
+    const int c = blockIdx.x * NT4 + threadIdx.x, bb = blockIdx.y;
     if (c >= g.C) return;
-    const int t0 = j * CL, n = min(CL, g.T - t0);
-    const Tin* kp = static_cast<const Tin*>(g.k);
-    const Tin* vp = static_cast<const Tin*>(g.v);
-    const int64_t elem0 = (int64_t(bb) * g.T + t0) * g.C;
-    const float w2 = g.w[c] * kLog2e;
-    float kk[CL], vv[CL];
-    load_chunk_row(kp, elem0, n, g.C, c, kk);
-    load_chunk_row(vp, elem0, n, g.C, c, vv);
-    Scaled s{0.f, 0.f, kNegBig};
-    auto step = [&](int i) {
-        s.P -= w2;
-        s = add_term(s, kk[i] * kLog2e, vv[i]);
-    };
-    if (n == CL) {
-        #pragma unroll
-        for (int i = 0; i < CL; ++i) step(i);
-    } else {
-        #pragma unroll
-        for (int i = 0; i < CL; ++i)
-            if (i < n) step(i);
-    }
-    float* o = g.ws + ((int64_t(bb) * g.nch + j) * 3) * g.C + c;
-    o[0] = s.A;
-    o[g.C] = s.Bd;
-    o[2 * g.C] = s.P;
-}
-
-// Step 2: incoming state of every chunk (in place of its local state); the final state.
-__global__ __launch_bounds__(NT4) void wkv4_scan_kernel(Wkv4Args g) {
-    const int c = blockIdx.x * NT4 + threadIdx.x;
-    const int bb = blockIdx.y;
-    if (c >= g.C) return;
-    const float w2 = g.w[c] * kLog2e;
-    Scaled cur{0.f, 0.f, kNegBig};
+    float* s1 = g.s1 + int64_t(bb) * 3 * g.C + c;
     if (g.s0) {
-        const float* s = g.s0 + int64_t(bb) * 3 * g.C + c;
-        cur = Scaled{s[0], s[g.C], s[2 * g.C] * kLog2e};
-    }
-    // Chunks in groups of 16: the group's local states are loaded before the
-    // first merge, so the loads overlap instead of forming a chain.
-    constexpr int G = 16;
-    for (int j0 = 0; j0 < g.nch; j0 += G) {
-        Scaled loc[G];
-        #pragma unroll
-        for (int q = 0; q < G; ++q) {
-            const int j = min(j0 + q, g.nch - 1);
-            const float* o = g.ws + ((int64_t(bb) * g.nch + j) * 3) * g.C + c;
-            loc[q] = Scaled{o[0], o[g.C], o[2 * g.C]};
-        }
-        #pragma unroll
-        for (int q = 0; q < G; ++q) {
-            const int j = j0 + q;
-            if (j < g.nch) {
-                float* o = g.ws + ((int64_t(bb) * g.nch + j) * 3) * g.C + c;
-                o[0] = cur.A;
-                o[g.C] = cur.Bd;
-                o[2 * g.C] = cur.P;
-                const int n = min(CL, g.T - j * CL);
-                cur.P -= w2 * float(n);
-                cur = merge(cur, loc[q]);
-            }
-        }
-    }
-    if (g.s1) {
-        float* s = g.s1 + int64_t(bb) * 3 * g.C + c;
-        s[0] = cur.A;
-        s[g.C] = cur.Bd;
-        s[2 * g.C] = cur.P * (1.f / kLog2e);
+        const float* s0 = g.s0 + int64_t(bb) * 3 * g.C + c;
+        const float A = s0[0], Bd = s0[g.C], P = s0[2 * g.C];
+        s1[0] = A;
+        s1[g.C] = Bd;
+        s1[2 * g.C] = P;
+    } else {
+        s1[0] = 0.f;
+        s1[g.C] = 0.f;
+        s1[2 * g.C] = kNegBig * (1.f / kLog2e);
     }
 }
 
-// Step 3: outputs of chunk j from its incoming state.
+constexpr uint32_t kNotReady = 0x7fbadbadu;   // a NaN pattern the arithmetic here does not produce
+constexpr int kSpinMax = 1 << 18;              // bound of one wait (tens of ms)
+
+// Mark every state not ready and reset the ticket counter.
+__global__ __launch_bounds__(256) void wkv4_reset_kernel(uint32_t* __restrict__ st, int64_t n, int* ticket) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0;
+    for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < n; e += int64_t(gridDim.x) * 256)
+        st[e] = kNotReady;
+}
+
+__device__ __forceinline__ void publish(float* p, int C, Scaled s) {
+    __hip_atomic_store(p, s.A, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p + C, s.Bd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p + 2 * C, s.P, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool ready_read(const float* p, int C, Scaled& s) {
+    s.A = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s.Bd = __hip_atomic_load(p + C, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s.P = __hip_atomic_load(p + 2 * C, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __float_as_uint(s.A) != kNotReady && __float_as_uint(s.Bd) != kNotReady &&
+           __float_as_uint(s.P) != kNotReady;
+}
+
 template <typename Tin, typename Ty>
-__global__ __launch_bounds__(NT4) void wkv4_out_kernel(Wkv4Args g) {
-    const int c = blockIdx.x * NT4 + threadIdx.x;
-    const int j = blockIdx.y, bb = blockIdx.z;
-    if (c >= g.C) return;
+__global__ __launch_bounds__(NT4) void wkv4_onepass_kernel(Wkv4Args g) {
+    __shared__ int s_ticket;
+    const int tid = threadIdx.x;
+    if (tid == 0) s_ticket = atomicAdd(g.ticket, 1);
+    __syncthreads();
+    const int ncb = (g.C + NT4 - 1) / NT4;
+    const int per_j = ncb * g.B;
+    const int j = s_ticket / per_j, rem = s_ticket - j * per_j;
+    const int bb = rem / ncb, cb = rem - bb * ncb;
+    const int c = cb * NT4 + tid;
+    if (c >= g.C) return;   // no barrier below
     const int t0 = j * CL, n = min(CL, g.T - t0);
     const Tin* kp = static_cast<const Tin*>(g.k);
     const Tin* vp = static_cast<const Tin*>(g.v);
     Ty* yp = static_cast<Ty*>(g.y);
     const int64_t elem0 = (int64_t(bb) * g.T + t0) * g.C;
-    const int64_t base = elem0 + c;
     const float w2 = g.w[c] * kLog2e, u2 = g.u[c] * kLog2e;
     float kk[CL], vv[CL];
     load_chunk_row(kp, elem0, n, g.C, c, kk);
     load_chunk_row(vp, elem0, n, g.C, c, vv);
-    const float* o = g.ws + ((int64_t(bb) * g.nch + j) * 3) * g.C + c;
-    Scaled s{o[0], o[g.C], o[2 * g.C]};
+
+    // 1. Local state, published.
+    Scaled loc{0.f, 0.f, kNegBig};
     auto step = [&](int i) {
-        const float x = kk[i] * kLog2e;
-        // wkv = (a + e^{u+k} v) / (b + e^{u+k}) from the state before this token.
-        const Scaled q = add_term(s, u2 + x, vv[i]);
-        st1(yp, base + int64_t(i) * g.C, q.A * __builtin_amdgcn_rcpf(q.Bd));
-        s.P -= w2;
-        s = add_term(s, x, vv[i]);
+        loc.P -= w2;
+        loc = add_term(loc, kk[i] * kLog2e, vv[i]);
     };
     if (n == CL) {
         #pragma unroll
@@ -193,33 +172,99 @@ __global__ __launch_bounds__(NT4) void wkv4_out_kernel(Wkv4Args g) {
         for (int i = 0; i < CL; ++i)
             if (i < n) step(i);
     }
+    float* const loc_ws = g.ws + c;
+    float* const inc_ws = g.ws + int64_t(g.B) * g.nch * 3 * g.C + c;
+    auto row = [&](int k) { return (int64_t(bb) * g.nch + k) * 3 * g.C; };
+    publish(loc_ws + row(j), g.C, loc);
+
+    // 2. Look back: the incoming state at the start of chunk j (the end of chunk j - 1).
+    Scaled in{0.f, 0.f, kNegBig};
+    bool complete = false;   // an inclusive state was reached
+    for (int k = j - 1; k >= 0 && !complete; --k) {
+        Scaled x;
+        for (int it = 0;; ++it) {
+            if (ready_read(inc_ws + row(k), g.C, x)) {
+                complete = true;
+                break;
+            }
+            if (ready_read(loc_ws + row(k), g.C, x)) break;
+            if (it == kSpinMax) {   // bounded: give up (the result is then wrong, not hung)
+                complete = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        x.P -= w2 * float((j - 1 - k) * CL);   // full chunks k + 1 .. j - 1 lie in between
+        in = merge(x, in);
+    }
+    if (!complete && g.s0) {
+        const float* s0 = g.s0 + int64_t(bb) * 3 * g.C + c;
+        Scaled x{s0[0], s0[g.C], s0[2 * g.C] * kLog2e};
+        x.P -= w2 * float(t0);
+        in = merge(x, in);
+    }
+
+    // 3. Inclusive state, published; then the outputs from the incoming state.
+    Scaled inc = in;
+    inc.P -= w2 * float(n);
+    inc = merge(inc, loc);
+    publish(inc_ws + row(j), g.C, inc);
+    if (j == g.nch - 1 && g.s1) {
+        float* s1 = g.s1 + int64_t(bb) * 3 * g.C + c;
+        s1[0] = inc.A;
+        s1[g.C] = inc.Bd;
+        s1[2 * g.C] = inc.P * (1.f / kLog2e);
+    }
+    const int64_t base = elem0 + c;
+    Scaled st = in;
+    auto out = [&](int i) {
+        const float x = kk[i] * kLog2e;
+        // wkv = (a + e^{u+k} v) / (b + e^{u+k}) from the state before this token.
+        const Scaled q = add_term(st, u2 + x, vv[i]);
+        st1(yp, base + int64_t(i) * g.C, q.A * __builtin_amdgcn_rcpf(q.Bd));
+        st.P -= w2;
+        st = add_term(st, x, vv[i]);
+    };
+    if (n == CL) {
+        #pragma unroll
+        for (int i = 0; i < CL; ++i) out(i);
+    } else {
+        #pragma unroll
+        for (int i = 0; i < CL; ++i)
+            if (i < n) out(i);
+    }
 }
 
 template <typename Tin, typename Ty>
 hipError_t launch_t(const Wkv4Args& g, hipStream_t stream) {
-    const dim3 blk(NT4);
-    const unsigned cb = unsigned((g.C + NT4 - 1) / NT4);
-    hipLaunchKernelGGL(wkv4_local_kernel<Tin>, dim3(cb, unsigned(g.nch), unsigned(g.B)), blk, 0, stream, g);
-    hipLaunchKernelGGL(wkv4_scan_kernel, dim3(cb, unsigned(g.B)), blk, 0, stream, g);
-    hipLaunchKernelGGL((wkv4_out_kernel<Tin, Ty>), dim3(cb, unsigned(g.nch), unsigned(g.B)), blk, 0, stream, g);
+    const int64_t ncb = (g.C + NT4 - 1) / NT4;
+    const int64_t nst = 2 * int64_t(g.B) * g.nch * 3 * g.C;
+    const int64_t rb = (nst + 255) / 256;
+    hipLaunchKernelGGL(wkv4_reset_kernel, dim3(unsigned(rb < 8192 ? rb : 8192)), dim3(256), 0, stream,
+                       reinterpret_cast<uint32_t*>(g.ws), nst, g.ticket);
+    hipLaunchKernelGGL((wkv4_onepass_kernel<Tin, Ty>), dim3(unsigned(ncb * g.nch * g.B)), dim3(NT4), 0, stream, g);
     return hipGetLastError();
 }
 
 }  // namespace
 
+// Layout: local states [B][nch][3][C], inclusive states likewise, then the ticket
+// counter (256 bytes); 0 when there is nothing to compute.
 int64_t wkv4_workspace_bytes_internal(int B, int T, int C) {
     const int64_t nch = (int64_t(T) + CL - 1) / CL;
-    return int64_t(B) * nch * 3 * C * 4;
+    if (int64_t(B) * nch * C == 0) return 0;
+    return ((2 * int64_t(B) * nch * 3 * C * 4 + 255) & ~int64_t(255)) + 256;
 }
 
 hipError_t launch_wkv4(const Wkv4Params& p, hipStream_t stream) {
-    Wkv4Args g{p.w, p.u, p.k, p.v, p.y, p.s0, p.s1, static_cast<float*>(p.ws), p.B, p.T, p.C,
-               int((p.T + CL - 1) / CL)};
+    const int nch = int((p.T + CL - 1) / CL);
+    const int64_t states = (2 * int64_t(p.B) * nch * 3 * p.C * 4 + 255) & ~int64_t(255);
+    Wkv4Args g{p.w, p.u, p.k, p.v, p.y, p.s0, p.s1, static_cast<float*>(p.ws),
+               reinterpret_cast<int*>(static_cast<char*>(p.ws) + states), p.B, p.T, p.C, nch};
     if (p.T == 0) {   // state_out <- state_in (or the zero state)
         if (!p.s1) return hipSuccess;
-        g.nch = 0;
-        hipLaunchKernelGGL(wkv4_scan_kernel, dim3(unsigned((p.C + NT4 - 1) / NT4), unsigned(p.B)), dim3(NT4), 0,
-                           stream, g);
+        hipLaunchKernelGGL(wkv4_copy_state_kernel, dim3(unsigned((p.C + NT4 - 1) / NT4), unsigned(p.B)), dim3(NT4),
+                           0, stream, g);
         return hipGetLastError();
     }
     if (p.in_dtype == WKV7_BF16)

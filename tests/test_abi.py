@@ -263,7 +263,9 @@ def _wkv4(desc, **over):
 def test_wkv4_argument_rules():
     lib = W.load_library()
     good4 = lambda **kw: W.Wkv4Desc(**{**dict(B=2, T=100, C=64, in_dtype=1, y_dtype=1, reserved=0), **kw})
-    assert W.wkv4_workspace_bytes(2, 100, 64) == 2 * 2 * 3 * 64 * 4
+    al = lambda x: (x + 255) // 256 * 256
+    assert W.wkv4_workspace_bytes(2, 100, 64) == al(2 * 2 * 2 * 3 * 64 * 4) + 256
+    assert W.wkv4_workspace_bytes(8, 4096, 4096) == al(2 * 8 * 64 * 3 * 4096 * 4) + 256
     assert W.wkv4_workspace_bytes(2, 0, 64) == 0
     assert _wkv4(None) == W.WKV7_EINVAL
     assert _wkv4(good4(reserved=1)) == W.WKV7_EINVAL
