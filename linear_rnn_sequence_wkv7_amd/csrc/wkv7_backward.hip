@@ -33,10 +33,15 @@
 // is processed in slices of 32 rows: the key-axis matrices of a chunk are
 // built once and each slice adds its share to the key-axis gradients.
 //
-// Mapping: one 512-thread workgroup per (b, h).  A forward sweep over the
-// chunks stores the state at every chunk boundary (fp32, in the workspace);
-// the backward sweep walks the chunks in reverse with U = dL/dS in the
-// workspace too, one 32-row slice at a time.  All
+// Mapping: 512-thread workgroups, P per (b, h), each owning a group of the
+// 32-row value slices (P grows while B H P <= 256, so that small B H still
+// fills the chip).  A forward sweep over the chunks stores the group's rows of
+// the state at every chunk boundary (fp32, in the workspace); the backward
+// sweep walks the chunks in reverse with the group's rows of U = dL/dS in the
+// workspace too, one slice at a time.  Rows of S, U, dS0 and columns of dV
+// belong to one group; the key-axis gradients are sums over all slices, so
+// groups 1 .. P - 1 write their shares to workspace slots that a reduce kernel
+// adds to group 0's in group order.  All
 // products run on v_mfma_f32_16x16x4f32 with fp32 operands staged in LDS
 // (lane l: A[l & 15][l >> 4], B[l >> 4][l & 15], C[4 (l >> 4) + r][l & 15]).
 // Masked tokens and tokens past the end are identity tokens (r, k, a, b, v,
