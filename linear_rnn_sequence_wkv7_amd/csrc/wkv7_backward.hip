@@ -166,6 +166,10 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
     constexpr int NA = (2 * TC) / 8;     // tiles per wave of one [32][D] matrix
     constexpr int UNI = (2 * BSL * PD > 4 * BL * PL) ? 2 * BSL * PD : 4 * BL * PL;
     constexpr int FU = D == 64 ? 2 : 1;   // unroll of the fused k-loops
+    // At D = 128 a group's first slice of a chunk is fetched together with the chunk's
+    // inputs (faster there: hxa07D runs one slice per group); at D = 64 each slice is
+    // fetched at its start (faster there).
+    constexpr bool PF0 = D == 128;
     static_assert(BSL == BL, "slice and chunk share the 32-wide LDS pitch");
     static_assert(BL * D <= 4 * BL * PL, "the w-derivative table fits VS .. DZS (ZS holds the suffix-sum partials)");
 
@@ -415,11 +419,12 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
         const int c0 = c * BL;
         float* sn = ck + int64_t(c + 1) * D * D;
         issue_chunk(c, false);
+        if constexpr (PF0) fetch_slice(c, s_begin, false);   // in flight with the chunk's loads
         load_chunk(c, false);
         build_LL(c, false);
         #pragma unroll 1
         for (int s = s_begin; s < s_end; ++s) {
-            fetch_slice(c, s, false);
+            if (!PF0 || s != s_begin) fetch_slice(c, s, false);
             #pragma unroll
             for (int u = 0; u < NSE; ++u) {
                 const int e = tid + BNT * u;
@@ -480,6 +485,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
         #pragma unroll
         for (int u = 0; u < NVE; ++u) dbp[u] = 0.f;
         issue_chunk(c, true);
+        if constexpr (PF0) fetch_slice(c, s_begin, true);    // in flight with the chunk's loads
         load_chunk(c, true);
         build_LL(c, true);
 
@@ -492,7 +498,7 @@ __global__ __launch_bounds__(BNT) void bwd_kernel(BwdArgs g) {
 
         #pragma unroll 1
         for (int s = s_begin; s < s_end; ++s) {
-            fetch_slice(c, s, true);
+            if (!PF0 || s != s_begin) fetch_slice(c, s, true);
             // S0 slice, dM = U diag(d), V and y_scale dy slices; diag(S_L^T U) and dy . v shares.
             #pragma unroll
             for (int u = 0; u < NSE; ++u) {
