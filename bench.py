@@ -125,9 +125,38 @@ def cpu_baseline(wl, x, n_pairs: int):
                       f"fp64 numpy, single thread, {dt:.1f} s"}
 
 
+def cpu_baseline_decode(wl, x, n_pairs: int):
+    """The fp64 oracle, as it stands, on n_pairs sequences over all the workload's
+    decode steps (successive tokens from the same state: one forward over them)."""
+    import numpy as np
+    from oracle import wkv7_oracle as O
+    from tests import parity as P
+    pairs = P.sample_pairs(wl, n_pairs, seed=wl.seed)[:n_pairs]
+    bs = np.array([p[0] for p in pairs])
+    hs = np.array([p[1] for p in pairs])
+    hks = hs // (wl.H // wl.H_kv)
+    seq = {}
+    for n in ("r", "w", "a", "b", "k", "v"):
+        if x.get(n) is None:
+            seq[n] = None
+            continue
+        cols = hks if n in ("k", "v") else hs
+        seq[n] = np.ascontiguousarray(x[n][:, bs, 0, cols][None])   # [1, steps, pairs, D]
+    s0 = None if x.get("state0") is None else x["state0"][bs, hs][None]
+    r_k = None if x.get("r_k") is None else x["r_k"][hs]
+    t0 = time.perf_counter()
+    O.wkv7_forward(seq["r"], seq["w"], seq["k"], seq["v"], seq["a"], seq["b"], s0, w_mode=wl.w_mode,
+                   r_k=r_k, y_scale=wl.y_scale, kk_from_k=wl.ab_mode == "from_k")
+    dt = time.perf_counter() - t0
+    return {"value": len(pairs) * wl.steps / dt, "unit": "head-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(pairs)} of {wl.B * wl.H} (batch, head) sequences x all {wl.steps} decode steps, "
+                      f"fp64 numpy, single thread, {dt:.2f} s"}
+
+
 def cpu_baseline_backward(wl, x, gi, n_pairs: int):
-    """The fp64 oracle's backward, as it stands, on n_pairs whole sequences (one KV
-    head each, so only workloads with H_kv == H)."""
+    """The fp64 oracle's backward, as it stands, on n_pairs whole sequences (each
+    with its own KV head, so grouped heads are not summed: the same work per
+    head-token)."""
     import numpy as np
     from oracle import wkv7_oracle as O
     from tests import parity as P
@@ -383,8 +412,10 @@ def main(argv=None) -> int:
         "roofline": roof,
         "wall_s_timed_region": t_wall,
     }
-    if a.cpu_pairs > 0 and a.backward and wl.H_kv == wl.H:
-        out["cpu_baseline"] = cpu_baseline_backward(wl, x, gi, min(a.cpu_pairs, 16))
+    if a.cpu_pairs > 0 and a.backward:
+        out["cpu_baseline"] = cpu_baseline_backward(wl, x, gi, min(a.cpu_pairs, 16 if wl.D == 64 else 4))
+    elif a.cpu_pairs > 0 and wl.kind == "decode":
+        out["cpu_baseline"] = cpu_baseline_decode(wl, x, a.cpu_pairs)
     elif a.cpu_pairs > 0 and wl.kind == "forward" and not a.backward:
         out["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_pairs)
     else:
