@@ -413,7 +413,7 @@ def main(argv=None) -> int:
         "wall_s_timed_region": t_wall,
     }
     if a.cpu_pairs > 0 and a.backward:
-        out["cpu_baseline"] = cpu_baseline_backward(wl, x, gi, min(a.cpu_pairs, 16 if wl.D == 64 else 4))
+        out["cpu_baseline"] = cpu_baseline_backward(wl, x, gi, min(a.cpu_pairs, 16 if wl.D == 64 else 1))
     elif a.cpu_pairs > 0 and wl.kind == "decode":
         out["cpu_baseline"] = cpu_baseline_decode(wl, x, a.cpu_pairs)
     elif a.cpu_pairs > 0 and wl.kind == "forward" and not a.backward:
