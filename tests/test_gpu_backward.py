@@ -170,3 +170,30 @@ def test_backward_workload_hxa07d():
         drk += ref["r_k"]
     errs["r_k"] = P.check("dr_k", got["r_k"][4 * grp:4 * grp + 4], drk, TAU)
     announce("  " + " ".join(f"{n} {e:.1e}" for n, e in errs.items()))
+
+
+def test_backward_workload_hxa07d_full():
+    """The full hxa07D workload (B2 T16384, four value-slice groups per head, the
+    launch configuration the benchmark times): the last KV group of the last
+    sequence, every gradient of its four heads over all 16384 tokens."""
+    wl = G.WORKLOADS["hxa07d_bf16_b2_t16384_h32_kv8_d128"]
+    x = G.make_inputs(wl)
+    gi = G.make_grad_inputs(wl)
+    d = dev_inputs(x)
+    out = W().wkv7_backward(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], to_dev(gi["dy"]), d["state0"],
+                            to_dev(gi["dstate"]), w_mode=wl.w_mode, y_scale=wl.y_scale, r_k=d["r_k"])
+    torch().cuda.synchronize()
+    b, grp = wl.B - 1, wl.H_kv - 1
+    rep = wl.H // wl.H_kv
+    sl = slice(rep * grp, rep * grp + rep)
+    announce(f"{wl.name}: oracle backward of batch {b}, heads {sl.start}..{sl.stop - 1}")
+    ref = O.wkv7_backward(*(x[n][b:b + 1, :, sl] if n not in ("k", "v") else x[n][b:b + 1, :, grp:grp + 1]
+                            for n in NAMES), None, gi["dy"][b:b + 1, :, sl], gi["dstate"][b:b + 1, sl],
+                          w_mode=wl.w_mode, r_k=x["r_k"][sl], y_scale=wl.y_scale)
+    errs = {}
+    for n in ("r", "w", "a", "b"):
+        errs[n] = P.check(f"d{n}", to_host(out[n][b, :, sl]), ref[n][0], TAU)
+    for n in ("k", "v"):
+        errs[n] = P.check(f"d{n}", to_host(out[n][b, :, grp]), ref[n][0, :, 0], TAU)
+    errs["S0"] = P.check("dS0", to_host(out["state"][b, sl]), ref["state0"][0], TAU)
+    announce("  " + " ".join(f"d{n} {e:.1e}" for n, e in errs.items()))
