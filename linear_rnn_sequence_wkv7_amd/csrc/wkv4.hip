@@ -30,7 +30,8 @@
 // per chunk would write back or invalidate an XCD's whole L2 each time.
 // Workgroups take their chunk from a ticket counter in the order they start,
 // chunk-major, so a thread only waits for chunks whose workgroups are already
-// running; each wait is also bounded.  One thread per channel, so each wave's
+// running; each wait is also bounded (past the bound the chunk's outputs are
+// NaN, never a hang).  One thread per channel, so each wave's
 // loads of a token row are 64 consecutive channels.
 #include "wkv7_internal.h"
 #include "wkv7_device.h"
@@ -188,7 +189,8 @@ __global__ __launch_bounds__(NT4) void wkv4_onepass_kernel(Wkv4Args g) {
                 break;
             }
             if (ready_read(loc_ws + row(k), g.C, x)) break;
-            if (it == kSpinMax) {   // bounded: give up (the result is then wrong, not hung)
+            if (it == kSpinMax) {   // bounded: give up with NaN outputs from here on, never hang
+                x = Scaled{__uint_as_float(0x7fc00000u), __uint_as_float(0x7fc00000u), 0.f};
                 complete = true;
                 break;
             }
