@@ -457,49 +457,56 @@ void prep128_kernel(PrepArgs g) {
 
         // ---------------- Q1: the four L x L matrices; Dinv ----------------
         // Tiles (tb, sb) of the lower triangle: 0 = (0,0), 1 = (1,0), 2 = (1,1).
+        // prod(C(X^T), C(Y)) = C(X Y), operands split hi + lo.
+        auto prod = [&](const f32x4 xt, const f32x4 y) {
+            s16x4 xh, xl, yh, yl;
+            to_operand(xt, xh, xl);
+            to_operand(y, yh, yl);
+            const f32x4 cc = mfma32(cat(xh, xl), cat(yh, yh), zero);
+            return mfma32(cat(xh, z4), cat(yl, z4), cc);
+        };
+        f32x4 I4;
+        #pragma unroll
+        for (int r = 0; r < 4; ++r) I4[r] = (4 * lq + r == lr) ? 1.f : 0.f;
+        // (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8) for the strictly lower block
+        // N; Nt = C(N^T) (t = lr, s = 4 lq + r), Nn = C(N).  Returns C(D^T).
+        auto chain = [&](const f32x4 cab, const f32x4 csw) {
+            f32x4 Nn, Nt;
+            #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                Nt[r] = 4 * lq + r >= lr ? 0.f : cab[r];
+                Nn[r] = lr >= 4 * lq + r ? 0.f : csw[r];
+            }
+            const f32x4 N2 = prod(Nt, Nn), N2t = prod(Nn, Nt);
+            const f32x4 N4 = prod(N2t, N2), N4t = prod(N2, N2t);
+            const f32x4 N8 = prod(N4t, N4);
+            const f32x4 Gt = prod(N2 + I4, Nt + I4);
+            const f32x4 G4t = prod(N4 + I4, Gt);
+            return prod(N8 + I4, G4t);            // lane holds D[lr][4 lq + r]
+        };
+        auto store_blk = [&](int row0, int col0, const f32x4 v) {
+            uint32_t h0, l0, h1, l1;
+            split2(v[0], v[1], h0, l0);
+            split2(v[2], v[3], h1, l1);
+            const int o = ((row0 + lr) * PT + pairpos(col0 + 4 * lq)) * 2;
+            sts<uint2>(smem + P_DIH, o, make_uint2(h0, h1));
+            sts<uint2>(smem + P_DIL, o, make_uint2(l0, l1));
+        };
+        // The block inverse of I - A_ab: D0 on wave 0, D1 on wave 1 (the two doubling
+        // chains run on different SIMDs), then D10 = D1 A10 D0 on wave 0.
+        f32x4 Tm = zero;   // A10 D0 (wave 0), kept across the exchange below
         if (w == 0) {
-            // A_ab, and the block inverse of I - A_ab: D0, D1 by the doubling chain,
-            // D10 = D1 A10 D0.  C'[s][t] orientation: lane t = lr, s = 4 lq + r.
-            f32x4 ab[3] = {zero, zero, zero}, nsw[2] = {zero, zero};
+            // A_ab tiles 0, 1 and block 0 swapped.  C'[s][t] orientation: lane t = lr, s = 4 lq + r.
+            f32x4 ab[2] = {zero, zero}, nsw0 = zero;
             #pragma unroll
             for (int kq = 0; kq < 4; ++kq) {
-                const bf16x8 B0 = lds<bf16x8>(smem + P_BT, opK(0, kq)), B1 = lds<bf16x8>(smem + P_BT, opK(1, kq));
+                const bf16x8 B0 = lds<bf16x8>(smem + P_BT, opK(0, kq));
                 const bf16x8 A0 = lds<bf16x8>(smem + P_AT, opK(0, kq)), A1 = lds<bf16x8>(smem + P_AT, opK(1, kq));
                 ab[0] = mfma32(B0, A0, ab[0]);
                 ab[1] = mfma32(B0, A1, ab[1]);
-                ab[2] = mfma32(B1, A1, ab[2]);
-                nsw[0] = mfma32(A0, B0, nsw[0]);
-                nsw[1] = mfma32(A1, B1, nsw[1]);
+                nsw0 = mfma32(A0, B0, nsw0);
             }
-            // prod(C(X^T), C(Y)) = C(X Y), operands split hi + lo.
-            auto prod = [&](const f32x4 xt, const f32x4 y) {
-                s16x4 xh, xl, yh, yl;
-                to_operand(xt, xh, xl);
-                to_operand(y, yh, yl);
-                const f32x4 cc = mfma32(cat(xh, xl), cat(yh, yh), zero);
-                return mfma32(cat(xh, z4), cat(yl, z4), cc);
-            };
-            f32x4 I4;
-            #pragma unroll
-            for (int r = 0; r < 4; ++r) I4[r] = (4 * lq + r == lr) ? 1.f : 0.f;
-            // (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8) for the strictly lower block
-            // N; Nt = C(N^T) (t = lr, s = 4 lq + r), Nn = C(N).  Returns C(D^T).
-            auto chain = [&](const f32x4 cab, const f32x4 csw) {
-                f32x4 Nn, Nt;
-                #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    Nt[r] = 4 * lq + r >= lr ? 0.f : cab[r];
-                    Nn[r] = lr >= 4 * lq + r ? 0.f : csw[r];
-                }
-                const f32x4 N2 = prod(Nt, Nn), N2t = prod(Nn, Nt);
-                const f32x4 N4 = prod(N2t, N2), N4t = prod(N2, N2t);
-                const f32x4 N8 = prod(N4t, N4);
-                const f32x4 Gt = prod(N2 + I4, Nt + I4);
-                const f32x4 G4t = prod(N4 + I4, Gt);
-                return prod(N8 + I4, G4t);            // lane holds D[lr][4 lq + r]
-            };
-            const f32x4 Dt0 = chain(ab[0], nsw[0]);
-            const f32x4 Dt1 = chain(ab[2], nsw[1]);
+            const f32x4 Dt0 = chain(ab[0], nsw0);
             // D0^T to LDS (wave-private), hi / lo: D0[lr][4 lq + r] -> row 4 lq + r, column lr.
             {
                 uint32_t h0, l0, h1, l1;
@@ -518,7 +525,6 @@ void prep128_kernel(PrepArgs g) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             // T = A10 D0 (C layout: t = 4 lq + r, s = lr).  ab[1] is C(A10^T), i.e. the
             // 16-deep A operand of A10; D0 as the B operand from D0^T rows.
-            f32x4 Tm;
             {
                 s16x4 ah, al;
                 to_operand(ab[1], ah, al);
@@ -527,21 +533,21 @@ void prep128_kernel(PrepArgs g) {
                 Tm = mfma32(cat(ah, ah), cat(dh, dl), zero);
                 Tm = mfma32(cat(al, z4), cat(dh, z4), Tm);
             }
-            // C(D10^T) = prod(C(T), C(D1^T)) = C(T^T D1^T): lane holds D10[lr][4 lq + r].
-            const f32x4 D10t = prod(Tm, Dt1);
-            auto store_blk = [&](int row0, int col0, const f32x4 v) {
-                uint32_t h0, l0, h1, l1;
-                split2(v[0], v[1], h0, l0);
-                split2(v[2], v[3], h1, l1);
-                const int o = ((row0 + lr) * PT + pairpos(col0 + 4 * lq)) * 2;
-                sts<uint2>(smem + P_DIH, o, make_uint2(h0, h1));
-                sts<uint2>(smem + P_DIL, o, make_uint2(l0, l1));
-            };
             store_blk(0, 0, Dt0);
             store_blk(0, 16, zero);
-            store_blk(16, 0, D10t);
-            store_blk(16, 16, Dt1);
         } else {
+            if (w == 1) {   // D1 from A_ab block 1; C(D1^T) to the U^T area (free until Q2) for wave 0
+                f32x4 ab2 = zero, nsw1 = zero;
+                #pragma unroll
+                for (int kq = 0; kq < 4; ++kq) {
+                    const bf16x8 B1 = lds<bf16x8>(smem + P_BT, opK(1, kq)), A1 = lds<bf16x8>(smem + P_AT, opK(1, kq));
+                    ab2 = mfma32(B1, A1, ab2);
+                    nsw1 = mfma32(A1, B1, nsw1);
+                }
+                const f32x4 Dt1 = chain(ab2, nsw1);
+                sts<float4>(smem + P_UTH, (16 * lq + lr) * 16, make_float4(Dt1[0], Dt1[1], Dt1[2], Dt1[3]));
+                store_blk(16, 16, Dt1);
+            }
             // Waves 1..3: A_rk; 4..6: A_ak (swapped orientation); 7: all three tiles of A_rb.
             auto tile_tb = [](int n) { return n == 0 ? 0 : 1; };
             auto tile_sb = [](int n) { return n == 2 ? 1 : 0; };
@@ -615,6 +621,12 @@ void prep128_kernel(PrepArgs g) {
                 // A_rb row block 0 at s >= 16 is zero.
                 sts<uint2>(smem + P_ARB, (lr * PT + pairpos(16 + 4 * lq)) * 2, make_uint2(0, 0));
             }
+        }
+        __syncthreads();
+        if (w == 0) {
+            // C(D10^T) = prod(C(T), C(D1^T)) = C(T^T D1^T): lane holds D10[lr][4 lq + r].
+            const float4 x = lds<float4>(smem + P_UTH, (16 * lq + lr) * 16);
+            store_blk(16, 0, prod(Tm, f32x4{x.x, x.y, x.z, x.w}));
         }
         __syncthreads();
 
