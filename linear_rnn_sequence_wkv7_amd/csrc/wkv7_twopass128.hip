@@ -989,6 +989,10 @@ void scan128_kernel(ScanArgs g) {
             sts<s16x4>(smem + S_XOH, (kp * 64 + l) * 8, xh);
             sts<s16x4>(smem + S_XOL, (kp * 64 + l) * 8, xl);
         }
+        // The last operand group, issued before this chunk's y stores: a wait for a
+        // load also waits for every store issued before it.
+        load_p(cn, nxt);
+        asm volatile("" ::: "memory");
         // Y tile (ty, sy) = sum of partials + P V; epilogue; store.
         {
             f32x4 ys = lds<f32x4>(smem + S_PART, ((4 + kp) * 64 + l) * 16);
@@ -1019,8 +1023,6 @@ void scan128_kernel(ScanArgs g) {
                 Buf<Ty>::store1(Ry, uint32_t(tl0 + r) * sty + uint32_t(h * DK + DV * q + i_loc) * SY, yv);
             }
         }
-        load_p(cn, nxt);
-        asm volatile("" ::: "memory");
         __syncthreads();   // reduced X tiles visible
 
         // S <- S + X Bh, X of strip sg as the B operand (k = token, n = value row).
