@@ -196,19 +196,8 @@ def run_wkv4(a, wl, G, wkv7, torch, np):
     def one_step():
         wkv7.wkv4_forward(d["w"], d["u"], d["k"], d["v"], d["state"], y_dtype=wl.y_dtype, y=y, state_out=s_out,
                           workspace=ws)
-    for _ in range(a.warmup):
-        one_step()
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(a.steps):
-        one_step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = ev0.elapsed_time(ev1) / a.steps
+    ms_total, t_wall = time_steps(torch, a, lambda i: one_step(), stream)
+    ms = ms_total / a.steps
     sin = 2 if wl.in_dtype == "bf16" else 4
     sy = 2 if wl.y_dtype == "bf16" else 4
     # Algorithmic bytes: k, v read once, y written once, w and u, the final state written.
@@ -224,7 +213,7 @@ def run_wkv4(a, wl, G, wkv7, torch, np):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profile("wkv4", wl.name),
                      "kernel": "wkv4", "algorithmic_bytes": nbytes},
-        "wall_s_timed_region": t_wall,
+        "wall_s_timed_region": t_wall, "launch": "hip_graph" if a.graph else "host_per_step",
     }
     if a.cpu_pairs > 0:
         from oracle import wkv4_oracle as O4
@@ -241,6 +230,39 @@ def run_wkv4(a, wl, G, wkv7, torch, np):
     return 0
 
 
+def time_steps(torch, a, one_step, stream):
+    """Warm-up steps, then the timed region: a.steps steps between two HIP events
+    on the stream the kernels run on, with a synchronisation on both sides.  By
+    default the a.steps launches are captured once, before the timed region, into
+    one HIP graph and the timed region is that graph's replay: the same kernels on
+    the same inputs, with the host's per-launch dispatch taken out (--no-graph
+    launches each step from the host instead)."""
+    for i in range(a.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    graph = None
+    if a.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(a.steps):
+                one_step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(a.steps):
+            one_step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1), time.perf_counter() - t_wall
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,6 +273,8 @@ def main(argv=None) -> int:
     ap.add_argument("--ab-mode", default="given", choices=["given", "from_k"])
     ap.add_argument("--mask", default="", choices=["", "pad", "holes"])
     ap.add_argument("--backward", action="store_true", help="time wkv7_backward instead of the forward")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="launch each timed step from the host instead of replaying them as one captured HIP graph")
     ap.add_argument("--cpu-pairs", type=int, default=256, help="sequences in the CPU-oracle sample (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (a reference for the "
@@ -362,20 +386,9 @@ def main(argv=None) -> int:
         nbytes = algorithmic_bytes(wl)
         flops = algorithmic_flops(wl)
 
-    for i in range(a.warmup):
-        one_step(i)
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    ev0.record(stream)
-    for i in range(a.steps):
-        one_step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
+    ms_total, t_wall = time_steps(torch, a, one_step, stream)
     # One launch per step (two for the two-pass form, timed together): the step's average duration.
-    ms = ev0.elapsed_time(ev1) / a.steps
+    ms = ms_total / a.steps
 
     value = head_tokens_per_step / (ms / 1e3)
     if kind == "backward":
@@ -410,7 +423,7 @@ def main(argv=None) -> int:
         "config": {"workload": label, "B": wl.B, "T": wl.T, "H": wl.H, "H_kv": wl.H_kv, "D": wl.D,
                    "io_dtype": wl.in_dtype, "y_dtype": wl.y_dtype, "kernel": kind},
         "roofline": roof,
-        "wall_s_timed_region": t_wall,
+        "wall_s_timed_region": t_wall, "launch": "hip_graph" if a.graph else "host_per_step",
     }
     if a.cpu_pairs > 0 and a.backward:
         out["cpu_baseline"] = cpu_baseline_backward(wl, x, gi, min(a.cpu_pairs, 16 if wl.D == 64 else 1))
