@@ -4,7 +4,9 @@
 Default workload: bf16 forward, B=8, T=1024, H=32, D=64 (C=2048), zero
 initial state, bf16 y and fp32 final state.  Inputs are resident in HBM before
 the timed region; K steps are bracketed by a device synchronisation on both
-sides and timed with HIP events on the stream the kernels are launched on.
+sides and timed with HIP events on the stream the kernels are launched on.  The
+K steps are captured once into a HIP graph and the timed region replays it
+(--no-graph launches each step from the host instead).
 
 Prints one JSON line with the throughput (head-tokens/s), the roofline of the
 dominant kernel and the fp64 CPU oracle timed on a bounded sample.
