@@ -1,26 +1,32 @@
 #!/usr/bin/env python3
 """Benchmark: one step = one wkv7_forward over the whole synthetic batch.
 
-Default workload: bf16 forward, B=8, T=1024, H=32, D=64 (C=2048), zero
-initial state, bf16 y and fp32 final state.  Inputs are resident in HBM before
-the timed region; K steps are bracketed by a device synchronisation on both
-sides and timed with HIP events on the stream the kernels are launched on.  The
-K steps are captured once into a HIP graph and the timed region replays it
-(--no-graph launches each step from the host instead).
+Default workload: the hxa07D-style long-context forward, B=2, T=16384, H=32,
+8 KV heads (GQA x4), D=128, log-decay input, fused epilogue (y_scale =
+128^-1/2, r_k bonus term), bf16 inputs and y, fp32 state, zero initial state;
+at D = 128 the two-pass chunked form runs (two kernels per step, workspace
+allocated before the timed region; the roofline covers the whole step).
+Inputs are resident in HBM before the timed region; K steps are bracketed by a
+device synchronisation on both sides and timed with HIP events on the stream
+the kernels are launched on.  The K steps are captured once into a HIP graph
+and the timed region replays it (--no-graph launches each step from the host
+instead).
 
 Prints one JSON line with the throughput (head-tokens/s), the roofline of the
-dominant kernel and the fp64 CPU oracle timed on a bounded sample.
+dominant kernel and the fp64 CPU oracle timed on a bounded sample over a pool
+of host processes (run before the GPU is touched).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--algo auto|scan|chunked|two_pass]
                     [--ab-mode given|from_k] [--mask pad|holes] [--backward]
+                    [--cpu-pairs N] [--cpu-workers N]
 
-At D = 128 "auto" runs the two-pass form (two kernels per step, workspace
-allocated before the timed region); its roofline covers the whole step.
---ab-mode from_k passes alpha in place of a and no b: the kernels form
-a = -kk, b = kk alpha and k (1 - decay + alpha) themselves.  --mask adds an
-attention mask drawn by the named recipe.  --backward times wkv7_backward
-(every input gradient, dS0 and dr_k) for the workload, with seeded upstream
-gradients dy and dS_T resident before the timed region.
+--workload fwd_bf16_b8_t1024_h32_d64 (and the other names in inputs.WORKLOADS
+and inputs.WKV4_WORKLOADS) selects another workload.  --ab-mode from_k passes
+alpha in place of a and no b: the kernels form a = -kk, b = kk alpha and
+k (1 - decay + alpha) themselves.  --mask adds an attention mask drawn by the
+named recipe.  --backward times wkv7_backward (every input gradient, dS0 and
+dr_k) for the workload, with seeded upstream gradients dy and dS_T resident
+before the timed region.
 """
 from __future__ import annotations
 
@@ -114,67 +120,100 @@ def traffic_from_profile(kind: str, workload: str):
     return int(rec["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(wl, x, n_pairs: int):
-    """The fp64 oracle, as it stands, on n_pairs whole sequences of the workload."""
-    from oracle import wkv7_oracle  # noqa: F401  (CPU baseline leg only)
-    from tests import parity as P
-    pairs = P.sample_pairs(wl, n_pairs, seed=wl.seed)
-    t0 = time.perf_counter()
-    P.oracle_pairs(x, wl, pairs)
-    dt = time.perf_counter() - t0
-    return {"value": len(pairs) * wl.T / dt, "unit": "head-tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(pairs)} of {wl.B * wl.H} (batch, head) sequences x all {wl.T} tokens, "
-                      f"fp64 numpy, single thread, {dt:.1f} s"}
+# ------------------------- CPU oracle baseline -------------------------
+#
+# The fp64 oracle, as it stands, on a bounded sample of the workload's
+# (batch, head) sequences, spread over a pool of worker processes (one BLAS
+# thread each).  The pool is forked before this process touches the GPU.
+
+_CPU_JOB = {}
 
 
-def cpu_baseline_decode(wl, x, n_pairs: int):
-    """The fp64 oracle, as it stands, on n_pairs sequences over all the workload's
-    decode steps (successive tokens from the same state: one forward over them)."""
+def _cpu_worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:     # the pool still runs; BLAS may use more threads
+        pass
+
+
+def _cpu_noop(_):
+    return os.getpid()
+
+
+def _cpu_work(pairs):
+    """Oracle work on one share of the sampled pairs; returns its compute time."""
     import numpy as np
     from oracle import wkv7_oracle as O
     from tests import parity as P
-    pairs = P.sample_pairs(wl, n_pairs, seed=wl.seed)[:n_pairs]
-    bs = np.array([p[0] for p in pairs])
-    hs = np.array([p[1] for p in pairs])
-    hks = hs // (wl.H // wl.H_kv)
-    seq = {}
-    for n in ("r", "w", "a", "b", "k", "v"):
-        if x.get(n) is None:
-            seq[n] = None
-            continue
-        cols = hks if n in ("k", "v") else hs
-        seq[n] = np.ascontiguousarray(x[n][:, bs, 0, cols][None])   # [1, steps, pairs, D]
-    s0 = None if x.get("state0") is None else x["state0"][bs, hs][None]
-    r_k = None if x.get("r_k") is None else x["r_k"][hs]
+    kind, wl, x, gi = _CPU_JOB["kind"], _CPU_JOB["wl"], _CPU_JOB["x"], _CPU_JOB["gi"]
     t0 = time.perf_counter()
-    O.wkv7_forward(seq["r"], seq["w"], seq["k"], seq["v"], seq["a"], seq["b"], s0, w_mode=wl.w_mode,
-                   r_k=r_k, y_scale=wl.y_scale, kk_from_k=wl.ab_mode == "from_k")
-    dt = time.perf_counter() - t0
-    return {"value": len(pairs) * wl.steps / dt, "unit": "head-tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(pairs)} of {wl.B * wl.H} (batch, head) sequences x all {wl.steps} decode steps, "
-                      f"fp64 numpy, single thread, {dt:.2f} s"}
+    if kind == "forward":
+        P.oracle_pairs(x, wl, pairs)
+    elif kind == "decode":
+        # Successive decode tokens from the same state: one forward over the steps.
+        bs = np.array([p[0] for p in pairs])
+        hs = np.array([p[1] for p in pairs])
+        hks = hs // (wl.H // wl.H_kv)
+        seq = {}
+        for n in ("r", "w", "a", "b", "k", "v"):
+            if x.get(n) is None:
+                seq[n] = None
+                continue
+            cols = hks if n in ("k", "v") else hs
+            seq[n] = np.ascontiguousarray(x[n][:, bs, 0, cols][None])   # [1, steps, pairs, D]
+        s0 = None if x.get("state0") is None else x["state0"][bs, hs][None]
+        r_k = None if x.get("r_k") is None else x["r_k"][hs]
+        O.wkv7_forward(seq["r"], seq["w"], seq["k"], seq["v"], seq["a"], seq["b"], s0, w_mode=wl.w_mode,
+                       r_k=r_k, y_scale=wl.y_scale, kk_from_k=wl.ab_mode == "from_k")
+    elif kind == "backward":
+        # Each pair with its own KV head, so grouped heads are not summed: the
+        # same work per head-token.
+        sel = P.select_pairs(x, wl, pairs)
+        bs = np.array([p[0] for p in pairs])
+        hs = np.array([p[1] for p in pairs])
+        dy = np.ascontiguousarray(np.moveaxis(gi["dy"][bs, :, hs], 0, 1)[None])
+        ds = gi["dstate"][bs, hs][None]
+        O.wkv7_backward(sel["r"], sel["w"], sel["k"], sel["v"], sel["a"], sel["b"], sel["state0"], dy, ds,
+                        w_mode=wl.w_mode, r_k=sel["r_k"], y_scale=wl.y_scale)
+    else:
+        raise ValueError(kind)
+    return time.perf_counter() - t0
 
 
-def cpu_baseline_backward(wl, x, gi, n_pairs: int):
-    """The fp64 oracle's backward, as it stands, on n_pairs whole sequences (each
-    with its own KV head, so grouped heads are not summed: the same work per
-    head-token)."""
-    import numpy as np
-    from oracle import wkv7_oracle as O
+def default_cpu_workers() -> int:
+    """Host cores this process may use, capped at 16 (one GPU's share of a host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(kind: str, wl, x, gi, n_pairs: int, workers: int):
+    """Time the oracle on n_pairs sampled sequences split over `workers` forked
+    processes.  The value is head-tokens of the sample over the wall time of the
+    parallel region (pool already started)."""
+    import multiprocessing as mp
     from tests import parity as P
     pairs = P.sample_pairs(wl, n_pairs, seed=wl.seed)[:n_pairs]
-    sel = P.select_pairs(x, wl, pairs)
-    bs = np.array([p[0] for p in pairs])
-    hs = np.array([p[1] for p in pairs])
-    dy = np.ascontiguousarray(np.moveaxis(gi["dy"][bs, :, hs], 0, 1)[None])
-    ds = gi["dstate"][bs, hs][None]
-    t0 = time.perf_counter()
-    O.wkv7_backward(sel["r"], sel["w"], sel["k"], sel["v"], sel["a"], sel["b"], sel["state0"], dy, ds,
-                    w_mode=wl.w_mode, r_k=sel["r_k"], y_scale=wl.y_scale)
-    dt = time.perf_counter() - t0
-    return {"value": len(pairs) * wl.T / dt, "unit": "head-tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"backward of {len(pairs)} of {wl.B * wl.H} (batch, head) sequences x all {wl.T} tokens, "
-                      f"fp64 numpy, single thread, {dt:.1f} s"}
+    n_w = max(1, min(workers, len(pairs)))
+    shares = [pairs[i::n_w] for i in range(n_w)]
+    _CPU_JOB.update(kind=kind, wl=wl, x=x, gi=gi)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(n_w, initializer=_cpu_worker_init) as pool:
+        pool.map(_cpu_noop, range(n_w), chunksize=1)
+        t0 = time.perf_counter()
+        busy = pool.map(_cpu_work, shares, chunksize=1)
+        dt = time.perf_counter() - t0
+    _CPU_JOB.clear()
+    steps = wl.steps if kind == "decode" else wl.T
+    what = {"forward": "whole sequences", "decode": f"sequences x all {wl.steps} decode steps",
+            "backward": "whole sequences, backward"}[kind]
+    return {"value": len(pairs) * steps / dt, "unit": "head-tokens/s", "cores": n_w, "kind": "oracle",
+            "sample": f"{len(pairs)} of {wl.B * wl.H} (batch, head) {what} ({steps} tokens each), fp64 numpy, "
+                      f"{n_w} worker processes with one BLAS thread each, "
+                      f"{dt:.1f} s wall, {sum(busy):.1f} s of worker compute"}
 
 
 def run_wkv4(a, wl, G, wkv7, torch, np):
@@ -217,9 +256,9 @@ def run_wkv4(a, wl, G, wkv7, torch, np):
                      "kernel": "wkv4", "algorithmic_bytes": nbytes},
         "wall_s_timed_region": t_wall, "launch": "hip_graph" if a.graph else "host_per_step",
     }
-    if a.cpu_pairs > 0:
+    if a.cpu_pairs is None or a.cpu_pairs > 0:
         from oracle import wkv4_oracle as O4
-        n = min(a.cpu_pairs, 8)
+        n = min(8 if a.cpu_pairs is None else a.cpu_pairs, 8)
         t0 = time.perf_counter()
         O4.wkv4_forward(x["w"][:n], x["u"][:n], x["k"][:1, :, :n], x["v"][:1, :, :n])
         dt = time.perf_counter() - t0
@@ -270,14 +309,18 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwd_bf16_b8_t1024_h32_d64")
+    ap.add_argument("--workload", default="hxa07d_bf16_b2_t16384_h32_kv8_d128")
     ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunked", "two_pass"])
     ap.add_argument("--ab-mode", default="given", choices=["given", "from_k"])
     ap.add_argument("--mask", default="", choices=["", "pad", "holes"])
     ap.add_argument("--backward", action="store_true", help="time wkv7_backward instead of the forward")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="launch each timed step from the host instead of replaying them as one captured HIP graph")
-    ap.add_argument("--cpu-pairs", type=int, default=256, help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-pairs", type=int, default=None,
+                    help="sequences in the CPU-oracle sample (0: skip; default: a per-workload sample of "
+                         "roughly 10-30 s of oracle work)")
+    ap.add_argument("--cpu-workers", type=int, default=None,
+                    help="worker processes of the CPU-oracle baseline (default: usable host cores, at most 16)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (a reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -302,18 +345,37 @@ def main(argv=None) -> int:
         return 2
 
     import numpy as np  # noqa: F401
-    import torch
 
     from linear_rnn_sequence_wkv7_amd import inputs as G
-    from linear_rnn_sequence_wkv7_amd import wkv7
 
+    workers = a.cpu_workers or default_cpu_workers()
     if a.workload in G.WKV4_WORKLOADS:
+        import torch
+        from linear_rnn_sequence_wkv7_amd import wkv7
         torch.cuda.set_device(0)
         return run_wkv4(a, G.WKV4_WORKLOADS[a.workload], G, wkv7, torch, np)
     wl = dataclasses.replace(G.WORKLOADS[a.workload], ab_mode=a.ab_mode, mask=a.mask)
+    if a.backward and wl.kind != "forward":
+        print("--backward needs a forward workload", file=sys.stderr)
+        return 2
     label = workload_label(wl)
-    torch.cuda.set_device(0)
     x = G.make_inputs(wl)
+    gi = G.make_grad_inputs(wl) if a.backward else None
+
+    # The CPU-oracle baseline runs first, in processes forked before any GPU call.
+    base_kind = "backward" if a.backward else wl.kind
+    n_cpu = a.cpu_pairs
+    if n_cpu is None:
+        # About 10-30 s of oracle work in total, spread over the workers.
+        n_cpu = {"forward": 256 if wl.D == 64 else 16, "decode": 4096,
+                 "backward": 4 * workers if wl.D == 64 else workers}[base_kind]
+    cpu = cpu_baseline(base_kind, wl, x, gi, n_cpu, workers) if n_cpu > 0 else None
+
+    import torch
+
+    from linear_rnn_sequence_wkv7_amd import wkv7
+
+    torch.cuda.set_device(0)
 
     def dev(arr):
         if arr is None:
@@ -326,11 +388,7 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream()
 
     if a.backward:
-        if wl.kind != "forward":
-            print("--backward needs a forward workload", file=sys.stderr)
-            return 2
         kind = "backward"
-        gi = G.make_grad_inputs(wl)
         dy, dst = dev(gi["dy"]), dev(gi["dstate"])
         ws_bytes = wkv7.wkv7_backward_workspace_bytes(
             wl.B, wl.T, wl.H, wl.D, H_kv=wl.H_kv, in_dtype=wl.in_dtype, y_dtype=wl.y_dtype, w_mode=wl.w_mode,
@@ -427,14 +485,7 @@ def main(argv=None) -> int:
         "roofline": roof,
         "wall_s_timed_region": t_wall, "launch": "hip_graph" if a.graph else "host_per_step",
     }
-    if a.cpu_pairs > 0 and a.backward:
-        out["cpu_baseline"] = cpu_baseline_backward(wl, x, gi, min(a.cpu_pairs, 16 if wl.D == 64 else 1))
-    elif a.cpu_pairs > 0 and wl.kind == "decode":
-        out["cpu_baseline"] = cpu_baseline_decode(wl, x, a.cpu_pairs)
-    elif a.cpu_pairs > 0 and wl.kind == "forward" and not a.backward:
-        out["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_pairs)
-    else:
-        out["cpu_baseline"] = None
+    out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
     return 0
 

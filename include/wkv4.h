@@ -48,7 +48,8 @@ int64_t wkv4_workspace_bytes(const wkv4_desc* desc);
 
 /* y <- wkv over T tokens from state_in (or zero); state_out (may be NULL) gets
  * the state after the last token.  state_in == state_out is allowed.
- * workspace: at least wkv4_workspace_bytes(desc) bytes (may be NULL when 0). */
+ * workspace: at least wkv4_workspace_bytes(desc) bytes (may be NULL when 0),
+ * sharing no byte with w, u, k, v, y or the states (EINVAL otherwise). */
 int wkv4_forward(const wkv4_desc* desc, const float* w, const float* u,
                  const void* k, const void* v, const float* state_in,
                  void* y, float* state_out, void* workspace, int64_t workspace_bytes,

@@ -139,8 +139,9 @@ int wkv7_forward(const wkv7_desc* desc,
  * desc->algo == AUTO whenever wkv7_workspace_bytes(desc) > 0 (ab_mode
  * included); otherwise the call is wkv7_forward.  The workspace contents are scratch: not read before
  * they are written, undefined afterwards.  Calls that share a workspace must
- * be ordered (same stream).  EINVAL if the workspace is NULL, misaligned or
- * smaller than needed. */
+ * be ordered (same stream).  EINVAL if the workspace is NULL, misaligned,
+ * smaller than needed, or shares a byte with any array of the call (inputs,
+ * y, state_in, state_out, mask, r_k). */
 int wkv7_forward_ws(const wkv7_desc* desc,
                     const void* r, const void* w, const void* k, const void* v,
                     const void* a, const void* b,
@@ -154,10 +155,14 @@ int wkv7_forward_ws(const wkv7_desc* desc,
  * only: no HIP call. */
 int64_t wkv7_workspace_bytes(const wkv7_desc* desc);
 
-/* One decode token per sequence (desc->T must be 1): the same operation as
- * wkv7_forward with T = 1, run by a kernel that streams the B*H states
- * through HBM once (read state_in, write state_out).  state_in may be NULL
- * (zeros); state_out must not be NULL. */
+/* One decode token per sequence (desc->T must be 1): the recurrent (RNN)
+ * mode of the model, in which each new token costs the same work and the
+ * state is the only memory carried between tokens (104case.com translation of
+ * the RWKV paper, part 2, "RNN-like sequential decoding"; youngju.dev RWKV-7
+ * article, "inference mode").  The same operation as wkv7_forward with T = 1,
+ * run by a kernel that streams the B*H states through HBM once (read
+ * state_in, write state_out).  state_in may be NULL (zeros); state_out must
+ * not be NULL; state_in == state_out (in place) is allowed. */
 int wkv7_decode_step(const wkv7_desc* desc,
                      const void* r, const void* w, const void* k, const void* v,
                      const void* a, const void* b,
@@ -178,7 +183,8 @@ int wkv7_decode_step(const wkv7_desc* desc,
  *   dr_k        : [H, D] fp32, summed over the batch; required exactly when
  *                 desc->r_k is given.
  *   workspace   : device memory of at least wkv7_backward_workspace_bytes(desc)
- *                 bytes, 16-byte aligned (scratch: not read before it is written).
+ *                 bytes, 16-byte aligned (scratch: not read before it is written),
+ *                 sharing no byte with any other array of the call (EINVAL).
  * desc->algo and desc->chunk_len are ignored; ab_mode FROM_K is EUNSUPPORTED.
  * Every pointer is device memory, 16-byte aligned, owned by the caller; outputs
  * must not overlap inputs or the workspace.  Runs one forward sweep that keeps

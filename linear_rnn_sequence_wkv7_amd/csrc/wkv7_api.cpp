@@ -26,6 +26,40 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A named device range [p, p + bytes) for the workspace overlap checks.
+struct Span {
+    const void* p;
+    int64_t bytes;
+    const char* name;
+};
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    if (!a || !b || na <= 0 || nb <= 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + uint64_t(nb) && y < x + uint64_t(na);
+}
+
+// The workspace is written before it is read, so it must not share a byte with
+// any array the call reads or writes.
+int check_workspace_disjoint(const void* ws, int64_t need, const Span* spans, int n) {
+    for (int i = 0; i < n; ++i)
+        if (overlap(ws, need, spans[i].p, spans[i].bytes))
+            return fail(WKV7_EINVAL, "workspace overlaps %s", spans[i].name);
+    return WKV7_OK;
+}
+
+// Byte sizes of the arrays of one wkv7 call.
+struct Sizes {
+    int64_t q, kv, y, state, mask, rk;
+};
+
+Sizes sizes_of(const wkv7::Params& p) {
+    const int64_t sin = p.in_dtype == WKV7_BF16 ? 2 : 4, sy = p.y_dtype == WKV7_BF16 ? 2 : 4;
+    const int64_t bt = int64_t(p.B) * p.T;
+    return {bt * p.H * p.D * sin, bt * p.H_kv * p.D * sin, bt * p.H * p.D * sy,
+            int64_t(p.B) * p.H * p.D * p.D * 4, bt, int64_t(p.H) * p.D * 4};
+}
+
 // 0 = unchecked, 1 = gfx950, 2 = other architecture.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_state[kMaxDevices];
@@ -158,6 +192,12 @@ int forward_impl(const wkv7_desc* desc, const void* r, const void* w, const void
             return fail(WKV7_EINVAL, "workspace has %lld bytes, %lld needed",
                         (long long)workspace_bytes_given, (long long)need);
         if (workspace == y) return fail(WKV7_EINVAL, "y aliases the workspace");
+        const Sizes z = sizes_of(p);
+        const Span spans[11] = {{r, z.q, "r"}, {w, z.q, "w"}, {k, z.kv, "k"}, {v, z.kv, "v"}, {a, z.q, "a"},
+                                {p.ab_mode == WKV7_AB_FROM_K ? nullptr : b, z.q, "b"}, {y, z.y, "y"},
+                                {state_in, z.state, "state_in"}, {state_out, z.state, "state_out"},
+                                {p.mask, z.mask, "mask"}, {p.r_k, z.rk, "r_k"}};
+        if ((rc = check_workspace_disjoint(workspace, need, spans, 11))) return rc;
     }
     p.r = r; p.w = w; p.k = k; p.v = v; p.a = a; p.b = b;
     p.s0 = state_in; p.y = y; p.s1 = state_out;
@@ -263,6 +303,16 @@ int wkv7_backward(const wkv7_desc* desc, const void* r, const void* w, const voi
         if (workspace_bytes_given < need)
             return fail(WKV7_EINVAL, "workspace has %lld bytes, %lld needed",
                         (long long)workspace_bytes_given, (long long)need);
+        const Sizes z = sizes_of(p);
+        const int64_t gq = z.y / (p.y_dtype == WKV7_BF16 ? 2 : 4) * 4;     // fp32 [B, T, H, D]
+        const int64_t gkv = gq / p.H * p.H_kv;                              // fp32 [B, T, H_kv, D]
+        const Span spans[19] = {{r, z.q, "r"}, {w, z.q, "w"}, {k, z.kv, "k"}, {v, z.kv, "v"}, {a, z.q, "a"},
+                                {b, z.q, "b"}, {state_in, z.state, "state_in"}, {dy, z.y, "dy"},
+                                {dstate_out, z.state, "dstate_out"}, {dr, gq, "dr"}, {dw, gq, "dw"},
+                                {dk, gkv, "dk"}, {dv, gkv, "dv"}, {da, gq, "da"}, {db, gq, "db"},
+                                {dstate_in, z.state, "dstate_in"}, {dr_k, z.rk, "dr_k"},
+                                {p.mask, z.mask, "mask"}, {p.r_k, z.rk, "r_k"}};
+        if ((rc = check_workspace_disjoint(workspace, need, spans, 19))) return rc;
     }
     p.r = r; p.w = w; p.k = k; p.v = v; p.a = a; p.b = b;
     p.s0 = state_in; p.y = nullptr; p.s1 = nullptr;
@@ -334,6 +384,12 @@ int wkv4_forward(const wkv4_desc* desc, const float* w, const float* u, const vo
         if (workspace_bytes_given < need)
             return fail(WKV7_EINVAL, "workspace has %lld bytes, %lld needed",
                         (long long)workspace_bytes_given, (long long)need);
+        const int64_t btc = bc * desc->T;
+        const int64_t sin = desc->in_dtype == WKV7_BF16 ? 2 : 4, sy = desc->y_dtype == WKV7_BF16 ? 2 : 4;
+        const Span spans[7] = {{w, int64_t(desc->C) * 4, "w"}, {u, int64_t(desc->C) * 4, "u"},
+                               {k, btc * sin, "k"}, {v, btc * sin, "v"}, {y, btc * sy, "y"},
+                               {state_in, bc * 3 * 4, "state_in"}, {state_out, bc * 3 * 4, "state_out"}};
+        if ((rc = check_workspace_disjoint(workspace, need, spans, 7))) return rc;
     }
     if (bc == 0) return WKV7_OK;
     if (!has_tokens && !state_out) return WKV7_OK;

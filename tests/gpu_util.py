@@ -1,5 +1,6 @@
 """Host <-> device conversion for GPU tests (numpy arrays from the generator,
 bf16 kept as uint16 bit patterns on the host)."""
+import os
 import sys
 
 import numpy as np
@@ -11,8 +12,15 @@ def torch():
 
 
 def announce(what):
+    """Name the case (and report measured errors) on the process's stderr, which
+    output capture does not hold back; also appended to the file named by
+    WKV7_TEST_LOG when that is set."""
     sys.__stderr__.write(f"[gpu] {what}\n")
     sys.__stderr__.flush()
+    path = os.environ.get("WKV7_TEST_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(f"{what}\n")
 
 
 def to_dev(x):

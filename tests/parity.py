@@ -77,10 +77,23 @@ def oracle_pairs(x, wl, pairs):
 
 
 def sample_pairs(wl, n, seed=0):
-    """n distinct (b, h) pairs, always including the first and the last."""
+    """min(n, B*H) distinct (b, h) pairs, stratified: the flat pair index range
+    [0, B*H) is cut into that many equal strata and one pair is drawn from each,
+    except that the first stratum gives pair 0 and the last gives pair B*H - 1.
+    So the first and the last pair are always in, and the sample spreads over
+    every batch and head range (and so over the KV groups) instead of leaning
+    to one end."""
     rng = np.random.default_rng(seed)
     total = wl.B * wl.H
-    idx = set([0, total - 1])
-    idx |= set(rng.choice(total, size=min(n, total), replace=False).tolist())
-    idx = sorted(idx)[:max(n, 2)]
+    n = min(max(n, 2), total)
+    edges = [(i * total) // n for i in range(n + 1)]
+    idx = []
+    for i in range(n):
+        lo, hi = edges[i], edges[i + 1]
+        if i == 0:
+            idx.append(0)
+        elif i == n - 1:
+            idx.append(total - 1)
+        else:
+            idx.append(int(rng.integers(lo, hi)))
     return [(i // wl.H, i % wl.H) for i in idx]

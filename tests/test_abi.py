@@ -294,3 +294,54 @@ def test_no_kernel_spills_to_scratch():
     assert usage, "empty build record"
     bad = {k: v for k, v in usage.items() if v}
     assert not bad, f"kernels using scratch: {bad}"
+
+
+SP = 1 << 26          # 64 MiB between fake arrays: disjoint unless a test makes them overlap
+BASE = 1 << 36
+
+
+def test_forward_workspace_must_not_overlap_any_array():
+    lib = W.load_library()
+    B, T, H, D = 2, 64, 4, 128
+    need = W.wkv7_workspace_bytes(B, T, H, D)
+    state = B * H * D * D * 4
+    q = B * T * H * D * 2
+    names = ("r", "w", "k", "v", "a", "b", "y", "s0", "s1")
+    ptrs = {n: BASE + i * SP for i, n in enumerate(names)}
+    sizes = dict(r=q, w=q, k=q, v=q, a=q, b=q, y=q, s0=state, s1=state)
+    label = dict(s0="state_in", s1="state_out")
+    for n in names:
+        # The workspace's last 16 bytes on the array's first 16, then its first 16 on the array's last 16.
+        for ws in (ptrs[n] - need + 16, ptrs[n] + sizes[n] - 16):
+            assert _call(good(B=B, T=T, H=H, D=D), {**ptrs, "ws": ws, "ws_bytes": need},
+                         fn="wkv7_forward_ws") == W.WKV7_EINVAL
+            assert f"workspace overlaps {label.get(n, n)}".encode() in lib.wkv7_last_error(), n
+    # Adjacent is not an overlap: with the workspace right before r (or right after
+    # state_in) only the state_out placed across it is reported.
+    for n, ws in (("r", ptrs["r"] - need), ("s0", ptrs["s0"] + state)):
+        assert _call(good(B=B, T=T, H=H, D=D), {**ptrs, "s1": ws + need - 16, "ws": ws, "ws_bytes": need},
+                     fn="wkv7_forward_ws") == W.WKV7_EINVAL
+        assert lib.wkv7_last_error() == b"workspace overlaps state_out", n
+
+
+def test_backward_workspace_must_not_overlap_any_array():
+    lib = W.load_library()
+    B, T, H, D = 2, 8, 4, 64
+    need = W.wkv7_backward_workspace_bytes(B, T, H, D)
+    names = ("r", "w", "k", "v", "a", "b", "s0", "dy", "ds1", "dr", "dw", "dk", "dv", "da", "db", "ds0", "drk")
+    ptrs = {n: BASE + i * SP for i, n in enumerate(names)}
+    ptrs["drk"] = None
+    for n in ("k", "s0", "dy", "ds1", "dr", "dv", "ds0"):
+        assert _bwd(good(B=B, T=T, H=H, D=D), **ptrs, ws=ptrs[n] + 16, ws_bytes=need) == W.WKV7_EINVAL
+        assert b"workspace overlaps" in lib.wkv7_last_error(), n
+
+
+def test_wkv4_workspace_must_not_overlap_any_array():
+    lib = W.load_library()
+    desc = W.Wkv4Desc(B=2, T=100, C=64, in_dtype=1, y_dtype=1, reserved=0)
+    need = W.wkv4_workspace_bytes(2, 100, 64)
+    names = ("w", "u", "k", "v", "s0", "y", "s1")
+    ptrs = {n: BASE + i * SP for i, n in enumerate(names)}
+    for n in names:
+        assert _wkv4(desc, **ptrs, ws=ptrs[n] + 16, ws_bytes=need) == W.WKV7_EINVAL
+        assert b"workspace overlaps" in lib.wkv7_last_error(), n

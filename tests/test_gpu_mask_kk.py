@@ -161,7 +161,7 @@ def test_workload_hxa07d_from_k(algo):
     benchmark times."""
     wl = G.workload("hxa07d_bf16_b2_t16384_h32_kv8_d128", ab_mode="from_k")
     x = G.make_inputs(wl)
-    pairs = P.sample_pairs(wl, 4, seed=wl.seed)
+    pairs = P.sample_pairs(wl, 8, seed=wl.seed)
     announce(f"{wl.name} from_k algo={algo} pairs={len(pairs)}")
     y, s = run(wl, x, algo)
     y_ref, s_ref = P.oracle_pairs(x, wl, pairs)

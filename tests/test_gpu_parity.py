@@ -200,12 +200,25 @@ def test_workload_small_f32(algo):
     P.check("state", s, s_ref, TAU[algo])
 
 
+_ORACLE = {}
+
+
+def _oracle_pairs_cached(wl, x, pairs):
+    """The oracle on the sampled pairs, kept for the other kernels and y dtypes
+    of the same workload (the oracle does not depend on either)."""
+    key = (wl.name, tuple(pairs))
+    if key not in _ORACLE:
+        _ORACLE.clear()
+        _ORACLE[key] = P.oracle_pairs(x, wl, pairs)
+    return _ORACLE[key]
+
+
 def _sampled(wl, algo, n_pairs, y_dtype=None):
     x = inputs_of(wl.name)
     pairs = P.sample_pairs(wl, n_pairs, seed=wl.seed)
     announce(f"{wl.name} algo={algo} y={y_dtype or wl.y_dtype} pairs={len(pairs)}")
     y, s = run_forward(wl, x, algo, y_dtype=y_dtype)
-    y_ref, s_ref = P.oracle_pairs(x, wl, pairs)
+    y_ref, s_ref = _oracle_pairs_cached(wl, x, pairs)
     bs = [p[0] for p in pairs]
     hs = [p[1] for p in pairs]
     ydt = y_dtype or wl.y_dtype
@@ -214,6 +227,8 @@ def _sampled(wl, algo, n_pairs, y_dtype=None):
     announce(f"  max err / rms: y {e_y:.3e}  state {e_s:.3e}")
 
 
+# fp32 y holds every kernel to the literal bound (no bf16 rounding allowance);
+# bf16 y is the workload as stated.
 @pytest.mark.parametrize("y_dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("algo", FWD_ALGOS)
 def test_workload_fwd_bf16(algo, y_dtype):
@@ -221,21 +236,26 @@ def test_workload_fwd_bf16(algo, y_dtype):
     _sampled(G.WORKLOADS["fwd_bf16_b8_t1024_h32_d64"], algo, 16, y_dtype=y_dtype)
 
 
+@pytest.mark.parametrize("y_dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("algo", FWD_ALGOS)
-def test_workload_prefill(algo):
+def test_workload_prefill(algo, y_dtype):
     need_algo(algo, 64)
-    _sampled(G.WORKLOADS["prefill_bf16_b4_t4096_h40_d64_l64"], algo, 8)
+    _sampled(G.WORKLOADS["prefill_bf16_b4_t4096_h40_d64_l64"], algo, 16, y_dtype=y_dtype)
 
 
+@pytest.mark.parametrize("y_dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("algo", FWD_ALGOS)
-def test_workload_hxa07d(algo):
-    _sampled(G.WORKLOADS["hxa07d_bf16_b2_t16384_h32_kv8_d128"], algo, 4)
+def test_workload_hxa07d(algo, y_dtype):
+    """16 of the 64 sequences: both batches, every KV group."""
+    _sampled(G.WORKLOADS["hxa07d_bf16_b2_t16384_h32_kv8_d128"], algo, 16, y_dtype=y_dtype)
 
 
-def test_workload_decode_32_steps():
+@pytest.mark.parametrize("y_dtype", ["bf16", "f32"])
+def test_workload_decode_32_steps(y_dtype):
     wl = G.WORKLOADS["decode_bf16_b256_h64_d64_x32"]
     x = inputs_of(wl.name)
     pairs = P.sample_pairs(wl, 128, seed=wl.seed)
+    announce(f"{wl.name} y={y_dtype} pairs={len(pairs)}")
     bs = np.array([p[0] for p in pairs])
     hs = np.array([p[1] for p in pairs])
     dv = {k: to_dev(x[k]) for k in ("r", "w", "k", "v", "a", "b")}
@@ -243,17 +263,20 @@ def test_workload_decode_32_steps():
     sb = torch().empty_like(sa)
     ys = []
     for step in range(wl.steps):
-        y, _ = W().wkv7_decode_step(*(dv[k][step] for k in ("r", "w", "k", "v", "a", "b")), sa, state_out=sb)
+        y, _ = W().wkv7_decode_step(*(dv[k][step] for k in ("r", "w", "k", "v", "a", "b")), sa, state_out=sb,
+                                    y_dtype=y_dtype)
         ys.append(to_host(y)[bs, 0, hs])
         sa, sb = sb, sa
     torch().cuda.synchronize()
     # Oracle: the sampled sequences, step by step from the same state.
     S = x["state0"][bs, hs][None].astype(np.float64)     # [1, n, D, D]
+    e_y = 0.0
     for step in range(wl.steps):
         # [n, 1, D] -> [1, 1, n, D]: the sampled sequences as heads of one batch (H_kv == H here).
         sel = {k: np.ascontiguousarray(x[k][step][bs, :, hs][:, :, None, :].transpose(2, 1, 0, 3))
                for k in ("r", "w", "k", "v", "a", "b")}
         y_ref, S = O.wkv7_forward(sel["r"], sel["w"], sel["k"], sel["v"], sel["a"], sel["b"], S)
-        P.check(f"decode y step {step}", ys[step], y_ref[0, 0], P.TAU_SCAN, bf16_out=True)
+        e_y = max(e_y, P.check(f"decode y step {step}", ys[step], y_ref[0, 0], P.TAU_SCAN,
+                               bf16_out=y_dtype == "bf16"))
     e = P.check("decode final state", to_host(sa)[bs, hs], S[0], P.TAU_SCAN)
-    announce(f"  final state max err / rms {e:.3e}")
+    announce(f"  max err / rms: y (worst step) {e_y:.3e}  final state {e:.3e}")
