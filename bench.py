@@ -321,10 +321,14 @@ def main(argv=None) -> int:
                          "roughly 10-30 s of oracle work)")
     ap.add_argument("--cpu-workers", type=int, default=None,
                     help="worker processes of the CPU-oracle baseline (default: usable host cores, at most 16)")
+    ap.add_argument("--decode-states", type=int, default=4,
+                    help="decode workloads: independent state sets used round robin, each updated in place")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (a reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
     a = ap.parse_args(argv)
+    if a.decode_states < 1:
+        ap.error("--decode-states must be at least 1")
 
     if a.copy_calibration_mib > 0:
         import torch
@@ -367,7 +371,7 @@ def main(argv=None) -> int:
     n_cpu = a.cpu_pairs
     if n_cpu is None:
         # About 10-30 s of oracle work in total, spread over the workers.
-        n_cpu = {"forward": 256 if wl.D == 64 else 16, "decode": 4096,
+        n_cpu = {"forward": 256 if wl.D == 64 else 16, "decode": 16384,
                  "backward": 4 * workers if wl.D == 64 else workers}[base_kind]
     cpu = cpu_baseline(base_kind, wl, x, gi, n_cpu, workers) if n_cpu > 0 else None
 
@@ -410,17 +414,20 @@ def main(argv=None) -> int:
         flops = backward_flops(wl)
     elif wl.kind == "decode":
         kind = "decode"
-        sa = d["state0"]
-        sb = torch.empty_like(sa)
+        # a.decode_states independent state sets (the layers of a model), each
+        # updated in place, used round robin: a step's state was last touched
+        # decode_states - 1 steps earlier, with (decode_states - 1) x 2 x 256 MiB
+        # of other state traffic in between, so with 4 sets it is not served from
+        # the 256 MB memory-side cache.
+        bufs = [d["state0"]] + [d["state0"].clone() for _ in range(a.decode_states - 1)]
         y = torch.empty((wl.B, 1, wl.H, wl.D), dtype=torch.bfloat16, device="cuda")
-        bufs = [sa, sb]
         n_steps_avail = wl.steps
 
         def one_step(i):
-            s_in, s_out = bufs[i % 2], bufs[(i + 1) % 2]
+            st = bufs[i % len(bufs)]
             j = i % n_steps_avail
             wkv7.wkv7_decode_step(*(None if d[k] is None else d[k][j] for k in ("r", "w", "k", "v", "a", "b")),
-                                  s_in, w_mode=wl.w_mode, y_scale=wl.y_scale, r_k=d["r_k"], y=y, state_out=s_out,
+                                  st, w_mode=wl.w_mode, y_scale=wl.y_scale, r_k=d["r_k"], y=y, state_out=st,
                                   ab_mode=wl.ab_mode, mask=None if d["mask"] is None else d["mask"][j])
         head_tokens_per_step = wl.B * wl.H
         n_q = 4 if wl.ab_mode == "from_k" else 5          # r, w, a (, b) and y
@@ -481,7 +488,8 @@ def main(argv=None) -> int:
         "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": label, "B": wl.B, "T": wl.T, "H": wl.H, "H_kv": wl.H_kv, "D": wl.D,
-                   "io_dtype": wl.in_dtype, "y_dtype": wl.y_dtype, "kernel": kind},
+                   "io_dtype": wl.in_dtype, "y_dtype": wl.y_dtype, "kernel": kind,
+                   **({"state_sets": a.decode_states} if kind == "decode" else {})},
         "roofline": roof,
         "wall_s_timed_region": t_wall, "launch": "hip_graph" if a.graph else "host_per_step",
     }
