@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define WKV7_ABI_VERSION 4
+#define WKV7_ABI_VERSION 5
 
 enum wkv7_status {
     WKV7_OK = 0,
@@ -147,6 +147,36 @@ int wkv7_forward_ws(const wkv7_desc* desc,
                     const void* a, const void* b,
                     const float* state_in, void* y, float* state_out,
                     void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of the device scratch that wkv7_forward_noalloc works in, per device. */
+#define WKV7_NOALLOC_SCRATCH_BYTES (64LL << 20)
+
+/* wkv7_forward_ws for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same operation, arguments (minus the workspace) and algorithm choice as
+ * wkv7_forward_ws; calls no hipMalloc, hipFree or other allocating routine.
+ *
+ * The two-pass form keeps its per-chunk records, and the state carried between
+ * windows when state_out is NULL, in a static device array of
+ * WKV7_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on
+ * until the process ends.  The chunks run in windows of as many 32-token chunks
+ * per (b, h) as fit (B * H * 54272 bytes per chunk, after B * H * D * D * 4
+ * bytes of state carry when state_out is NULL): pass 1 then pass 2 per
+ * window, the state passed on through state_out (or the carry).  The results
+ * are those of wkv7_forward_ws bit for bit.  EUNSUPPORTED when not even one
+ * chunk per (b, h) fits.  Nothing in the scratch needs to start at zero (each
+ * window's records and the carry are written before they are read).
+ *
+ * Every call on a device shares that device's scratch, which keeps the last
+ * call's contents: calls that may overlap on one device (different streams,
+ * several host threads) race, and the caller must order them.  The scratch's
+ * device address is looked up once per device, on the first call that runs
+ * the two-pass form with that device current. */
+int wkv7_forward_noalloc(const wkv7_desc* desc,
+                         const void* r, const void* w, const void* k, const void* v,
+                         const void* a, const void* b,
+                         const float* state_in, void* y, float* state_out,
+                         void* stream);
 
 /* Workspace bytes wkv7_forward_ws uses for this descriptor: for D = 128 with
  * algo AUTO and T >= the chunk length, or algo TWO_PASS and T >= 1, it is

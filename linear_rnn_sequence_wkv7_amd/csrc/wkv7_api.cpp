@@ -171,21 +171,25 @@ int finish_launch(hipError_t e, const char* what) {
     return WKV7_OK;
 }
 
+// How a forward call gets the two-pass form's workspace.
+enum class WsMode { kNone, kCaller, kStatic };
+
 int forward_impl(const wkv7_desc* desc, const void* r, const void* w, const void* k,
                  const void* v, const void* a, const void* b, const float* state_in,
                  void* y, float* state_out, void* workspace, int64_t workspace_bytes_given,
-                 bool ws_call, void* stream) {
+                 WsMode ws_mode, void* stream) {
     g_last_error[0] = '\0';
     wkv7::Params p{};
     int rc = check_desc(desc, &p);
     if (rc) return rc;
-    if (!ws_call && desc->algo == WKV7_ALGO_TWO_PASS)
-        return fail(WKV7_EINVAL, "algo TWO_PASS needs a workspace: call wkv7_forward_ws");
+    if (ws_mode == WsMode::kNone && desc->algo == WKV7_ALGO_TWO_PASS)
+        return fail(WKV7_EINVAL, "algo TWO_PASS needs a workspace: call wkv7_forward_ws or wkv7_forward_noalloc");
     const void* in6[6] = {r, w, k, v, a, b};
     if ((rc = check_ptrs(p, in6, y, state_in, state_out))) return rc;
-    const int algo = resolve_algo(p, desc->algo, ws_call);
-    const int64_t need = int64_t(p.B) * p.H > 0 ? workspace_bytes(p, algo) : 0;
-    if (need > 0) {
+    const int algo = resolve_algo(p, desc->algo, ws_mode != WsMode::kNone);
+    const bool has_work = int64_t(p.B) * p.H > 0 && p.T > 0;
+    const int64_t need = has_work ? workspace_bytes(p, algo) : 0;
+    if (need > 0 && ws_mode == WsMode::kCaller) {
         if (!workspace) return fail(WKV7_EINVAL, "workspace is NULL (%lld bytes needed)", (long long)need);
         if (!aligned16(workspace)) return fail(WKV7_EINVAL, "workspace is not 16-byte aligned");
         if (workspace_bytes_given < need)
@@ -199,6 +203,15 @@ int forward_impl(const wkv7_desc* desc, const void* r, const void* w, const void
                                 {p.mask, z.mask, "mask"}, {p.r_k, z.rk, "r_k"}};
         if ((rc = check_workspace_disjoint(workspace, need, spans, 11))) return rc;
     }
+    if (need > 0 && ws_mode == WsMode::kStatic) {
+        p.s1 = state_out;   // the window size depends on whether the carry needs room
+        if (wkv7::twopass128_noalloc_window(p) < 1)
+            return fail(WKV7_EUNSUPPORTED,
+                        "B*H=%lld needs %lld bytes of scratch for one chunk per (b, h)%s; the static scratch "
+                        "holds %lld", (long long)(int64_t(p.B) * p.H),
+                        (long long)(int64_t(p.B) * p.H * wkv7::twopass128_record_bytes()),
+                        state_out ? "" : " plus the state carry", (long long)WKV7_NOALLOC_SCRATCH_BYTES);
+    }
     p.r = r; p.w = w; p.k = k; p.v = v; p.a = a; p.b = b;
     p.s0 = state_in; p.y = y; p.s1 = state_out;
     if (int64_t(p.B) * p.H == 0) return WKV7_OK;
@@ -208,7 +221,18 @@ int forward_impl(const wkv7_desc* desc, const void* r, const void* w, const void
         if (!state_out) return WKV7_OK;
         return finish_launch(wkv7::launch_state_copy(p, s), "state copy");
     }
-    if (algo == WKV7_ALGO_TWO_PASS) return finish_launch(wkv7::launch_twopass128(p, workspace, s), "two-pass (D=128)");
+    if (algo == WKV7_ALGO_TWO_PASS && ws_mode == WsMode::kStatic) {
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess) return fail(WKV7_EDEVICE, "hipGetDevice failed");
+        const hipError_t e = wkv7::noalloc_scratch_init(dev);
+        if (e != hipSuccess)
+            return fail(WKV7_EDEVICE, "device address of the static scratch on device %d: %s", dev,
+                        hipGetErrorString(e));
+        return finish_launch(wkv7::launch_twopass128_noalloc(p, dev, s), "two-pass (D=128, static scratch)");
+    }
+    if (algo == WKV7_ALGO_TWO_PASS)
+        return finish_launch(wkv7::launch_twopass128(p, workspace, (p.T + p.chunk_len - 1) / p.chunk_len, nullptr, s),
+                             "two-pass (D=128)");
     if (algo == WKV7_ALGO_CHUNKED)
         return p.D == 64 ? finish_launch(wkv7::launch_chunked(p, s), "chunked")
                          : finish_launch(wkv7::launch_chunked128(p, s), "chunked (D=128)");
@@ -222,7 +246,7 @@ extern "C" {
 int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void* k,
                  const void* v, const void* a, const void* b, const float* state_in,
                  void* y, float* state_out, void* stream) {
-    return forward_impl(desc, r, w, k, v, a, b, state_in, y, state_out, nullptr, 0, false, stream);
+    return forward_impl(desc, r, w, k, v, a, b, state_in, y, state_out, nullptr, 0, WsMode::kNone, stream);
 }
 
 int wkv7_forward_ws(const wkv7_desc* desc, const void* r, const void* w, const void* k,
@@ -230,7 +254,13 @@ int wkv7_forward_ws(const wkv7_desc* desc, const void* r, const void* w, const v
                     void* y, float* state_out, void* workspace, int64_t workspace_bytes_given,
                     void* stream) {
     return forward_impl(desc, r, w, k, v, a, b, state_in, y, state_out, workspace,
-                        workspace_bytes_given, true, stream);
+                        workspace_bytes_given, WsMode::kCaller, stream);
+}
+
+int wkv7_forward_noalloc(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                         const void* v, const void* a, const void* b, const float* state_in,
+                         void* y, float* state_out, void* stream) {
+    return forward_impl(desc, r, w, k, v, a, b, state_in, y, state_out, nullptr, 0, WsMode::kStatic, stream);
 }
 
 int64_t wkv7_workspace_bytes(const wkv7_desc* desc) {

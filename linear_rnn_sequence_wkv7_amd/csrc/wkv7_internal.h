@@ -32,8 +32,21 @@ hipError_t launch_scan(const Params& p, hipStream_t stream);
 hipError_t launch_chunked(const Params& p, hipStream_t stream);      // D = 64, L = 64
 hipError_t launch_chunked128(const Params& p, hipStream_t stream);   // D = 128, L = 32
 // Two-pass form at D = 128: per-chunk matrices into `ws`, then the recurrence.
+// With win_chunks below the chunk count the chunks run in windows of that many
+// per (b, h) (ws holds B H win_chunks records); the state passes from window to
+// window through state_out, or through `carry` ([B, H, D, D] fp32) when state_out
+// is null.
 int64_t twopass128_workspace_bytes(int B, int H, int T);
-hipError_t launch_twopass128(const Params& p, void* ws, hipStream_t stream);
+int64_t twopass128_record_bytes();
+hipError_t launch_twopass128(const Params& p, void* ws, int win_chunks, float* carry, hipStream_t stream);
+// Allocation-free two-pass form: the records and the state carry live in the
+// library's static device scratch (WKV7_NOALLOC_SCRATCH_BYTES per device).
+// noalloc_scratch_init looks up the scratch's device address once per device
+// (call it with that device current); the window is the chunks per (b, h) that
+// fit (0: not even one).
+hipError_t noalloc_scratch_init(int device);
+int twopass128_noalloc_window(const Params& p);
+hipError_t launch_twopass128_noalloc(const Params& p, int device, hipStream_t stream);
 hipError_t launch_decode(const Params& p, hipStream_t stream);
 // state_out <- state_in (or zeros) for T == 0.
 hipError_t launch_state_copy(const Params& p, hipStream_t stream);

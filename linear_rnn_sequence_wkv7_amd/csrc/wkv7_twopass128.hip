@@ -40,6 +40,8 @@
 // row thread reduces |k|^2 over its 8 keys, the 16 threads of a token meet in
 // LDS (one extra barrier inside the scaling step), and the operands take
 // a = -kk, b = kk alpha and k (1 - decay + alpha) in place of the inputs.
+#include <mutex>
+
 #include "wkv7_internal.h"
 #include "wkv7_device.h"
 
@@ -273,7 +275,9 @@ struct PrepArgs {
     const float* r_k;
     const uint8_t* mask;
     char* ws;
-    int T, H, H_kv, nch, items;
+    // Chunks cb .. cb + nwin - 1 of every (b, h): items = B H nwin; the record of
+    // (b h, cb + i) is record b h * nrec + i of the workspace.
+    int T, H, H_kv, cb, nwin, nrec, items;
 };
 
 template <typename Tin> struct ItemRows {
@@ -293,13 +297,13 @@ void prep128_kernel(PrepArgs g) {
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, lr = l & 15, lq = l >> 4;
-    const int H = g.H, T = g.T, nch = g.nch;
+    const int H = g.H, T = g.T, nwin = g.nwin;
     const uint32_t stq = uint32_t(H) * DK * SI, stkv = uint32_t(g.H_kv) * DK * SI;
     // Row threads: token t of the chunk, keys j0 .. j0 + 7.
     const int t = l & 31, j0 = 8 * (2 * w + (l >> 5));
 
     auto load_item = [&](int item, ItemRows<Tin>& x) {
-        const int bh = item / nch, c = item - bh * nch;
+        const int bh = item / nwin, c = g.cb + (item - bh * nwin);
         const int bb = bh / H, h = bh - bb * H, hk = h / (H / g.H_kv);
         const int64_t tok0 = int64_t(bb) * T;
         const int c0 = c * L;
@@ -343,9 +347,9 @@ void prep128_kernel(PrepArgs g) {
     }
     for (; item < g.items; item += gridDim.x) {
         cur = nxt;
-        const int bh = item / nch, c = item - bh * nch;
-        const int c0 = c * L;
-        char* rec = g.ws + (int64_t(bh) * nch + c) * WS_CHUNK;
+        const int bh = item / nwin, cw = item - bh * nwin;
+        const int c0 = (g.cb + cw) * L;
+        char* rec = g.ws + (int64_t(bh) * g.nrec + cw) * WS_CHUNK;
 
         // ---------------- Q0: decay prefix and the scaled operands (row threads) ----------------
         {
@@ -789,7 +793,9 @@ struct ScanArgs {
     float* s1;
     void* y;
     const char* ws;
-    int T, H, H_kv, BH, nch;
+    // Chunks cb .. ce - 1 from state s0 (or zero) to s1 (or not written); the record
+    // of chunk c of (b, h) is record b h * nrec + c - cb of the workspace.
+    int T, H, H_kv, BH, cb, ce, nrec;
     float y_scale;
 };
 
@@ -851,11 +857,13 @@ void scan128_kernel(ScanArgs g) {
     const int tid = threadIdx.x;
     const int kp = __builtin_amdgcn_readfirstlane(tid >> 6);   // key pair of this wave
     const int l = tid & 63, lr = l & 15, lq = l >> 4;
-    const int H = g.H, T = g.T, nch = g.nch;
+    const int H = g.H, T = g.T, cb = g.cb, ce = g.ce;
     const int bb = bh / H, h = bh - bb * H, hk = h / (H / g.H_kv);
     const uint32_t stkv = uint32_t(g.H_kv) * DK * SI, sty = uint32_t(H) * DK * SY;
     const int64_t tok0 = int64_t(bb) * T;
-    const char* recs = g.ws + int64_t(bh) * nch * WS_CHUNK;
+    // Record of chunk c (cb <= c < ce) of this (b, h).
+    const int64_t rec0 = int64_t(bh) * g.nrec - cb;
+    auto rec_of = [&](int c) { return g.ws + (rec0 + c) * WS_CHUNK; };
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
     // State tiles ST[sg][u][r] = S[32 q + 16 sg + lr][16 (2 kp + u) + 4 lq + r]: the
@@ -877,7 +885,7 @@ void scan128_kernel(ScanArgs g) {
     // backs up and the issuing waves stall): W and Q (first needed), Bh and E,
     // then P, d and the bonus.
     auto load_wq = [&](int c, Ops& o) {
-        const char* kb = recs + int64_t(c) * WS_CHUNK + kp * WS_KP + l * 16;
+        const char* kb = rec_of(c) + kp * WS_KP + l * 16;
         #pragma unroll
         for (int i = 0; i < 2; ++i) {
             o.W[i] = *reinterpret_cast<const bf16x8*>(kb + (BLK_W + i) * WS_BLK);
@@ -886,7 +894,7 @@ void scan128_kernel(ScanArgs g) {
         }
     };
     auto load_be = [&](int c, Ops& o) {
-        const char* kb = recs + int64_t(c) * WS_CHUNK + kp * WS_KP + l * 16;
+        const char* kb = rec_of(c) + kp * WS_KP + l * 16;
         #pragma unroll
         for (int i = 0; i < 2; ++i) {
             o.Bh[i] = *reinterpret_cast<const bf16x8*>(kb + (BLK_BH + i) * WS_BLK);
@@ -895,7 +903,7 @@ void scan128_kernel(ScanArgs g) {
         }
     };
     auto load_p = [&](int c, Ops& o) {   // P, d and the bonus
-        const char* rec = recs + int64_t(c) * WS_CHUNK;
+        const char* rec = rec_of(c);
         o.Ph = *reinterpret_cast<const bf16x8*>(rec + WS_P + ty * WS_BLK + l * 16);
         o.Pl = *reinterpret_cast<const bf16x8*>(rec + WS_P + (2 + ty) * WS_BLK + l * 16);
         #pragma unroll
@@ -930,11 +938,11 @@ void scan128_kernel(ScanArgs g) {
     // loop below alternates two operand sets, so no prefetched register is copied
     // (a copy would wait for the load); each load is waited for at its first use.
     auto chunk = [&](const int c, Ops& cur, Ops& nxt) {
-        const int c0 = c * L, buf = c & 1;
+        const int c0 = c * L, buf = (c - cb) & 1;
         // Next chunk: V rows first (their LDS store closes this iteration), then W, Q.
         // The last iteration loads its own chunk again (unused): unconditional loads
         // keep the compiler's wait counts exact.
-        const int cn = min(c + 1, nch - 1);
+        const int cn = min(c + 1, ce - 1);
         load_v(cn);
         load_wq(cn, nxt);
         asm volatile("" ::: "memory");
@@ -1041,8 +1049,8 @@ void scan128_kernel(ScanArgs g) {
         store_v(buf ^ 1);
     };
     Ops opa, opb;
-    load_v(0);
-    load_ops(0, opa);
+    load_v(cb);
+    load_ops(cb, opa);
     store_v(0);
     // The first operand set completes here: its load order would otherwise enter
     // the compiler's wait counts of every loop iteration.
@@ -1052,12 +1060,12 @@ void scan128_kernel(ScanArgs g) {
         asm volatile("" : "+v"(opa.d[i]));
     }
     asm volatile("" : "+v"(opa.Ph), "+v"(opa.Pl), "+v"(opa.bon));
-    int c = 0;
-    for (; c + 1 < nch; c += 2) {
+    int c = cb;
+    for (; c + 1 < ce; c += 2) {
         chunk(c, opa, opb);
         chunk(c + 1, opb, opa);
     }
-    if (c < nch) chunk(c, opa, opb);
+    if (c < ce) chunk(c, opa, opb);
 
     if (g.s1) {
         #pragma unroll
@@ -1069,11 +1077,13 @@ void scan128_kernel(ScanArgs g) {
     }
 }
 
+// Runs the chunks in windows of `win` chunks per (b, h): pass 1 then pass 2 for
+// each window, the state carried from window to window in `carry` (state_out
+// itself when given).  win >= the chunk count is the one-window form.
 template <typename Tin, typename Ty, bool LOGW, bool EPI, bool KK>
-hipError_t launch_t(const Params& p, void* ws, hipStream_t stream) {
+hipError_t launch_t(const Params& p, void* ws, int win, float* carry, hipStream_t stream) {
     const int bh = p.B * p.H, nch = (p.T + L - 1) / L;
-    const int items = bh * nch;
-    PrepArgs pa{p.r, p.w, p.k, p.a, p.b, p.r_k, p.mask, static_cast<char*>(ws), p.T, p.H, p.H_kv, nch, items};
+    const int nrec = win < nch ? win : nch;
     auto prep = prep128_kernel<Tin, LOGW, EPI, KK>;
     static bool attr_set = false;   // per template instance; idempotent if raced
     if (!attr_set) {
@@ -1082,30 +1092,44 @@ hipError_t launch_t(const Params& p, void* ws, hipStream_t stream) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    // Persistent: one workgroup per compute unit walks the (b, h, chunk) items.
-    const int grid1 = items < kPrepGrid ? items : kPrepGrid;
-    hipLaunchKernelGGL(prep, dim3(grid1), dim3(NTHR_PREP), SMEM_PREP, stream, pa);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    ScanArgs sa{p.v, p.s0, p.s1, p.y, static_cast<const char*>(ws), p.T, p.H, p.H_kv, bh, nch, p.y_scale};
+    float* s_carry = p.s1 ? p.s1 : carry;
     constexpr int smem2 = sizeof(Tin) == 4 ? SMEM_SCAN_F32 : SMEM_SCAN_BF16;
     // 32 workgroups per group of 8 (b, h): 8 heads x 4 value slices.
     const unsigned groups = unsigned((bh + 7) / 8);
-    hipLaunchKernelGGL((scan128_kernel<Tin, Ty, EPI>), dim3(groups * 32u), dim3(NTHR_SCAN), smem2, stream, sa);
-    return hipGetLastError();
+    for (int cb = 0; cb < nch; cb += nrec) {
+        const int nw = nch - cb < nrec ? nch - cb : nrec;
+        const bool last = cb + nw == nch;
+        const int items = bh * nw;
+        PrepArgs pa{p.r, p.w, p.k, p.a, p.b, p.r_k, p.mask, static_cast<char*>(ws), p.T, p.H, p.H_kv,
+                    cb, nw, nrec, items};
+        // Persistent: one workgroup per compute unit walks the (b, h, chunk) items.
+        const int grid1 = items < kPrepGrid ? items : kPrepGrid;
+        hipLaunchKernelGGL(prep, dim3(grid1), dim3(NTHR_PREP), SMEM_PREP, stream, pa);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        ScanArgs sa{p.v, cb == 0 ? p.s0 : s_carry, last ? p.s1 : s_carry, p.y, static_cast<const char*>(ws),
+                    p.T, p.H, p.H_kv, bh, cb, cb + nw, nrec, p.y_scale};
+        hipLaunchKernelGGL((scan128_kernel<Tin, Ty, EPI>), dim3(groups * 32u), dim3(NTHR_SCAN), smem2, stream, sa);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <typename Tin, typename Ty, bool KK>
-hipError_t dispatch_epi(const Params& p, void* ws, hipStream_t s) {
+hipError_t dispatch_epi(const Params& p, void* ws, int win, float* carry, hipStream_t s) {
     const bool logw = p.w_mode == WKV7_W_LOGNEGLOG;
     const bool epi = p.r_k != nullptr;
-    if (logw) return epi ? launch_t<Tin, Ty, true, true, KK>(p, ws, s) : launch_t<Tin, Ty, true, false, KK>(p, ws, s);
-    return epi ? launch_t<Tin, Ty, false, true, KK>(p, ws, s) : launch_t<Tin, Ty, false, false, KK>(p, ws, s);
+    if (logw) return epi ? launch_t<Tin, Ty, true, true, KK>(p, ws, win, carry, s)
+                         : launch_t<Tin, Ty, true, false, KK>(p, ws, win, carry, s);
+    return epi ? launch_t<Tin, Ty, false, true, KK>(p, ws, win, carry, s)
+               : launch_t<Tin, Ty, false, false, KK>(p, ws, win, carry, s);
 }
 
 template <typename Tin, typename Ty>
-hipError_t dispatch_modes(const Params& p, void* ws, hipStream_t s) {
-    return p.ab_mode == WKV7_AB_FROM_K ? dispatch_epi<Tin, Ty, true>(p, ws, s) : dispatch_epi<Tin, Ty, false>(p, ws, s);
+hipError_t dispatch_modes(const Params& p, void* ws, int win, float* carry, hipStream_t s) {
+    return p.ab_mode == WKV7_AB_FROM_K ? dispatch_epi<Tin, Ty, true>(p, ws, win, carry, s)
+                                       : dispatch_epi<Tin, Ty, false>(p, ws, win, carry, s);
 }
 
 }  // namespace
@@ -1114,12 +1138,65 @@ int64_t twopass128_workspace_bytes(int B, int H, int T) {
     return int64_t(B) * H * ((int64_t(T) + L - 1) / L) * WS_CHUNK;
 }
 
-hipError_t launch_twopass128(const Params& p, void* ws, hipStream_t stream) {
-    if (p.D != DK || p.chunk_len != L) return hipErrorInvalidValue;
+int64_t twopass128_record_bytes() { return WS_CHUNK; }
+
+// ---------------------------- allocation-free variant ----------------------------
+//
+// The scratch of wkv7_forward_noalloc: a file-scope device array, one copy per
+// device, held until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it names a stand-in, not device memory): the device
+// address is looked up once per device with hipGetSymbolAddress and kept.
+static __device__ __align__(256) char scratch[WKV7_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxScratchDevices] = {};
+
+int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+hipError_t noalloc_scratch_init(int device) {
+    if (device < 0 || device >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[device]) return hipSuccess;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = static_cast<char*>(ptr);
+    return hipSuccess;
+}
+
+int twopass128_noalloc_window(const Params& p) {
+    const int64_t nch = (int64_t(p.T) + L - 1) / L;
+    const int64_t carry = p.s1 ? 0 : round256(int64_t(p.B) * p.H * DK * DK * 4);
+    const int64_t per_chunk = int64_t(p.B) * p.H * WS_CHUNK;
+    if (per_chunk <= 0) return 0;
+    const int64_t win = (WKV7_NOALLOC_SCRATCH_BYTES - carry) / per_chunk;
+    return int(win < nch ? win : nch);
+}
+
+hipError_t launch_twopass128_noalloc(const Params& p, int device, hipStream_t stream) {
+    char* base = (device >= 0 && device < kMaxScratchDevices) ? g_scratch_ptr[device] : nullptr;
+    const int win = twopass128_noalloc_window(p);
+    if (!base || win < 1) return hipErrorInvalidValue;
+    // [state carry when state_out is null][records of one window]
+    const int64_t carry = p.s1 ? 0 : round256(int64_t(p.B) * p.H * DK * DK * 4);
+    return launch_twopass128(p, base + carry, win, p.s1 ? nullptr : reinterpret_cast<float*>(base), stream);
+}
+
+hipError_t launch_twopass128(const Params& p, void* ws, int win_chunks, float* carry, hipStream_t stream) {
+    if (p.D != DK || p.chunk_len != L || win_chunks < 1) return hipErrorInvalidValue;
     if (int64_t(L) * p.H * DK * 4 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    const int nch = (p.T + L - 1) / L;
+    if (win_chunks < nch && !p.s1 && !carry) return hipErrorInvalidValue;
     if (p.in_dtype == WKV7_BF16)
-        return p.y_dtype == WKV7_BF16 ? dispatch_modes<bf16_t, bf16_t>(p, ws, stream) : dispatch_modes<bf16_t, float>(p, ws, stream);
-    return p.y_dtype == WKV7_BF16 ? dispatch_modes<float, bf16_t>(p, ws, stream) : dispatch_modes<float, float>(p, ws, stream);
+        return p.y_dtype == WKV7_BF16 ? dispatch_modes<bf16_t, bf16_t>(p, ws, win_chunks, carry, stream)
+                                      : dispatch_modes<bf16_t, float>(p, ws, win_chunks, carry, stream);
+    return p.y_dtype == WKV7_BF16 ? dispatch_modes<float, bf16_t>(p, ws, win_chunks, carry, stream)
+                                  : dispatch_modes<float, float>(p, ws, win_chunks, carry, stream);
 }
 
 }  // namespace wkv7

@@ -14,7 +14,7 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "wkv7_forward", "wkv7_backward", "wkv7_decode_step", "wkv7_resolve_algo", "wkv7_workspace_bytes",
+    "wkv7_forward", "wkv7_forward_noalloc", "wkv7_backward", "wkv7_decode_step", "wkv7_resolve_algo", "wkv7_workspace_bytes",
     "wkv7_backward_workspace_bytes", "wkv4_forward", "wkv4_workspace_bytes", "Wkv7Error",
     "lib_path", "load_library",
     "WKV7_OK", "WKV7_EINVAL", "WKV7_EUNSUPPORTED", "WKV7_EDEVICE", "WKV7_ELAUNCH",
@@ -26,7 +26,7 @@ _DTYPES = {"f32": 0, "bf16": 1}
 W_MODES = {"decay": 0, "logneglog": 1}
 ALGOS = {"auto": 0, "scan": 1, "chunked": 2, "two_pass": 3}
 AB_MODES = {"given": 0, "from_k": 1}
-EXPORTED_SYMBOLS = ("wkv7_forward", "wkv7_forward_ws", "wkv7_workspace_bytes", "wkv7_decode_step",
+EXPORTED_SYMBOLS = ("wkv7_forward", "wkv7_forward_ws", "wkv7_forward_noalloc", "wkv7_workspace_bytes", "wkv7_decode_step",
                     "wkv7_backward", "wkv7_backward_workspace_bytes", "wkv4_forward", "wkv4_workspace_bytes",
                     "wkv7_resolve_algo", "wkv7_strerror", "wkv7_last_error", "wkv7_abi_version")
 
@@ -72,7 +72,7 @@ def load_library():
     lib = ctypes.CDLL(path)
     vp = ctypes.c_void_p
     sig = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    for name in ("wkv7_forward", "wkv7_decode_step"):
+    for name in ("wkv7_forward", "wkv7_decode_step", "wkv7_forward_noalloc"):
         fn = getattr(lib, name)
         fn.argtypes = sig
         fn.restype = ctypes.c_int
@@ -237,6 +237,30 @@ def wkv7_forward(r, w, k, v, a, b, state=None, *, w_mode: str = "decay", y_dtype
     else:
         _call("wkv7_forward", desc, r, w, k, v, a, b, state, y, state_out)
     return y, state_out
+
+
+def wkv7_forward_noalloc(r, w, k, v, a, b, state=None, *, w_mode: str = "decay", y_dtype: Optional[str] = None,
+                         algo: str = "auto", chunk_len: int = 0, y_scale: float = 1.0, r_k=None,
+                         ab_mode: str = "given", mask=None, y=None, state_out=None,
+                         return_state: bool = True) -> Tuple[object, object]:
+    """wkv7_forward through the allocation-free entry point: no workspace, the
+    two-pass form runs in the library's static device scratch.  Arguments as in
+    wkv7_forward; `y` and `state_out` are allocated here unless given."""
+    torch = _torch()
+    B, T, H, H_kv, D = _check_inputs(r, w, k, v, a, b, state, r_k, mask, ab_mode)
+    ydt = y_dtype or _dtype_name(r)
+    if y is None:
+        y = torch.empty((B, T, H, D), dtype=torch.float32 if ydt == "f32" else torch.bfloat16, device=r.device)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=r.device)
+    desc = make_desc(B, T, H, D, H_kv=H_kv, in_dtype=_dtype_name(r), y_dtype=ydt, w_mode=w_mode, algo=algo,
+                     chunk_len=chunk_len, y_scale=y_scale, r_k_ptr=_ptr(r_k), ab_mode=ab_mode,
+                     mask_ptr=_ptr(mask))
+    _call("wkv7_forward_noalloc", desc, r, w, k, v, a, b, state, y, state_out)
+    return y, state_out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def wkv7_decode_step(r, w, k, v, a, b, state, *, w_mode: str = "decay", y_dtype: Optional[str] = None,

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_strerror():
     lib = W.load_library()
-    assert lib.wkv7_abi_version() == 4
+    assert lib.wkv7_abi_version() == 5
     assert lib.wkv7_strerror(0) == b"ok"
     assert lib.wkv7_strerror(W.WKV7_EINVAL) == b"invalid argument"
     assert lib.wkv7_strerror(99) == b"unknown status"
@@ -345,3 +345,23 @@ def test_wkv4_workspace_must_not_overlap_any_array():
     for n in names:
         assert _wkv4(desc, **ptrs, ws=ptrs[n] + 16, ws_bytes=need) == W.WKV7_EINVAL
         assert b"workspace overlaps" in lib.wkv7_last_error(), n
+
+
+def test_noalloc_rejects_more_heads_than_the_scratch_holds():
+    """wkv7_forward_noalloc: one 32-token chunk record per (b, h) must fit the static
+    scratch; B H = 2048 at D = 128 needs 111 MB > 64 MiB.  Rejected before any HIP call."""
+    lib = W.load_library()
+    ptrs = [BASE + i * SP for i in range(8)]
+    desc = W.make_desc(1, 64, 2048, 128)
+    assert lib.wkv7_forward_noalloc(ctypes.byref(desc), *ptrs[:6], None, ptrs[6], ptrs[7], None) == W.WKV7_EUNSUPPORTED
+    assert b"static scratch" in lib.wkv7_last_error()
+    # Without state_out the state carry takes room too: 1000 heads fit with it given, not without.
+    need = 1000 * 54272
+    assert need < W.NOALLOC_SCRATCH_BYTES < need + 1000 * 128 * 128 * 4
+    desc = W.make_desc(1, 64, 1000, 128)
+    assert lib.wkv7_forward_noalloc(ctypes.byref(desc), *ptrs[:6], None, ptrs[6], None, None) == W.WKV7_EUNSUPPORTED
+    assert b"state carry" in lib.wkv7_last_error()
+    # Other argument errors are those of wkv7_forward_ws.
+    assert lib.wkv7_forward_noalloc(None, *ptrs[:6], None, ptrs[6], ptrs[7], None) == W.WKV7_EINVAL
+    desc = W.make_desc(2, 64, 4, 128)
+    assert lib.wkv7_forward_noalloc(ctypes.byref(desc), *ptrs[:6], None, ptrs[0], ptrs[7], None) == W.WKV7_EINVAL
