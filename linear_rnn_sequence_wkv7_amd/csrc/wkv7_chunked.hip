@@ -43,6 +43,15 @@
 // whenever the two issued close together (the compiler's wait states did not
 // cover it), so a single 16-deep term is padded to 32 with zeros instead.
 //
+// Kernel vectors from k (KK): the a slot carries alpha and b is not read; per
+// token kk = k / n with n = max(|k|, 1e-12), a = -kk, b = kk alpha and
+// k' = k (1 - decay + alpha) (the hxa07D article's preparation before its
+// kernel call, section 8).  The eight row threads of a token hold its 64 keys,
+// so they form |k|^2 by an 8-lane sum and publish 1 / n in LDS.  The column
+// threads, one chunk ahead, form k' and k alpha 2^(g_L - g) without it, and
+// scale their Bh^T by 1 / n after the row phase of the chunk, so both layouts
+// use the same 1 / n.  Row threads also read the decay row for k'.
+//
 // Global memory is read and written through buffer descriptors that cover
 // the valid tokens of one chunk of one sequence: tokens past the end read as
 // zero (identity tokens: a = b = k = v = r = 0; w is set to 1 explicitly) and
@@ -104,7 +113,8 @@ constexpr int OFF_XS = OFF_BONUS + 256;    // state halves exchanged by the two 
 constexpr int XS_BYTES = 4 * 2 * 2 * 64 * 16;   // [strip][half][hi/lo][lane] 16 B
 constexpr int OFF_TOT = OFF_XS + XS_BYTES; // fp32 [8][64] column-segment totals (own slot: written during P5)
 constexpr int OFF_RK = OFF_TOT + 8 * 64 * 4;  // fp32 [64] r_k of this head (epilogue)
-constexpr int OFF_VTL = OFF_RK + 64 * 4;      // V^T lo part (fp32 inputs only)
+constexpr int OFF_INVN = OFF_RK + 64 * 4;     // fp32 [64] 1 / max(|k_t|, 1e-12) of the chunk's tokens (KK)
+constexpr int OFF_VTL = OFF_INVN + 64 * 4;    // V^T lo part (fp32 inputs only)
 constexpr int SMEM_BF16 = OFF_VTL;
 constexpr int SMEM_F32 = OFF_VTL + MAT;
 static_assert(2 * 64 * PE * 4 <= 4 * MAT, "decay tables fit");
@@ -238,7 +248,7 @@ template <int V> struct IC { static constexpr int value = V; };
 // balances the triangular products A_rk V and A_rb SA between the two halves.
 __host__ __device__ constexpr int ytile(int hf, int u) { return hf ? 1 + u : 3 * u; }
 
-template <typename Tin, typename Ty, bool LOGW, bool EPI, bool MASK>
+template <typename Tin, typename Ty, bool LOGW, bool EPI, bool MASK, bool KK>
 __global__ __launch_bounds__(NTHR)
 void chunked_kernel(ChunkArgs g) {
     constexpr bool VSPLIT = sizeof(Tin) == 4;   // fp32 v is not exact in bf16
@@ -311,6 +321,7 @@ void chunked_kernel(ChunkArgs g) {
     const uint32_t row_kv = uint32_t(tr) * stkv + uint32_t(hk * DH + 8 * qr) * SI;
 
     uint32_t cw[8], cb[8], ck[8], cv[8];
+    // Row loads; KK: rb holds the decay input row w (b is not read).
     Row8<Tin> rr, ra, rb, rkv;
     // Mask bytes (1 without a mask): lane l of a column wave holds token 8 pc + (l & 7)'s,
     // a row thread its token's.  Masked tokens become identity tokens (zeros, decay 1).
@@ -323,7 +334,8 @@ void chunked_kernel(ChunkArgs g) {
         return make_rsrc(base + t0 * stride, uint32_t(nv) * stride);
     };
     auto load_cols = [&](int c0) {
-        const rsrc_t Rw = chunk_rsrc(c0, wp, stq), Rb = chunk_rsrc(c0, bp, stq);
+        // KK: the b slot of the column loads carries alpha (the a input); b is not read.
+        const rsrc_t Rw = chunk_rsrc(c0, wp, stq), Rb = chunk_rsrc(c0, KK ? ap : bp, stq);
         const rsrc_t Rk = chunk_rsrc(c0, kp, stkv), Rv = chunk_rsrc(c0, vp, stkv);
         if constexpr (MASK) cm = __builtin_amdgcn_raw_buffer_load_b8(chunk_rsrc(c0, mp, 1u), uint32_t(8 * pc + (l & 7)), 0, 0);
         uint32_t oq[8], okv[8];
@@ -353,7 +365,7 @@ void chunked_kernel(ChunkArgs g) {
     auto load_rows = [&](int c0) {
         rr.load(chunk_rsrc(c0, rp, stq), row_q);
         ra.load(chunk_rsrc(c0, ap, stq), row_q);
-        rb.load(chunk_rsrc(c0, bp, stq), row_q);
+        rb.load(chunk_rsrc(c0, KK ? wp : bp, stq), row_q);
         rkv.load(chunk_rsrc(c0, kp, stkv), row_kv);
         if constexpr (MASK) rm = __builtin_amdgcn_raw_buffer_load_b8(chunk_rsrc(c0, mp, 1u), uint32_t(tr), 0, 0);
     };
@@ -377,6 +389,7 @@ void chunked_kernel(ChunkArgs g) {
     // begins.
     float pre[8];
     uint32_t d_bh4[4], d_khh[4], d_khl[4], d_vh[4], d_vl[4];
+    float d_bhf[KK ? 8 : 1];   // KK: Bh^T column values before their 1 / n
     float d_EL = 0.f;
     auto p1a_prefix = [&](int c0) {
         float run = LOGW ? 0.f : 1.f;
@@ -385,13 +398,26 @@ void chunked_kernel(ChunkArgs g) {
             const float x = __uint_as_float(cw[e]);
             // Wave-uniform; w = 1 past the end and for masked tokens, whose b and k are zeroed.
             const bool ok = c0 + 8 * pc + e < T && (!MASK || __builtin_amdgcn_readlane(int(cm), e) != 0);
-            if constexpr (LOGW) run += ok ? -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e : 0.f;
-            else run *= ok ? x : 1.f;
+            float dec;   // this token's decay (KK: the k (1 - decay + alpha) factor)
+            if constexpr (LOGW) {
+                const float lw = -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e;
+                run += ok ? lw : 0.f;
+                dec = KK ? __builtin_amdgcn_exp2f(lw) : 0.f;
+            } else {
+                run *= ok ? x : 1.f;
+                dec = x;
+            }
             if constexpr (MASK) {
                 cb[e] = ok ? cb[e] : 0u;
                 ck[e] = ok ? ck[e] : 0u;
             }
             pre[e] = run;
+            if constexpr (KK) {
+                // b without its 1 / n (applied to Bh^T after the row phase), k' = k (1 - decay + alpha).
+                const float kv = __uint_as_float(ck[e]), al = __uint_as_float(cb[e]);
+                cb[e] = __float_as_uint(kv * al);
+                ck[e] = __float_as_uint(kv * (1.f - dec + al));
+            }
         }
         sts<float>(smem + OFF_TOT, (pc * 64 + jc) * 4, run);
     };
@@ -430,7 +456,12 @@ void chunked_kernel(ChunkArgs g) {
             }
             const float b0 = __uint_as_float(cb[e]), b1 = __uint_as_float(cb[e + 1]);
             const float k0 = __uint_as_float(ck[e]), k1 = __uint_as_float(ck[e + 1]);
-            d_bh4[e / 2] = pack_bf16(b0 * Eh[0], b1 * Eh[1]);
+            if constexpr (KK) {
+                d_bhf[e] = b0 * Eh[0];
+                d_bhf[e + 1] = b1 * Eh[1];
+            } else {
+                d_bh4[e / 2] = pack_bf16(b0 * Eh[0], b1 * Eh[1]);
+            }
             split2(k0 * Eh[0], k1 * Eh[1], d_khh[e / 2], d_khl[e / 2]);
             if constexpr (VSPLIT) {
                 split2(__uint_as_float(cv[e]), __uint_as_float(cv[e + 1]), d_vh[e / 2], d_vl[e / 2]);
@@ -448,8 +479,21 @@ void chunked_kernel(ChunkArgs g) {
         if constexpr (VSPLIT) sts<uint4>(smem + OFF_VTL, o, make_uint4(d_vl[0], d_vl[1], d_vl[2], d_vl[3]));
         // Bh^T on the pair-interleaved token axis: tokens 8 pc + (0..3) and 8 pc + (4..7).
         const int ob = (jc * P72 + pairpos(8 * pc)) * 2;
-        sts<uint2>(smem + OFF_BHT, ob, make_uint2(d_bh4[0], d_bh4[1]));
-        sts<uint2>(smem + OFF_BHT, ob + 16, make_uint2(d_bh4[2], d_bh4[3]));
+        if constexpr (!KK) {
+            sts<uint2>(smem + OFF_BHT, ob, make_uint2(d_bh4[0], d_bh4[1]));
+            sts<uint2>(smem + OFF_BHT, ob + 16, make_uint2(d_bh4[2], d_bh4[3]));
+        }
+    };
+    // KK: Bh^T of the chunk once its row phase has published 1 / n per token.
+    auto store_bh_kk = [&]() {
+        const float4 n0 = lds<float4>(smem + OFF_INVN, 32 * pc), n1 = lds<float4>(smem + OFF_INVN, 32 * pc + 16);
+        const float invn[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
+        uint32_t bh4[4];
+        #pragma unroll
+        for (int e = 0; e < 8; e += 2) bh4[e / 2] = pack_bf16(d_bhf[e] * invn[e], d_bhf[e + 1] * invn[e + 1]);
+        const int ob = (jc * P72 + pairpos(8 * pc)) * 2;
+        sts<uint2>(smem + OFF_BHT, ob, make_uint2(bh4[0], bh4[1]));
+        sts<uint2>(smem + OFF_BHT, ob + 16, make_uint2(bh4[2], bh4[3]));
     };
     p1a_prefix(0);
     __syncthreads();
@@ -499,13 +543,40 @@ void chunked_kernel(ChunkArgs g) {
                 rk8[0] = q0.x; rk8[1] = q0.y; rk8[2] = q0.z; rk8[3] = q0.w;
                 rk8[4] = q1.x; rk8[5] = q1.y; rk8[6] = q1.z; rk8[7] = q1.w;
             }
+            // KK: 1 / n of this token from its 64 keys, held by the 8 row threads of the
+            // token (lanes 8 m .. 8 m + 7 of one wave); published for the column threads.
+            float invn = 0.f;
+            if constexpr (KK) {
+                float ss = 0.f;
+                #pragma unroll
+                for (int e = 0; e < 8; ++e) ss = fmaf(rkv.get(e), rkv.get(e), ss);
+                ss += dpp<kDppQuadXor1>(ss);
+                ss += dpp<kDppQuadXor2>(ss);
+                ss += dpp<kDppRowHalfMirror>(ss);
+                invn = inv_key_norm(ss);
+                if (qr == 0) sts<float>(smem + OFF_INVN, tr * 4, invn);
+            }
             #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 const float r0 = rr.get(e), r1 = rr.get(e + 1);
-                const float k0 = rkv.get(e), k1 = rkv.get(e + 1);
-                at[e / 2] = pack_bf16(ra.get(e) * Ep[e], ra.get(e + 1) * Ep[e + 1]);
+                float a0, a1, b0, b1, k0, k1;
+                if constexpr (KK) {
+                    // a = -k / n, b = k alpha / n, k' = k (1 - decay + alpha); ra holds alpha, rb the w row.
+                    const float kr0 = rkv.get(e), kr1 = rkv.get(e + 1);
+                    const float al0 = ra.get(e), al1 = ra.get(e + 1);
+                    const float d0 = LOGW ? decay_from_logneglog(rb.get(e)) : rb.get(e);
+                    const float d1 = LOGW ? decay_from_logneglog(rb.get(e + 1)) : rb.get(e + 1);
+                    a0 = -kr0 * invn; a1 = -kr1 * invn;
+                    b0 = kr0 * al0 * invn; b1 = kr1 * al1 * invn;
+                    k0 = kr0 * (1.f - d0 + al0); k1 = kr1 * (1.f - d1 + al1);
+                } else {
+                    a0 = ra.get(e); a1 = ra.get(e + 1);
+                    b0 = rb.get(e); b1 = rb.get(e + 1);
+                    k0 = rkv.get(e); k1 = rkv.get(e + 1);
+                }
+                at[e / 2] = pack_bf16(a0 * Ep[e], a1 * Ep[e + 1]);
                 split2(r0 * E[e], r1 * E[e + 1], rth[e / 2], rtl[e / 2]);
-                bt[e / 2] = pack_bf16(rb.get(e) * Ei[e], rb.get(e + 1) * Ei[e + 1]);
+                bt[e / 2] = pack_bf16(b0 * Ei[e], b1 * Ei[e + 1]);
                 split2(k0 * Ei[e], k1 * Ei[e + 1], kth[e / 2], ktl[e / 2]);
                 if constexpr (EPI) bonus_part += r0 * k0 * rk8[e] + r1 * k1 * rk8[e + 1];
             }
@@ -533,6 +604,7 @@ void chunked_kernel(ChunkArgs g) {
         }
         load_rows(c0 + L);   // next chunk's rows, for its P1b
         __syncthreads();
+        if constexpr (KK) store_bh_kk();   // read in P7, after the barriers to come
 
         // ---------------- P2: the four L x L matrices; inverses of the diagonal blocks ----------------
         // Tile ids 0..9 list (tb, sb), sb <= tb, in row order.  Waves 0..3 take the
@@ -842,10 +914,10 @@ void chunked_kernel(ChunkArgs g) {
     }
 }
 
-template <typename Tin, typename Ty, bool LOGW, bool EPI, bool MASK>
+template <typename Tin, typename Ty, bool LOGW, bool EPI, bool MASK, bool KK>
 hipError_t launch_t(const Params& p, hipStream_t stream) {
     ChunkArgs g{p.r, p.w, p.k, p.v, p.a, p.b, p.s0, p.r_k, p.mask, p.y, p.s1, p.T, p.H, p.H_kv, p.y_scale};
-    auto kern = chunked_kernel<Tin, Ty, LOGW, EPI, MASK>;
+    auto kern = chunked_kernel<Tin, Ty, LOGW, EPI, MASK, KK>;
     constexpr int smem = sizeof(Tin) == 4 ? SMEM_F32 : SMEM_BF16;
     static bool attr_set = false;   // per template instance; idempotent if raced
     if (!attr_set) {
@@ -858,17 +930,22 @@ hipError_t launch_t(const Params& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename Tin, typename Ty, bool MASK>
+template <typename Tin, typename Ty, bool MASK, bool KK>
 hipError_t dispatch_epi(const Params& p, hipStream_t s) {
     const bool logw = p.w_mode == WKV7_W_LOGNEGLOG;
     const bool epi = p.r_k != nullptr;
-    if (logw) return epi ? launch_t<Tin, Ty, true, true, MASK>(p, s) : launch_t<Tin, Ty, true, false, MASK>(p, s);
-    return epi ? launch_t<Tin, Ty, false, true, MASK>(p, s) : launch_t<Tin, Ty, false, false, MASK>(p, s);
+    if (logw) return epi ? launch_t<Tin, Ty, true, true, MASK, KK>(p, s) : launch_t<Tin, Ty, true, false, MASK, KK>(p, s);
+    return epi ? launch_t<Tin, Ty, false, true, MASK, KK>(p, s) : launch_t<Tin, Ty, false, false, MASK, KK>(p, s);
+}
+
+template <typename Tin, typename Ty, bool KK>
+hipError_t dispatch_mask(const Params& p, hipStream_t s) {
+    return p.mask ? dispatch_epi<Tin, Ty, true, KK>(p, s) : dispatch_epi<Tin, Ty, false, KK>(p, s);
 }
 
 template <typename Tin, typename Ty>
 hipError_t dispatch_modes(const Params& p, hipStream_t s) {
-    return p.mask ? dispatch_epi<Tin, Ty, true>(p, s) : dispatch_epi<Tin, Ty, false>(p, s);
+    return p.ab_mode == WKV7_AB_FROM_K ? dispatch_mask<Tin, Ty, true>(p, s) : dispatch_mask<Tin, Ty, false>(p, s);
 }
 
 }  // namespace
