@@ -87,9 +87,8 @@ enum wkv7_w_mode {
 enum wkv7_ab_mode {
     WKV7_AB_GIVEN = 0,      /* a and b are inputs */
     WKV7_AB_FROM_K = 1      /* a holds alpha, b is unused (may be NULL); a, b and the scaled k
-                               are formed from k, alpha and the decay (see above).  Runs in the
-                               scan, the decode step, the two-pass form and the D = 64 chunked
-                               kernel; ALGO_CHUNKED at D = 128 rejects it with EUNSUPPORTED. */
+                               are formed from k, alpha and the decay (see above).  Every
+                               algorithm and the decode step support it. */
 };
 
 enum wkv7_algo {
@@ -240,7 +239,7 @@ int64_t wkv7_backward_workspace_bytes(const wkv7_desc* desc);
 /* Which algorithm wkv7_forward would run for this descriptor (WKV7_ALGO_SCAN or
  * WKV7_ALGO_CHUNKED), or a negative wkv7_status if the descriptor is invalid.
  * AUTO picks the chunked form once T covers one chunk (T >= chunk length),
- * the scan otherwise; with ab_mode FROM_K at D = 128 it picks the scan.  An explicit
+ * the scan otherwise.  An explicit
  * WKV7_ALGO_TWO_PASS is returned as is (wkv7_forward rejects it;
  * wkv7_forward_ws runs it).  Host only: no HIP call. */
 int wkv7_resolve_algo(const wkv7_desc* desc);

@@ -104,9 +104,6 @@ int check_desc(const wkv7_desc* d, wkv7::Params* p) {
         return fail(WKV7_EINVAL, "algo %d unknown", d->algo);
     if (d->ab_mode != WKV7_AB_GIVEN && d->ab_mode != WKV7_AB_FROM_K)
         return fail(WKV7_EINVAL, "ab_mode %d unknown", d->ab_mode);
-    if (d->ab_mode == WKV7_AB_FROM_K && d->algo == WKV7_ALGO_CHUNKED && d->D != 64)
-        return fail(WKV7_EUNSUPPORTED, "ab_mode FROM_K runs in the scan, the decode step, the two-pass form and "
-                    "the D=64 chunked kernel, not in algo CHUNKED at D=%d", d->D);
     if (d->algo == WKV7_ALGO_TWO_PASS && d->D != 128)
         return fail(WKV7_EUNSUPPORTED, "the two-pass form needs D=128 (got %d)", d->D);
     // Each chunked kernel has one chunk length: 64 at D = 64, 32 at D = 128.
@@ -150,14 +147,12 @@ int check_ptrs(const wkv7::Params& p, const void* const* in6, const void* y,
 }
 
 // AUTO: the chunked matrix-core form once a sequence spans at least one full
-// chunk; with a workspace at D = 128 its two-pass variant.  The scan otherwise,
-// and for kernel vectors formed from k at D = 128 without a workspace (the
-// one-pass D = 128 kernel does not form them).
+// chunk; with a workspace at D = 128 its two-pass variant.  The scan otherwise.
 int resolve_algo(const wkv7::Params& p, int requested, bool with_workspace) {
     if (requested != WKV7_ALGO_AUTO) return requested;
     if (p.T < p.chunk_len) return WKV7_ALGO_SCAN;
     if (with_workspace && p.D == 128) return WKV7_ALGO_TWO_PASS;
-    return p.ab_mode == WKV7_AB_FROM_K && p.D == 128 ? WKV7_ALGO_SCAN : WKV7_ALGO_CHUNKED;
+    return WKV7_ALGO_CHUNKED;
 }
 
 int64_t workspace_bytes(const wkv7::Params& p, int algo) {

@@ -31,6 +31,11 @@
 // every accumulator chain uses the single 16x16x32 opcode, and global memory
 // goes through per-chunk buffer descriptors (tokens past the end read as zero,
 // their stores are dropped).
+// Kernel vectors from k (KK) as in the D = 64 kernel: the a slot carries alpha,
+// b is not read; the 16 row threads of a token form 1 / n, n = max(|k|, 1e-12),
+// and publish it in LDS; the column threads form k' = k (1 - decay + alpha) and
+// k alpha one chunk ahead and scale their Bh^T by 1 / n after the row phase
+// (the hxa07D article's preparation before its kernel call, section 8).
 #include "wkv7_internal.h"
 #include "wkv7_device.h"
 
@@ -84,7 +89,8 @@ constexpr int OFF_EL = OFF_DINV + 2 * 16 * PD * 2;  // fp32 [DK] 2^g_L
 constexpr int OFF_BONUS = OFF_EL + DK * 4;          // fp32 [L]
 constexpr int OFF_XS = OFF_BONUS + L * 4;           // [strip][pair][hi/lo][lane] 16 B
 constexpr int XS_BYTES = 2 * 4 * 2 * 64 * 16;
-constexpr int OFF_VTL = OFF_XS + XS_BYTES;          // V^T lo part (fp32 inputs only)
+constexpr int OFF_INVN = OFF_XS + XS_BYTES;         // fp32 [L] 1 / max(|k_t|, 1e-12) of the chunk (KK)
+constexpr int OFF_VTL = OFF_INVN + L * 4;           // V^T lo part (fp32 inputs only)
 constexpr int SMEM_BF16 = OFF_VTL;
 constexpr int SMEM_F32 = OFF_VTL + MATV;
 static_assert(6 * MATV <= 3 * MATK, "L x L matrices fit region 1");
@@ -202,7 +208,7 @@ template <> struct Row8<float> {
 
 template <int V> struct IC { static constexpr int value = V; };
 
-template <typename Tin, typename Ty, bool LOGW, bool EPI, bool MASK>
+template <typename Tin, typename Ty, bool LOGW, bool EPI, bool MASK, bool KK>
 __global__ __launch_bounds__(NTHR)
 void chunked128_kernel(Args g) {
     constexpr bool VSPLIT = sizeof(Tin) == 4;
@@ -276,6 +282,7 @@ void chunked128_kernel(Args g) {
     const uint32_t row_kv = uint32_t(tr) * stkv + uint32_t(hk * DK + 8 * qr) * SI;
 
     uint32_t cw[8], cb[8], ck[8], cv[8];
+    // Row loads; KK: rb holds the decay input row w (b is not read).
     Row8<Tin> rr, ra, rb, rkv;
     // Mask bytes (1 without a mask): lane l of a column wave holds token 8 pc + (l & 7)'s,
     // a row thread its token's.  Masked tokens become identity tokens (zeros, decay 1).
@@ -289,7 +296,8 @@ void chunked128_kernel(Args g) {
         return make_rsrc(base + t0 * stride, uint32_t(nv) * stride);
     };
     auto load_cols = [&](int c0) {
-        const rsrc_t Rw = chunk_rsrc(c0, wp, stq), Rb = chunk_rsrc(c0, bp, stq);
+        // KK: the b slot of the column loads carries alpha (the a input); b is not read.
+        const rsrc_t Rw = chunk_rsrc(c0, wp, stq), Rb = chunk_rsrc(c0, KK ? ap : bp, stq);
         const rsrc_t Rk = chunk_rsrc(c0, kp_, stkv), Rv = chunk_rsrc(c0, vp, stkv);
         if constexpr (MASK) cm = __builtin_amdgcn_raw_buffer_load_b8(chunk_rsrc(c0, mp, 1u), uint32_t(8 * pc + (l & 7)), 0, 0);
         #pragma unroll
@@ -303,7 +311,7 @@ void chunked128_kernel(Args g) {
     auto load_rows = [&](int c0) {
         rr.load(chunk_rsrc(c0, rp, stq), row_q);
         ra.load(chunk_rsrc(c0, ap, stq), row_q);
-        rb.load(chunk_rsrc(c0, bp, stq), row_q);
+        rb.load(chunk_rsrc(c0, KK ? wp : bp, stq), row_q);
         rkv.load(chunk_rsrc(c0, kp_, stkv), row_kv);
         if constexpr (MASK) rm = __builtin_amdgcn_raw_buffer_load_b8(chunk_rsrc(c0, mp, 1u), uint32_t(tr), 0, 0);
     };
@@ -321,6 +329,7 @@ void chunked128_kernel(Args g) {
     // (Kh^T, V^T, Bh^T, 2^g_L) stay in registers (d_*) until chunk c + 1 begins.
     float pre[8];
     uint32_t d_bh4[4], d_khh[4], d_khl[4], d_vh[4], d_vl[4];
+    float d_bhf[KK ? 8 : 1];   // KK: Bh^T column values before their 1 / n
     float d_EL = 0.f;
     auto p1a_prefix = [&](int c0) {
         float run = LOGW ? 0.f : 1.f;
@@ -329,13 +338,26 @@ void chunked128_kernel(Args g) {
             const float x = __uint_as_float(cw[e]);
             // Wave-uniform; w = 1 past the end and for masked tokens, whose b and k are zeroed.
             const bool ok = c0 + 8 * pc + e < T && (!MASK || __builtin_amdgcn_readlane(int(cm), e) != 0);
-            if constexpr (LOGW) run += ok ? -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e : 0.f;
-            else run *= ok ? x : 1.f;
+            float dec;   // this token's decay (KK: the k (1 - decay + alpha) factor)
+            if constexpr (LOGW) {
+                const float lw = -__builtin_amdgcn_exp2f(x * kLog2e) * kLog2e;
+                run += ok ? lw : 0.f;
+                dec = KK ? __builtin_amdgcn_exp2f(lw) : 0.f;
+            } else {
+                run *= ok ? x : 1.f;
+                dec = x;
+            }
             if constexpr (MASK) {
                 cb[e] = ok ? cb[e] : 0u;
                 ck[e] = ok ? ck[e] : 0u;
             }
             pre[e] = run;
+            if constexpr (KK) {
+                // b without its 1 / n (applied to Bh^T after the row phase), k' = k (1 - decay + alpha).
+                const float kv = __uint_as_float(ck[e]), al = __uint_as_float(cb[e]);
+                cb[e] = __float_as_uint(kv * al);
+                ck[e] = __float_as_uint(kv * (1.f - dec + al));
+            }
         }
         sts<float>(smem + OFF_TOT, (pc * DK + jc) * 4, run);
     };
@@ -374,7 +396,12 @@ void chunked128_kernel(Args g) {
             }
             const float b0 = __uint_as_float(cb[e]), b1 = __uint_as_float(cb[e + 1]);
             const float k0 = __uint_as_float(ck[e]), k1 = __uint_as_float(ck[e + 1]);
-            d_bh4[e / 2] = pack_bf16(b0 * Eh[0], b1 * Eh[1]);
+            if constexpr (KK) {
+                d_bhf[e] = b0 * Eh[0];
+                d_bhf[e + 1] = b1 * Eh[1];
+            } else {
+                d_bh4[e / 2] = pack_bf16(b0 * Eh[0], b1 * Eh[1]);
+            }
             split2(k0 * Eh[0], k1 * Eh[1], d_khh[e / 2], d_khl[e / 2]);
             if constexpr (VSPLIT) {
                 split2(__uint_as_float(cv[e]), __uint_as_float(cv[e + 1]), d_vh[e / 2], d_vl[e / 2]);
@@ -389,12 +416,25 @@ void chunked128_kernel(Args g) {
         sts<uint4>(smem + OFF_KHTH, o, make_uint4(d_khh[0], d_khh[1], d_khh[2], d_khh[3]));
         sts<uint4>(smem + OFF_KHTL, o, make_uint4(d_khl[0], d_khl[1], d_khl[2], d_khl[3]));
         const int ob = (jc * PT + pairpos(8 * pc)) * 2;
-        sts<uint2>(smem + OFF_BHT, ob, make_uint2(d_bh4[0], d_bh4[1]));
-        sts<uint2>(smem + OFF_BHT, ob + 16, make_uint2(d_bh4[2], d_bh4[3]));
+        if constexpr (!KK) {
+            sts<uint2>(smem + OFF_BHT, ob, make_uint2(d_bh4[0], d_bh4[1]));
+            sts<uint2>(smem + OFF_BHT, ob + 16, make_uint2(d_bh4[2], d_bh4[3]));
+        }
         if (jc < DV) {
             sts<uint4>(smem + OFF_VT, o, make_uint4(d_vh[0], d_vh[1], d_vh[2], d_vh[3]));
             if constexpr (VSPLIT) sts<uint4>(smem + OFF_VTL, o, make_uint4(d_vl[0], d_vl[1], d_vl[2], d_vl[3]));
         }
+    };
+    // KK: Bh^T of the chunk once its row phase has published 1 / n per token.
+    auto store_bh_kk = [&]() {
+        const float4 n0 = lds<float4>(smem + OFF_INVN, 32 * pc), n1 = lds<float4>(smem + OFF_INVN, 32 * pc + 16);
+        const float invn[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
+        uint32_t bh4[4];
+        #pragma unroll
+        for (int e = 0; e < 8; e += 2) bh4[e / 2] = pack_bf16(d_bhf[e] * invn[e], d_bhf[e + 1] * invn[e + 1]);
+        const int ob = (jc * PT + pairpos(8 * pc)) * 2;
+        sts<uint2>(smem + OFF_BHT, ob, make_uint2(bh4[0], bh4[1]));
+        sts<uint2>(smem + OFF_BHT, ob + 16, make_uint2(bh4[2], bh4[3]));
     };
     p1a_prefix(0);
     __syncthreads();
@@ -435,13 +475,41 @@ void chunked128_kernel(Args g) {
             }
             uint32_t at[4], rth[4], rtl[4], bt[4], kth[4], ktl[4];
             float bonus_part = 0.f;
+            // KK: 1 / n of this token from its 128 keys, held by its 16 row threads (8
+            // consecutive lanes and the same 8 lanes + 32); published for the column threads.
+            float invn = 0.f;
+            if constexpr (KK) {
+                float ss = 0.f;
+                #pragma unroll
+                for (int e = 0; e < 8; ++e) ss = fmaf(rkv.get(e), rkv.get(e), ss);
+                ss += dpp<kDppQuadXor1>(ss);
+                ss += dpp<kDppQuadXor2>(ss);
+                ss += dpp<kDppRowHalfMirror>(ss);
+                ss += __shfl_xor(ss, 32);
+                invn = inv_key_norm(ss);
+                if (qr == 0) sts<float>(smem + OFF_INVN, tr * 4, invn);
+            }
             #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 const float r0 = rr.get(e), r1 = rr.get(e + 1);
-                const float k0 = rkv.get(e), k1 = rkv.get(e + 1);
-                at[e / 2] = pack_bf16(ra.get(e) * Ep[e], ra.get(e + 1) * Ep[e + 1]);
+                float a0, a1, b0, b1, k0, k1;
+                if constexpr (KK) {
+                    // a = -k / n, b = k alpha / n, k' = k (1 - decay + alpha); ra holds alpha, rb the w row.
+                    const float kr0 = rkv.get(e), kr1 = rkv.get(e + 1);
+                    const float al0 = ra.get(e), al1 = ra.get(e + 1);
+                    const float d0 = LOGW ? decay_from_logneglog(rb.get(e)) : rb.get(e);
+                    const float d1 = LOGW ? decay_from_logneglog(rb.get(e + 1)) : rb.get(e + 1);
+                    a0 = -kr0 * invn; a1 = -kr1 * invn;
+                    b0 = kr0 * al0 * invn; b1 = kr1 * al1 * invn;
+                    k0 = kr0 * (1.f - d0 + al0); k1 = kr1 * (1.f - d1 + al1);
+                } else {
+                    a0 = ra.get(e); a1 = ra.get(e + 1);
+                    b0 = rb.get(e); b1 = rb.get(e + 1);
+                    k0 = rkv.get(e); k1 = rkv.get(e + 1);
+                }
+                at[e / 2] = pack_bf16(a0 * Ep[e], a1 * Ep[e + 1]);
                 split2(r0 * E[e], r1 * E[e + 1], rth[e / 2], rtl[e / 2]);
-                bt[e / 2] = pack_bf16(rb.get(e) * Ei[e], rb.get(e + 1) * Ei[e + 1]);
+                bt[e / 2] = pack_bf16(b0 * Ei[e], b1 * Ei[e + 1]);
                 split2(k0 * Ei[e], k1 * Ei[e + 1], kth[e / 2], ktl[e / 2]);
                 if constexpr (EPI) bonus_part += r0 * k0 * rk8[e] + r1 * k1 * rk8[e + 1];
             }
@@ -469,6 +537,7 @@ void chunked128_kernel(Args g) {
         }
         load_rows(c0 + L);
         __syncthreads();
+        if constexpr (KK) store_bh_kk();   // read in P7, after the barriers to come
 
         // ---------------- P2: the four L x L matrices; inverses of the diagonal blocks ----------------
         // Units (tile, group) of tiles 0 = (0,0), 1 = (1,0), 2 = (1,1) and groups
@@ -710,11 +779,11 @@ void chunked128_kernel(Args g) {
     }
 }
 
-template <typename Tin, typename Ty, bool LOGW, bool EPI, bool MASK>
+template <typename Tin, typename Ty, bool LOGW, bool EPI, bool MASK, bool KK>
 hipError_t launch_t(const Params& p, hipStream_t stream) {
     const int bh = p.B * p.H;
     Args g{p.r, p.w, p.k, p.v, p.a, p.b, p.s0, p.r_k, p.mask, p.y, p.s1, p.T, p.H, p.H_kv, bh, p.y_scale};
-    auto kern = chunked128_kernel<Tin, Ty, LOGW, EPI, MASK>;
+    auto kern = chunked128_kernel<Tin, Ty, LOGW, EPI, MASK, KK>;
     constexpr int smem = sizeof(Tin) == 4 ? SMEM_F32 : SMEM_BF16;
     static bool attr_set = false;   // per template instance; idempotent if raced
     if (!attr_set) {
@@ -729,17 +798,22 @@ hipError_t launch_t(const Params& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename Tin, typename Ty, bool MASK>
+template <typename Tin, typename Ty, bool MASK, bool KK>
 hipError_t dispatch_epi(const Params& p, hipStream_t s) {
     const bool logw = p.w_mode == WKV7_W_LOGNEGLOG;
     const bool epi = p.r_k != nullptr;
-    if (logw) return epi ? launch_t<Tin, Ty, true, true, MASK>(p, s) : launch_t<Tin, Ty, true, false, MASK>(p, s);
-    return epi ? launch_t<Tin, Ty, false, true, MASK>(p, s) : launch_t<Tin, Ty, false, false, MASK>(p, s);
+    if (logw) return epi ? launch_t<Tin, Ty, true, true, MASK, KK>(p, s) : launch_t<Tin, Ty, true, false, MASK, KK>(p, s);
+    return epi ? launch_t<Tin, Ty, false, true, MASK, KK>(p, s) : launch_t<Tin, Ty, false, false, MASK, KK>(p, s);
+}
+
+template <typename Tin, typename Ty, bool KK>
+hipError_t dispatch_mask(const Params& p, hipStream_t s) {
+    return p.mask ? dispatch_epi<Tin, Ty, true, KK>(p, s) : dispatch_epi<Tin, Ty, false, KK>(p, s);
 }
 
 template <typename Tin, typename Ty>
 hipError_t dispatch_modes(const Params& p, hipStream_t s) {
-    return p.mask ? dispatch_epi<Tin, Ty, true>(p, s) : dispatch_epi<Tin, Ty, false>(p, s);
+    return p.ab_mode == WKV7_AB_FROM_K ? dispatch_mask<Tin, Ty, true>(p, s) : dispatch_mask<Tin, Ty, false>(p, s);
 }
 
 }  // namespace

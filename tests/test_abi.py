@@ -172,20 +172,21 @@ def test_desc_layout():
 
 
 def test_ab_mode_from_k_rules():
-    # The one-pass D = 128 chunked kernel does not form the kernel vectors from k; the
-    # D = 64 one does (B = 0: accepted without any device call).
-    assert _call(good(D=128, T=64, algo="chunked", ab_mode="from_k")) == W.WKV7_EUNSUPPORTED
-    assert _call(good(B=0, T=64, algo="chunked", ab_mode="from_k")) == W.WKV7_OK
+    # Every algorithm forms the kernel vectors from k (B = 0: accepted without any device call).
+    for D in (64, 128):
+        for algo in ("scan", "chunked"):
+            assert _call(good(B=0, D=D, T=64, algo=algo, ab_mode="from_k")) == W.WKV7_OK
     # b is not read: NULL passes its check (the call then fails on the misaligned y).
     assert _call(good(ab_mode="from_k"), {"b": None, "y": FAKE + 4096 + 8}) == W.WKV7_EINVAL
     assert b"y is not" in W.load_library().wkv7_last_error()
     assert _call(good(), {"b": None}) == W.WKV7_EINVAL
     assert b"b is NULL" in W.load_library().wkv7_last_error()
-    # AUTO: the chunked kernel at D = 64 once T covers a chunk; at D = 128 the scan
-    # without a workspace and the two-pass form with one.
+    # AUTO: the chunked kernels once T covers a chunk (the two-pass form with a
+    # workspace at D = 128), the scan below that.
     assert W.wkv7_resolve_algo(2, 64, 4, 64, ab_mode="from_k") == "chunked"
     assert W.wkv7_resolve_algo(2, 63, 4, 64, ab_mode="from_k") == "scan"
-    assert W.wkv7_resolve_algo(2, 64, 4, 128, ab_mode="from_k") == "scan"
+    assert W.wkv7_resolve_algo(2, 64, 4, 128, ab_mode="from_k") == "chunked"
+    assert W.wkv7_resolve_algo(2, 31, 4, 128, ab_mode="from_k") == "scan"
     assert W.wkv7_workspace_bytes(2, 64, 4, 128, ab_mode="from_k") == 2 * 4 * 2 * 54272
     assert W.wkv7_workspace_bytes(2, 64, 4, 64, ab_mode="from_k") == 0
 

@@ -68,7 +68,7 @@ def run(wl, x, algo):
 def supported(algo, D, ab_mode):
     if algo == "two_pass" and D != 128:
         pytest.skip("the two-pass form exists for D = 128 only")
-    return not (algo == "chunked" and ab_mode == "from_k" and D == 128)
+    return True
 
 
 SWEEP = [
@@ -154,7 +154,7 @@ def test_decode_mask_and_from_k(case):
     np.testing.assert_array_equal(s[1], x["state0"][1].astype(np.float64))
 
 
-@pytest.mark.parametrize("algo", ["scan", "two_pass"])
+@pytest.mark.parametrize("algo", ["scan", "chunked", "two_pass"])
 def test_workload_hxa07d_from_k(algo):
     """The hxa07D long-context workload with the kernel vectors formed in the
     kernel, sampled (batch, head) pairs, in the launch configuration the
