@@ -80,9 +80,10 @@ def test_graph_decode_chain():
     check_replays(g, lambda: st_g.copy_(s0), outputs, expected)
 
 
-@pytest.mark.parametrize("D,algo", [(64, "chunked"), (128, "two_pass")])
-def test_graph_forward(D, algo):
-    wl = G.workload("hxa07d_bf16_b2_t16384_h32_kv8_d128", B=2, T=100, H=4, H_kv=2, D=D)
+@pytest.mark.parametrize("D,algo,T", [(64, "chunked", 100), (128, "two_pass", 100), (128, "two_pass", 4096)])
+def test_graph_forward(D, algo, T):
+    """D = 128 at T = 4096: 128 chunks per (b, h) through the two-pass form."""
+    wl = G.workload("hxa07d_bf16_b2_t16384_h32_kv8_d128", B=2, T=T, H=4, H_kv=2, D=D)
     x = G.make_inputs(wl)
     d = dev_inputs(x)
     ws = None
