@@ -209,23 +209,31 @@ template <> struct Row8<float> {
 // Token-axis (pair-interleaved) store of one token's 8 values, rows row0 .. row0 + 7,
 // packed in pairs in v, into a [row][PT] bf16 matrix.  Lanes l and l ^ 1 hold
 // tokens t and t ^ 1: the even lane writes rows row0 .. row0 + 3, the odd lane
-// row0 + 4 .. row0 + 7, each a 32-bit pair of the two tokens.
-__device__ __forceinline__ void pair_col_store(char* base, int row0, int t, const uint32_t (&v)[4]) {
-    uint32_t pv[4];
-    #pragma unroll
-    for (int i = 0; i < 4; ++i) pv[i] = dpp_u32_xor1(v[i]);
+// row0 + 4 .. row0 + 7, each a 32-bit pair of the two tokens (even token low).
+// Each lane sends its partner the two words the partner writes, then forms its
+// own words with one byte permute each (v_perm_b32: bytes 0..3 of the second
+// source, 4..7 of the first; sel[h] takes half h of both words, in the order
+// that puts the even token low).
+struct PairSel {
+    uint32_t sel[2];
+    __device__ __forceinline__ explicit PairSel(int t) {
+        const bool odd = t & 1;
+        sel[0] = odd ? 0x01000504u : 0x05040100u;
+        sel[1] = odd ? 0x03020706u : 0x07060302u;
+    }
+};
+__device__ __forceinline__ void pair_col_store(char* base, int row0, int t, const uint32_t (&v)[4], const PairSel& ps) {
     const bool odd = t & 1;
     const int ocol = pairpos(t & ~1);
     #pragma unroll
-    for (int xx = 0; xx < 4; ++xx) {
-        const int i_e = xx >> 1, i_o = 2 + (xx >> 1);
-        const uint32_t own = odd ? v[i_o] : v[i_e];
-        const uint32_t oth = odd ? pv[i_o] : pv[i_e];
-        const uint32_t own16 = (xx & 1) ? own >> 16 : own & 0xffffu;
-        const uint32_t oth16 = (xx & 1) ? oth >> 16 : oth & 0xffffu;
-        const uint32_t word = odd ? (oth16 | (own16 << 16)) : (own16 | (oth16 << 16));
-        const int row = row0 + (odd ? 4 : 0) + xx;
-        sts<uint32_t>(base, (row * PT + ocol) * 2, word);
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t own = odd ? v[2 + k] : v[k];
+        const uint32_t oth = dpp_u32_xor1(odd ? v[k] : v[2 + k]);
+        #pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = row0 + (odd ? 4 : 0) + 2 * k + h;
+            sts<uint32_t>(base, (row * PT + ocol) * 2, __builtin_amdgcn_perm(oth, own, ps.sel[h]));
+        }
     }
 }
 
@@ -301,6 +309,7 @@ void prep128_kernel(PrepArgs g) {
     const uint32_t stq = uint32_t(H) * DK * SI, stkv = uint32_t(g.H_kv) * DK * SI;
     // Row threads: token t of the chunk, keys j0 .. j0 + 7.
     const int t = l & 31, j0 = 8 * (2 * w + (l >> 5));
+    const PairSel psel(t);
 
     auto load_item = [&](int item, ItemRows<Tin>& x) {
         const int bh = item / nwin, c = g.cb + (item - bh * nwin);
@@ -385,9 +394,9 @@ void prep128_kernel(PrepArgs g) {
                 Eix[x] = __builtin_amdgcn_exp2f(-gg);
                 const float prev = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(Ex[x]), 0x138, 0xF, 0xF, false));   // wave_shr:1
                 Epx[x] = t == 0 ? 1.f : prev;
-                const float d31 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ex[x]), 31));
-                const float d63 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ex[x]), 63));
-                dx[x] = l < 32 ? d31 : d63;
+                // Lane 31 of each 32-lane half to the whole half: swizzle in bit mode,
+                // source lane ((lane & 0) | 31) ^ 0.
+                dx[x] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(Ex[x]), 31 << 5));
             }
             // KK: the token's |k|^2 from the 8 waves' partials.
             float inv = 0.f;
@@ -442,8 +451,8 @@ void prep128_kernel(PrepArgs g) {
             sts<uint2>(smem + P_RTL, o, make_uint2(rtl[0], rtl[1]));
             sts<uint2>(smem + P_RTL, o + 16, make_uint2(rtl[2], rtl[3]));
             // Key-major copies of At and Bh.
-            pair_col_store(smem + P_ATT, j0, t, at);
-            pair_col_store(smem + P_BHT, j0, t, bhat);
+            pair_col_store(smem + P_ATT, j0, t, at, psel);
+            pair_col_store(smem + P_BHT, j0, t, bhat, psel);
             if (t == 0) {
                 sts<float4>(smem + P_DL, j0 * 4, make_float4(dx[0], dx[1], dx[2], dx[3]));
                 sts<float4>(smem + P_DL, j0 * 4 + 16, make_float4(dx[4], dx[5], dx[6], dx[7]));
@@ -552,11 +561,13 @@ void prep128_kernel(PrepArgs g) {
                 sts<float4>(smem + P_UTH, (16 * lq + lr) * 16, make_float4(Dt1[0], Dt1[1], Dt1[2], Dt1[3]));
                 store_blk(16, 16, Dt1);
             }
-            // Waves 1..3: A_rk; 4..6: A_ak (swapped orientation); 7: all three tiles of A_rb.
+            // Wave 1 runs the D1 chain only.  A_rk tiles: waves 2, 3, 6; A_ak (swapped
+            // orientation): waves 4, 5, 6; A_rb, all three tiles: wave 7.  (Waves w and
+            // w + 4 share a SIMD: the partners of the chain waves 0 and 1 stay light.)
             auto tile_tb = [](int n) { return n == 0 ? 0 : 1; };
             auto tile_sb = [](int n) { return n == 2 ? 1 : 0; };
-            if (w <= 3) {
-                const int n = w - 1, tb = tile_tb(n), sb = tile_sb(n);
+            auto a_rk = [&](int n) {
+                const int tb = tile_tb(n), sb = tile_sb(n);
                 f32x4 acc = zero;
                 #pragma unroll
                 for (int kq = 0; kq < 4; ++kq) {
@@ -575,8 +586,9 @@ void prep128_kernel(PrepArgs g) {
                 const int o = ((16 * tb + lr) * PT + 16 * sb + 4 * lq) * 2;
                 sts<uint2>(smem + P_ARKH, o, make_uint2(h0, h1));
                 sts<uint2>(smem + P_ARKL, o, make_uint2(l0, l1));
-            } else if (w <= 6) {
-                const int n = w - 4, tb = tile_tb(n), sb = tile_sb(n);
+            };
+            auto a_ak = [&](int n) {
+                const int tb = tile_tb(n), sb = tile_sb(n);
                 f32x4 acc = zero;
                 #pragma unroll
                 for (int kq = 0; kq < 4; ++kq) {
@@ -593,13 +605,19 @@ void prep128_kernel(PrepArgs g) {
                 const int o = ((16 * sb + lr) * PT + pairpos(16 * tb + 4 * lq)) * 2;
                 sts<uint2>(smem + P_AKTH, o, make_uint2(h0, h1));
                 sts<uint2>(smem + P_AKTL, o, make_uint2(l0, l1));
-                if (w == 6) {
+                if (n == 2) {
                     // A_ak^T rows s >= 16 at tokens t < 16 are zero (strictly lower).
                     const int oz = ((16 + lr) * PT + pairpos(4 * lq)) * 2;
                     sts<uint2>(smem + P_AKTH, oz, make_uint2(0, 0));
                     sts<uint2>(smem + P_AKTL, oz, make_uint2(0, 0));
                 }
-            } else {
+            };
+            if (w == 2 || w == 3) {
+                a_rk(w - 1);
+            } else if (w >= 4 && w <= 6) {
+                if (w == 6) a_rk(0);
+                a_ak(w - 4);
+            } else if (w == 7) {
                 f32x4 acc[3] = {zero, zero, zero};
                 #pragma unroll
                 for (int kq = 0; kq < 4; ++kq) {
