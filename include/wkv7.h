@@ -65,14 +65,15 @@
 extern "C" {
 #endif
 
-#define WKV7_ABI_VERSION 5
+#define WKV7_ABI_VERSION 6
 
 enum wkv7_status {
     WKV7_OK = 0,
     WKV7_EINVAL = 1,        /* null/misaligned pointer, negative size, H % H_kv != 0, bad enum */
     WKV7_EUNSUPPORTED = 2,  /* D not 64/128, unsupported mode/algorithm combination */
     WKV7_EDEVICE = 3,       /* current device is not gfx950, or a HIP device query failed */
-    WKV7_ELAUNCH = 4        /* a kernel launch reported an error */
+    WKV7_ELAUNCH = 4,       /* a kernel launch reported an error */
+    WKV7_ETIMEOUT = 5       /* a bounded device-side wait gave up (wkv4_wait_status) */
 };
 
 enum wkv7_dtype { WKV7_F32 = 0, WKV7_BF16 = 1 };

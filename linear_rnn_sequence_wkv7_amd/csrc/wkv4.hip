@@ -31,8 +31,9 @@
 // Workgroups take their chunk from a ticket counter in the order they start,
 // chunk-major, so a thread only waits for chunks whose workgroups are already
 // running; each wait is also bounded (past the bound the chunk's outputs are
-// NaN, never a hang).  One thread per channel, so each wave's
-// loads of a token row are 64 consecutive channels.
+// NaN, never a hang; each wait that gives up is counted in the workspace, and
+// wkv4_wait_status reports the count after the call).  One thread per channel,
+// so each wave's loads of a token row are 64 consecutive channels.
 #include "wkv7_internal.h"
 #include "wkv7_device.h"
 
@@ -51,8 +52,9 @@ struct Wkv4Args {
     const float* s0;     // [B, 3, C] (A, B, P natural-log units) or null
     float* s1;           // [B, 3, C] or null
     float* ws;           // [B, nch, 3, C] local states, then the inclusive ones likewise
-    int* ticket;         // chunk ticket counter
+    int* ticket;         // chunk ticket counter; ticket[1]: waits that gave up
     int B, T, C, nch;
+    int spin_max;        // polls before a wait gives up
 };
 
 struct Scaled {
@@ -115,11 +117,12 @@ __global__ __launch_bounds__(NT4) void wkv4_copy_state_kernel(Wkv4Args g) {
 }
 
 constexpr uint32_t kNotReady = 0x7fbadbadu;   // a NaN pattern the arithmetic here does not produce
-constexpr int kSpinMax = 1 << 18;              // bound of one wait (tens of ms)
+constexpr int kSpinMax = 1 << 18;              // default bound of one wait (tens of ms)
 
-// Mark every state not ready and reset the ticket counter.
+// Mark every state not ready and reset the ticket counter and the count of
+// waits that gave up.
 __global__ __launch_bounds__(256) void wkv4_reset_kernel(uint32_t* __restrict__ st, int64_t n, int* ticket) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0;
+    if (blockIdx.x == 0 && threadIdx.x < 2) ticket[threadIdx.x] = 0;
     for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < n; e += int64_t(gridDim.x) * 256)
         st[e] = kNotReady;
 }
@@ -189,8 +192,9 @@ __global__ __launch_bounds__(NT4) void wkv4_onepass_kernel(Wkv4Args g) {
                 break;
             }
             if (ready_read(loc_ws + row(k), g.C, x)) break;
-            if (it == kSpinMax) {   // bounded: give up with NaN outputs from here on, never hang
+            if (it >= g.spin_max) {   // bounded: give up with NaN outputs from here on, never hang
                 x = Scaled{__uint_as_float(0x7fc00000u), __uint_as_float(0x7fc00000u), 0.f};
+                __hip_atomic_fetch_add(g.ticket + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 complete = true;
                 break;
             }
@@ -250,19 +254,25 @@ hipError_t launch_t(const Wkv4Args& g, hipStream_t stream) {
 
 }  // namespace
 
-// Layout: local states [B][nch][3][C], inclusive states likewise, then the ticket
-// counter (256 bytes); 0 when there is nothing to compute.
+// Layout: local states [B][nch][3][C], inclusive states likewise, then 256 bytes
+// holding the ticket counter and the count of waits that gave up; 0 when there is
+// nothing to compute.
 int64_t wkv4_workspace_bytes_internal(int B, int T, int C) {
     const int64_t nch = (int64_t(T) + CL - 1) / CL;
     if (int64_t(B) * nch * C == 0) return 0;
     return ((2 * int64_t(B) * nch * 3 * C * 4 + 255) & ~int64_t(255)) + 256;
 }
 
+int64_t wkv4_wait_counter_offset(int B, int T, int C) {
+    return wkv4_workspace_bytes_internal(B, T, C) - 256 + 4;
+}
+
 hipError_t launch_wkv4(const Wkv4Params& p, hipStream_t stream) {
     const int nch = int((p.T + CL - 1) / CL);
     const int64_t states = (2 * int64_t(p.B) * nch * 3 * p.C * 4 + 255) & ~int64_t(255);
     Wkv4Args g{p.w, p.u, p.k, p.v, p.y, p.s0, p.s1, static_cast<float*>(p.ws),
-               reinterpret_cast<int*>(static_cast<char*>(p.ws) + states), p.B, p.T, p.C, nch};
+               reinterpret_cast<int*>(static_cast<char*>(p.ws) + states), p.B, p.T, p.C, nch,
+               p.spin_limit > 0 ? p.spin_limit : kSpinMax};
     if (p.T == 0) {   // state_out <- state_in (or the zero state)
         if (!p.s1) return hipSuccess;
         hipLaunchKernelGGL(wkv4_copy_state_kernel, dim3(unsigned((p.C + NT4 - 1) / NT4), unsigned(p.B)), dim3(NT4),

@@ -354,7 +354,7 @@ namespace {
 
 int check_wkv4(const wkv4_desc* d) {
     if (!d) return fail(WKV7_EINVAL, "desc is NULL");
-    if (d->reserved != 0) return fail(WKV7_EINVAL, "desc->reserved must be 0");
+    if (d->spin_limit < 0) return fail(WKV7_EINVAL, "desc->spin_limit must be >= 0 (got %d)", d->spin_limit);
     if (d->B < 0 || d->T < 0 || d->C < 0)
         return fail(WKV7_EINVAL, "negative size (B=%d T=%d C=%d)", d->B, d->T, d->C);
     if (d->in_dtype != WKV7_F32 && d->in_dtype != WKV7_BF16)
@@ -420,9 +420,32 @@ int wkv4_forward(const wkv4_desc* desc, const float* w, const float* u, const vo
     if (bc == 0) return WKV7_OK;
     if (!has_tokens && !state_out) return WKV7_OK;
     if ((rc = check_device())) return rc;
-    wkv7::Wkv4Params p{desc->B, desc->T, desc->C, desc->in_dtype, desc->y_dtype, w, u, k, v, y,
+    wkv7::Wkv4Params p{desc->B, desc->T, desc->C, desc->in_dtype, desc->y_dtype, desc->spin_limit, w, u, k, v, y,
                        state_in, state_out, workspace};
     return finish_launch(wkv7::launch_wkv4(p, reinterpret_cast<hipStream_t>(stream)), "wkv4");
+}
+
+int wkv4_wait_status(const wkv4_desc* desc, const void* workspace, int64_t workspace_bytes_given, void* stream) {
+    g_last_error[0] = '\0';
+    int rc = check_wkv4(desc);
+    if (rc) return rc;
+    const bool has_tokens = int64_t(desc->B) * desc->T * desc->C > 0;
+    const int64_t need = has_tokens ? wkv7::wkv4_workspace_bytes_internal(desc->B, desc->T, desc->C) : 0;
+    if (need == 0) return WKV7_OK;
+    if (!workspace) return fail(WKV7_EINVAL, "workspace is NULL (%lld bytes needed)", (long long)need);
+    if (workspace_bytes_given < need)
+        return fail(WKV7_EINVAL, "workspace has %lld bytes, %lld needed", (long long)workspace_bytes_given,
+                    (long long)need);
+    if ((rc = check_device())) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int32_t count = 0;
+    const char* src = static_cast<const char*>(workspace) + wkv7::wkv4_wait_counter_offset(desc->B, desc->T, desc->C);
+    hipError_t e = hipMemcpyAsync(&count, src, sizeof(count), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(WKV7_EDEVICE, "reading the wait count: %s", hipGetErrorString(e));
+    if (count > 0)
+        return fail(WKV7_ETIMEOUT, "%d look-back wait(s) gave up; y is NaN in their chunks", int(count));
+    return WKV7_OK;
 }
 
 int wkv7_resolve_algo(const wkv7_desc* desc) {
@@ -439,6 +462,7 @@ const char* wkv7_strerror(int code) {
         case WKV7_EUNSUPPORTED: return "unsupported configuration";
         case WKV7_EDEVICE: return "unsupported or unavailable device";
         case WKV7_ELAUNCH: return "kernel launch failed";
+        case WKV7_ETIMEOUT: return "a bounded device-side wait gave up";
         default: return "unknown status";
     }
 }

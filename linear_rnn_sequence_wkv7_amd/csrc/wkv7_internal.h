@@ -65,6 +65,7 @@ int64_t backward_workspace_bytes(const Params& p);
 // RWKV-4 WKV (wkv4.hip).
 struct Wkv4Params {
     int B, T, C, in_dtype, y_dtype;
+    int spin_limit;   // polls before a look-back wait gives up (0: the default bound)
     const float *w, *u;
     const void *k, *v;
     void* y;
@@ -73,6 +74,8 @@ struct Wkv4Params {
     void* ws;
 };
 int64_t wkv4_workspace_bytes_internal(int B, int T, int C);
+// Byte offset in the workspace of the int32 count of look-back waits that gave up.
+int64_t wkv4_wait_counter_offset(int B, int T, int C);
 hipError_t launch_wkv4(const Wkv4Params& p, hipStream_t stream);
 hipError_t launch_backward(const Params& p, const BwdIo& io, void* ws, hipStream_t stream);
 

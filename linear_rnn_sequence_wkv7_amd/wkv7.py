@@ -15,20 +15,20 @@ from typing import Optional, Tuple
 
 __all__ = [
     "wkv7_forward", "wkv7_forward_noalloc", "wkv7_backward", "wkv7_decode_step", "wkv7_resolve_algo", "wkv7_workspace_bytes",
-    "wkv7_backward_workspace_bytes", "wkv4_forward", "wkv4_workspace_bytes", "Wkv7Error",
+    "wkv7_backward_workspace_bytes", "wkv4_forward", "wkv4_workspace_bytes", "wkv4_wait_status", "Wkv7Error",
     "lib_path", "load_library",
-    "WKV7_OK", "WKV7_EINVAL", "WKV7_EUNSUPPORTED", "WKV7_EDEVICE", "WKV7_ELAUNCH",
+    "WKV7_OK", "WKV7_EINVAL", "WKV7_EUNSUPPORTED", "WKV7_EDEVICE", "WKV7_ELAUNCH", "WKV7_ETIMEOUT",
     "ALGOS", "W_MODES", "AB_MODES", "Desc", "EXPORTED_SYMBOLS",
 ]
 
-WKV7_OK, WKV7_EINVAL, WKV7_EUNSUPPORTED, WKV7_EDEVICE, WKV7_ELAUNCH = 0, 1, 2, 3, 4
+WKV7_OK, WKV7_EINVAL, WKV7_EUNSUPPORTED, WKV7_EDEVICE, WKV7_ELAUNCH, WKV7_ETIMEOUT = 0, 1, 2, 3, 4, 5
 _DTYPES = {"f32": 0, "bf16": 1}
 W_MODES = {"decay": 0, "logneglog": 1}
 ALGOS = {"auto": 0, "scan": 1, "chunked": 2, "two_pass": 3}
 AB_MODES = {"given": 0, "from_k": 1}
 EXPORTED_SYMBOLS = ("wkv7_forward", "wkv7_forward_ws", "wkv7_forward_noalloc", "wkv7_workspace_bytes", "wkv7_decode_step",
                     "wkv7_backward", "wkv7_backward_workspace_bytes", "wkv4_forward", "wkv4_workspace_bytes",
-                    "wkv7_resolve_algo", "wkv7_strerror", "wkv7_last_error", "wkv7_abi_version")
+                    "wkv4_wait_status", "wkv7_resolve_algo", "wkv7_strerror", "wkv7_last_error", "wkv7_abi_version")
 
 
 class Wkv7Error(RuntimeError):
@@ -51,7 +51,7 @@ class Desc(ctypes.Structure):
 class Wkv4Desc(ctypes.Structure):
     """Mirror of struct wkv4_desc."""
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("C", ctypes.c_int32),
-                ("in_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("in_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32), ("spin_limit", ctypes.c_int32)]
 
 
 def lib_path() -> str:
@@ -88,6 +88,8 @@ def load_library():
     lib.wkv4_forward.restype = ctypes.c_int
     lib.wkv4_workspace_bytes.argtypes = [ctypes.POINTER(Wkv4Desc)]
     lib.wkv4_workspace_bytes.restype = ctypes.c_int64
+    lib.wkv4_wait_status.argtypes = [ctypes.POINTER(Wkv4Desc), vp, ctypes.c_int64, vp]
+    lib.wkv4_wait_status.restype = ctypes.c_int
     lib.wkv7_resolve_algo.argtypes = [ctypes.POINTER(Desc)]
     lib.wkv7_resolve_algo.restype = ctypes.c_int
     lib.wkv7_strerror.argtypes = [ctypes.c_int]
@@ -351,7 +353,7 @@ def wkv7_backward(r, w, k, v, a, b, dy, state=None, dstate=None, *, w_mode: str 
 
 def wkv4_workspace_bytes(B, T, C, *, in_dtype="bf16", y_dtype="bf16") -> int:
     """Workspace bytes of wkv4_forward for these sizes."""
-    d = Wkv4Desc(B=B, T=T, C=C, in_dtype=_DTYPES[in_dtype], y_dtype=_DTYPES[y_dtype], reserved=0)
+    d = Wkv4Desc(B=B, T=T, C=C, in_dtype=_DTYPES[in_dtype], y_dtype=_DTYPES[y_dtype], spin_limit=0)
     n = load_library().wkv4_workspace_bytes(ctypes.byref(d))
     if n < 0:
         raise Wkv7Error(int(-n), "wkv4_workspace_bytes", load_library().wkv7_last_error().decode())
@@ -359,9 +361,11 @@ def wkv4_workspace_bytes(B, T, C, *, in_dtype="bf16", y_dtype="bf16") -> int:
 
 
 def wkv4_forward(w, u, k, v, state=None, *, y_dtype: Optional[str] = None, y=None, state_out=None,
-                 return_state: bool = True, workspace=None) -> Tuple[object, object]:
+                 return_state: bool = True, workspace=None, spin_limit: int = 0) -> Tuple[object, object]:
     """RWKV-4 WKV on torch GPU tensors: w, u [C] float32; k, v [B, T, C] float32 or bfloat16;
-    state [B, 3, C] float32 (A, Bs, P with a = A e^P, b = Bs e^P) or None.  Returns (y, state_out)."""
+    state [B, 3, C] float32 (A, Bs, P with a = A e^P, b = Bs e^P) or None.  Returns (y, state_out).
+    spin_limit: polls before a look-back wait gives up (0: the library's bound); pass a
+    `workspace` to read the count of such waits afterwards with wkv4_wait_status."""
     torch = _torch()
     if k.dim() != 3 or tuple(v.shape) != tuple(k.shape):
         raise ValueError("k and v must be [B, T, C] with the same shape")
@@ -380,7 +384,7 @@ def wkv4_forward(w, u, k, v, state=None, *, y_dtype: Optional[str] = None, y=Non
         y = torch.empty((B, T, C), dtype=torch.float32 if ydt == "f32" else torch.bfloat16, device=dev)
     if state_out is None and return_state:
         state_out = torch.empty((B, 3, C), dtype=torch.float32, device=dev)
-    d = Wkv4Desc(B=B, T=T, C=C, in_dtype=_DTYPES[_dtype_name(k)], y_dtype=_DTYPES[ydt], reserved=0)
+    d = Wkv4Desc(B=B, T=T, C=C, in_dtype=_DTYPES[_dtype_name(k)], y_dtype=_DTYPES[ydt], spin_limit=spin_limit)
     lib = load_library()
     need = lib.wkv4_workspace_bytes(ctypes.byref(d))
     if need < 0:
@@ -395,3 +399,21 @@ def wkv4_forward(w, u, k, v, state=None, *, y_dtype: Optional[str] = None, y=Non
     if rc != WKV7_OK:
         raise Wkv7Error(rc, "wkv4_forward", lib.wkv7_last_error().decode())
     return y, state_out
+
+
+def wkv4_wait_status(k, workspace, *, y_dtype: Optional[str] = None) -> int:
+    """After wkv4_forward(..., workspace=workspace) with this k: WKV7_OK, or WKV7_ETIMEOUT if
+    any look-back wait of that call gave up (y is NaN in its chunk).  Waits for the
+    current stream."""
+    torch = _torch()
+    B, T, C = k.shape
+    d = Wkv4Desc(B=B, T=T, C=C, in_dtype=_DTYPES[_dtype_name(k)], y_dtype=_DTYPES[y_dtype or _dtype_name(k)],
+                 spin_limit=0)
+    lib = load_library()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(k.device).cuda_stream
+    with torch.cuda.device(k.device):
+        rc = lib.wkv4_wait_status(ctypes.byref(d), _ptr(workspace), ws_bytes, stream)
+    if rc not in (WKV7_OK, WKV7_ETIMEOUT):
+        raise Wkv7Error(rc, "wkv4_wait_status", lib.wkv7_last_error().decode())
+    return rc

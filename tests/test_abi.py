@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_strerror():
     lib = W.load_library()
-    assert lib.wkv7_abi_version() == 5
+    assert lib.wkv7_abi_version() == 6
     assert lib.wkv7_strerror(0) == b"ok"
     assert lib.wkv7_strerror(W.WKV7_EINVAL) == b"invalid argument"
     assert lib.wkv7_strerror(99) == b"unknown status"
@@ -266,13 +266,13 @@ def _wkv4(desc, **over):
 
 def test_wkv4_argument_rules():
     lib = W.load_library()
-    good4 = lambda **kw: W.Wkv4Desc(**{**dict(B=2, T=100, C=64, in_dtype=1, y_dtype=1, reserved=0), **kw})
+    good4 = lambda **kw: W.Wkv4Desc(**{**dict(B=2, T=100, C=64, in_dtype=1, y_dtype=1, spin_limit=0), **kw})
     al = lambda x: (x + 255) // 256 * 256
     assert W.wkv4_workspace_bytes(2, 100, 64) == al(2 * 2 * 2 * 3 * 64 * 4) + 256
     assert W.wkv4_workspace_bytes(8, 4096, 4096) == al(2 * 8 * 64 * 3 * 4096 * 4) + 256
     assert W.wkv4_workspace_bytes(2, 0, 64) == 0
     assert _wkv4(None) == W.WKV7_EINVAL
-    assert _wkv4(good4(reserved=1)) == W.WKV7_EINVAL
+    assert _wkv4(good4(spin_limit=-1)) == W.WKV7_EINVAL
     assert _wkv4(good4(T=-1)) == W.WKV7_EINVAL
     assert _wkv4(good4(in_dtype=5)) == W.WKV7_EINVAL
     assert _wkv4(good4(C=1 << 24)) == W.WKV7_EUNSUPPORTED
@@ -284,6 +284,22 @@ def test_wkv4_argument_rules():
     assert _wkv4(good4(), ws_bytes=10) == W.WKV7_EINVAL
     assert b"needed" in lib.wkv7_last_error()
     assert _wkv4(good4(B=0)) == W.WKV7_OK                          # empty: no device call
+
+
+def test_wkv4_wait_status_argument_rules():
+    """wkv4_wait_status validates before touching the device: a bad descriptor, a
+    missing or too small workspace are EINVAL; nothing to compute is OK."""
+    lib = W.load_library()
+    good4 = lambda **kw: W.Wkv4Desc(**{**dict(B=2, T=100, C=64, in_dtype=1, y_dtype=1, spin_limit=0), **kw})
+    need = W.wkv4_workspace_bytes(2, 100, 64)
+    st = lambda d, ws, n: lib.wkv4_wait_status(ctypes.byref(d) if d is not None else None, ws, n, None)
+    assert st(None, FAKE, need) == W.WKV7_EINVAL
+    assert st(good4(spin_limit=-3), FAKE, need) == W.WKV7_EINVAL
+    assert st(good4(), None, need) == W.WKV7_EINVAL
+    assert st(good4(), FAKE, need - 1) == W.WKV7_EINVAL
+    assert b"needed" in lib.wkv7_last_error()
+    assert st(good4(T=0), None, 0) == W.WKV7_OK
+    assert lib.wkv7_strerror(W.WKV7_ETIMEOUT) == b"a bounded device-side wait gave up"
 
 
 def test_no_kernel_spills_to_scratch():
@@ -342,7 +358,7 @@ def test_backward_workspace_must_not_overlap_any_array():
 
 def test_wkv4_workspace_must_not_overlap_any_array():
     lib = W.load_library()
-    desc = W.Wkv4Desc(B=2, T=100, C=64, in_dtype=1, y_dtype=1, reserved=0)
+    desc = W.Wkv4Desc(B=2, T=100, C=64, in_dtype=1, y_dtype=1, spin_limit=0)
     need = W.wkv4_workspace_bytes(2, 100, 64)
     names = ("w", "u", "k", "v", "s0", "y", "s1")
     ptrs = {n: BASE + i * SP for i, n in enumerate(names)}

@@ -110,3 +110,34 @@ def test_wkv4_workload():
         P.check(f"y b{b} c{c}", y[b:b + 1, :, c:c + 1], y_ref, TAU, bf16_out=True)
         a, bb = ab_of(s[b:b + 1, :, c:c + 1])
         P.check(f"state b{b} c{c}", np.stack([a, bb]) / b_ref.max(), np.stack([a_ref, b_ref]) / b_ref.max(), TAU)
+
+
+def test_wkv4_wait_status_reports_exactly_the_waits_that_gave_up():
+    """The look-back waits are bounded.  With the default bound none gives up and the
+    status is OK with every output finite.  With the smallest bound (two polls) on
+    a long sequence, waits may give up: the status must say so exactly when y holds
+    NaN (a wait that gives up makes its chunk's y NaN in its channel, and that of
+    later chunks that take their incoming state from it), and every finite output
+    still matches the default run (to rounding: which earlier chunks' states a
+    look-back merges depends on timing)."""
+    t = torch()
+    g = t.Generator(device="cuda")
+    g.manual_seed(11)
+    B, T, C = 4, 1 << 15, 1024
+    k = t.randn((B, T, C), generator=g, device="cuda").to(t.bfloat16)
+    v = t.randn((B, T, C), generator=g, device="cuda").to(t.bfloat16)
+    w = t.rand((C,), generator=g, device="cuda") * 0.5
+    u = t.randn((C,), generator=g, device="cuda") * 0.5
+    ws = t.empty(W().wkv4_workspace_bytes(B, T, C), dtype=t.uint8, device="cuda")
+    y0, _ = W().wkv4_forward(w, u, k, v, None, y_dtype="f32", workspace=ws)
+    assert W().wkv4_wait_status(k, ws, y_dtype="f32") == W().WKV7_OK
+    assert bool(t.isfinite(y0).all())
+    gave_up = 0
+    for rep in range(3):
+        y1, _ = W().wkv4_forward(w, u, k, v, None, y_dtype="f32", workspace=ws, spin_limit=1)
+        st = W().wkv4_wait_status(k, ws, y_dtype="f32")
+        nan = t.isnan(y1)
+        assert (st == W().WKV7_ETIMEOUT) == bool(nan.any()), f"status {st}, NaN {int(nan.sum())}"
+        assert t.allclose(y1[~nan], y0[~nan], rtol=1e-5, atol=1e-6)
+        gave_up += st == W().WKV7_ETIMEOUT
+    announce(f"  smallest bound: {gave_up} of 3 calls had waits that gave up")
