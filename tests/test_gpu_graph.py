@@ -169,7 +169,7 @@ def test_graph_wkv4():
 
 
 def test_graph_forward_bench_workload_full_size():
-    """The bench's timed region at its full size (B8 T1024 H32 D64 bf16): two
+    """The B8 T1024 H32 D64 bf16 workload's timed region at its full size: two
     forward steps captured as one graph; every replay equals the eager launch."""
     wl = G.WORKLOADS["fwd_bf16_b8_t1024_h32_d64"]
     d = dev_inputs(G.make_inputs(wl))
@@ -177,6 +177,37 @@ def test_graph_forward_bench_workload_full_size():
     def run(y, s):
         W().wkv7_forward(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state0"], w_mode=wl.w_mode,
                          y_dtype=wl.y_dtype, chunk_len=wl.chunk_len, y=y, state_out=s)
+
+    y_e = torch().empty((wl.B, wl.T, wl.H, wl.D), dtype=torch().bfloat16, device="cuda")
+    s_e = torch().empty((wl.B, wl.H, wl.D, wl.D), dtype=torch().float32, device="cuda")
+    run(y_e, s_e)
+    torch().cuda.synchronize()
+    expected = {"y": to_host(y_e), "state": to_host(s_e)}
+    y_g, s_g = torch().empty_like(y_e), torch().empty_like(s_e)
+    g = torch().cuda.CUDAGraph()
+    with torch().cuda.graph(g):
+        run(y_g, s_g)
+        run(y_g, s_g)
+
+    def reset():
+        y_g.zero_()
+        s_g.zero_()
+    check_replays(g, reset, {"y": y_g, "state": s_g}, expected)
+
+
+def test_graph_forward_headline_full_size():
+    """The bench's default timed region at its full size (hxa07D B2 T16384 H32 H_kv8
+    D128, two-pass, workspace allocated once): two forward steps captured as one
+    graph; every replay equals the eager launch bit for bit."""
+    wl = G.WORKLOADS["hxa07d_bf16_b2_t16384_h32_kv8_d128"]
+    d = dev_inputs(G.make_inputs(wl))
+    ws = torch().empty(W().wkv7_workspace_bytes(wl.B, wl.T, wl.H, wl.D, H_kv=wl.H_kv, algo="two_pass"),
+                       dtype=torch().uint8, device="cuda")
+
+    def run(y, s):
+        W().wkv7_forward(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state0"], w_mode=wl.w_mode,
+                         y_dtype=wl.y_dtype, algo="two_pass", y_scale=wl.y_scale, r_k=d["r_k"],
+                         ab_mode=wl.ab_mode, y=y, state_out=s, workspace=ws)
 
     y_e = torch().empty((wl.B, wl.T, wl.H, wl.D), dtype=torch().bfloat16, device="cuda")
     s_e = torch().empty((wl.B, wl.H, wl.D, wl.D), dtype=torch().float32, device="cuda")

@@ -28,3 +28,18 @@ def test_sample_pairs_spreads_over_batches_and_kv_groups():
     for name in ("fwd_bf16_b8_t1024_h32_d64", "prefill_bf16_b4_t4096_h40_d64_l64"):
         wl = G.WORKLOADS[name]
         assert {b for b, _ in P.sample_pairs(wl, 16, seed=wl.seed)} == set(range(wl.B))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 (or a multi-rank launch) exits with
+    status 2 and a message, before touching any device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for args, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *args], capture_output=True, text=True,
+                           env={**os.environ, **env}, timeout=120)
+        assert r.returncode == 2, r.stderr
+        assert "one GPU only" in r.stderr
+        assert r.stdout.strip() == ""
