@@ -97,3 +97,84 @@ def sample_pairs(wl, n, seed=0):
         else:
             idx.append(int(rng.integers(lo, hi)))
     return [(i // wl.H, i % wl.H) for i in idx]
+
+
+# ---------------- every (batch, head) pair, the oracle in worker processes ----------------
+#
+# Workers are spawned (fresh interpreters that never touch the GPU), regenerate
+# the workload's inputs from its seed, run the oracle on their share of the
+# pairs and compare it with the GPU outputs, which they read from shared memory.
+# They return sums, so the bound uses the rms over all pairs, as check() does.
+
+_AP = {}
+
+
+def _ap_init(name, overrides, y_name, y_shape, s_name, s_shape):
+    from multiprocessing import shared_memory
+    from linear_rnn_sequence_wkv7_amd import inputs as G
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:
+        pass
+    wl = G.workload(name, **overrides)
+    _AP["wl"] = wl
+    _AP["x"] = G.make_inputs(wl)
+    _AP["shm"] = [shared_memory.SharedMemory(name=y_name), shared_memory.SharedMemory(name=s_name)]
+    _AP["y"] = np.ndarray(y_shape, dtype=np.float32, buffer=_AP["shm"][0].buf)
+    _AP["s"] = np.ndarray(s_shape, dtype=np.float32, buffer=_AP["shm"][1].buf)
+
+
+def _ap_work(pairs):
+    wl, x = _AP["wl"], _AP["x"]
+    y_ref, s_ref = oracle_pairs(x, wl, pairs)
+    bs = [p[0] for p in pairs]
+    hs = [p[1] for p in pairs]
+    y = _AP["y"][bs, :, hs].astype(np.float64)
+    s = _AP["s"][bs, hs].astype(np.float64)
+    finite = bool(np.all(np.isfinite(y)) and np.all(np.isfinite(s)))
+    return (float(np.abs(y - y_ref).max()), float(np.sum(y_ref * y_ref)), y_ref.size,
+            float(np.abs(s - s_ref).max()), float(np.sum(s_ref * s_ref)), s_ref.size, finite)
+
+
+def check_all_pairs(name, overrides, y, s, tau, workers=8):
+    """GPU y [B, T, H, D] and final state [B, H, D, D] (host float32 arrays) of
+    workload `name` (with `overrides`) against the oracle on every (batch, head)
+    pair: max|x - x_ref| <= tau * rms(x_ref) over all pairs, for y and the state.
+    Returns the two normalised errors."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+    from linear_rnn_sequence_wkv7_amd import inputs as G
+    wl = G.workload(name, **overrides)
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    assert y.shape == (wl.B, wl.T, wl.H, wl.D) and s.shape == (wl.B, wl.H, wl.D, wl.D)
+    shm = [shared_memory.SharedMemory(create=True, size=max(1, y.nbytes)),
+           shared_memory.SharedMemory(create=True, size=max(1, s.nbytes))]
+    try:
+        np.ndarray(y.shape, dtype=np.float32, buffer=shm[0].buf)[...] = y
+        np.ndarray(s.shape, dtype=np.float32, buffer=shm[1].buf)[...] = s
+        pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+        n = max(1, min(workers, len(pairs)))
+        # Pairs of one sequence stay together (a mask row is shared by them).
+        shares = [pairs[i::n] for i in range(n)] if wl.mask == "" else \
+            [[p for p in pairs if p[0] % n == i] for i in range(n)]
+        shares = [sh for sh in shares if sh]
+        # A worker that dies (or fails to start) breaks the pool with an error
+        # instead of leaving the map waiting.
+        with cf.ProcessPoolExecutor(len(shares), mp_context=mp.get_context("spawn"), initializer=_ap_init,
+                                    initargs=(name, overrides, shm[0].name, y.shape, shm[1].name, s.shape)) as ex:
+            res = list(ex.map(_ap_work, shares))
+    finally:
+        for m in shm:
+            m.close()
+            m.unlink()
+    assert all(r[6] for r in res), f"{name}: non-finite GPU values"
+    out = []
+    for i, what in ((0, "y"), (3, "state")):
+        err = max(r[i] for r in res)
+        scale = float(np.sqrt(sum(r[i + 1] for r in res) / sum(r[i + 2] for r in res)))
+        assert err <= tau * scale, f"{name} {what}: max|x - x_ref| {err:.4g} > {tau} * rms {scale:.4g}"
+        out.append(err / scale)
+    return tuple(out)

@@ -250,6 +250,27 @@ def test_workload_hxa07d(algo, y_dtype):
     _sampled(G.WORKLOADS["hxa07d_bf16_b2_t16384_h32_kv8_d128"], algo, 16, y_dtype=y_dtype)
 
 
+EVERY_PAIR = [
+    ("hxa07d_bf16_b2_t16384_h32_kv8_d128", "two_pass"),
+    ("fwd_bf16_b8_t1024_h32_d64", "chunked"),
+    ("prefill_bf16_b4_t4096_h40_d64_l64", "chunked"),
+]
+
+
+@pytest.mark.parametrize("name,algo", EVERY_PAIR)
+def test_workload_every_pair(name, algo):
+    """Every (batch, head) pair of the full-size forward workload, fp32 y, in the
+    launch configuration the benchmark times; the oracle runs in worker processes
+    that regenerate the inputs from the same seed."""
+    wl = G.WORKLOADS[name]
+    need_algo(algo, wl.D)
+    x = inputs_of(name)
+    announce(f"{name} algo={algo} y=f32 pairs={wl.B * wl.H}")
+    y, s = run_forward(wl, x, algo, y_dtype="f32")
+    e_y, e_s = P.check_all_pairs(name, dict(y_dtype="f32"), y, s, TAU[algo], workers=8)
+    announce(f"  max err / rms over every pair: y {e_y:.3e}  state {e_s:.3e}")
+
+
 @pytest.mark.parametrize("y_dtype", ["bf16", "f32"])
 def test_workload_decode_32_steps(y_dtype):
     wl = G.WORKLOADS["decode_bf16_b256_h64_d64_x32"]

@@ -43,3 +43,30 @@ def test_bench_refuses_more_than_one_gpu():
         assert r.returncode == 2, r.stderr
         assert "one GPU only" in r.stderr
         assert r.stdout.strip() == ""
+
+
+def test_check_all_pairs_compares_every_pair():
+    """The every-pair check (oracle in spawned workers, GPU outputs in shared memory),
+    with the oracle's own outputs standing in for the GPU's: passes at fp32 rounding,
+    and catches one wrong element, a non-finite value and a masked workload's pairs."""
+    import numpy as np
+    name = "fwd_f32_b1_t64_h2_d64"
+    for ov in (dict(B=2, T=40, H=3, H_kv=3), dict(B=3, T=33, H=2, H_kv=1, mask="holes")):
+        wl = G.workload(name, **ov)
+        x = G.make_inputs(wl)
+        pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+        y_ref, s_ref = P.oracle_pairs(x, wl, pairs)
+        y = np.zeros((wl.B, wl.T, wl.H, wl.D), np.float32)
+        s = np.zeros((wl.B, wl.H, wl.D, wl.D), np.float32)
+        for i, (b, h) in enumerate(pairs):
+            y[b, :, h] = y_ref[i]
+            s[b, h] = s_ref[i]
+        ey, es = P.check_all_pairs(name, ov, y, s, 1e-6, workers=2)
+        assert ey < 1e-6 and es < 1e-6
+    y[wl.B - 1, 5, wl.H - 1, 7] += 1.0
+    with pytest.raises(AssertionError, match="y: max"):
+        P.check_all_pairs(name, ov, y, s, 1e-2, workers=2)
+    y[wl.B - 1, 5, wl.H - 1, 7] -= 1.0
+    s[0, 0, 1, 1] = np.inf
+    with pytest.raises(AssertionError, match="non-finite"):
+        P.check_all_pairs(name, ov, y, s, 1e-2, workers=2)
