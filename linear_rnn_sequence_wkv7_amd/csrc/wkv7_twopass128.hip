@@ -250,33 +250,41 @@ __device__ __forceinline__ rsrc_t chunk_rsrc(const char* base, int64_t tok0, int
 // At, Bt, Kt hi / lo, Rt hi / lo.  Key-major (token axis pair-interleaved):
 // At^T, Bh^T.  L x L matrices: A_rb [t][s~], A_ak^T hi / lo [s][t~], A_rk hi / lo
 // [t][s], Dinv hi / lo [t][s~], U^T hi / lo [s'][s~] (~: pair-interleaved).
+// Areas are reused once their contents are dead, so that two workgroups fit
+// in one compute unit's LDS: At and Bt are read in the L x L phase only, after
+// which their area holds At^T and U^T; Rt is last read in the W, Q phase,
+// after which its area holds Bh^T; the |k|^2 partials' area holds D1^T for
+// the block inverse.  (At^T and Bh^T stay in the row threads' registers until
+// their areas are free.)
 constexpr int P_AT = 0;
 constexpr int P_BT = P_AT + MATK;
 constexpr int P_KTH = P_BT + MATK;
 constexpr int P_KTL = P_KTH + MATK;
 constexpr int P_RTH = P_KTL + MATK;
 constexpr int P_RTL = P_RTH + MATK;
-constexpr int P_ATT = P_RTL + MATK;
-constexpr int P_BHT = P_ATT + MATT;
-constexpr int P_ARB = P_BHT + MATT;
+constexpr int P_ARB = P_RTL + MATK;
 constexpr int P_AKTH = P_ARB + MATL;
 constexpr int P_AKTL = P_AKTH + MATL;
 constexpr int P_ARKH = P_AKTL + MATL;
 constexpr int P_ARKL = P_ARKH + MATL;
 constexpr int P_DIH = P_ARKL + MATL;
 constexpr int P_DIL = P_DIH + MATL;
-constexpr int P_UTH = P_DIL + MATL;
-constexpr int P_UTL = P_UTH + MATL;
-constexpr int P_D0T = P_UTL + MATL;              // D0^T hi / lo, [16][PD] each
+constexpr int P_D0T = P_DIL + MATL;              // D0^T hi / lo, [16][PD] each
 constexpr int P_DL = P_D0T + 2 * 16 * PD * 2;    // fp32 [DK] 2^g_L
 constexpr int P_BON = P_DL + DK * 4;             // fp32 [8 waves][L] bonus partials
 constexpr int P_KSQ = P_BON + 8 * L * 4;         // fp32 [L][8 waves] |k|^2 partials (KK)
 constexpr int SMEM_PREP = P_KSQ + L * 8 * 4;
-static_assert(SMEM_PREP <= 160 * 1024, "LDS budget");
+// Reused areas.
+constexpr int P_ATT = P_AT;                      // from the D10 step on
+constexpr int P_UTH = P_ATT + MATT;              // from the U, W, Q phase on
+constexpr int P_UTL = P_UTH + MATL;
+constexpr int P_BHT = P_RTH;                     // from the E, P phase on
+constexpr int P_D1T = P_KSQ;                     // fp32 16 x 16, L x L phase to the D10 step
+static_assert(P_UTL + MATL <= P_KTH && P_BHT + MATT <= P_ARB && 16 * 16 * 4 <= L * 8 * 4, "reused areas");
+static_assert(2 * SMEM_PREP <= 160 * 1024, "two workgroups per compute unit");
 static_assert(P_ATT % 16 == 0 && P_ARB % 16 == 0 && P_D0T % 16 == 0 && P_DL % 16 == 0, "alignment");
 
-constexpr int NTHR_PREP = 512;
-constexpr int kPrepGrid = 256;   // one persistent workgroup per compute unit of MI355X
+constexpr int NTHR_PREP = 512;   // one workgroup per (b, h, chunk) item; two fit in a compute unit
 
 struct PrepArgs {
     const void *r, *w, *k, *a, *b;
@@ -293,12 +301,9 @@ template <typename Tin> struct ItemRows {
     float rk[8];
     uint32_t m;   // mask byte of the row's token (1 without a mask, 0 past the end)
 };
-// (One dword per load instruction suffices: the wait is per instruction.)
-__device__ __forceinline__ void settle_row(Row8<bf16_t>& x) { asm volatile("" : "+v"(x.x.x)); }
-__device__ __forceinline__ void settle_row(Row8<float>& x) { asm volatile("" : "+v"(x.x[0].x), "+v"(x.x[1].x)); }
 
 template <typename Tin, bool LOGW, bool EPI, bool KK>
-__global__ __launch_bounds__(NTHR_PREP)
+__global__ __launch_bounds__(NTHR_PREP) __attribute__((amdgpu_waves_per_eu(4)))
 void prep128_kernel(PrepArgs g) {
     constexpr uint32_t SI = sizeof(Tin);
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -311,8 +316,19 @@ void prep128_kernel(PrepArgs g) {
     const int t = l & 31, j0 = 8 * (2 * w + (l >> 5));
     const PairSel psel(t);
 
+    // Items run chunk-major and from the last chunk of the window to the first:
+    // the pass that follows starts at the first chunk, so the records it reads
+    // first are the ones written last, still in the memory-side cache
+    // (1.33 against 1.37 ms per step on the hxa07D workload).
+    auto item_pos = [&](int item, int& bh, int& cw) {
+        const int nbh = g.items / nwin, q = item / nbh;
+        bh = item - q * nbh;
+        cw = nwin - 1 - q;
+    };
     auto load_item = [&](int item, ItemRows<Tin>& x) {
-        const int bh = item / nwin, c = g.cb + (item - bh * nwin);
+        int bh, c;
+        item_pos(item, bh, c);
+        c += g.cb;
         const int bb = bh / H, h = bh - bb * H, hk = h / (H / g.H_kv);
         const int64_t tok0 = int64_t(bb) * T;
         const int c0 = c * L;
@@ -341,25 +357,20 @@ void prep128_kernel(PrepArgs g) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const s16x4 z4 = {0, 0, 0, 0};
 
-    ItemRows<Tin> cur, nxt;
-    auto settle_item = [&](ItemRows<Tin>& x) {
-        settle_row(x.r); settle_row(x.w); settle_row(x.k); settle_row(x.a);
-        if constexpr (!KK) settle_row(x.b);
-        asm volatile("" : "+v"(x.m));
-        #pragma unroll
-        for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(x.rk[e]));
-    };
-    int item = blockIdx.x;
-    if (item < g.items) {
-        load_item(item, nxt);
-        settle_item(nxt);
-    }
-    for (; item < g.items; item += gridDim.x) {
-        cur = nxt;
-        const int bh = item / nwin, cw = item - bh * nwin;
+    ItemRows<Tin> cur;
+    // One item per workgroup.  (A persistent loop over items with the next item's
+    // rows prefetched needs more than the 128 registers that let two workgroups
+    // share a compute unit; the other workgroup covers the load latency instead.)
+    const int item = blockIdx.x;
+    if (item >= g.items) return;
+    {
+        load_item(item, cur);
+        int bh, cw;
+        item_pos(item, bh, cw);
         const int c0 = (g.cb + cw) * L;
         char* rec = g.ws + (int64_t(bh) * g.nrec + cw) * WS_CHUNK;
 
+        uint32_t at[4], bhat[4];   // At and Bh of the row thread's token and keys (bf16 pairs)
         // ---------------- Q0: decay prefix and the scaled operands (row threads) ----------------
         {
             // Tokens past the end (and masked ones) decay by 1 and carry zeros.
@@ -405,7 +416,7 @@ void prep128_kernel(PrepArgs g) {
                 const float4 s0 = lds<float4>(smem + P_KSQ, t * 32), s1 = lds<float4>(smem + P_KSQ, t * 32 + 16);
                 inv = inv_key_norm(((s0.x + s0.y) + (s0.z + s0.w)) + ((s1.x + s1.y) + (s1.z + s1.w)));
             }
-            uint32_t at[4], rth[4], rtl[4], bt[4], kth[4], ktl[4], bhat[4];
+            uint32_t rth[4], rtl[4], bt[4], kth[4], ktl[4];
             float bonus_part = 0.f;
             #pragma unroll
             for (int e = 0; e < 8; e += 2) {
@@ -450,9 +461,6 @@ void prep128_kernel(PrepArgs g) {
             sts<uint2>(smem + P_RTH, o + 16, make_uint2(rth[2], rth[3]));
             sts<uint2>(smem + P_RTL, o, make_uint2(rtl[0], rtl[1]));
             sts<uint2>(smem + P_RTL, o + 16, make_uint2(rtl[2], rtl[3]));
-            // Key-major copies of At and Bh.
-            pair_col_store(smem + P_ATT, j0, t, at, psel);
-            pair_col_store(smem + P_BHT, j0, t, bhat, psel);
             if (t == 0) {
                 sts<float4>(smem + P_DL, j0 * 4, make_float4(dx[0], dx[1], dx[2], dx[3]));
                 sts<float4>(smem + P_DL, j0 * 4 + 16, make_float4(dx[4], dx[5], dx[6], dx[7]));
@@ -462,10 +470,6 @@ void prep128_kernel(PrepArgs g) {
                 if (l < 32) sts<float>(smem + P_BON, (w * L + t) * 4, bonus_part);
             }
         }
-        // Next item's rows: this item's are consumed.  (Pinned here so that the loads
-        // are not sunk towards their use in the next iteration.)
-        if (item + int(gridDim.x) < g.items) load_item(item + gridDim.x, nxt);
-        asm volatile("" ::: "memory");
         __syncthreads();
 
         // ---------------- Q1: the four L x L matrices; Dinv ----------------
@@ -549,7 +553,7 @@ void prep128_kernel(PrepArgs g) {
             store_blk(0, 0, Dt0);
             store_blk(0, 16, zero);
         } else {
-            if (w == 1) {   // D1 from A_ab block 1; C(D1^T) to the U^T area (free until Q2) for wave 0
+            if (w == 1) {   // D1 from A_ab block 1; C(D1^T) to LDS for wave 0
                 f32x4 ab2 = zero, nsw1 = zero;
                 #pragma unroll
                 for (int kq = 0; kq < 4; ++kq) {
@@ -558,7 +562,7 @@ void prep128_kernel(PrepArgs g) {
                     nsw1 = mfma32(A1, B1, nsw1);
                 }
                 const f32x4 Dt1 = chain(ab2, nsw1);
-                sts<float4>(smem + P_UTH, (16 * lq + lr) * 16, make_float4(Dt1[0], Dt1[1], Dt1[2], Dt1[3]));
+                sts<float4>(smem + P_D1T, (16 * lq + lr) * 16, make_float4(Dt1[0], Dt1[1], Dt1[2], Dt1[3]));
                 store_blk(16, 16, Dt1);
             }
             // Wave 1 runs the D1 chain only.  A_rk tiles: waves 2, 3, 6; A_ak (swapped
@@ -644,12 +648,21 @@ void prep128_kernel(PrepArgs g) {
                 sts<uint2>(smem + P_ARB, (lr * PT + pairpos(16 + 4 * lq)) * 2, make_uint2(0, 0));
             }
         }
+        {
+            // The row thread's own At values, read back for the key-major copy below
+            // (cheaper than keeping them in registers through this phase).
+            const int o = (t * PK + pairpos(j0)) * 2;
+            const uint2 a01 = lds<uint2>(smem + P_AT, o), a23 = lds<uint2>(smem + P_AT, o + 16);
+            at[0] = a01.x; at[1] = a01.y; at[2] = a23.x; at[3] = a23.y;
+        }
         __syncthreads();
         if (w == 0) {
             // C(D10^T) = prod(C(T), C(D1^T)) = C(T^T D1^T): lane holds D10[lr][4 lq + r].
-            const float4 x = lds<float4>(smem + P_UTH, (16 * lq + lr) * 16);
+            const float4 x = lds<float4>(smem + P_D1T, (16 * lq + lr) * 16);
             store_blk(16, 0, prod(Tm, f32x4{x.x, x.y, x.z, x.w}));
         }
+        // Key-major copy of At into the At / Bt area (read for the last time above).
+        pair_col_store(smem + P_ATT, j0, t, at, psel);
         __syncthreads();
 
         // ---------------- Q2: U = Dinv A_ak; W and Q for key pair kp, token block tb ----------------
@@ -721,6 +734,9 @@ void prep128_kernel(PrepArgs g) {
             *reinterpret_cast<bf16x8*>(rec + kp * WS_KP + (BLK_QL + tb) * WS_BLK + l * 16) = ql;
         }
         __syncthreads();
+        // Key-major copy of Bh into the Rt area (read for the last time above).
+        pair_col_store(smem + P_BHT, j0, t, bhat, psel);
+        __syncthreads();
 
         // ---------------- Q3: E = Kh + U^T Bh and Bh for key tile jt; P; d; bonus ----------------
         {
@@ -782,10 +798,6 @@ void prep128_kernel(PrepArgs g) {
                 }
             }
         }
-        // Prefetched rows complete here, not across the loop back-edge, where the
-        // compiler's wait counting would also wait for this item's stores.
-        settle_item(nxt);
-        __syncthreads();   // LDS is rewritten by the next item
     }
 }
 
@@ -1120,9 +1132,7 @@ hipError_t launch_t(const Params& p, void* ws, int win, float* carry, hipStream_
         const int items = bh * nw;
         PrepArgs pa{p.r, p.w, p.k, p.a, p.b, p.r_k, p.mask, static_cast<char*>(ws), p.T, p.H, p.H_kv,
                     cb, nw, nrec, items};
-        // Persistent: one workgroup per compute unit walks the (b, h, chunk) items.
-        const int grid1 = items < kPrepGrid ? items : kPrepGrid;
-        hipLaunchKernelGGL(prep, dim3(grid1), dim3(NTHR_PREP), SMEM_PREP, stream, pa);
+        hipLaunchKernelGGL(prep, dim3(items), dim3(NTHR_PREP), SMEM_PREP, stream, pa);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         ScanArgs sa{p.v, cb == 0 ? p.s0 : s_carry, last ? p.s1 : s_carry, p.y, static_cast<const char*>(ws),
