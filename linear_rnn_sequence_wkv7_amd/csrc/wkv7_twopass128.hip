@@ -252,10 +252,11 @@ __device__ __forceinline__ rsrc_t chunk_rsrc(const char* base, int64_t tok0, int
 // [t][s], Dinv hi / lo [t][s~], U^T hi / lo [s'][s~] (~: pair-interleaved).
 // Areas are reused once their contents are dead, so that two workgroups fit
 // in one compute unit's LDS: At and Bt are read in the L x L phase only, after
-// which their area holds At^T and U^T; Rt is last read in the W, Q phase,
-// after which its area holds Bh^T; the |k|^2 partials' area holds D1^T for
-// the block inverse.  (At^T and Bh^T stay in the row threads' registers until
-// their areas are free.)
+// which their area holds At^T and U^T; Rt is last read in the D10 step (the
+// part that Q adds is read into registers there), after which its area holds
+// Bh^T; the |k|^2 partials' area holds D1^T for the block inverse.  (At is read
+// back by its row threads for the key-major copy; Bh stays in their registers
+// until its area is free.)
 constexpr int P_AT = 0;
 constexpr int P_BT = P_AT + MATK;
 constexpr int P_KTH = P_BT + MATK;
@@ -278,7 +279,7 @@ constexpr int SMEM_PREP = P_KSQ + L * 8 * 4;
 constexpr int P_ATT = P_AT;                      // from the D10 step on
 constexpr int P_UTH = P_ATT + MATT;              // from the U, W, Q phase on
 constexpr int P_UTL = P_UTH + MATL;
-constexpr int P_BHT = P_RTH;                     // from the E, P phase on
+constexpr int P_BHT = P_RTH;                     // from the U, W, Q phase on
 constexpr int P_D1T = P_KSQ;                     // fp32 16 x 16, L x L phase to the D10 step
 static_assert(P_UTL + MATL <= P_KTH && P_BHT + MATT <= P_ARB && 16 * 16 * 4 <= L * 8 * 4, "reused areas");
 static_assert(2 * SMEM_PREP <= 160 * 1024, "two workgroups per compute unit");
@@ -663,9 +664,24 @@ void prep128_kernel(PrepArgs g) {
         }
         // Key-major copy of At into the At / Bt area (read for the last time above).
         pair_col_store(smem + P_ATT, j0, t, at, psel);
+        // The Rt values this wave adds to Q below, read now so that the Rt area is
+        // free from the next barrier on (Bh^T goes there).
+        uint2 rtq[2][2];   // [u][hi, lo]
+        {
+            const int kp = w >> 1, tb = w & 1;
+            #pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int orow = ((16 * tb + lr) * PK + pairpos(16 * (2 * kp + u) + 4 * lq)) * 2;
+                rtq[u][0] = lds<uint2>(smem + P_RTH, orow);
+                rtq[u][1] = lds<uint2>(smem + P_RTL, orow);
+            }
+        }
         __syncthreads();
 
         // ---------------- Q2: U = Dinv A_ak; W and Q for key pair kp, token block tb ----------------
+        // Key-major copy of Bh into the Rt area (read for the last time above); read
+        // in Q3, after this phase's barrier.
+        pair_col_store(smem + P_BHT, j0, t, bhat, psel);
         if (w < 3) {
             // C(U) tile (sb, s'b): lane s = 16 sb + 4 lq + r, s' = 16 s'b + lr.
             const int sb = w == 0 ? 0 : 1, spb = w == 2 ? 1 : 0;
@@ -720,8 +736,7 @@ void prep128_kernel(PrepArgs g) {
             f32x4 qt[2];
             #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const int orow = ((16 * tb + lr) * PK + pairpos(16 * (2 * kp + u) + 4 * lq)) * 2;
-                const uint2 rh = lds<uint2>(smem + P_RTH, orow), rl = lds<uint2>(smem + P_RTL, orow);
+                const uint2 rh = rtq[u][0], rl = rtq[u][1];
                 f32x4 acc = {lo_f32(rh.x) + lo_f32(rl.x), hi_f32(rh.x) + hi_f32(rl.x),
                              lo_f32(rh.y) + lo_f32(rl.y), hi_f32(rh.y) + hi_f32(rl.y)};
                 acc = mfma32(cat(wh[0][u], wh[1][u]), Ar8, acc);
@@ -733,9 +748,6 @@ void prep128_kernel(PrepArgs g) {
             *reinterpret_cast<bf16x8*>(rec + kp * WS_KP + (BLK_QH + tb) * WS_BLK + l * 16) = qh;
             *reinterpret_cast<bf16x8*>(rec + kp * WS_KP + (BLK_QL + tb) * WS_BLK + l * 16) = ql;
         }
-        __syncthreads();
-        // Key-major copy of Bh into the Rt area (read for the last time above).
-        pair_col_store(smem + P_BHT, j0, t, bhat, psel);
         __syncthreads();
 
         // ---------------- Q3: E = Kh + U^T Bh and Bh for key tile jt; P; d; bonus ----------------
@@ -1129,7 +1141,12 @@ hipError_t launch_t(const Params& p, void* ws, int win, float* carry, hipStream_
     for (int cb = 0; cb < nch; cb += nrec) {
         const int nw = nch - cb < nrec ? nch - cb : nrec;
         const bool last = cb + nw == nch;
-        const int items = bh * nw;
+        // One pass-1 workgroup per item: the grid's work-items must fit in 32 bits (a
+        // workspace for that many records would not fit in memory, so this does not
+        // bind in practice).
+        const int64_t items64 = int64_t(bh) * nw;
+        if (items64 * NTHR_PREP > int64_t(0xffffffffu)) return hipErrorInvalidConfiguration;
+        const int items = int(items64);
         PrepArgs pa{p.r, p.w, p.k, p.a, p.b, p.r_k, p.mask, static_cast<char*>(ws), p.T, p.H, p.H_kv,
                     cb, nw, nrec, items};
         hipLaunchKernelGGL(prep, dim3(items), dim3(NTHR_PREP), SMEM_PREP, stream, pa);
