@@ -44,6 +44,13 @@ EXTRA = {
 }
 
 
+# Host-side sanitizers for the CPU tests of the library's host code: each flag
+# follows -Xarch_host, so it reaches the host compilation only and the device code
+# is compiled as in the product build.  The library then leaves the sanitizer
+# runtime's symbols undefined; the process that loads it preloads that runtime.
+SANITIZE_HOST = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined -Xarch_host -fno-omit-frame-pointer".split()
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -107,6 +114,37 @@ def build(asm: bool = False, verbose: bool = False) -> str:
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
     return LIB
+
+
+def sanitizer_runtime() -> str | None:
+    """The clang AddressSanitizer runtime (it carries the UndefinedBehaviorSanitizer
+    handlers too) of the ROCm toolchain, or None."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    for base in (os.path.join(root, "lib", "llvm"), root):
+        hits = sorted(glob.glob(os.path.join(base, "lib", "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so")))
+        if hits:
+            return hits[-1]
+    return None
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """Compile every source with SANITIZE_HOST (and -O1 -g) into out_dir and link
+    out_dir/libwkv7_hostsan.so; returns its path."""
+    os.makedirs(out_dir, exist_ok=True)
+    cc = hipcc()
+    common = [f for f in COMMON if f != "-O3"] + ["-O1", "-g"]
+    jobs, objs = [], []
+    for src in SOURCES:
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        jobs.append([cc, *common, *EXTRA.get(src, []), *SANITIZE_HOST, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        list(ex.map(_run, jobs))
+    lib = os.path.join(out_dir, "libwkv7_hostsan.so")
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", lib, *objs])
+    return lib
 
 
 def main(argv=None):
