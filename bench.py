@@ -141,15 +141,24 @@ def _cpu_noop(_):
     return os.getpid()
 
 
+# The forward sample's oracle outputs come back at every REF_TOKEN_STRIDE-th token
+# (and the final states), for the parity figures of the bench line.
+REF_TOKEN_STRIDE = 16
+
+
 def _cpu_work(pairs):
-    """Oracle work on one share of the sampled pairs; returns its compute time."""
+    """Oracle work on one share of the sampled pairs; returns its compute time and,
+    for the forward, the oracle's y at every REF_TOKEN_STRIDE-th token and the
+    final states of the share."""
     import numpy as np
     from oracle import wkv7_oracle as O
     from tests import parity as P
     kind, wl, x, gi = _CPU_JOB["kind"], _CPU_JOB["wl"], _CPU_JOB["x"], _CPU_JOB["gi"]
     t0 = time.perf_counter()
     if kind == "forward":
-        P.oracle_pairs(x, wl, pairs)
+        y_ref, s_ref = P.oracle_pairs(x, wl, pairs)
+        dt = time.perf_counter() - t0
+        return dt, np.ascontiguousarray(y_ref[:, ::REF_TOKEN_STRIDE]), s_ref
     elif kind == "decode":
         # Successive decode tokens from the same state: one forward over the steps.
         bs = np.array([p[0] for p in pairs])
@@ -178,7 +187,7 @@ def _cpu_work(pairs):
                         w_mode=wl.w_mode, r_k=sel["r_k"], y_scale=wl.y_scale)
     else:
         raise ValueError(kind)
-    return time.perf_counter() - t0
+    return time.perf_counter() - t0, None, None
 
 
 def default_cpu_workers() -> int:
@@ -193,7 +202,9 @@ def default_cpu_workers() -> int:
 def cpu_baseline(kind: str, wl, x, gi, n_pairs: int, workers: int):
     """Time the oracle on n_pairs sampled sequences split over `workers` forked
     processes.  The value is head-tokens of the sample over the wall time of the
-    parallel region (pool already started)."""
+    parallel region (pool already started).  Returns the baseline record and, for
+    the forward, the oracle outputs of the sample ({"pairs", "y", "s"}; y at every
+    REF_TOKEN_STRIDE-th token), else None."""
     import multiprocessing as mp
     from tests import parity as P
     pairs = P.sample_pairs(wl, n_pairs, seed=wl.seed)[:n_pairs]
@@ -204,16 +215,49 @@ def cpu_baseline(kind: str, wl, x, gi, n_pairs: int, workers: int):
     with ctx.Pool(n_w, initializer=_cpu_worker_init) as pool:
         pool.map(_cpu_noop, range(n_w), chunksize=1)
         t0 = time.perf_counter()
-        busy = pool.map(_cpu_work, shares, chunksize=1)
+        res = pool.map(_cpu_work, shares, chunksize=1)
         dt = time.perf_counter() - t0
     _CPU_JOB.clear()
+    busy = [r[0] for r in res]
+    ref = None
+    if kind == "forward":
+        import numpy as np
+        ref = {"pairs": [p for sh in shares for p in sh], "y": np.concatenate([r[1] for r in res]),
+               "s": np.concatenate([r[2] for r in res])}
     steps = wl.steps if kind == "decode" else wl.T
     what = {"forward": "whole sequences", "decode": f"sequences x all {wl.steps} decode steps",
             "backward": "whole sequences, backward"}[kind]
     return {"value": len(pairs) * steps / dt, "unit": "head-tokens/s", "cores": n_w, "kind": "oracle",
             "sample": f"{len(pairs)} of {wl.B * wl.H} (batch, head) {what} ({steps} tokens each), fp64 numpy, "
                       f"{n_w} worker processes with one BLAS thread each, "
-                      f"{dt:.1f} s wall, {sum(busy):.1f} s of worker compute"}
+                      f"{dt:.1f} s wall, {sum(busy):.1f} s of worker compute"}, ref
+
+
+# Parity bound of the forward kernels: max|x - x_ref| <= tau rms(x_ref), widened by
+# the bf16 half-ulp 2^-8 |x_ref| elementwise for a bf16 y.
+PARITY_TAU = {"scan": 5e-3, "chunked": 1e-2, "chunked128": 1e-2, "twopass128": 1e-2}
+
+
+def forward_parity(kind, ref, y, s_out, y_bf16: bool):
+    """The GPU forward's y (at the sample's tokens) and final states against the
+    oracle outputs of the CPU baseline's sample."""
+    import numpy as np
+    import torch
+    bs = torch.tensor([p[0] for p in ref["pairs"]], device=y.device)
+    hs = torch.tensor([p[1] for p in ref["pairs"]], device=y.device)
+    yg = y[bs, ::REF_TOKEN_STRIDE, hs].double().cpu().numpy()
+    sg = s_out[bs, hs].double().cpu().numpy()
+    tau = PARITY_TAU[kind]
+    out = {"pairs": len(ref["pairs"]), "token_stride": REF_TOKEN_STRIDE, "tau": tau, "bf16_y_allowance": y_bf16}
+    ok = True
+    for name, got, want, allow in (("y", yg, ref["y"], y_bf16), ("state", sg, ref["s"], False)):
+        scale = float(np.sqrt(np.mean(want * want)))
+        diff = np.abs(got - want)
+        bound = tau * scale + (2.0 ** -8 * np.abs(want) if allow else 0.0)
+        out[f"{name}_max_err_over_rms"] = float(diff.max() / scale)
+        ok = ok and bool(np.all(np.isfinite(got))) and bool(np.all(diff <= bound))
+    out["within_bound"] = ok
+    return out
 
 
 def run_wkv4(a, wl, G, wkv7, torch, np):
@@ -373,7 +417,7 @@ def main(argv=None) -> int:
         # About 10-30 s of oracle work in total, spread over the workers.
         n_cpu = {"forward": 256 if wl.D == 64 else 16, "decode": 16384,
                  "backward": 4 * workers if wl.D == 64 else workers}[base_kind]
-    cpu = cpu_baseline(base_kind, wl, x, gi, n_cpu, workers) if n_cpu > 0 else None
+    cpu, ref = cpu_baseline(base_kind, wl, x, gi, n_cpu, workers) if n_cpu > 0 else (None, None)
 
     import torch
 
@@ -494,6 +538,9 @@ def main(argv=None) -> int:
         "wall_s_timed_region": t_wall, "launch": "hip_graph" if a.graph else "host_per_step",
     }
     out["cpu_baseline"] = cpu
+    # The forward's outputs after the timed steps (each step recomputes them from
+    # the same inputs) against the oracle outputs of the CPU sample.
+    out["parity"] = forward_parity(kind, ref, y, s_out, wl.y_dtype == "bf16") if ref is not None else None
     print(json.dumps(out), flush=True)
     return 0
 
