@@ -304,13 +304,22 @@ def run_wkv4(a, wl, G, wkv7, torch, np):
         from oracle import wkv4_oracle as O4
         n = min(8 if a.cpu_pairs is None else a.cpu_pairs, 8)
         t0 = time.perf_counter()
-        O4.wkv4_forward(x["w"][:n], x["u"][:n], x["k"][:1, :, :n], x["v"][:1, :, :n])
+        y_ref, _ = O4.wkv4_forward(x["w"][:n], x["u"][:n], x["k"][:1, :, :n], x["v"][:1, :, :n])
         dt = time.perf_counter() - t0
         out["cpu_baseline"] = {"value": n * wl.T / dt, "unit": "channel-tokens/s", "cores": 1, "kind": "oracle",
                                "sample": f"{n} channels of batch 0 x all {wl.T} tokens (the oracle evaluates "
                                          f"the sum definition, O(T^2) per channel), fp64 numpy, {dt:.1f} s"}
+        # The GPU's y of the same channels (from the zero state, as the oracle) against it.
+        got = y[:1, :, :n].double().cpu().numpy()
+        scale = float(np.sqrt(np.mean(y_ref * y_ref)))
+        diff = np.abs(got - y_ref)
+        bound = PARITY_TAU["scan"] * scale + (2.0 ** -8 * np.abs(y_ref) if wl.y_dtype == "bf16" else 0.0)
+        out["parity"] = {"channels": n, "tau": PARITY_TAU["scan"], "bf16_y_allowance": wl.y_dtype == "bf16",
+                         "y_max_err_over_rms": float(diff.max() / scale),
+                         "within_bound": bool(np.all(np.isfinite(got)) and np.all(diff <= bound))}
     else:
         out["cpu_baseline"] = None
+        out["parity"] = None
     print(json.dumps(out), flush=True)
     return 0
 
