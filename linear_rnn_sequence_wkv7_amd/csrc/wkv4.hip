@@ -61,17 +61,28 @@ struct Scaled {
     float A, Bd, P;   // a = A 2^P, b = Bd 2^P (P in log2 units)
 };
 
+// The two rescaling factors 2^(a - max(a, b)) and 2^(b - max(a, b)): one of them is
+// 2^0 = 1, so one exp2 of -|a - b| gives both.
+__device__ __forceinline__ void rescale2(float a, float b, float& ea, float& eb, float& p) {
+    const float d = b - a;
+    const float e = __builtin_amdgcn_exp2f(-fabsf(d));
+    const bool b_larger = d > 0.f;
+    ea = b_larger ? e : 1.f;
+    eb = b_larger ? 1.f : e;
+    p = b_larger ? b : a;
+}
+
 // (A, B, P) + e^x (v, 1), x in log2 units.
 __device__ __forceinline__ Scaled add_term(Scaled s, float x, float v) {
-    const float p = fmaxf(s.P, x);
-    const float e1 = __builtin_amdgcn_exp2f(s.P - p), e2 = __builtin_amdgcn_exp2f(x - p);
+    float e1, e2, p;
+    rescale2(s.P, x, e1, e2, p);
     return Scaled{fmaf(e1, s.A, e2 * v), fmaf(e1, s.Bd, e2), p};
 }
 
 // Merge two states (sums of both).
 __device__ __forceinline__ Scaled merge(Scaled s, Scaled t) {
-    const float p = fmaxf(s.P, t.P);
-    const float e1 = __builtin_amdgcn_exp2f(s.P - p), e2 = __builtin_amdgcn_exp2f(t.P - p);
+    float e1, e2, p;
+    rescale2(s.P, t.P, e1, e2, p);
     return Scaled{fmaf(e1, s.A, e2 * t.A), fmaf(e1, s.Bd, e2 * t.Bd), p};
 }
 
