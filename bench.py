@@ -51,7 +51,9 @@ KERNEL_SOURCES = {
     "scan": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_scan.hip",
     "chunked": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_chunked.hip",
     "chunked128": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_chunked128.hip",
-    "twopass128": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_twopass128.hip",
+    "twopass128": ("linear_rnn_sequence_wkv7_amd/csrc/wkv7_twopass128.hip",
+                   "linear_rnn_sequence_wkv7_amd/csrc/wkv7_twopass128_scan.hip",
+                   "linear_rnn_sequence_wkv7_amd/csrc/wkv7_twopass128.h"),
     "decode": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_decode.hip",
     "backward": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_backward.hip",
     "wkv4": "linear_rnn_sequence_wkv7_amd/csrc/wkv4.hip",
@@ -60,7 +62,8 @@ KERNEL_SOURCES = {
 
 def source_sha(kind: str) -> str:
     h = hashlib.sha256()
-    for rel in (KERNEL_SOURCES[kind], "linear_rnn_sequence_wkv7_amd/csrc/wkv7_device.h"):
+    srcs = KERNEL_SOURCES[kind]
+    for rel in (*((srcs,) if isinstance(srcs, str) else srcs), "linear_rnn_sequence_wkv7_amd/csrc/wkv7_device.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

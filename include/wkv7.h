@@ -98,7 +98,11 @@ enum wkv7_algo {
     WKV7_ALGO_CHUNKED = 2,  /* chunk-parallel form on bf16 matrix cores, fp32 accumulation */
     WKV7_ALGO_TWO_PASS = 3  /* D = 128 only, wkv7_forward_ws only: the chunked form split in two
                                kernels, the state-independent matrices of every chunk first (in
-                               parallel over chunks, into the workspace), then the recurrence */
+                               parallel over chunks, into the workspace, as fp16), then the
+                               recurrence on fp16 matrix cores (fp32 accumulation).  Range: the
+                               state, v and the per-chunk matrices must stay below 65504 in
+                               magnitude (fp16's largest finite value); past it y and the state
+                               come out infinite or NaN.  The other algorithms keep bf16's range */
 };
 
 typedef struct wkv7_desc {
@@ -160,7 +164,7 @@ int wkv7_forward_ws(const wkv7_desc* desc,
  * windows when state_out is NULL, in a static device array of
  * WKV7_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on
  * until the process ends.  The chunks run in windows of as many 32-token chunks
- * per (b, h) as fit (B * H * 54272 bytes per chunk, after B * H * D * D * 4
+ * per (b, h) as fit (B * H * 37632 bytes per chunk, after B * H * D * D * 4
  * bytes of state carry when state_out is NULL): pass 1 then pass 2 per
  * window, the state passed on through state_out (or the carry).  The results
  * are those of wkv7_forward_ws bit for bit.  EUNSUPPORTED when not even one
@@ -180,7 +184,7 @@ int wkv7_forward_noalloc(const wkv7_desc* desc,
 
 /* Workspace bytes wkv7_forward_ws uses for this descriptor: for D = 128 with
  * algo AUTO and T >= the chunk length, or algo TWO_PASS and T >= 1, it is
- * B * H * ceil(T / 32) * 54272 (one 53 KiB record of operands per chunk);
+ * B * H * ceil(T / 32) * 37632 (one 36.75 KiB record of operands per chunk);
  * 0 otherwise.  A negative wkv7_status if the descriptor is invalid.  Host
  * only: no HIP call. */
 int64_t wkv7_workspace_bytes(const wkv7_desc* desc);

@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libwkv7.so")
 ARCH = "gfx950"
 
 SOURCES = ["wkv7_api.cpp", "wkv7_scan.hip", "wkv7_decode.hip", "wkv7_chunked.hip", "wkv7_chunked128.hip",
-           "wkv7_twopass128.hip", "wkv7_backward.hip", "wkv4.hip"]
+           "wkv7_twopass128.hip", "wkv7_twopass128_scan.hip", "wkv7_backward.hip", "wkv4.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -41,6 +41,7 @@ COMMON = [
 # AGPR <-> VGPR copies.
 EXTRA = {
     "wkv7_twopass128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "wkv7_twopass128_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -1,5 +1,6 @@
-// Two-pass chunked WKV-7 forward for head size D = 128 on gfx950 bf16 matrix
-// cores (fp32 accumulation).
+// Two-pass chunked WKV-7 forward for head size D = 128 on gfx950 matrix cores
+// (fp32 accumulation): pass 1 here on bf16 operands, pass 2 in
+// wkv7_twopass128_scan.hip on fp16 operands.
 //
 // The chunk algebra is that of the one-pass kernels (unrolling S_t = S_{t-1}
 // (diag(w_t) + a_t b_t^T) + v_t k_t^T over a chunk of L tokens; wiki note
@@ -20,8 +21,8 @@
 // Pass 1 (prep) computes W, Q, E, Bh, P, d and the epilogue's per-token
 // bonus for every (b, h, chunk) in parallel -- one D = 128 head per chunk, no
 // replication across value slices -- and writes them to a caller-provided
-// workspace in the exact lane order of the matrix-core operands that pass 2
-// loads.  Pass 2 (scan) runs the chunk recurrence: per chunk four products
+// workspace, as fp16, in the exact lane order of the matrix-core operands that
+// pass 2 loads.  Pass 2 (scan) runs the chunk recurrence: per chunk four products
 // against the state and two small ones, with no L x L algebra left on the
 // sequential path.  Four workgroups per (b, h) each own 32 value rows; their
 // ids are 8 apart, so under round-robin dispatch they share one XCD's L2 and
@@ -30,8 +31,10 @@
 // Operand conventions as in the one-pass kernels: bf16 hi + lo splits where
 // a rounding would decide the result, 32-deep contraction axes stored
 // pair-interleaved (position 8 q + 4 e + r of a 32-block holds index
-// 16 e + 4 q + r), and every accumulator chain uses the single 16x16x32
-// opcode (never a result of one MFMA opcode as the accumulator of another).
+// 16 e + 4 q + r), and every accumulator chain uses the single 16x16x32 bf16
+// opcode (never a result of one MFMA opcode as the accumulator of another; pass
+// 2's fp16 opcode lives in its own kernel and source).  The L x L products keep
+// bf16 because their scaled operands (b, k times 2^-g) exceed fp16's range.
 //
 // Only pass 1 reads r, w, k, a, b, so both input options live there.  A
 // masked token is the identity token (r, k, a, b = 0, decay 1): its rows and
@@ -42,50 +45,17 @@
 // a = -kk, b = kk alpha and k (1 - decay + alpha) in place of the inputs.
 #include <mutex>
 
-#include "wkv7_internal.h"
-#include "wkv7_device.h"
+#include "wkv7_twopass128.h"
 
 namespace wkv7 {
+namespace tp128 {
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-constexpr int L = 32;          // chunk length
-constexpr int DK = 128;        // head size
-constexpr int DV = 32;         // value rows per pass-2 workgroup
-constexpr int NSLICE = DK / DV;
 constexpr int PK = 136;        // bf16 pitch of [L][DK] token-major operands
-constexpr int PT = 40;         // bf16 pitch of [*][L] operands
 constexpr int PD = 20;         // bf16 pitch of a 16 x 16 block
 constexpr int MATK = L * PK * 2;
 constexpr int MATT = DK * PT * 2;
 constexpr int MATL = L * PT * 2;
-
-// Workspace record of one (b, h, chunk).  Blocks of 1 KB hold one bf16x8
-// operand per lane (lane l at byte 16 l).  Per key pair kp (keys 32 kp ..
-// 32 kp + 31), block:
-//   0, 1   W   as the A operand of W (m = token of block tb, k = key), tb = 0, 1
-//   2..5   Q   hi (tb = 0, 1), lo (tb = 0, 1), same layout as W
-//   6, 7   Bh  as the A operand of Bh^T (m = key of tile 2 kp + u, k = token), u = 0, 1
-//   8..11  E   hi (u = 0, 1), lo (u = 0, 1), same layout as Bh
-// then P (A operand, m = token of block tb, k = token): hi tb 0, 1, lo tb 0, 1;
-// d[128] fp32; bonus[32] fp32.
-constexpr int WS_BLK = 1024;
-constexpr int WS_KP = 12 * WS_BLK;
-constexpr int BLK_W = 0, BLK_QH = 2, BLK_QL = 4, BLK_BH = 6, BLK_EH = 8, BLK_EL = 10;
-constexpr int WS_P = 4 * WS_KP;
-constexpr int WS_D = WS_P + 4 * WS_BLK;
-constexpr int WS_BON = WS_D + DK * 4;
-constexpr int WS_CHUNK = 54272;
-static_assert(WS_BON + L * 4 <= WS_CHUNK && WS_CHUNK % 256 == 0, "workspace record");
-
-__host__ __device__ constexpr int pairpos(int k) {
-    return 32 * (k >> 5) + 8 * ((k >> 2) & 3) + 4 * ((k >> 4) & 1) + (k & 3);
-}
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -121,19 +91,6 @@ __device__ __forceinline__ void to_operand2(const f32x4 c0, const f32x4 c1, bf16
     hi = cat(h0, h1);
     lo = cat(l0, l1);
 }
-template <typename T> __device__ __forceinline__ T lds(const char* base, int byte_off) {
-    return *reinterpret_cast<const T*>(base + byte_off);
-}
-template <typename T> __device__ __forceinline__ void sts(char* base, int byte_off, T v) {
-    *reinterpret_cast<T*>(base + byte_off) = v;
-}
-__device__ __forceinline__ f32x4 ld_f32x4(const char* p) {
-    const float4 x = *reinterpret_cast<const float4*>(p);
-    return f32x4{x.x, x.y, x.z, x.w};
-}
-__device__ __forceinline__ uint32_t dpp_u32_xor1(uint32_t x) {
-    return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), kDppQuadXor1, 0xF, 0xF, false));
-}
 // Inclusive prefix sums over lanes 0..31 and, separately, 32..63, of 8 values per
 // lane, step by step across the 8 (a DPP read of a value written by the previous
 // instruction would need wait states).
@@ -150,27 +107,6 @@ __device__ __forceinline__ void scan32x8(float (&x)[8]) {
     dpp_add8<0x118, 0xF>(x);   // row_shr:8
     dpp_add8<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3 only: lane 15 (47) of the row below
 }
-
-constexpr int kRsrcWord3 = 0x00020000;
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
-    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), 0, int(n), kRsrcWord3);
-}
-
-template <typename T> struct Buf;
-template <> struct Buf<bf16_t> {
-    static __device__ __forceinline__ void store1(rsrc_t r, uint32_t off, float x) {
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), r, off, 0, 0);
-    }
-};
-template <> struct Buf<float> {
-    static __device__ __forceinline__ void store1(rsrc_t r, uint32_t off, float x) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
-    }
-};
 
 // 8 consecutive elements of one token row.
 template <typename Tin> struct Row8;
@@ -237,12 +173,6 @@ __device__ __forceinline__ void pair_col_store(char* base, int row0, int t, cons
     }
 }
 
-// Chunk descriptor: tokens [c0, c0 + L) of sequence bb, clipped at T (the rest reads 0).
-__device__ __forceinline__ rsrc_t chunk_rsrc(const char* base, int64_t tok0, int c0, int T, uint32_t stride) {
-    const int nv = max(0, min(T - c0, L));
-    const int64_t t0 = nv > 0 ? tok0 + c0 : 0;
-    return make_rsrc(base + t0 * stride, uint32_t(nv) * stride);
-}
 
 // ============================== pass 1: per-chunk matrices ==============================
 
@@ -719,9 +649,7 @@ void prep128_kernel(PrepArgs g) {
             #pragma unroll
             for (int u = 0; u < 2; ++u) wt[u] = mfma32(At8[u], DlT, mfma32(At8[u], DhT, zero));
             {
-                const uint4 o4 = make_uint4(pack_bf16(wt[0][0], wt[0][1]), pack_bf16(wt[0][2], wt[0][3]),
-                                            pack_bf16(wt[1][0], wt[1][1]), pack_bf16(wt[1][2], wt[1][3]));
-                *reinterpret_cast<uint4*>(rec + kp * WS_KP + (BLK_W + tb) * WS_BLK + l * 16) = o4;
+                *reinterpret_cast<f16x8*>(rec + kp * WS_KP + (BLK_W + tb) * WS_BLK + l * 16) = to_f16x8(wt[0], wt[1]);
             }
             // C(W) tiles (token block sb, key tile 2 kp + u): lane token 4 lq + r, key lr.
             // As A operands they are W^T with the token axis as k.
@@ -743,10 +671,7 @@ void prep128_kernel(PrepArgs g) {
                 acc = mfma32(cat(wl[0][u], wl[1][u]), Ar8, acc);
                 qt[u] = acc;
             }
-            bf16x8 qh, ql;
-            to_operand2(qt[0], qt[1], qh, ql);
-            *reinterpret_cast<bf16x8*>(rec + kp * WS_KP + (BLK_QH + tb) * WS_BLK + l * 16) = qh;
-            *reinterpret_cast<bf16x8*>(rec + kp * WS_KP + (BLK_QL + tb) * WS_BLK + l * 16) = ql;
+            *reinterpret_cast<f16x8*>(rec + kp * WS_KP + (BLK_Q + tb) * WS_BLK + l * 16) = to_f16x8(qt[0], qt[1]);
         }
         __syncthreads();
 
@@ -754,7 +679,14 @@ void prep128_kernel(PrepArgs g) {
         {
             const int kp = w >> 1, u = w & 1, jt = 2 * kp + u;
             const bf16x8 Bh8 = lds<bf16x8>(smem + P_BHT, opT(jt));
-            *reinterpret_cast<bf16x8*>(rec + kp * WS_KP + (BLK_BH + u) * WS_BLK + l * 16) = Bh8;
+            {
+                // Bh is bf16 here (the operand of E below); fp16 holds each value exactly
+                // inside fp16's normal range.
+                const uint4 b4 = __builtin_bit_cast(uint4, Bh8);
+                *reinterpret_cast<uint4*>(rec + kp * WS_KP + (BLK_BH + u) * WS_BLK + l * 16) =
+                    make_uint4(pack_f16(lo_f32(b4.x), hi_f32(b4.x)), pack_f16(lo_f32(b4.y), hi_f32(b4.y)),
+                               pack_f16(lo_f32(b4.z), hi_f32(b4.z)), pack_f16(lo_f32(b4.w), hi_f32(b4.w)));
+            }
             const float dj = lds<float>(smem + P_DL, (16 * jt + lr) * 4);
             const int kpos = pairpos(16 * jt + lr);
             f32x4 e[2];
@@ -771,10 +703,7 @@ void prep128_kernel(PrepArgs g) {
                 acc = mfma32(lds<bf16x8>(smem + P_UTL, opT(tb)), Bh8, acc);
                 e[tb] = acc;
             }
-            bf16x8 eh, el;
-            to_operand2(e[0], e[1], eh, el);
-            *reinterpret_cast<bf16x8*>(rec + kp * WS_KP + (BLK_EH + u) * WS_BLK + l * 16) = eh;
-            *reinterpret_cast<bf16x8*>(rec + kp * WS_KP + (BLK_EL + u) * WS_BLK + l * 16) = el;
+            *reinterpret_cast<f16x8*>(rec + kp * WS_KP + (BLK_E + u) * WS_BLK + l * 16) = to_f16x8(e[0], e[1]);
         }
         if (w == 0) {
             // C(P^T) tiles (s'b, tb): P^T = A_rk^T + U^T A_rb^T; lane s' = 16 s'b + 4 lq + r, t = 16 tb + lr.
@@ -791,13 +720,13 @@ void prep128_kernel(PrepArgs g) {
                 acc = mfma32(lds<bf16x8>(smem + P_UTL, opT(spb)), Ar8, acc);
                 pt[n] = acc;
             }
-            bf16x8 ph, pl;
-            to_operand2(pt[0], zero, ph, pl);
-            *reinterpret_cast<bf16x8*>(rec + WS_P + 0 * WS_BLK + l * 16) = ph;
-            *reinterpret_cast<bf16x8*>(rec + WS_P + 2 * WS_BLK + l * 16) = pl;
-            to_operand2(pt[1], pt[2], ph, pl);
-            *reinterpret_cast<bf16x8*>(rec + WS_P + 1 * WS_BLK + l * 16) = ph;
-            *reinterpret_cast<bf16x8*>(rec + WS_P + 3 * WS_BLK + l * 16) = pl;
+            f16x8 ph, pl;
+            to_operand2_h(pt[0], zero, ph, pl);
+            *reinterpret_cast<f16x8*>(rec + WS_P + 0 * WS_BLK + l * 16) = ph;
+            *reinterpret_cast<f16x8*>(rec + WS_P + 2 * WS_BLK + l * 16) = pl;
+            to_operand2_h(pt[1], pt[2], ph, pl);
+            *reinterpret_cast<f16x8*>(rec + WS_P + 1 * WS_BLK + l * 16) = ph;
+            *reinterpret_cast<f16x8*>(rec + WS_P + 3 * WS_BLK + l * 16) = pl;
         } else if (w == 1) {
             if (l < 32) *reinterpret_cast<float4*>(rec + WS_D + l * 16) = lds<float4>(smem + P_DL, l * 16);
         } else if (w == 2) {
@@ -813,311 +742,6 @@ void prep128_kernel(PrepArgs g) {
     }
 }
 
-
-// ============================== pass 2: the chunk recurrence ==============================
-
-// LDS map of pass 2 (bytes): the four waves' partial X and Y tiles, the reduced X
-// tiles as bf16 hi / lo operands, and V^T of the slice (two chunk buffers).
-constexpr int NTHR_SCAN = 256;
-constexpr int S_PART = 0;                          // f32x4 [wave][tile 0..7][lane]
-constexpr int S_XOH = S_PART + 4 * 8 * 64 * 16;    // s16x4 [tile 0..3][lane]
-constexpr int S_XOL = S_XOH + 4 * 64 * 8;
-constexpr int VS_BYTES = DV * PT * 2;
-constexpr int S_VS = S_XOL + 4 * 64 * 8;           // bf16 [buffer][DV][PT] V^T hi
-constexpr int S_VSL = S_VS + 2 * VS_BYTES;         // lo (fp32 inputs)
-constexpr int SMEM_SCAN_BF16 = S_VSL;
-constexpr int SMEM_SCAN_F32 = S_VSL + 2 * VS_BYTES;
-static_assert(SMEM_SCAN_F32 <= 64 * 1024, "default dynamic LDS limit");
-
-struct ScanArgs {
-    const void* v;
-    const float* s0;
-    float* s1;
-    void* y;
-    const char* ws;
-    // Chunks cb .. ce - 1 from state s0 (or zero) to s1 (or not written); the record
-    // of chunk c of (b, h) is record b h * nrec + c - cb of the workspace.
-    int T, H, H_kv, BH, cb, ce, nrec;
-    float y_scale;
-};
-
-// 4 consecutive elements of one token row.
-template <typename Tin> struct Row4;
-template <> struct Row4<bf16_t> {
-    uint2 x;
-    __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
-        x = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-    }
-    __device__ __forceinline__ float get(int e) const {
-        const uint32_t d = e < 2 ? x.x : x.y;
-        return (e & 1) ? __uint_as_float(d & 0xffff0000u) : __uint_as_float(d << 16);
-    }
-};
-template <> struct Row4<float> {
-    uint4 x;
-    __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
-        x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    }
-    __device__ __forceinline__ float get(int e) const {
-        return __uint_as_float(e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w);
-    }
-};
-
-// As pair_col_store for 4 rows: the even lane writes row0, row0 + 1, the odd lane
-// row0 + 2, row0 + 3.
-__device__ __forceinline__ void pair_col_store4(char* base, int row0, int t, const uint32_t (&v)[2]) {
-    const uint32_t pv0 = dpp_u32_xor1(v[0]), pv1 = dpp_u32_xor1(v[1]);
-    const bool odd = t & 1;
-    const int ocol = pairpos(t & ~1);
-    const uint32_t own = odd ? v[1] : v[0], oth = odd ? pv1 : pv0;
-    #pragma unroll
-    for (int xx = 0; xx < 2; ++xx) {
-        const uint32_t own16 = xx ? own >> 16 : own & 0xffffu;
-        const uint32_t oth16 = xx ? oth >> 16 : oth & 0xffffu;
-        const uint32_t word = odd ? (oth16 | (own16 << 16)) : (own16 | (oth16 << 16));
-        sts<uint32_t>(base, ((row0 + (odd ? 2 : 0) + xx) * PT + ocol) * 2, word);
-    }
-}
-
-// One chunk's workspace operands as this wave loads them.
-struct Ops {
-    bf16x8 W[2], Qh[2], Ql[2], Bh[2], Eh[2], El[2], Ph, Pl;
-    f32x4 d[2], bon;
-};
-
-template <typename Tin, typename Ty, bool EPI>
-__global__ __launch_bounds__(NTHR_SCAN)
-void scan128_kernel(ScanArgs g) {
-    constexpr bool VSPLIT = sizeof(Tin) == 4;
-    constexpr uint32_t SI = sizeof(Tin), SY = sizeof(Ty);
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    // Workgroup -> (b, h, value slice q); the 4 slices of a (b, h) are 8 ids apart.
-    const int gid = blockIdx.x;
-    const int q = (gid >> 3) & (NSLICE - 1);
-    const int bh = (gid & 7) + 8 * (gid >> 5);
-    if (bh >= g.BH) return;
-    const int tid = threadIdx.x;
-    const int kp = __builtin_amdgcn_readfirstlane(tid >> 6);   // key pair of this wave
-    const int l = tid & 63, lr = l & 15, lq = l >> 4;
-    const int H = g.H, T = g.T, cb = g.cb, ce = g.ce;
-    const int bb = bh / H, h = bh - bb * H, hk = h / (H / g.H_kv);
-    const uint32_t stkv = uint32_t(g.H_kv) * DK * SI, sty = uint32_t(H) * DK * SY;
-    const int64_t tok0 = int64_t(bb) * T;
-    // Record of chunk c (cb <= c < ce) of this (b, h).
-    const int64_t rec0 = int64_t(bh) * g.nrec - cb;
-    auto rec_of = [&](int c) { return g.ws + (rec0 + c) * WS_CHUNK; };
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-
-    // State tiles ST[sg][u][r] = S[32 q + 16 sg + lr][16 (2 kp + u) + 4 lq + r]: the
-    // C layout of S^T, i.e. B operands of S^T with the key axis as k.
-    const int64_t sbase = int64_t(bh) * DK * DK;
-    f32x4 ST[2][2];
-    #pragma unroll
-    for (int sg = 0; sg < 2; ++sg)
-        #pragma unroll
-        for (int u = 0; u < 2; ++u)
-            ST[sg][u] = g.s0 ? ld_f32x4(reinterpret_cast<const char*>(
-                                   g.s0 + sbase + int64_t(DV * q + 16 * sg + lr) * DK + 16 * (2 * kp + u) + 4 * lq))
-                             : zero;
-
-    // This wave finishes Y tile (token block ty, value strip sy) and X tile 2 ty + sy.
-    const int ty = kp >> 1, sy = kp & 1;
-    // The next chunk's operands are requested in three groups spread over the
-    // chunk (when every wave of the chip issues them at once the memory pipeline
-    // backs up and the issuing waves stall): W and Q (first needed), Bh and E,
-    // then P, d and the bonus.
-    auto load_wq = [&](int c, Ops& o) {
-        const char* kb = rec_of(c) + kp * WS_KP + l * 16;
-        #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            o.W[i] = *reinterpret_cast<const bf16x8*>(kb + (BLK_W + i) * WS_BLK);
-            o.Qh[i] = *reinterpret_cast<const bf16x8*>(kb + (BLK_QH + i) * WS_BLK);
-            o.Ql[i] = *reinterpret_cast<const bf16x8*>(kb + (BLK_QL + i) * WS_BLK);
-        }
-    };
-    auto load_be = [&](int c, Ops& o) {
-        const char* kb = rec_of(c) + kp * WS_KP + l * 16;
-        #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            o.Bh[i] = *reinterpret_cast<const bf16x8*>(kb + (BLK_BH + i) * WS_BLK);
-            o.Eh[i] = *reinterpret_cast<const bf16x8*>(kb + (BLK_EH + i) * WS_BLK);
-            o.El[i] = *reinterpret_cast<const bf16x8*>(kb + (BLK_EL + i) * WS_BLK);
-        }
-    };
-    auto load_p = [&](int c, Ops& o) {   // P, d and the bonus
-        const char* rec = rec_of(c);
-        o.Ph = *reinterpret_cast<const bf16x8*>(rec + WS_P + ty * WS_BLK + l * 16);
-        o.Pl = *reinterpret_cast<const bf16x8*>(rec + WS_P + (2 + ty) * WS_BLK + l * 16);
-        #pragma unroll
-        for (int i = 0; i < 2; ++i) o.d[i] = ld_f32x4(rec + WS_D + (16 * (2 * kp + i) + 4 * lq) * 4);
-        if constexpr (EPI) o.bon = ld_f32x4(rec + WS_BON + (16 * ty + 4 * lq) * 4);
-    };
-    auto load_ops = [&](int c, Ops& o) {
-        load_wq(c, o);
-        load_be(c, o);
-        load_p(c, o);
-    };
-    // V of the slice: thread (vt, vg) loads token vt, values 32 q + 4 vg .. + 3.
-    const char* vp = static_cast<const char*>(g.v);
-    const int vt = tid & 31, vg = tid >> 5;
-    Row4<Tin> vrow;
-    auto load_v = [&](int c) {
-        vrow.load(chunk_rsrc(vp, tok0, c * L, T, stkv), uint32_t(vt) * stkv + uint32_t(hk * DK + DV * q + 4 * vg) * SI);
-    };
-    auto store_v = [&](int buf) {   // V^T [i][t~] of the slice
-        uint32_t vh[2], vl[2];
-        #pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-            if constexpr (VSPLIT) split2(vrow.get(e), vrow.get(e + 1), vh[e / 2], vl[e / 2]);
-            else vh[e / 2] = pack_bf16(vrow.get(e), vrow.get(e + 1));
-        }
-        pair_col_store4(smem + S_VS + buf * VS_BYTES, 4 * vg, vt, vh);
-        if constexpr (VSPLIT) pair_col_store4(smem + S_VSL + buf * VS_BYTES, 4 * vg, vt, vl);
-    };
-
-    char* yp = static_cast<char*>(g.y);
-    // One chunk: operands in `cur`, the next chunk's prefetched into `nxt`.  The
-    // loop below alternates two operand sets, so no prefetched register is copied
-    // (a copy would wait for the load); each load is waited for at its first use.
-    auto chunk = [&](const int c, Ops& cur, Ops& nxt) {
-        const int c0 = c * L, buf = (c - cb) & 1;
-        // Next chunk: V rows first (their LDS store closes this iteration), then W, Q.
-        // The last iteration loads its own chunk again (unused): unconditional loads
-        // keep the compiler's wait counts exact.
-        const int cn = min(c + 1, ce - 1);
-        load_v(cn);
-        load_wq(cn, nxt);
-        asm volatile("" ::: "memory");
-        // X and Y over this wave's 32 keys: X^T (t x i) = W S^T, Y (t x i) = Q S^T.
-        bf16x8 SBh[2], SBl[2];
-        #pragma unroll
-        for (int sg = 0; sg < 2; ++sg) to_operand2(ST[sg][0], ST[sg][1], SBh[sg], SBl[sg]);
-        #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-            #pragma unroll
-            for (int sg = 0; sg < 2; ++sg) {
-                f32x4 xp = mfma32(cur.W[tb], SBh[sg], zero);
-                xp = mfma32(cur.W[tb], SBl[sg], xp);
-                f32x4 yq = mfma32(cur.Qh[tb], SBh[sg], zero);
-                yq = mfma32(cur.Qh[tb], SBl[sg], yq);
-                yq = mfma32(cur.Ql[tb], SBh[sg], yq);
-                sts<f32x4>(smem + S_PART, ((kp * 8 + 2 * tb + sg) * 64 + l) * 16, xp);
-                sts<f32x4>(smem + S_PART, ((kp * 8 + 4 + 2 * tb + sg) * 64 + l) * 16, yq);
-            }
-        __syncthreads();   // partial tiles and V^T of this chunk visible
-        load_be(cn, nxt);
-        asm volatile("" ::: "memory");
-        // Keep the S diag(d) update below this point (d is among the last operands to
-        // arrive; hoisted to the top of the chunk it would wait for them there).
-        asm volatile("" : "+v"(ST[0][0]), "+v"(ST[0][1]), "+v"(ST[1][0]), "+v"(ST[1][1]));
-
-        const char* vs = smem + S_VS + buf * VS_BYTES;
-        bf16x8 VB[2], VBl[2];
-        #pragma unroll
-        for (int sg = 0; sg < 2; ++sg) {
-            VB[sg] = lds<bf16x8>(vs, ((16 * sg + lr) * PT + 8 * lq) * 2);
-            if constexpr (VSPLIT) VBl[sg] = lds<bf16x8>(smem + S_VSL + buf * VS_BYTES, ((16 * sg + lr) * PT + 8 * lq) * 2);
-        }
-        // S <- S diag(d) + V^T E (the X-independent part of the update).
-        #pragma unroll
-        for (int sg = 0; sg < 2; ++sg)
-            #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                f32x4 acc = ST[sg][u] * cur.d[u];
-                acc = mfma32(cur.Eh[u], VB[sg], acc);
-                acc = mfma32(cur.El[u], VB[sg], acc);
-                if constexpr (VSPLIT) acc = mfma32(cur.Eh[u], VBl[sg], acc);
-                ST[sg][u] = acc;
-            }
-        // Reduce X tile kp over the four key pairs -> bf16 hi / lo operand tile.
-        {
-            f32x4 xs = lds<f32x4>(smem + S_PART, (kp * 64 + l) * 16);
-            #pragma unroll
-            for (int k2 = 1; k2 < 4; ++k2) xs += lds<f32x4>(smem + S_PART, ((k2 * 8 + kp) * 64 + l) * 16);
-            s16x4 xh, xl;
-            to_operand(xs, xh, xl);
-            sts<s16x4>(smem + S_XOH, (kp * 64 + l) * 8, xh);
-            sts<s16x4>(smem + S_XOL, (kp * 64 + l) * 8, xl);
-        }
-        // The last operand group, issued before this chunk's y stores: a wait for a
-        // load also waits for every store issued before it.
-        load_p(cn, nxt);
-        asm volatile("" ::: "memory");
-        // Y tile (ty, sy) = sum of partials + P V; epilogue; store.
-        {
-            f32x4 ys = lds<f32x4>(smem + S_PART, ((4 + kp) * 64 + l) * 16);
-            #pragma unroll
-            for (int k2 = 1; k2 < 4; ++k2) ys += lds<f32x4>(smem + S_PART, ((k2 * 8 + 4 + kp) * 64 + l) * 16);
-            // V of strip sy loaded again rather than indexed by the wave-dependent sy.
-            const int ov = ((16 * sy + lr) * PT + 8 * lq) * 2;
-            const bf16x8 VBy = lds<bf16x8>(vs, ov);
-            ys = mfma32(cur.Ph, VBy, ys);
-            ys = mfma32(cur.Pl, VBy, ys);
-            if constexpr (VSPLIT) ys = mfma32(cur.Ph, lds<bf16x8>(smem + S_VSL + buf * VS_BYTES, ov), ys);
-            const int i_loc = 16 * sy + lr, tl0 = 16 * ty + 4 * lq;
-            float vtr[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (EPI) {
-                const uint2 vr = lds<uint2>(vs, (i_loc * PT + pairpos(tl0)) * 2);
-                vtr[0] = lo_f32(vr.x); vtr[1] = hi_f32(vr.x); vtr[2] = lo_f32(vr.y); vtr[3] = hi_f32(vr.y);
-                if constexpr (VSPLIT) {
-                    const uint2 vl = lds<uint2>(smem + S_VSL + buf * VS_BYTES, (i_loc * PT + pairpos(tl0)) * 2);
-                    vtr[0] += lo_f32(vl.x); vtr[1] += hi_f32(vl.x); vtr[2] += lo_f32(vl.y); vtr[3] += hi_f32(vl.y);
-                }
-            }
-            const int nv = max(0, min(T - c0, L));
-            const rsrc_t Ry = make_rsrc(yp + (tok0 + c0) * sty, uint32_t(nv) * sty);
-            #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float yv = ys[r] * g.y_scale;
-                if constexpr (EPI) yv = fmaf(cur.bon[r], vtr[r], yv);
-                Buf<Ty>::store1(Ry, uint32_t(tl0 + r) * sty + uint32_t(h * DK + DV * q + i_loc) * SY, yv);
-            }
-        }
-        __syncthreads();   // reduced X tiles visible
-
-        // S <- S + X Bh, X of strip sg as the B operand (k = token, n = value row).
-        #pragma unroll
-        for (int sg = 0; sg < 2; ++sg) {
-            const bf16x8 xh = cat(lds<s16x4>(smem + S_XOH, (sg * 64 + l) * 8), lds<s16x4>(smem + S_XOH, ((2 + sg) * 64 + l) * 8));
-            const bf16x8 xl = cat(lds<s16x4>(smem + S_XOL, (sg * 64 + l) * 8), lds<s16x4>(smem + S_XOL, ((2 + sg) * 64 + l) * 8));
-            #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                f32x4 acc = mfma32(cur.Bh[u], xh, ST[sg][u]);
-                ST[sg][u] = mfma32(cur.Bh[u], xl, acc);
-            }
-        }
-        // V^T of chunk c + 1 into the other buffer (last read during chunk c - 1); the
-        // barrier after the next chunk's partial products publishes it.
-        store_v(buf ^ 1);
-    };
-    Ops opa, opb;
-    load_v(cb);
-    load_ops(cb, opa);
-    store_v(0);
-    // The first operand set completes here: its load order would otherwise enter
-    // the compiler's wait counts of every loop iteration.
-    #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        asm volatile("" : "+v"(opa.W[i]), "+v"(opa.Qh[i]), "+v"(opa.Ql[i]), "+v"(opa.Bh[i]), "+v"(opa.Eh[i]), "+v"(opa.El[i]));
-        asm volatile("" : "+v"(opa.d[i]));
-    }
-    asm volatile("" : "+v"(opa.Ph), "+v"(opa.Pl), "+v"(opa.bon));
-    int c = cb;
-    for (; c + 1 < ce; c += 2) {
-        chunk(c, opa, opb);
-        chunk(c + 1, opb, opa);
-    }
-    if (c < ce) chunk(c, opa, opb);
-
-    if (g.s1) {
-        #pragma unroll
-        for (int sg = 0; sg < 2; ++sg)
-            #pragma unroll
-            for (int u = 0; u < 2; ++u)
-                *reinterpret_cast<float4*>(g.s1 + sbase + int64_t(DV * q + 16 * sg + lr) * DK + 16 * (2 * kp + u) + 4 * lq) =
-                    make_float4(ST[sg][u][0], ST[sg][u][1], ST[sg][u][2], ST[sg][u][3]);
-    }
-}
 
 // Runs the chunks in windows of `win` chunks per (b, h): pass 1 then pass 2 for
 // each window, the state carried from window to window in `carry` (state_out
@@ -1135,9 +759,6 @@ hipError_t launch_t(const Params& p, void* ws, int win, float* carry, hipStream_
         attr_set = true;
     }
     float* s_carry = p.s1 ? p.s1 : carry;
-    constexpr int smem2 = sizeof(Tin) == 4 ? SMEM_SCAN_F32 : SMEM_SCAN_BF16;
-    // 32 workgroups per group of 8 (b, h): 8 heads x 4 value slices.
-    const unsigned groups = unsigned((bh + 7) / 8);
     for (int cb = 0; cb < nch; cb += nrec) {
         const int nw = nch - cb < nrec ? nch - cb : nrec;
         const bool last = cb + nw == nch;
@@ -1154,8 +775,7 @@ hipError_t launch_t(const Params& p, void* ws, int win, float* carry, hipStream_
         if (e != hipSuccess) return e;
         ScanArgs sa{p.v, cb == 0 ? p.s0 : s_carry, last ? p.s1 : s_carry, p.y, static_cast<const char*>(ws),
                     p.T, p.H, p.H_kv, bh, cb, cb + nw, nrec, p.y_scale};
-        hipLaunchKernelGGL((scan128_kernel<Tin, Ty, EPI>), dim3(groups * 32u), dim3(NTHR_SCAN), smem2, stream, sa);
-        e = hipGetLastError();
+        e = launch_scan128(sa, sizeof(Tin) == 4, sizeof(Ty) == 4, EPI, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -1178,6 +798,9 @@ hipError_t dispatch_modes(const Params& p, void* ws, int win, float* carry, hipS
 }
 
 }  // namespace
+}  // namespace tp128
+
+using namespace tp128;
 
 int64_t twopass128_workspace_bytes(int B, int H, int T) {
     return int64_t(B) * H * ((int64_t(T) + L - 1) / L) * WS_CHUNK;

@@ -131,7 +131,7 @@ def test_resolve_algo():
 
 
 def test_workspace_bytes():
-    rec = 54272   # one record per (b, h, chunk of 32 tokens)
+    rec = 37632   # one record per (b, h, chunk of 32 tokens)
     assert W.wkv7_workspace_bytes(2, 64, 4, 128) == 2 * 4 * 2 * rec
     assert W.wkv7_workspace_bytes(2, 70, 4, 128) == 2 * 4 * 3 * rec     # ragged last chunk
     assert W.wkv7_workspace_bytes(2, 31, 4, 128) == 0                  # AUTO: the scan below one chunk
@@ -187,7 +187,7 @@ def test_ab_mode_from_k_rules():
     assert W.wkv7_resolve_algo(2, 63, 4, 64, ab_mode="from_k") == "scan"
     assert W.wkv7_resolve_algo(2, 64, 4, 128, ab_mode="from_k") == "chunked"
     assert W.wkv7_resolve_algo(2, 31, 4, 128, ab_mode="from_k") == "scan"
-    assert W.wkv7_workspace_bytes(2, 64, 4, 128, ab_mode="from_k") == 2 * 4 * 2 * 54272
+    assert W.wkv7_workspace_bytes(2, 64, 4, 128, ab_mode="from_k") == 2 * 4 * 2 * 37632
     assert W.wkv7_workspace_bytes(2, 64, 4, 64, ab_mode="from_k") == 0
 
 
@@ -369,14 +369,14 @@ def test_wkv4_workspace_must_not_overlap_any_array():
 
 def test_noalloc_rejects_more_heads_than_the_scratch_holds():
     """wkv7_forward_noalloc: one 32-token chunk record per (b, h) must fit the static
-    scratch; B H = 2048 at D = 128 needs 111 MB > 64 MiB.  Rejected before any HIP call."""
+    scratch; B H = 2048 at D = 128 needs 77 MB > 64 MiB.  Rejected before any HIP call."""
     lib = W.load_library()
     ptrs = [BASE + i * SP for i in range(8)]
     desc = W.make_desc(1, 64, 2048, 128)
     assert lib.wkv7_forward_noalloc(ctypes.byref(desc), *ptrs[:6], None, ptrs[6], ptrs[7], None) == W.WKV7_EUNSUPPORTED
     assert b"static scratch" in lib.wkv7_last_error()
     # Without state_out the state carry takes room too: 1000 heads fit with it given, not without.
-    need = 1000 * 54272
+    need = 1000 * 37632
     assert need < W.NOALLOC_SCRATCH_BYTES < need + 1000 * 128 * 128 * 4
     desc = W.make_desc(1, 64, 1000, 128)
     assert lib.wkv7_forward_noalloc(ctypes.byref(desc), *ptrs[:6], None, ptrs[6], None, None) == W.WKV7_EUNSUPPORTED

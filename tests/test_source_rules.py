@@ -60,4 +60,5 @@ def test_mfma_sources_are_known():
         "wkv7_chunked.hip": "__builtin_amdgcn_mfma_f32_16x16x32_bf16",
         "wkv7_chunked128.hip": "__builtin_amdgcn_mfma_f32_16x16x32_bf16",
         "wkv7_twopass128.hip": "__builtin_amdgcn_mfma_f32_16x16x32_bf16",
+        "wkv7_twopass128_scan.hip": "__builtin_amdgcn_mfma_f32_16x16x32_f16",
     }, found

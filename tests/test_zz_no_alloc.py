@@ -28,7 +28,7 @@ def W():
 def _window(B, H, nch, with_state_out, D=128):
     """Chunks per (b, h) per window, as the library sizes it."""
     carry = 0 if with_state_out else (B * H * D * D * 4 + 255) // 256 * 256
-    return min(nch, (W().NOALLOC_SCRATCH_BYTES - carry) // (B * H * 54272))
+    return min(nch, (W().NOALLOC_SCRATCH_BYTES - carry) // (B * H * 37632))
 
 
 def _run_both(wl, x, with_state_out):
