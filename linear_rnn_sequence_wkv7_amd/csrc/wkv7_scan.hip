@@ -425,7 +425,8 @@ hipError_t dispatch_types(const Params& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_scan(const Params& p, hipStream_t stream) {
-    return p.D == 64 ? dispatch_types<64>(p, stream) : dispatch_types<128>(p, stream);
+    if (p.D == 64) return scan64_fits(p) ? launch_scan64(p, stream) : dispatch_types<64>(p, stream);
+    return dispatch_types<128>(p, stream);
 }
 
 }  // namespace wkv7
