@@ -1,4 +1,7 @@
-// Token-by-token scan of the WKV-7 recurrence on gfx950.
+// Token-by-token scan of the WKV-7 recurrence on gfx950: the dispatch of the
+// scan algorithm, and its earlier form, kept for the calls the DPP-row scan
+// (wkv7_scan_dpp.hip) does not take (rows so wide that the byte offsets of a few
+// tokens overflow 32 bits, or grids beyond 2^32 work-items).
 //
 //   sa_t = S_{t-1} a_t;  S_t = S_{t-1} diag(w_t) + sa_t b_t^T + v_t k_t^T;  y_t = S_t r_t
 //
@@ -425,8 +428,8 @@ hipError_t dispatch_types(const Params& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_scan(const Params& p, hipStream_t stream) {
-    if (p.D == 64) return scan64_fits(p) ? launch_scan64(p, stream) : dispatch_types<64>(p, stream);
-    return dispatch_types<128>(p, stream);
+    if (scan_dpp_fits(p)) return launch_scan_dpp(p, stream);
+    return p.D == 64 ? dispatch_types<64>(p, stream) : dispatch_types<128>(p, stream);
 }
 
 }  // namespace wkv7
