@@ -9,12 +9,13 @@
 // readout after the update as in the youngju.dev RWKV-7 article).
 //
 // Matrix cores in fp16 (v_mfma_f32_16x16x32_f16, fp32 accumulation): the
-// record's W, Q, Bh and E are single fp16 operands, P is an fp16 hi + lo pair,
-// the state and X = S W^T are split hi + lo, and V is fp16 (exact for bf16
-// inputs of magnitude below 2^16 down to 2^-14; hi + lo for fp32 inputs).  fp16
-// carries 11 significant bits against bf16's 8, so one fp16 operand does the work
-// of a bf16 hi + lo pair wherever the values stay inside fp16's range: state
-// entries, v and the chunk operands must stay below 65504 in magnitude (the
+// record's W, Q, Bh and E, the state (fp32 in registers, rounded to fp16 as the
+// operand of S W^T and Q S^T) and the reduced X = S W^T are single fp16
+// operands, P is an fp16 hi + lo pair, and V is fp16 (exact for bf16 inputs of
+// magnitude below 2^16 down to 2^-14; hi + lo for fp32 inputs).  fp16 carries
+// 11 significant bits against bf16's 8, so a single fp16 operand rounds 8x
+// finer than a single bf16 one; the values must stay inside fp16's range:
+// state entries, v and the chunk operands below 65504 in magnitude (the
 // one-pass kernels have bf16's range).  Every accumulator chain uses this one
 // opcode.
 //
@@ -43,13 +44,12 @@ template <> struct Buf<float> {
 };
 
 // LDS map of pass 2 (bytes): the four waves' partial X and Y tiles, the reduced X
-// tiles as fp16 hi / lo operands, and V^T of the slice (two chunk buffers).
+// tiles as fp16 operands, and V^T of the slice (two chunk buffers).
 constexpr int NTHR_SCAN = 256;
 constexpr int S_PART = 0;                          // f32x4 [wave][tile 0..7][lane]
 constexpr int S_XOH = S_PART + 4 * 8 * 64 * 16;    // fp16x4 [tile 0..3][lane]
-constexpr int S_XOL = S_XOH + 4 * 64 * 8;
 constexpr int VS_BYTES = DV * PT * 2;
-constexpr int S_VS = S_XOL + 4 * 64 * 8;           // fp16 [buffer][DV][PT] V^T hi
+constexpr int S_VS = S_XOH + 4 * 64 * 8;           // fp16 [buffer][DV][PT] V^T hi
 constexpr int S_VSL = S_VS + 2 * VS_BYTES;         // lo (fp32 inputs)
 constexpr int SMEM_SCAN_BF16 = S_VSL;
 constexpr int SMEM_SCAN_F32 = S_VSL + 2 * VS_BYTES;
@@ -203,17 +203,15 @@ void scan128_kernel(ScanArgs g) {
         load_wq(cn, nxt);
         asm volatile("" ::: "memory");
         // X and Y over this wave's 32 keys: X^T (t x i) = W S^T, Y (t x i) = Q S^T.
-        f16x8 SBh[2], SBl[2];
+        f16x8 SBh[2];
         #pragma unroll
-        for (int sg = 0; sg < 2; ++sg) to_operand2_h(ST[sg][0], ST[sg][1], SBh[sg], SBl[sg]);
+        for (int sg = 0; sg < 2; ++sg) SBh[sg] = to_f16x8(ST[sg][0], ST[sg][1]);
         #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
             #pragma unroll
             for (int sg = 0; sg < 2; ++sg) {
                 f32x4 xp = mfma16(cur.W[tb], SBh[sg], zero);
-                xp = mfma16(cur.W[tb], SBl[sg], xp);
                 f32x4 yq = mfma16(cur.Q[tb], SBh[sg], zero);
-                yq = mfma16(cur.Q[tb], SBl[sg], yq);
                 sts<f32x4>(smem + S_PART, ((kp * 8 + 2 * tb + sg) * 64 + l) * 16, xp);
                 sts<f32x4>(smem + S_PART, ((kp * 8 + 4 + 2 * tb + sg) * 64 + l) * 16, yq);
             }
@@ -241,15 +239,12 @@ void scan128_kernel(ScanArgs g) {
                 if constexpr (VSPLIT) acc = mfma16(cur.E[u], VBl[sg], acc);
                 ST[sg][u] = acc;
             }
-        // Reduce X tile kp over the four key pairs -> fp16 hi / lo operand tile.
+        // Reduce X tile kp over the four key pairs -> fp16 operand tile.
         {
             f32x4 xs = lds<f32x4>(smem + S_PART, (kp * 64 + l) * 16);
             #pragma unroll
             for (int k2 = 1; k2 < 4; ++k2) xs += lds<f32x4>(smem + S_PART, ((k2 * 8 + kp) * 64 + l) * 16);
-            uint2 xh, xl;
-            to_operand_h(xs, xh, xl);
-            sts<uint2>(smem + S_XOH, (kp * 64 + l) * 8, xh);
-            sts<uint2>(smem + S_XOL, (kp * 64 + l) * 8, xl);
+            sts<uint2>(smem + S_XOH, (kp * 64 + l) * 8, make_uint2(pack_f16(xs[0], xs[1]), pack_f16(xs[2], xs[3])));
         }
         // The last operand group, issued before this chunk's y stores: a wait for a
         // load also waits for every store issued before it.
@@ -292,12 +287,8 @@ void scan128_kernel(ScanArgs g) {
         #pragma unroll
         for (int sg = 0; sg < 2; ++sg) {
             const f16x8 xh = cat16(lds<uint2>(smem + S_XOH, (sg * 64 + l) * 8), lds<uint2>(smem + S_XOH, ((2 + sg) * 64 + l) * 8));
-            const f16x8 xl = cat16(lds<uint2>(smem + S_XOL, (sg * 64 + l) * 8), lds<uint2>(smem + S_XOL, ((2 + sg) * 64 + l) * 8));
             #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                f32x4 acc = mfma16(cur.Bh[u], xh, ST[sg][u]);
-                ST[sg][u] = mfma16(cur.Bh[u], xl, acc);
-            }
+            for (int u = 0; u < 2; ++u) ST[sg][u] = mfma16(cur.Bh[u], xh, ST[sg][u]);
         }
         // V^T of chunk c + 1 into the other buffer (last read during chunk c - 1); the
         // barrier after the next chunk's partial products publishes it.
