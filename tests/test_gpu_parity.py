@@ -85,6 +85,24 @@ def test_forward_sweep(case, algo):
     P.check("state", s, s_ref, TAU[algo])
 
 
+# The scan keeps PF tokens of loads in flight (8 for bf16 and 4 for fp32 at
+# D = 64; 4 and 2 at D = 128) and runs the last T mod PF tokens outside its
+# unrolled loop: every tail length, with and without whole ring turns before it.
+SCAN_TAILS = [(D, dt, T) for D, dt, pf in [(64, "bf16", 8), (64, "f32", 4), (128, "bf16", 4), (128, "f32", 2)]
+              for T in sorted({1, pf - 1, pf, pf + 1, 3 * pf - 1, 3 * pf + 1})]
+
+
+@pytest.mark.parametrize("D,in_dtype,T", SCAN_TAILS, ids=lambda v: str(v))
+def test_scan_ring_tails(D, in_dtype, T):
+    wl = make_case(D, 2, T, 3, 3, in_dtype, "f32", "logneglog" if T % 2 else "decay", 0.1, T % 3 == 0,
+                   seed=100 + T)
+    x = G.make_inputs(wl)
+    y_ref, s_ref = oracle_full(wl, x)
+    y, s = run_forward(wl, x, "scan")
+    P.check("y", y, y_ref, TAU["scan"])
+    P.check("state", s, s_ref, TAU["scan"])
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("algo", FWD_ALGOS)
 def test_state_in_place_and_split(algo, D):
