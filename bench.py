@@ -48,7 +48,7 @@ PEAK_HBM_GBS = 8000.0             # MI355X HBM3E peak (AMD spec)
 PEAK_BF16_MFMA_TFLOPS = 2500.0    # dense bf16 matrix peak
 
 KERNEL_SOURCES = {
-    "scan": ("linear_rnn_sequence_wkv7_amd/csrc/wkv7_scan_dpp.hip", "linear_rnn_sequence_wkv7_amd/csrc/wkv7_scan.hip"),
+    "scan": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_scan.hip",
     "chunked": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_chunked.hip",
     "chunked128": "linear_rnn_sequence_wkv7_amd/csrc/wkv7_chunked128.hip",
     "twopass128": ("linear_rnn_sequence_wkv7_amd/csrc/wkv7_twopass128.hip",

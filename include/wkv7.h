@@ -94,7 +94,10 @@ enum wkv7_ab_mode {
 
 enum wkv7_algo {
     WKV7_ALGO_AUTO = 0,     /* library picks (see wkv7_resolve_algo) */
-    WKV7_ALGO_SCAN = 1,     /* token-by-token scan, state in registers */
+    WKV7_ALGO_SCAN = 1,     /* token-by-token scan, state in registers.  EUNSUPPORTED when a
+                               token row is too wide for its 32-bit offsets (H * D * 68 >= 2^32,
+                               about 6.3e7) or B * H workgroups (times 4 at D = 128) of 256
+                               threads exceed 2^32 work-items */
     WKV7_ALGO_CHUNKED = 2,  /* chunk-parallel form on bf16 matrix cores, fp32 accumulation */
     WKV7_ALGO_TWO_PASS = 3  /* D = 128 only, wkv7_forward_ws only: the chunked form split in two
                                kernels, the state-independent matrices of every chunk first (in

@@ -24,7 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwkv7.so")
 ARCH = "gfx950"
 
-SOURCES = ["wkv7_api.cpp", "wkv7_scan.hip", "wkv7_scan_dpp.hip", "wkv7_decode.hip", "wkv7_chunked.hip", "wkv7_chunked128.hip",
+SOURCES = ["wkv7_api.cpp", "wkv7_scan.hip", "wkv7_decode.hip", "wkv7_chunked.hip", "wkv7_chunked128.hip",
            "wkv7_twopass128.hip", "wkv7_twopass128_scan.hip", "wkv7_backward.hip", "wkv4.hip"]
 
 COMMON = [

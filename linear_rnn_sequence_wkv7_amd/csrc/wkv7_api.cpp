@@ -184,6 +184,9 @@ int forward_impl(const wkv7_desc* desc, const void* r, const void* w, const void
     if ((rc = check_ptrs(p, in6, y, state_in, state_out))) return rc;
     const int algo = resolve_algo(p, desc->algo, ws_mode != WsMode::kNone);
     const bool has_work = int64_t(p.B) * p.H > 0 && p.T > 0;
+    if (has_work && algo == WKV7_ALGO_SCAN && !wkv7::scan_fits(p))
+        return fail(WKV7_EUNSUPPORTED, "scan: H*D=%lld or B*H=%lld too large (rows of 32-bit offsets, 2^32 work-items)",
+                    (long long)(int64_t(p.H) * p.D), (long long)(int64_t(p.B) * p.H));
     const int64_t need = has_work ? workspace_bytes(p, algo) : 0;
     if (need > 0 && ws_mode == WsMode::kCaller) {
         if (!workspace) return fail(WKV7_EINVAL, "workspace is NULL (%lld bytes needed)", (long long)need);

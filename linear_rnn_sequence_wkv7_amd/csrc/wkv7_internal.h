@@ -1,5 +1,5 @@
 // Internal interface between the C-ABI entry points (wkv7_api.cpp) and the
-// kernel launchers (wkv7_scan.hip, wkv7_scan_dpp.hip, wkv7_chunked.hip, wkv7_chunked128.hip,
+// kernel launchers (wkv7_scan.hip, wkv7_chunked.hip, wkv7_chunked128.hip,
 // wkv7_twopass128.hip, wkv7_twopass128_scan.hip, wkv7_decode.hip, wkv7_backward.hip,
 // wkv4.hip).
 #pragma once
@@ -29,12 +29,11 @@ struct Params {
 
 // Each launcher enqueues its kernel(s) on `stream` and returns the HIP status
 // of the launch.  They assume Params passed validation in wkv7_api.cpp.
-hipError_t launch_scan(const Params& p, hipStream_t stream);     // to launch_scan_dpp where it fits
-// Scan with D / 16 independent waves per (b, h) and DPP row sums (wkv7_scan_dpp.hip);
-// for T >= 1 and byte offsets of one sequence's tokens that fit in 32 bits
-// (scan_dpp_fits).
-bool scan_dpp_fits(const Params& p);
-hipError_t launch_scan_dpp(const Params& p, hipStream_t stream);
+// Scan with D / 16 independent waves per (b, h) and DPP row sums; for T >= 1,
+// rows (H * D) narrow enough for 32-bit offsets over a few tokens and grids
+// within 2^32 work-items (scan_fits; checked by the entry points first).
+bool scan_fits(const Params& p);
+hipError_t launch_scan(const Params& p, hipStream_t stream);
 hipError_t launch_chunked(const Params& p, hipStream_t stream);      // D = 64, L = 64
 hipError_t launch_chunked128(const Params& p, hipStream_t stream);   // D = 128, L = 32
 // Two-pass form at D = 128: per-chunk matrices into `ws`, then the recurrence.

@@ -367,6 +367,19 @@ def test_wkv4_workspace_must_not_overlap_any_array():
         assert b"workspace overlaps" in lib.wkv7_last_error(), n
 
 
+def test_scan_rejects_rows_too_wide_for_32_bit_offsets():
+    """The scan addresses a few tokens of one row with 32-bit offsets: H * D * 68 must
+    stay below 2^32.  H = 2^20 at D = 64 is past it (EUNSUPPORTED before any HIP call);
+    the chunked form takes the same shape once T reaches a chunk."""
+    lib = W.load_library()
+    ptrs = [BASE + i * SP for i in range(8)]
+    desc = W.make_desc(1, 1, 1 << 20, 64)
+    assert lib.wkv7_forward(ctypes.byref(desc), *ptrs[:6], None, ptrs[6], ptrs[7], None) == W.WKV7_EUNSUPPORTED
+    assert b"scan" in lib.wkv7_last_error()
+    desc = W.make_desc(1, 1, 1 << 20, 64, algo="scan")
+    assert lib.wkv7_forward(ctypes.byref(desc), *ptrs[:6], None, ptrs[6], ptrs[7], None) == W.WKV7_EUNSUPPORTED
+
+
 def test_noalloc_rejects_more_heads_than_the_scratch_holds():
     """wkv7_forward_noalloc: one 32-token chunk record per (b, h) must fit the static
     scratch; B H = 2048 at D = 128 needs 77 MB > 64 MiB.  Rejected before any HIP call."""
