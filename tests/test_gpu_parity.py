@@ -272,6 +272,8 @@ EVERY_PAIR = [
     ("hxa07d_bf16_b2_t16384_h32_kv8_d128", "two_pass"),
     ("fwd_bf16_b8_t1024_h32_d64", "chunked"),
     ("prefill_bf16_b4_t4096_h40_d64_l64", "chunked"),
+    ("fwd_bf16_b8_t1024_h32_d64", "scan"),
+    ("hxa07d_bf16_b2_t16384_h32_kv8_d128", "scan"),
 ]
 
 
