@@ -138,10 +138,11 @@ void scan128_kernel(ScanArgs g) {
 
     // This wave finishes Y tile (token block ty, value strip sy) and X tile 2 ty + sy.
     const int ty = kp >> 1, sy = kp & 1;
-    // The next chunk's operands are requested in three groups spread over the
-    // chunk (when every wave of the chip issues them at once the memory pipeline
-    // backs up and the issuing waves stall): W and Q (first needed), Bh and E,
-    // then P, d and the bonus.
+    // The operands of the chunk after next are requested in three groups spread
+    // over the chunk (when every wave of the chip issues them at once the memory
+    // pipeline backs up and the issuing waves stall): W and Q (first needed), Bh
+    // and E, then P, d and the bonus.  Two chunks ahead, a record that has left
+    // the memory-side cache still arrives in time.
     auto load_wq = [&](int c, Ops& o) {
         const char* kb = rec_of(c) + kp * WS_KP + l * 16;
         #pragma unroll
@@ -190,16 +191,16 @@ void scan128_kernel(ScanArgs g) {
     };
 
     char* yp = static_cast<char*>(g.y);
-    // One chunk: operands in `cur`, the next chunk's prefetched into `nxt`.  The
-    // loop below alternates two operand sets, so no prefetched register is copied
+    // One chunk: operands in `cur`, those of chunk c + 2 prefetched into `nxt`.  The
+    // loop below rotates three operand sets, so no prefetched register is copied
     // (a copy would wait for the load); each load is waited for at its first use.
     auto chunk = [&](const int c, Ops& cur, Ops& nxt) {
         const int c0 = c * L, buf = (c - cb) & 1;
-        // Next chunk: V rows first (their LDS store closes this iteration), then W, Q.
-        // The last iteration loads its own chunk again (unused): unconditional loads
-        // keep the compiler's wait counts exact.
-        const int cn = min(c + 1, ce - 1);
-        load_v(cn);
+        // V rows of the next chunk first (their LDS store closes this iteration),
+        // then W, Q of chunk c + 2.  The last iterations load the last chunk again
+        // (unused): unconditional loads keep the compiler's wait counts exact.
+        const int cn = min(c + 2, ce - 1);
+        load_v(min(c + 1, ce - 1));
         load_wq(cn, nxt);
         asm volatile("" ::: "memory");
         // X and Y over this wave's 32 keys: X^T (t x i) = W S^T, Y (t x i) = Q S^T.
@@ -294,24 +295,31 @@ void scan128_kernel(ScanArgs g) {
         // barrier after the next chunk's partial products publishes it.
         store_v(buf ^ 1);
     };
-    Ops opa, opb;
+    Ops opa, opb, opc;
     load_v(cb);
     load_ops(cb, opa);
+    load_ops(min(cb + 1, ce - 1), opb);
     store_v(0);
-    // The first operand set completes here: its load order would otherwise enter
-    // the compiler's wait counts of every loop iteration.
+    // The first two operand sets complete here: their load order would otherwise
+    // enter the compiler's wait counts of every loop iteration.
     #pragma unroll
     for (int i = 0; i < 2; ++i) {
         asm volatile("" : "+v"(opa.W[i]), "+v"(opa.Q[i]), "+v"(opa.Bh[i]), "+v"(opa.E[i]));
         asm volatile("" : "+v"(opa.d[i]));
+        asm volatile("" : "+v"(opb.W[i]), "+v"(opb.Q[i]), "+v"(opb.Bh[i]), "+v"(opb.E[i]));
+        asm volatile("" : "+v"(opb.d[i]));
     }
     asm volatile("" : "+v"(opa.Ph), "+v"(opa.Pl), "+v"(opa.bon));
+    asm volatile("" : "+v"(opb.Ph), "+v"(opb.Pl), "+v"(opb.bon));
+    // Three operand sets in rotation: chunk c uses its set and loads chunk c + 2's.
     int c = cb;
-    for (; c + 1 < ce; c += 2) {
-        chunk(c, opa, opb);
+    for (; c + 2 < ce; c += 3) {
+        chunk(c, opa, opc);
         chunk(c + 1, opb, opa);
+        chunk(c + 2, opc, opb);
     }
-    if (c < ce) chunk(c, opa, opb);
+    if (c < ce) chunk(c, opa, opc);
+    if (c + 1 < ce) chunk(c + 1, opb, opa);
 
     if (g.s1) {
         #pragma unroll
