@@ -103,6 +103,20 @@ def test_scan_ring_tails(D, in_dtype, T):
     P.check("state", s, s_ref, TAU["scan"])
 
 
+@pytest.mark.parametrize("s0", [10.0, 100.0])
+def test_two_pass_large_state(s0):
+    """The two-pass form runs its recurrence on fp16 operands (single-operand state
+    and chunk matrices): relative rounding does not depend on scale, so an initial
+    state 100 and 1000 times the workloads' (std 10 and 100: entries up to a few
+    hundred, inside fp16's 65504) meets the same bound."""
+    wl = make_case(128, 1, 200, 4, 2, "bf16", "f32", "logneglog", s0, True, seed=31)
+    x = G.make_inputs(wl)
+    y_ref, s_ref = oracle_full(wl, x)
+    y, s = run_forward(wl, x, "two_pass")
+    P.check("y", y, y_ref, TAU["two_pass"])
+    P.check("state", s, s_ref, TAU["two_pass"])
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("algo", FWD_ALGOS)
 def test_state_in_place_and_split(algo, D):
