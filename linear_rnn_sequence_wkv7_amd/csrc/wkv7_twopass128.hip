@@ -57,6 +57,15 @@ constexpr int MATK = L * PK * 2;
 constexpr int MATT = DK * PT * 2;
 constexpr int MATL = L * PT * 2;
 
+// Workspace record stores: written once here, read once by the recurrence pass.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_rec(char* p, const f16x8 v) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void st_rec(char* p, const uint4 v) {
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
+
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -649,7 +658,7 @@ void prep128_kernel(PrepArgs g) {
             #pragma unroll
             for (int u = 0; u < 2; ++u) wt[u] = mfma32(At8[u], DlT, mfma32(At8[u], DhT, zero));
             {
-                *reinterpret_cast<f16x8*>(rec + kp * WS_KP + (BLK_W + tb) * WS_BLK + l * 16) = to_f16x8(wt[0], wt[1]);
+                st_rec(rec + kp * WS_KP + (BLK_W + tb) * WS_BLK + l * 16, to_f16x8(wt[0], wt[1]));
             }
             // C(W) tiles (token block sb, key tile 2 kp + u): lane token 4 lq + r, key lr.
             // As A operands they are W^T with the token axis as k.
@@ -671,7 +680,7 @@ void prep128_kernel(PrepArgs g) {
                 acc = mfma32(cat(wl[0][u], wl[1][u]), Ar8, acc);
                 qt[u] = acc;
             }
-            *reinterpret_cast<f16x8*>(rec + kp * WS_KP + (BLK_Q + tb) * WS_BLK + l * 16) = to_f16x8(qt[0], qt[1]);
+            st_rec(rec + kp * WS_KP + (BLK_Q + tb) * WS_BLK + l * 16, to_f16x8(qt[0], qt[1]));
         }
         __syncthreads();
 
@@ -683,9 +692,9 @@ void prep128_kernel(PrepArgs g) {
                 // Bh is bf16 here (the operand of E below); fp16 holds each value exactly
                 // inside fp16's normal range.
                 const uint4 b4 = __builtin_bit_cast(uint4, Bh8);
-                *reinterpret_cast<uint4*>(rec + kp * WS_KP + (BLK_BH + u) * WS_BLK + l * 16) =
+                st_rec(rec + kp * WS_KP + (BLK_BH + u) * WS_BLK + l * 16,
                     make_uint4(pack_f16(lo_f32(b4.x), hi_f32(b4.x)), pack_f16(lo_f32(b4.y), hi_f32(b4.y)),
-                               pack_f16(lo_f32(b4.z), hi_f32(b4.z)), pack_f16(lo_f32(b4.w), hi_f32(b4.w)));
+                               pack_f16(lo_f32(b4.z), hi_f32(b4.z)), pack_f16(lo_f32(b4.w), hi_f32(b4.w))));
             }
             const float dj = lds<float>(smem + P_DL, (16 * jt + lr) * 4);
             const int kpos = pairpos(16 * jt + lr);
@@ -703,7 +712,7 @@ void prep128_kernel(PrepArgs g) {
                 acc = mfma32(lds<bf16x8>(smem + P_UTL, opT(tb)), Bh8, acc);
                 e[tb] = acc;
             }
-            *reinterpret_cast<f16x8*>(rec + kp * WS_KP + (BLK_E + u) * WS_BLK + l * 16) = to_f16x8(e[0], e[1]);
+            st_rec(rec + kp * WS_KP + (BLK_E + u) * WS_BLK + l * 16, to_f16x8(e[0], e[1]));
         }
         if (w == 0) {
             // C(P^T) tiles (s'b, tb): P^T = A_rk^T + U^T A_rb^T; lane s' = 16 s'b + 4 lq + r, t = 16 tb + lr.
@@ -722,11 +731,11 @@ void prep128_kernel(PrepArgs g) {
             }
             f16x8 ph, pl;
             to_operand2_h(pt[0], zero, ph, pl);
-            *reinterpret_cast<f16x8*>(rec + WS_P + 0 * WS_BLK + l * 16) = ph;
-            *reinterpret_cast<f16x8*>(rec + WS_P + 2 * WS_BLK + l * 16) = pl;
+            st_rec(rec + WS_P + 0 * WS_BLK + l * 16, ph);
+            st_rec(rec + WS_P + 2 * WS_BLK + l * 16, pl);
             to_operand2_h(pt[1], pt[2], ph, pl);
-            *reinterpret_cast<f16x8*>(rec + WS_P + 1 * WS_BLK + l * 16) = ph;
-            *reinterpret_cast<f16x8*>(rec + WS_P + 3 * WS_BLK + l * 16) = pl;
+            st_rec(rec + WS_P + 1 * WS_BLK + l * 16, ph);
+            st_rec(rec + WS_P + 3 * WS_BLK + l * 16, pl);
         } else if (w == 1) {
             if (l < 32) *reinterpret_cast<float4*>(rec + WS_D + l * 16) = lds<float4>(smem + P_DL, l * 16);
         } else if (w == 2) {
