@@ -38,7 +38,8 @@ COMMON = [
 
 # Per-source extras.  The two-pass kernels do VALU work on their MFMA
 # accumulators (state tiles, partial products); kept in VGPRs they need no
-# AGPR <-> VGPR copies.
+# AGPR <-> VGPR copies (pass 2 without it: 1.093-1.097 against 1.063-1.069 ms
+# per hxa07D step on one box).
 EXTRA = {
     "wkv7_twopass128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "wkv7_twopass128_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
