@@ -167,7 +167,7 @@ int wkv7_forward_ws(const wkv7_desc* desc,
  * windows when state_out is NULL, in a static device array of
  * WKV7_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on
  * until the process ends.  The chunks run in windows of as many 32-token chunks
- * per (b, h) as fit (B * H * 37632 bytes per chunk, after B * H * D * D * 4
+ * per (b, h) as fit (B * H * 35584 bytes per chunk, after B * H * D * D * 4
  * bytes of state carry when state_out is NULL): pass 1 then pass 2 per
  * window, the state passed on through state_out (or the carry).  The results
  * are those of wkv7_forward_ws bit for bit.  EUNSUPPORTED when not even one
@@ -187,7 +187,7 @@ int wkv7_forward_noalloc(const wkv7_desc* desc,
 
 /* Workspace bytes wkv7_forward_ws uses for this descriptor: for D = 128 with
  * algo AUTO and T >= the chunk length, or algo TWO_PASS and T >= 1, it is
- * B * H * ceil(T / 32) * 37632 (one 36.75 KiB record of operands per chunk);
+ * B * H * ceil(T / 32) * 35584 (one 34.75 KiB record of operands per chunk);
  * 0 otherwise.  A negative wkv7_status if the descriptor is invalid.  Host
  * only: no HIP call. */
 int64_t wkv7_workspace_bytes(const wkv7_desc* desc);

@@ -24,24 +24,24 @@ constexpr int DV = 32;         // value rows per pass-2 workgroup
 constexpr int NSLICE = DK / DV;
 constexpr int PT = 40;         // 16-bit pitch of [*][L] operands (LDS)
 
-// Workspace record of one (b, h, chunk).  Every operand is fp16 (the recurrence's
-// matrix-core type; fp16's 11-bit significand makes a single W, Q, Bh or E operand
-// as accurate as the bf16 hi + lo pair it replaces in the error budget, at half the
-// bytes).  Blocks of 1 KB hold one fp16x8 operand per lane (lane l at byte 16 l).
+// Workspace record of one (b, h, chunk).  Every operand is a single fp16 value (the
+// recurrence's matrix-core type; fp16's 11-bit significand keeps a single W, Q, Bh,
+// E or P operand inside the error budget where bf16 needed hi + lo pairs for Q, E
+// and P, at half the bytes).  Blocks of 1 KB hold one fp16x8 operand per lane (lane l at byte 16 l).
 // Per key pair kp (keys 32 kp .. 32 kp + 31), block:
 //   0, 1   W   as the A operand of W (m = token of block tb, k = key), tb = 0, 1
 //   2, 3   Q   same layout as W
 //   4, 5   Bh  as the A operand of Bh^T (m = key of tile 2 kp + u, k = token), u = 0, 1
 //   6, 7   E   same layout as Bh
-// then P (A operand, m = token of block tb, k = token) as hi + lo: hi tb 0, 1,
-// lo tb 0, 1; d[128] fp32; bonus[32] fp32.
+// then P (A operand, m = token of block tb, k = token), tb = 0, 1; d[128] fp32;
+// bonus[32] fp32.
 constexpr int WS_BLK = 1024;
 constexpr int WS_KP = 8 * WS_BLK;
 constexpr int BLK_W = 0, BLK_Q = 2, BLK_BH = 4, BLK_E = 6;
 constexpr int WS_P = 4 * WS_KP;
-constexpr int WS_D = WS_P + 4 * WS_BLK;
+constexpr int WS_D = WS_P + 2 * WS_BLK;
 constexpr int WS_BON = WS_D + DK * 4;
-constexpr int WS_CHUNK = 37632;
+constexpr int WS_CHUNK = 35584;
 static_assert(WS_BON + L * 4 <= WS_CHUNK && WS_CHUNK % 256 == 0 && WS_CHUNK - 256 < WS_BON + L * 4,
               "workspace record");
 
@@ -89,18 +89,6 @@ __device__ __forceinline__ f16x8 cat16(uint2 a, uint2 b) {
 __device__ __forceinline__ void split2h(float x, float y, uint32_t& hi, uint32_t& lo) {
     hi = pack_f16(x, y);
     lo = pack_f16(x - f16lo_f32(hi), y - f16hi_f32(hi));
-}
-__device__ __forceinline__ void to_operand_h(const f32x4 c, uint2& hi, uint2& lo) {
-    split2h(c[0], c[1], hi.x, lo.x);
-    split2h(c[2], c[3], hi.y, lo.y);
-}
-// hi + lo of two C-layout tiles as one 32-deep fp16 operand each.
-__device__ __forceinline__ void to_operand2_h(const f32x4 c0, const f32x4 c1, f16x8& hi, f16x8& lo) {
-    uint2 h0, l0, h1, l1;
-    to_operand_h(c0, h0, l0);
-    to_operand_h(c1, h1, l1);
-    hi = cat16(h0, h1);
-    lo = cat16(l0, l1);
 }
 
 constexpr int kRsrcWord3 = 0x00020000;

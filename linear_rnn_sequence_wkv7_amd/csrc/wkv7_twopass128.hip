@@ -729,13 +729,8 @@ void prep128_kernel(PrepArgs g) {
                 acc = mfma32(lds<bf16x8>(smem + P_UTL, opT(spb)), Ar8, acc);
                 pt[n] = acc;
             }
-            f16x8 ph, pl;
-            to_operand2_h(pt[0], zero, ph, pl);
-            st_rec(rec + WS_P + 0 * WS_BLK + l * 16, ph);
-            st_rec(rec + WS_P + 2 * WS_BLK + l * 16, pl);
-            to_operand2_h(pt[1], pt[2], ph, pl);
-            st_rec(rec + WS_P + 1 * WS_BLK + l * 16, ph);
-            st_rec(rec + WS_P + 3 * WS_BLK + l * 16, pl);
+            st_rec(rec + WS_P + 0 * WS_BLK + l * 16, to_f16x8(pt[0], zero));
+            st_rec(rec + WS_P + 1 * WS_BLK + l * 16, to_f16x8(pt[1], pt[2]));
         } else if (w == 1) {
             if (l < 32) *reinterpret_cast<float4*>(rec + WS_D + l * 16) = lds<float4>(smem + P_DL, l * 16);
         } else if (w == 2) {

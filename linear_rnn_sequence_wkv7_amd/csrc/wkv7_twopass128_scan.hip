@@ -10,8 +10,8 @@
 //
 // Matrix cores in fp16 (v_mfma_f32_16x16x32_f16, fp32 accumulation): the
 // record's W, Q, Bh and E, the state (fp32 in registers, rounded to fp16 as the
-// operand of S W^T and Q S^T) and the reduced X = S W^T are single fp16
-// operands, P is an fp16 hi + lo pair, and V is fp16 (exact for bf16 inputs of
+// operand of S W^T and Q S^T), the reduced X = S W^T and P are single fp16
+// operands, and V is fp16 (exact for bf16 inputs of
 // magnitude below 2^16 down to 2^-14; hi + lo for fp32 inputs).  fp16 carries
 // 11 significant bits against bf16's 8, so a single fp16 operand rounds 8x
 // finer than a single bf16 one; the values must stay inside fp16's range:
@@ -97,7 +97,7 @@ __device__ __forceinline__ void pair_col_store4(char* base, int row0, int t, con
 
 // One chunk's workspace operands as this wave loads them.
 struct Ops {
-    f16x8 W[2], Q[2], Bh[2], E[2], Ph, Pl;
+    f16x8 W[2], Q[2], Bh[2], E[2], Ph;
     f32x4 d[2], bon;
 };
 
@@ -162,7 +162,6 @@ void scan128_kernel(ScanArgs g) {
     auto load_p = [&](int c, Ops& o) {   // P, d and the bonus
         const char* rec = rec_of(c);
         o.Ph = *reinterpret_cast<const f16x8*>(rec + WS_P + ty * WS_BLK + l * 16);
-        o.Pl = *reinterpret_cast<const f16x8*>(rec + WS_P + (2 + ty) * WS_BLK + l * 16);
         #pragma unroll
         for (int i = 0; i < 2; ++i) o.d[i] = ld_f32x4(rec + WS_D + (16 * (2 * kp + i) + 4 * lq) * 4);
         if constexpr (EPI) o.bon = ld_f32x4(rec + WS_BON + (16 * ty + 4 * lq) * 4);
@@ -260,7 +259,6 @@ void scan128_kernel(ScanArgs g) {
             const int ov = ((16 * sy + lr) * PT + 8 * lq) * 2;
             const f16x8 VBy = lds<f16x8>(vs, ov);
             ys = mfma16(cur.Ph, VBy, ys);
-            ys = mfma16(cur.Pl, VBy, ys);
             if constexpr (VSPLIT) ys = mfma16(cur.Ph, lds<f16x8>(smem + S_VSL + buf * VS_BYTES, ov), ys);
             const int i_loc = 16 * sy + lr, tl0 = 16 * ty + 4 * lq;
             float vtr[4] = {0.f, 0.f, 0.f, 0.f};
@@ -309,8 +307,8 @@ void scan128_kernel(ScanArgs g) {
         asm volatile("" : "+v"(opb.W[i]), "+v"(opb.Q[i]), "+v"(opb.Bh[i]), "+v"(opb.E[i]));
         asm volatile("" : "+v"(opb.d[i]));
     }
-    asm volatile("" : "+v"(opa.Ph), "+v"(opa.Pl), "+v"(opa.bon));
-    asm volatile("" : "+v"(opb.Ph), "+v"(opb.Pl), "+v"(opb.bon));
+    asm volatile("" : "+v"(opa.Ph), "+v"(opa.bon));
+    asm volatile("" : "+v"(opb.Ph), "+v"(opb.bon));
     // Three operand sets in rotation: chunk c uses its set and loads chunk c + 2's.
     int c = cb;
     for (; c + 2 < ce; c += 3) {

@@ -131,7 +131,7 @@ def test_resolve_algo():
 
 
 def test_workspace_bytes():
-    rec = 37632   # one record per (b, h, chunk of 32 tokens)
+    rec = 35584   # one record per (b, h, chunk of 32 tokens)
     assert W.wkv7_workspace_bytes(2, 64, 4, 128) == 2 * 4 * 2 * rec
     assert W.wkv7_workspace_bytes(2, 70, 4, 128) == 2 * 4 * 3 * rec     # ragged last chunk
     assert W.wkv7_workspace_bytes(2, 31, 4, 128) == 0                  # AUTO: the scan below one chunk
@@ -187,7 +187,7 @@ def test_ab_mode_from_k_rules():
     assert W.wkv7_resolve_algo(2, 63, 4, 64, ab_mode="from_k") == "scan"
     assert W.wkv7_resolve_algo(2, 64, 4, 128, ab_mode="from_k") == "chunked"
     assert W.wkv7_resolve_algo(2, 31, 4, 128, ab_mode="from_k") == "scan"
-    assert W.wkv7_workspace_bytes(2, 64, 4, 128, ab_mode="from_k") == 2 * 4 * 2 * 37632
+    assert W.wkv7_workspace_bytes(2, 64, 4, 128, ab_mode="from_k") == 2 * 4 * 2 * 35584
     assert W.wkv7_workspace_bytes(2, 64, 4, 64, ab_mode="from_k") == 0
 
 
@@ -389,7 +389,7 @@ def test_noalloc_rejects_more_heads_than_the_scratch_holds():
     assert lib.wkv7_forward_noalloc(ctypes.byref(desc), *ptrs[:6], None, ptrs[6], ptrs[7], None) == W.WKV7_EUNSUPPORTED
     assert b"static scratch" in lib.wkv7_last_error()
     # Without state_out the state carry takes room too: 1000 heads fit with it given, not without.
-    need = 1000 * 37632
+    need = 1000 * 35584
     assert need < W.NOALLOC_SCRATCH_BYTES < need + 1000 * 128 * 128 * 4
     desc = W.make_desc(1, 64, 1000, 128)
     assert lib.wkv7_forward_noalloc(ctypes.byref(desc), *ptrs[:6], None, ptrs[6], None, None) == W.WKV7_EUNSUPPORTED
