@@ -9,7 +9,10 @@
 // every addition rescales both terms to the larger exponent (the usual
 // log-sum-exp scaling): adding e^x v to (A, B, P) gives P' = max(P, x),
 // A' = A 2^(P - P') + v 2^(x - P'), B' likewise.  The ratio is then computed
-// from scaled terms that never exceed 1.
+// from scaled terms that never exceed 1.  A full chunk whose k (and u) span
+// less than 2^100 instead scales all its terms by one exponent per pass, the
+// largest that pass meets, so that a token costs one exp2 and no rescaling;
+// other chunks keep the running exponent.
 //
 // The recurrence is linear in (a, b) with a scalar decay per channel, so it
 // runs chunk-parallel over chunks of 64 tokens in a single pass with a
@@ -43,6 +46,8 @@ namespace {
 constexpr int CL = 64;        // chunk length (tokens)
 constexpr int NT4 = 256;      // threads per workgroup (channels)
 constexpr float kNegBig = -1e38f;   // exponent of the zero state
+constexpr float kFixedRange = 100.f; // log2 range of one chunk's terms under one exponent
+constexpr float kMaxU2 = 60.f;       // largest u log2(e) for 2^u2 as a factor
 
 struct Wkv4Args {
     const float* w;      // [C] decay rate
@@ -174,14 +179,39 @@ __global__ __launch_bounds__(NT4) void wkv4_onepass_kernel(Wkv4Args g) {
     load_chunk_row(vp, elem0, n, g.C, c, vv);
 
     // 1. Local state, published.
+    // Largest and smallest k of a full chunk: the fixed exponent of both passes.
+    float mx = 0.f, mn = 0.f;
+    if (n == CL) {
+        mx = kk[0];
+        mn = kk[0];
+        #pragma unroll
+        for (int i = 1; i < CL; ++i) {
+            mx = fmaxf(mx, kk[i]);
+            mn = fminf(mn, kk[i]);
+        }
+        mx *= kLog2e;
+        mn *= kLog2e;
+    }
+    const float dw = __builtin_amdgcn_exp2f(-w2);
     Scaled loc{0.f, 0.f, kNegBig};
     auto step = [&](int i) {
         loc.P -= w2;
         loc = add_term(loc, kk[i] * kLog2e, vv[i]);
     };
     if (n == CL) {
-        #pragma unroll
-        for (int i = 0; i < CL; ++i) step(i);
+        if (mn >= mx - kFixedRange) {   // every token's term within 2^-100 of the largest
+            float A = 0.f, Bd = 0.f;
+            #pragma unroll
+            for (int i = 0; i < CL; ++i) {
+                const float ex = __builtin_amdgcn_exp2f(fmaf(kk[i], kLog2e, -mx));
+                A = fmaf(A, dw, ex * vv[i]);
+                Bd = fmaf(Bd, dw, ex);
+            }
+            loc = Scaled{A, Bd, mx};
+        } else {
+            #pragma unroll
+            for (int i = 0; i < CL; ++i) step(i);
+        }
     } else {
         #pragma unroll
         for (int i = 0; i < CL; ++i)
@@ -243,8 +273,29 @@ __global__ __launch_bounds__(NT4) void wkv4_onepass_kernel(Wkv4Args g) {
         st = add_term(st, x, vv[i]);
     };
     if (n == CL) {
-        #pragma unroll
-        for (int i = 0; i < CL; ++i) out(i);
+        // With all of k in registers the output pass can scale every term by one
+        // exponent R, the largest it meets (the incoming state's, and e^k and
+        // e^{u+k} over the chunk): then a token costs one exp2 and no rescaling.
+        // Lanes where some token's own terms would fall more than 2^-100 below R
+        // (so that the sums could lose their leading terms to underflow), or where
+        // 2^u2 would be huge, keep the running-exponent form.
+        const float R = fmaxf(in.P, mx + fmaxf(u2, 0.f));
+        if (mn + fminf(u2, 0.f) >= R - kFixedRange && u2 <= kMaxU2) {
+            const float cu = __builtin_amdgcn_exp2f(u2);
+            const float sc = __builtin_amdgcn_exp2f(in.P - R), nR = -R;
+            float A = in.A * sc, Bd = in.Bd * sc;
+            #pragma unroll
+            for (int i = 0; i < CL; ++i) {
+                const float ex = __builtin_amdgcn_exp2f(fmaf(kk[i], kLog2e, nR));   // e^k / 2^R
+                const float eu = ex * cu;                                           // e^{u+k} / 2^R
+                st1(yp, base + int64_t(i) * g.C, fmaf(eu, vv[i], A) * __builtin_amdgcn_rcpf(Bd + eu));
+                A = fmaf(A, dw, ex * vv[i]);
+                Bd = fmaf(Bd, dw, ex);
+            }
+        } else {
+            #pragma unroll
+            for (int i = 0; i < CL; ++i) out(i);
+        }
     } else {
         #pragma unroll
         for (int i = 0; i < CL; ++i)
