@@ -10,9 +10,9 @@
 // log-sum-exp scaling): adding e^x v to (A, B, P) gives P' = max(P, x),
 // A' = A 2^(P - P') + v 2^(x - P'), B' likewise.  The ratio is then computed
 // from scaled terms that never exceed 1.  A full chunk whose k (and u) span
-// less than 2^100 instead scales all its terms by one exponent per pass, the
-// largest that pass meets, so that a token costs one exp2 and no rescaling;
-// other chunks keep the running exponent.
+// less than 2^100, with w >= 0, instead scales all its terms by one exponent
+// per pass, the largest that pass meets, so that a token costs one exp2 and no
+// rescaling; other chunks keep the running exponent.
 //
 // The recurrence is linear in (a, b) with a scalar decay per channel, so it
 // runs chunk-parallel over chunks of 64 tokens in a single pass with a
@@ -199,7 +199,9 @@ __global__ __launch_bounds__(NT4) void wkv4_onepass_kernel(Wkv4Args g) {
         loc = add_term(loc, kk[i] * kLog2e, vv[i]);
     };
     if (n == CL) {
-        if (mn >= mx - kFixedRange) {   // every token's term within 2^-100 of the largest
+        // Every token's term within 2^-100 of the largest, and no growth (w < 0 would
+        // let the sums outgrow the fixed exponent).
+        if (mn >= mx - kFixedRange && w2 >= 0.f) {
             float A = 0.f, Bd = 0.f;
             #pragma unroll
             for (int i = 0; i < CL; ++i) {
@@ -278,9 +280,9 @@ __global__ __launch_bounds__(NT4) void wkv4_onepass_kernel(Wkv4Args g) {
         // e^{u+k} over the chunk): then a token costs one exp2 and no rescaling.
         // Lanes where some token's own terms would fall more than 2^-100 below R
         // (so that the sums could lose their leading terms to underflow), or where
-        // 2^u2 would be huge, keep the running-exponent form.
+        // 2^u2 would be huge, or the state grows (w < 0), keep the running-exponent form.
         const float R = fmaxf(in.P, mx + fmaxf(u2, 0.f));
-        if (mn + fminf(u2, 0.f) >= R - kFixedRange && u2 <= kMaxU2) {
+        if (mn + fminf(u2, 0.f) >= R - kFixedRange && u2 <= kMaxU2 && w2 >= 0.f) {
             const float cu = __builtin_amdgcn_exp2f(u2);
             const float sc = __builtin_amdgcn_exp2f(in.P - R), nR = -R;
             float A = in.A * sc, Bd = in.Bd * sc;

@@ -76,7 +76,8 @@ def test_wkv4_lanes_outside_the_fixed_exponent_range():
     token's own terms lie within 2^100 of it, and with the running exponent
     elsewhere.  Channels here mix both forms inside one wave: a k spread of 80
     in one chunk (c = 0 mod 4), u = 45 (c = 1 mod 4), an initial state at
-    e^80 (c = 2 mod 4), plain inputs (c = 3 mod 4); T = 200 adds a ragged chunk."""
+    e^80 (c = 2 mod 4), plain inputs (c = 3 mod 4, of which c = 7 mod 8 grow:
+    w = -2, e^128 over a chunk); T = 200 adds a ragged chunk."""
     wl = G.Wkv4Workload("t", B=2, T=200, C=96, in_dtype="f32", y_dtype="f32", seed=17, state=True)
     x = G.make_wkv4_inputs(wl)
     c0, c1, c2 = np.arange(0, 96, 4), np.arange(1, 96, 4), np.arange(2, 96, 4)
@@ -84,9 +85,11 @@ def test_wkv4_lanes_outside_the_fixed_exponent_range():
     x["k"][:, 80, c0] = -40.0
     x["u"][c1] = 45.0
     x["state"][:, 2, c2] = 80.0
+    x["w"][7::8] = -2.0
     y_ref, (a_ref, b_ref) = oracle(x)
     y, s = run(x, wl)
-    for name, cs in (("spread", c0), ("u", c1), ("state", c2), ("plain", np.arange(3, 96, 4))):
+    for name, cs in (("spread", c0), ("u", c1), ("state", c2), ("plain", np.arange(3, 96, 8)),
+                     ("growing", np.arange(7, 96, 8))):
         P.check(f"y {name}", y[:, :, cs], y_ref[:, :, cs], TAU)
     a, b = ab_of(s)
     for j in range(wl.C):
